@@ -1,0 +1,186 @@
+/* verkv.h - C ABI of the VerKV decode path (PoissonComp at prefill, KVFetch at
+ * decode) for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Verify Before You Fetch: Reliable KV Cache Compression for LLM
+ * Inference" (arXiv 2611.11319).  The picx.dev summary page, section
+ * "Methodology", defines every operation named below: PoissonComp (eq. 3 and the
+ * Poisson sample), the bounded shrinkage estimator (Definition 2, eq. 5), the
+ * Bernstein certificate (Lemma 1, eq. 7) and KVFetch steps 1-5 (eqs. 9-10).  The
+ * paperdot.bitmofang.com abstract page states the setting: pivotal tokens and a
+ * token-level sketch resident on the GPU, the complete cache in CPU memory, and a
+ * user-specified (eps, delta) tolerance.
+ *
+ * Conventions for every entry point
+ *  - Pointers are device pointers unless marked [host] or [pinned host].  Pinned
+ *    host buffers must come from hipHostMalloc (or an allocator built on it); the
+ *    kernels read them directly over the host link.
+ *  - Every buffer is owned by the caller; the library allocates no device or
+ *    host memory in these calls.  Work is enqueued on `stream` (0 = the null
+ *    stream) and the calls return before it completes, except verkv_compress,
+ *    which synchronises `stream` once to read the pivot counts.
+ *  - Errors are returned as verkv_status; nothing else crosses the ABI.
+ *    Argument errors are detected on the host before any work is enqueued.  A
+ *    HIP runtime error maps to VERKV_EHIP (the message is kept per thread, see
+ *    verkv_last_error).
+ *  - head_dim must be 128.  GQA group G = (query heads)/(KV heads) in 1..8.
+ *
+ * Layouts (sequence-major, ragged batches of B sequences with lengths n_b):
+ *  - token arrays      [B][Hkv][n_b]           sequence b starts at Hkv * sum_{b'<b} n_b'
+ *  - bit arrays        [B][Hkv][ceil(n_b/32)]  token i is bit (i % 32) of word i / 32
+ *  - cache rows        [B][Hkv][n_b][128]      kv_dtype elements
+ *  - query rows        [B][Hq][128] float32    Hq = Hkv * G; row h uses KV head h / G
+ *  - per-row outputs   [B][Hq]
+ *  - pivot arrays      [B][Hkv][cap] and [B][Hkv][cap][128]
+ */
+#ifndef VERKV_H
+#define VERKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *verkv_stream_t;   /* the same object as hipStream_t */
+
+typedef enum {
+  VERKV_OK = 0,
+  VERKV_EINVAL = -1,        /* bad argument (range, null pointer, tau outside [0,1]) */
+  VERKV_EBUDGET = -2,       /* eta * n_b is below the sink + local token count        */
+  VERKV_ECAPACITY = -3,     /* a pivot set does not fit `cap`; *needed_cap is set     */
+  VERKV_EHIP = -4,          /* HIP runtime error                                       */
+  VERKV_EUNSUPPORTED = -5,  /* head_dim != 128, G > 8, too many sequences or tokens   */
+  VERKV_EWORKSPACE = -6     /* workspace smaller than the size helper returned        */
+} verkv_status;
+
+typedef enum { VERKV_BF16 = 0, VERKV_F32 = 1 } verkv_dtype;
+
+#define VERKV_HEAD_DIM 128
+#define VERKV_MAX_GROUP 8
+#define VERKV_MAX_BATCH 128
+#define VERKV_MAX_SEQ_LEN (1 << 20)
+
+/* Shape of one layer of a batch. */
+typedef struct {
+  int32_t batch;            /* B, 1..VERKV_MAX_BATCH                                   */
+  int32_t n_kv_heads;       /* Hkv >= 1                                                */
+  int32_t group;            /* G = Hq / Hkv, 1..VERKV_MAX_GROUP                        */
+  int32_t head_dim;         /* must be 128                                             */
+  const int32_t *seq_len;   /* [host][B], each 1..VERKV_MAX_SEQ_LEN                    */
+  int32_t n_sink;           /* first n_sink tokens are always kept (H)                 */
+  int32_t n_local;          /* last n_local tokens are always kept (H)                 */
+  int32_t kv_dtype;         /* verkv_dtype of the cache, the pivots and the sketch     */
+  uint32_t layer;           /* third Philox counter word                               */
+} verkv_shape;
+
+/* GPU-resident compressed state of one layer (written by verkv_compress). */
+typedef struct {
+  double *r;                /* [B][Hkv][n_b] inclusion probability, 1 on H             */
+  uint32_t *resident;       /* [B][Hkv][ceil(n_b/32)] bit set for tokens of H u S      */
+  int32_t *piv_idx;         /* [B][Hkv][cap] ascending token ids of H u S              */
+  int32_t *piv_count;       /* [B][Hkv] |H u S|                                        */
+  void *piv_k;              /* [B][Hkv][cap][128] kv_dtype: keys of H u S              */
+  void *piv_v;              /* [B][Hkv][cap][128] kv_dtype: values of H u S            */
+  int32_t cap;              /* pivot capacity per (sequence, KV head)                  */
+  const void *sketch;       /* [B][Hkv][n_b][128] kv_dtype token-level key sketch.     */
+                            /* Exact-sketch mode: the keys themselves, on the device.  */
+} verkv_state;
+
+/* Per-step results.  Row arrays are [B][Hq]; KV-head arrays are [B][Hkv]. */
+typedef struct {
+  /* written by verkv_decode_step */
+  double *m_hat;            /* largest sketch score q.k/sqrt(d) (the softmax shift)     */
+  double *d_sketch;         /* D = sum over all n_b tokens of exp(s_hat - m_hat)       */
+  double *beta_star;        /* self-consistent shrinkage bias (Definition 2)           */
+  double *eps_hat;          /* eps_hat(L) of eq. 7                                     */
+  uint8_t *certified;       /* 1 when eps_hat(L) < eps (no fetch for this row)          */
+  int32_t *kstar;           /* k* of eq. 10 (0 when certified)                         */
+  int32_t *fetch_idx;       /* [B][Hkv][fetch_cap] ascending union F over the group    */
+                            /* (may be NULL; lists longer than fetch_cap are cut)       */
+  int32_t fetch_cap;
+  int32_t *fetch_count;     /* |F| per KV head                                         */
+  int32_t *h2d_count;       /* |F \ S|: rows read from host memory per KV head         */
+  /* written by verkv_refine */
+  double *eps_after;        /* eps_hat(L \ F) with lambda frozen                       */
+  float *n_hat;             /* [B][Hq][128] N_hat (shifted by m_hat)                   */
+  float *d_hat;             /* D_hat (shifted by m_hat)                                */
+  float *o;                 /* [B][Hq][128] attention output N_hat / D_hat             */
+  float *lse;               /* m_hat + ln D_hat                                        */
+} verkv_step_out;
+
+/* PoissonComp (prefill), per (sequence b, KV head g): r_i = min(1, c tau_i) water-
+ * filled so that sum_i r_i = eta * n_b with the first n_sink and last n_local tokens
+ * forced to r = 1 (picx.dev summary, "POISSONCOMP", eq. 3); then Z_i ~ Bernoulli(r_i)
+ * from Philox4x32-10 with counter (i, g, layer, b) and key (seed mod 2^32, seed >> 32);
+ * H u S compacted in ascending order and their K/V rows copied from the pinned host
+ * cache into piv_k / piv_v.
+ *   tau       [B][Hkv][n_b] float32 importance scores in [0, 1] (device)
+ *   K_host,   [pinned host][B][Hkv][n_b][128] kv_dtype complete cache
+ *   V_host
+ *   eta       resident fraction, 0 < eta <= 1
+ *   workspace at least verkv_compress_workspace_bytes(s)
+ *   needed_cap [host, may be NULL] on VERKV_ECAPACITY: the largest |H u S|
+ * Returns VERKV_EBUDGET if fl(eta * n_b) < min(n_b, n_sink + n_local) for some b,
+ * VERKV_EINVAL if some tau is outside [0, 1] (detected on the device; state is then
+ * undefined).  Synchronises `stream` once. */
+verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *K_host,
+                            const void *V_host, double eta, uint64_t seed, verkv_state *st,
+                            void *workspace, size_t workspace_bytes, int32_t *needed_cap,
+                            verkv_stream_t stream);
+size_t verkv_compress_workspace_bytes(const verkv_shape *s);
+
+/* KVFetch steps 1-4 and the resident half of step 5 (picx.dev summary, "KVFETCH";
+ * Definition 2; Lemma 1): per query row, sketch weights over all n_b tokens, the
+ * self-consistent shrinkage bias, eps_hat(L), the certified flag, and when it fails
+ * the fetch order g (eq. 9) and k* (eq. 10); per KV head the union F of the
+ * group's fetch sets; then attention partials over the resident pivots H u S with
+ * coefficient 1 on H u (S n F) and lambda_i / r_i on S \ F.
+ *   q      [B][Hq][128] float32
+ *   beta   multiplier kappa of the bias term inside the clip: 1 is the paper's
+ *          estimator, +INFINITY gives lambda = 1 (Horvitz-Thompson), 0 gives
+ *          lambda = r; must be >= 0
+ *   eps    tolerance > 0;  delta  confidence parameter in (0, 1)
+ *   workspace at least verkv_decode_workspace_bytes(s, st->cap); pass the same
+ *          workspace to verkv_refine for this step.
+ * No host synchronisation and no host-memory traffic. */
+verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
+                               double beta, double eps, double delta, verkv_step_out *out,
+                               void *workspace, size_t workspace_bytes, verkv_stream_t stream);
+
+/* KVFetch step 5: reads the rows F \ S of K and V from the pinned host cache
+ * (zero-copy loads issued by the kernels), adds their exact terms, and finishes
+ * every row: o = N_hat / D_hat, lse, n_hat, d_hat and eps_after = eps_hat(L \ F).
+ * Must follow verkv_decode_step on the same stream with the same workspace, q, s
+ * and st.  Rows whose KV head fetched nothing are finished from the resident
+ * partials alone. */
+verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
+                          const void *K_host, const void *V_host, verkv_step_out *out,
+                          void *workspace, size_t workspace_bytes, verkv_stream_t stream);
+size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
+
+/* Optional kernel timing (instrumentation).  verkv_profile_begin creates 2*max_launches
+ * HIP events (the only allocation the library makes, done here and not per step) and
+ * turns recording on: every kernel launched afterwards by this library, up to
+ * max_launches, is bracketed by events on the stream it runs on.  verkv_profile_report
+ * waits for the recorded launches, writes per kernel kind the summed duration in ms
+ * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
+ * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
+ * 7 finish), and clears the record.  verkv_profile_end destroys the events.  Not
+ * thread safe; meant for benchmarks. */
+#define VERKV_PROFILE_KINDS 8
+int32_t verkv_profile_begin(int32_t max_launches);
+int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
+void verkv_profile_end(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *verkv_status_str(int32_t status);
+/* Last HIP error text recorded on this thread ("" if none; static thread storage). */
+const char *verkv_last_error(void);
+/* ABI version: 100 * major + minor. */
+int32_t verkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VERKV_H */

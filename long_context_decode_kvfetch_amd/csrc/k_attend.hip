@@ -1,0 +1,170 @@
+// Attention partials over a list of cache rows for gfx950: the estimator of
+// "Verify Before You Fetch" (picx.dev summary page, Definition 2 / eq. 5, extended to
+// the numerator N as the "Theoretical Foundation" section describes):
+//   D_hat = sum_{H u F} w_i + sum_{S \ F} (lambda_i / r_i) w_i,  N_hat likewise with w_i v_i,
+//   w_i = exp(q.k_i / sqrt(d) - m_hat)  (true keys, shifted by the largest sketch score).
+// Two sources share one kernel body:
+//   * resident pivots H u S (device rows, coefficient from the decision kernels): the
+//     HBM stream of every decode step;
+//   * rows F \ S read straight from the pinned host cache (zero-copy loads over the
+//     host link, coefficient 1): KVFetch step 5.
+// Each lane owns a 16-byte slice of a K row and of the matching V row; G query rows
+// stay in registers; scores are reduced across the lanes of a row with DPP; no MFMA
+// (one to eight query rows per KV head is far too thin for a matrix core).  m_hat is
+// known from the sketch pass, so no running maximum is needed.  Every workgroup writes
+// its partial (N[G][128], D[G]) so the finishing kernel sums a fixed set in a fixed order.
+#include "kernels.h"
+
+namespace verkv {
+
+constexpr int AT_NT = 256;
+constexpr int AT_NW = AT_NT / WAVE;
+
+template <bool BF16, int G, bool HOST>
+__global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
+  using RS = RowSlice<BF16>;
+  constexpr int EPL = RS::EPL;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = WAVE / LPT;
+  constexpr int STEP = AT_NW * TPW;          // rows per workgroup iteration
+  constexpr int U = 4;                       // iterations whose loads are in flight together
+  constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
+  constexpr int PS = D + 1;
+
+  __shared__ float s_acc[AT_NW][G][D];
+  __shared__ float s_den[AT_NW][G];
+
+  const int unit = blockIdx.y;
+  const int split = blockIdx.x;
+  const int b = unit / a.t.Hkv;
+  const int g = unit % a.t.Hkv;
+  const int Hq = a.t.Hkv * G;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wv = threadIdx.x / WAVE;
+  const int sub = lane % LPT;
+  const int grp = lane / LPT;
+  const int d0 = sub * EPL;
+
+  const int cnt = HOST ? a.count[unit] : min(a.count[unit], a.cap);
+  int per = (cnt + a.nsplit - 1) / a.nsplit;
+  per = ((per + STEP - 1) / STEP) * STEP;
+  const int p0 = split * per;
+  const int p1 = min(cnt, p0 + per);
+
+  float qf[G][EPL];
+  float mh[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int64_t qrow = (int64_t)b * Hq + g * G + j;
+    const float *qr = a.q + qrow * D + d0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * a.inv_sqrt_d;
+    mh[j] = (float)a.m_hat[qrow];
+  }
+
+  float acc[G][EPL];
+  float den[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    den[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
+  }
+
+  const int64_t src_base = HOST ? tok_base(a.t, b, g) : (int64_t)unit * a.cap;
+  const int32_t *list = HOST ? a.list + tok_base(a.t, b, g) : nullptr;
+  const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
+
+  for (int base = p0; base < p1; base += STEP * U) {
+    uint4 kr[U], vr[U];
+    int pp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + u * STEP + wv * TPW + grp;
+      pp[u] = p;
+      if (p < p1) {
+        const int64_t rowi = HOST ? src_base + list[p] : src_base + p;
+        kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+        vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[EPL];
+      RS::widen(kr[u], x);
+      float w[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
+        dot = sum16(dot);
+        if (LPT == 32) dot += shfl_xor_f(dot, 16);
+        float c = 1.0f;
+        if (!HOST && pp[u] < p1) c = a.coef[((int64_t)b * Hq + g * G + j) * a.cap + pp[u]];
+        w[j] = (pp[u] < p1) ? c * __expf(dot - mh[j]) : 0.0f;
+      }
+      float v[EPL];
+      RS::widen(vr[u], v);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        den[j] += w[j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(w[j], v[e], acc[j][e]);
+      }
+    }
+  }
+
+  // reduce over the row groups of the wave, then over waves
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    for (int m = LPT; m < WAVE; m <<= 1) {
+      den[j] += shfl_xor_f(den[j], m);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] += shfl_xor_f(acc[j][e], m);
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wv][j][d0 + e] = acc[j][e];
+      if (sub == 0) s_den[wv][j] = den[j];
+    }
+  }
+  __syncthreads();
+  float *out = a.part + ((int64_t)unit * a.nsplit + split) * G * PS;
+  for (int t = threadIdx.x; t < G * PS; t += AT_NT) {
+    const int j = t / PS, d = t % PS;
+    float s = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < AT_NW; ++w2) s += (d < D) ? s_acc[w2][j][d] : s_den[w2][j];
+    out[t] = s;
+  }
+}
+
+template <bool BF16, int G, bool HOST>
+static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st) {
+  hipLaunchKernelGGL((k_attend<BF16, G, HOST>), dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, hipStream_t st) {
+  const int key = (a.t.G * 2 + (bf16 ? 1 : 0)) * 2 + (host ? 1 : 0);
+  switch (key) {
+#define VERKV_AT_CASE(GG)                                                    \
+  case (GG * 2 + 1) * 2 + 1: return launch_attend_t<true, GG, true>(a, units, st);   \
+  case (GG * 2 + 1) * 2: return launch_attend_t<true, GG, false>(a, units, st);      \
+  case (GG * 2) * 2 + 1: return launch_attend_t<false, GG, true>(a, units, st);      \
+  case (GG * 2) * 2: return launch_attend_t<false, GG, false>(a, units, st);
+    VERKV_AT_CASE(1) VERKV_AT_CASE(2) VERKV_AT_CASE(3) VERKV_AT_CASE(4)
+    VERKV_AT_CASE(5) VERKV_AT_CASE(6) VERKV_AT_CASE(7) VERKV_AT_CASE(8)
+#undef VERKV_AT_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace verkv

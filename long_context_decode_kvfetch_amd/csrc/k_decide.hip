@@ -1,0 +1,546 @@
+// KVFetch steps 2-4 for gfx950, one workgroup of 1024 threads per query row, all in
+// float64 ("Verify Before You Fetch", picx.dev summary page, "Methodology"):
+//   * Definition 2: lambda_i = clip_[r_i,1](beta r_i / (w_i (1 - r_i))) with the bias
+//     beta = sum_L w_i (1 - lambda_i) taken self-consistent.  beta is the unique root
+//     of B = f(B), f piecewise linear and non-increasing; it is found by a safeguarded
+//     Newton iteration that stops once the root of the current linear piece lies on
+//     that piece (then it is exact).  kappa multiplies beta inside the clip.
+//   * Lemma 1 / eq. (7): eps_hat(L) = E(beta, V, b) / D with
+//     E = beta + b l/3 + sqrt((b l/3)^2 + 2 V l), l = log(2/delta), D = sum of all
+//     sketch weights; certified iff eps_hat < eps.
+//   * eqs. (9)-(10): g_i = eps_hat(L) - eps_hat(L \ {i}) with lambda frozen; the fetch
+//     set is the k* tokens of largest g (ties: lower token index first) where k* is
+//     the least k with eps_hat(L_g[k:]) < eps.
+// The k* cut is found without sorting L: a most-significant-digit search over the
+// bits of g (10-bit digits, then the token index for exact ties) keeps per-bucket
+// counts, sums of beta_i and V_i and the maximum b_i in LDS, walks the buckets in
+// ascending g to the first one whose inclusion pushes E(L') to eps*D, and recurses
+// into it until at most WIN tokens remain.  Those are sorted in LDS (bitonic) and
+// scanned against a deterministic re-sum of everything below them.  The tokens of F
+// are OR-ed into the KV head's fetch bitmask (the union over the GQA group).
+#include "kernels.h"
+
+namespace verkv {
+
+constexpr int DC_NT = 1024;
+constexpr int DC_NW = DC_NT / WAVE;
+constexpr int NBUCKET = 1024;
+constexpr int WIN = 1024;
+constexpr int MAX_CHUNKS = VERKV_MAX_SEQ_LEN / SKETCH_CHUNK;
+constexpr uint32_t IDX_MAX = (1u << 20) - 1;
+constexpr int NLEV = 9;
+__device__ __constant__ int c_lev_lo[NLEV] = {0, 0, 0, 0, 0, 0, 0, 1, 1};
+__device__ __constant__ int c_lev_shift[NLEV] = {53, 43, 33, 23, 13, 3, 0, 10, 0};
+__device__ __constant__ int c_lev_width[NLEV] = {10, 10, 10, 10, 10, 10, 3, 10, 10};
+
+__device__ __forceinline__ double lam_of(double w, double r, double B, double kappa) {
+  if (r == 0.0) return 0.0;
+  if (w == 0.0) return 1.0;
+  if (isinf(kappa)) return 1.0;
+  const double x = (kappa * B * r) / (w * (1.0 - r));
+  return fmin(1.0, fmax(r, x));
+}
+
+struct Terms { double beta, V, b; };
+__device__ __forceinline__ Terms terms_of(double w, double r, double lam) {
+  Terms t;
+  t.beta = w * (1.0 - lam);
+  if (r > 0.0) {
+    t.V = lam * lam * w * w * (1.0 - r) / r;
+    t.b = lam * w * fmax(r, 1.0 - r) / r;
+  } else {
+    t.V = 0.0;
+    t.b = 0.0;
+  }
+  return t;
+}
+
+__device__ __forceinline__ double bern_E(double beta, double V, double b, double l) {
+  const double t = b * l / 3.0;
+  return beta + t + sqrt(t * t + 2.0 * V * l);
+}
+
+// g_i of eq. (9), lambda frozen; sqrt(X) - sqrt(Y) evaluated as (X - Y)/(sqrt X + sqrt Y).
+__device__ __forceinline__ double g_of(const Terms &x, double V, double b1, double b2, double l,
+                                       double Dd) {
+  const double bm = (x.b == b1) ? b2 : b1;
+  const double t1 = b1 * l / 3.0, tm = bm * l / 3.0;
+  const double X = t1 * t1 + 2.0 * V * l;
+  const double Y = tm * tm + 2.0 * (V - x.V) * l;
+  const double dX = (t1 - tm) * (t1 + tm) + 2.0 * x.V * l;
+  const double den = sqrt(X) + sqrt(Y);
+  const double frac = den > 0.0 ? dX / den : 0.0;
+  const double g = (x.beta + (t1 - tm) + frac) / Dd;
+  return g > 0.0 ? g : 0.0;                     // maps -0 to +0
+}
+
+__device__ __forceinline__ uint64_t dbits(double v) { return (uint64_t)__double_as_longlong(v); }
+__device__ __forceinline__ double bitsd(uint64_t v) { return __longlong_as_double((long long)v); }
+
+// Position of the extended key (key, lo) relative to the window "prefix P at level lev":
+// -1 below, 0 inside, +1 above.  lev < 0 is the whole set.
+__device__ __forceinline__ int cmp_window(uint64_t key, uint32_t lo, int lev, uint64_t pkey,
+                                          uint32_t plo) {
+  if (lev < 0) return 0;
+  if (!c_lev_lo[lev]) {
+    const uint64_t kp = key >> c_lev_shift[lev];
+    return kp < pkey ? -1 : (kp > pkey ? 1 : 0);
+  }
+  if (key != pkey) return key < pkey ? -1 : 1;
+  const uint32_t lp = lo >> c_lev_shift[lev];
+  return lp < plo ? -1 : (lp > plo ? 1 : 0);
+}
+
+// Four fixed-order block reductions in one barrier round.
+struct Red4 { double s0, s1, mx, mn; };
+__device__ __forceinline__ Red4 block_red4(Red4 v, double *scr /*[4*DC_NW]*/) {
+  v.s0 = wave_sum(v.s0);
+  v.s1 = wave_sum(v.s1);
+  v.mx = wave_max(v.mx);
+  v.mn = wave_min(v.mn);
+  const int w = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == 0) {
+    scr[w] = v.s0; scr[DC_NW + w] = v.s1; scr[2 * DC_NW + w] = v.mx; scr[3 * DC_NW + w] = v.mn;
+  }
+  __syncthreads();
+  Red4 o{0.0, 0.0, scr[2 * DC_NW], scr[3 * DC_NW]};
+#pragma unroll
+  for (int i = 0; i < DC_NW; ++i) {
+    o.s0 += scr[i];
+    o.s1 += scr[DC_NW + i];
+    o.mx = fmax(o.mx, scr[2 * DC_NW + i]);
+    o.mn = fmin(o.mn, scr[3 * DC_NW + i]);
+  }
+  __syncthreads();
+  return o;
+}
+
+// Sums of beta and V, the maximum b and the runner-up b (multiset), fixed order.
+struct Cert { double beta, V, b1, b2; };
+__device__ __forceinline__ void top2_merge(double &a1, double &a2, double c1, double c2) {
+  const double hi = fmax(a1, c1);
+  const double lo2 = fmax(fmin(a1, c1), fmax(a2, c2));
+  a1 = hi;
+  a2 = lo2;
+}
+__device__ __forceinline__ Cert block_cert(Cert v, double *scr /*[4*DC_NW]*/) {
+  v.beta = wave_sum(v.beta);
+  v.V = wave_sum(v.V);
+  for (int m = 1; m < WAVE; m <<= 1) {
+    const double o1 = shfl_xor_d(v.b1, m), o2 = shfl_xor_d(v.b2, m);
+    top2_merge(v.b1, v.b2, o1, o2);
+  }
+  const int w = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == 0) {
+    scr[w] = v.beta; scr[DC_NW + w] = v.V; scr[2 * DC_NW + w] = v.b1; scr[3 * DC_NW + w] = v.b2;
+  }
+  __syncthreads();
+  Cert o{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < DC_NW; ++i) {
+    o.beta += scr[i];
+    o.V += scr[DC_NW + i];
+    top2_merge(o.b1, o.b2, scr[2 * DC_NW + i], scr[3 * DC_NW + i]);
+  }
+  __syncthreads();
+  return o;
+}
+
+__global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
+  __shared__ double s_scale[MAX_CHUNKS];
+  __shared__ double scr[4 * DC_NW];
+  __shared__ uint32_t h_cnt[NBUCKET];
+  __shared__ double h_beta[NBUCKET];
+  __shared__ double h_V[NBUCKET];
+  __shared__ uint64_t h_b[NBUCKET];
+  __shared__ uint64_t w_key[WIN];
+  __shared__ uint32_t w_lo[WIN];
+  __shared__ uint32_t w_slot[WIN];
+  __shared__ int32_t s_int[4];
+
+  const int row = blockIdx.x;
+  const int Hq = a.t.Hkv * a.t.G;
+  const int b = row / Hq;
+  const int h = row % Hq;
+  const int g = h / a.t.G;
+  const int n = a.t.s[b].n;
+  const int nch = chunks_of(n);
+  const int tid = threadIdx.x;
+  const double *wcr = a.wc + row_tok_base(a.t, b, h);
+  const double2 *cs = a.cstat + row_chunk_base(a.t, b, h);
+  const double *rr = a.r + tok_base(a.t, b, g);
+  uint32_t *fb = a.fbits + word_base(a.t, b, g);
+  const double kappa = a.kappa, l = a.l, eps = a.eps;
+
+  // ---- step 1 (finish): m_hat, per-chunk rescale, D = sum of all sketch weights
+  double mloc = -INFINITY;
+  for (int c = tid; c < nch; c += DC_NT) mloc = fmax(mloc, cs[c].x);
+  const double m_hat = block_max<DC_NT>(mloc, scr);
+  double dloc = 0.0;
+  for (int c = tid; c < nch; c += DC_NT) {
+    const double sc = exp(cs[c].x - m_hat);
+    s_scale[c] = sc;
+    a.cscale[row_chunk_base(a.t, b, h) + c] = sc;
+    dloc += sc * cs[c].y;
+  }
+  const double Dd = block_sum<DC_NT>(dloc, scr);      // barrier also publishes s_scale
+
+#define FOR_L(body)                                                   \
+  for (int i = tid; i < n; i += DC_NT) {                              \
+    const double ri = rr[i];                                          \
+    if (!(ri < 1.0)) continue;                                        \
+    const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];             \
+    body                                                              \
+  }
+
+  // ---- self-consistent beta (Definition 2)
+  double Bst;
+  if (isinf(kappa)) {
+    double acc = 0.0;
+    FOR_L(if (ri == 0.0) acc += wi;)
+    Bst = block_sum<DC_NT>(acc, scr);
+  } else if (kappa == 0.0) {
+    double acc = 0.0;
+    FOR_L(acc += wi * (1.0 - ri);)
+    Bst = block_sum<DC_NT>(acc, scr);
+  } else {
+    double acc = 0.0;
+    FOR_L(acc += (ri == 0.0) ? wi : wi * (1.0 - ri);)
+    const double f0 = block_sum<DC_NT>(acc, scr);     // f(0): the upper end of the bracket
+    double lo = 0.0, hi = f0, B = f0;
+    Bst = f0;
+    bool done = (f0 == 0.0);
+    int iter = 0;
+    for (; !done && iter < 200; ++iter) {
+      Red4 v{0.0, 0.0, 0.0, INFINITY};
+      FOR_L(
+        if (ri == 0.0) { v.s0 += wi; }
+        else if (wi != 0.0) {
+          const double aa = wi * (1.0 - ri) / kappa;
+          const double tt = aa / ri;
+          if (B <= aa) { v.s0 += wi * (1.0 - ri); v.mn = fmin(v.mn, aa); }
+          else if (B >= tt) { v.mx = fmax(v.mx, tt); }
+          else { v.s0 += wi; v.s1 += kappa * ri / (1.0 - ri); v.mx = fmax(v.mx, aa); v.mn = fmin(v.mn, tt); }
+        })
+      const Red4 o = block_red4(v, scr);
+      const double hB = B * (1.0 + o.s1) - o.s0;        // B - f(B)
+      const double Bn = o.s0 / (1.0 + o.s1);             // root of this linear piece
+      if (Bn >= o.mx && Bn <= o.mn) { Bst = Bn; done = true; break; }
+      if (hB == 0.0) { Bst = B; done = true; break; }
+      if (hB < 0.0) lo = B; else hi = B;
+      double Bnext = Bn;
+      if (!(Bnext > lo && Bnext < hi)) Bnext = 0.5 * (lo + hi);
+      if (Bnext == B || !(hi > lo)) { Bst = Bn; done = true; break; }
+      B = Bnext;
+      Bst = Bn;
+    }
+    if (!done && tid == 0) atomicOr(&a.status[0], 2);
+  }
+
+  // ---- eq. (7) certificate
+  Cert cl{0.0, 0.0, 0.0, 0.0};
+  int nL = 0;
+  FOR_L(
+    const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+    cl.beta += x.beta; cl.V += x.V; ++nL;
+    top2_merge(cl.b1, cl.b2, x.b, 0.0);)
+  const Cert ct = block_cert(cl, scr);
+  const double E_all = (block_sum<DC_NT>((double)nL, scr) > 0.0) ? bern_E(ct.beta, ct.V, ct.b1, l) : 0.0;
+  const double ehat = E_all / Dd;
+  const bool cert = ehat < eps;
+  if (tid == 0) {
+    if (row == 0) { a.params[0] = kappa; a.params[1] = l; }
+    a.m_hat[row] = m_hat;
+    a.d_sketch[row] = Dd;
+    a.beta_star[row] = Bst;
+    a.eps_hat[row] = ehat;
+    a.certified[row] = cert ? 1 : 0;
+    if (cert) a.kstar[row] = 0;
+  }
+  if (cert) return;
+
+  // ---- eqs. (9)-(10): MSD search for the k* cut over the bits of g
+  const double thr = eps * Dd;
+  double bel_beta = 0.0, bel_V = 0.0, bel_b = 0.0;     // tokens below the window
+  uint64_t pkey = 0;
+  uint32_t plo = 0;
+  int lev = -1;
+  bool above_mode = false;                               // cut above the whole window
+#define KEY_OF(wi, ri, x, key, lo)                                             \
+  const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));                \
+  const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));              \
+  const uint32_t lo = IDX_MAX - (uint32_t)i;
+
+  for (int L = 0; L < NLEV; ++L) {
+    for (int k = tid; k < NBUCKET; k += DC_NT) { h_cnt[k] = 0; h_beta[k] = 0.0; h_V[k] = 0.0; h_b[k] = 0; }
+    __syncthreads();
+    const int sh = c_lev_shift[L];
+    const uint32_t dmask = (1u << c_lev_width[L]) - 1u;
+    FOR_L(
+      KEY_OF(wi, ri, x, key, lo)
+      if (cmp_window(key, lo, lev, pkey, plo) == 0) {
+        const uint32_t dig = c_lev_lo[L] ? ((lo >> sh) & dmask) : (uint32_t)((key >> sh) & dmask);
+        atomicAdd(&h_cnt[dig], 1u);
+        atomicAdd(&h_beta[dig], x.beta);
+        atomicAdd(&h_V[dig], x.V);
+        atomicMax((unsigned long long *)&h_b[dig], (unsigned long long)dbits(x.b));
+      })
+    __syncthreads();
+    // inclusive scan over buckets (thread k owns bucket k): beta, V sums and max b
+    double sb = h_beta[tid], sv = h_V[tid], smx = bitsd(h_b[tid]);
+    const uint32_t mycnt = h_cnt[tid];
+    __syncthreads();
+    for (int off = 1; off < NBUCKET; off <<= 1) {
+      double ob = 0.0, ov = 0.0, om = 0.0;
+      if (tid >= off) { ob = h_beta[tid - off]; ov = h_V[tid - off]; om = bitsd(h_b[tid - off]); }
+      __syncthreads();
+      if (tid >= off) { sb += ob; sv += ov; smx = fmax(smx, om); }
+      h_beta[tid] = sb; h_V[tid] = sv; h_b[tid] = dbits(smx);
+      __syncthreads();
+    }
+    // h_* now hold inclusive prefixes; ensure the initial values are loaded before overwrite
+    if (tid == 0) s_int[0] = INT32_MAX;
+    __syncthreads();
+    const bool below_fails = bern_E(bel_beta, bel_V, bel_b, l) >= thr;
+    if (mycnt > 0 &&
+        (below_fails || bern_E(bel_beta + sb, bel_V + sv, fmax(bel_b, smx), l) >= thr))
+      atomicMin(&s_int[0], tid);
+    __syncthreads();
+    const int j = s_int[0];
+    if (j == INT32_MAX) { above_mode = true; break; }
+    // exclusive prefix of bucket j
+    const double eb = j > 0 ? h_beta[j - 1] : 0.0;
+    const double ev = j > 0 ? h_V[j - 1] : 0.0;
+    const double em = j > 0 ? bitsd(h_b[j - 1]) : 0.0;
+    bel_beta += eb; bel_V += ev; bel_b = fmax(bel_b, em);
+    if (!c_lev_lo[L]) {
+      pkey = (L == 0) ? (uint64_t)j : ((pkey << c_lev_width[L]) | (uint64_t)j);
+    } else {
+      plo = (L == NLEV - 2) ? (uint32_t)j : ((plo << c_lev_width[L]) | (uint32_t)j);
+    }
+    lev = L;
+    const uint32_t cntj = h_cnt[j];
+    __syncthreads();
+    if (cntj <= (uint32_t)WIN) break;
+  }
+
+  // ---- final window: deterministic re-sum below it, sort it, scan it
+  uint64_t tkey = 0;
+  uint32_t tlo = 0;
+  if (!above_mode) {
+    if (tid == 0) s_int[1] = 0;
+    for (int k = tid; k < WIN; k += DC_NT) { w_key[k] = ~0ull; w_lo[k] = ~0u; w_slot[k] = k; }
+    __syncthreads();
+    Red4 bel{0.0, 0.0, 0.0, 0.0};
+    FOR_L(
+      KEY_OF(wi, ri, x, key, lo)
+      const int cw = cmp_window(key, lo, lev, pkey, plo);
+      if (cw < 0) { bel.s0 += x.beta; bel.s1 += x.V; bel.mx = fmax(bel.mx, x.b); }
+      else if (cw == 0) {
+        const int p = atomicAdd(&s_int[1], 1);
+        if (p < WIN) { w_key[p] = key; w_lo[p] = lo; }
+      })
+    const Red4 bo = block_red4(bel, scr);
+    const int wcount = min(s_int[1], WIN);
+    // bitonic sort of (key, lo) ascending over WIN slots; w_slot follows
+    for (int k2 = 2; k2 <= WIN; k2 <<= 1) {
+      for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+        const int p = tid ^ j2;
+        if (p > tid) {
+          const uint64_t ka = w_key[tid], kb = w_key[p];
+          const uint32_t la = w_lo[tid], lb = w_lo[p];
+          const bool gt = (ka > kb) || (ka == kb && la > lb);
+          const bool up = (tid & k2) == 0;
+          if (gt == up) {
+            w_key[tid] = kb; w_key[p] = ka;
+            w_lo[tid] = lb; w_lo[p] = la;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // terms of the sorted window members (token = IDX_MAX - lo)
+    double tb = 0.0, tv = 0.0, tm = 0.0;
+    if (tid < wcount) {
+      const int i = (int)(IDX_MAX - w_lo[tid]);
+      const double ri = rr[i];
+      const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
+      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+      tb = x.beta; tv = x.V; tm = x.b;
+    }
+    // inclusive scan in sorted order (reuse the bucket arrays)
+    h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
+    __syncthreads();
+    for (int off = 1; off < WIN; off <<= 1) {
+      double ob = 0.0, ov = 0.0, om = 0.0;
+      if (tid >= off) { ob = h_beta[tid - off]; ov = h_V[tid - off]; om = bitsd(h_b[tid - off]); }
+      __syncthreads();
+      if (tid >= off) { tb += ob; tv += ov; tm = fmax(tm, om); }
+      h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
+      __syncthreads();
+    }
+    if (tid == 0) s_int[2] = INT32_MAX;
+    __syncthreads();
+    const bool bfail = bern_E(bo.s0, bo.s1, bo.mx, l) >= thr;
+    if (tid < wcount && (bfail || bern_E(bo.s0 + tb, bo.s1 + tv, fmax(bo.mx, tm), l) >= thr))
+      atomicMin(&s_int[2], tid);
+    __syncthreads();
+    const int jc = s_int[2];
+    if (jc == INT32_MAX) {
+      above_mode = true;                                 // every window token stays in L'
+    } else {
+      tkey = w_key[jc];
+      tlo = w_lo[jc];
+    }
+    __syncthreads();
+  }
+
+  // ---- mark F_h = tokens at or after the cut in g-descending order
+  int64_t kc = 0;
+  FOR_L(
+    KEY_OF(wi, ri, x, key, lo)
+    bool inF;
+    if (above_mode) inF = cmp_window(key, lo, lev, pkey, plo) > 0;
+    else inF = (key > tkey) || (key == tkey && lo >= tlo);
+    if (inF) { atomicOr(&fb[i >> 5], 1u << (i & 31)); ++kc; })
+  const int64_t ks = block_sum_i64<DC_NT>(kc, (int64_t *)scr);
+  if (tid == 0) a.kstar[row] = (int32_t)ks;
+#undef KEY_OF
+#undef FOR_L
+}
+
+// ------------------------------------------------------------------ union, lists, pivot coefficients
+constexpr int UN_NT = 1024;
+
+__global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
+  __shared__ int32_t iscr[UN_NT / WAVE];
+  const int unit = blockIdx.x;
+  const int b = unit / a.t.Hkv;
+  const int g = unit % a.t.Hkv;
+  const int n = a.t.s[b].n;
+  const int G = a.t.G;
+  const int Hq = a.t.Hkv * G;
+  const int tid = threadIdx.x;
+  const uint32_t *fb = a.fbits + word_base(a.t, b, g);
+  const uint32_t *res = a.resident + word_base(a.t, b, g);
+  const int W = words_of(n);
+  const int wpt = (W + UN_NT - 1) / UN_NT;
+  const int w0 = tid * wpt, w1 = min(W, w0 + wpt);
+  int32_t cf = 0, ch = 0;
+  for (int w = w0; w < w1; ++w) { cf += __popc(fb[w]); ch += __popc(fb[w] & ~res[w]); }
+  int32_t tf, th;
+  int32_t pf = block_excl_scan<UN_NT>(cf, iscr, &tf);
+  int32_t ph = block_excl_scan<UN_NT>(ch, iscr, &th);
+  int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
+  int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = fb[w];
+    const uint32_t rw = res[w];
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int tok = 32 * w + j;
+      if (fl && pf < a.fetch_cap) fl[pf] = tok;
+      ++pf;
+      if (!((rw >> j) & 1)) hl[ph++] = tok;
+    }
+  }
+  if (tid == 0) {
+    a.fetch_count[unit] = tf;
+    a.h2d_count[unit] = th;
+  }
+  // coefficients of the resident pivots: 1 on H and on S n F, lambda_i / r_i on S \ F
+  const int cnt = min(a.piv_count[unit], a.cap);
+  const int32_t *pidx = a.piv_idx + (int64_t)unit * a.cap;
+  const double *rr = a.r + tok_base(a.t, b, g);
+  for (int p = tid; p < cnt; p += UN_NT) {
+    const int tok = pidx[p];
+    const double ri = rr[tok];
+    const bool exact = (ri >= 1.0) || ((fb[tok >> 5] >> (tok & 31)) & 1);
+    for (int j = 0; j < G; ++j) {
+      const int h = g * G + j;
+      float cf32 = 1.0f;
+      if (!exact) {
+        const double wi = a.wc[row_tok_base(a.t, b, h) + tok] *
+                          a.cscale[row_chunk_base(a.t, b, h) + tok / SKETCH_CHUNK];
+        const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], a.kappa);
+        cf32 = (float)(lam / ri);
+      }
+      a.coef[((int64_t)b * Hq + h) * a.cap + p] = cf32;
+    }
+  }
+}
+
+hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_decide, dim3(rows), dim3(DC_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
+  hipLaunchKernelGGL(k_union, dim3(units), dim3(UN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ finish a row
+// N_hat and D_hat are the fixed-order sums of the partials of the resident pivots and
+// of the host rows; o = N_hat / D_hat, lse = m_hat + ln D_hat; eps_after = eps_hat(L \ F)
+// with lambda frozen (Lemma 1 on the tokens that remain sampled).
+__global__ __launch_bounds__(DC_NT) void k_finish(FinishArgs a) {
+  __shared__ double scr[4 * DC_NW];
+  __shared__ float s_d;
+  const int row = blockIdx.x;
+  const int Hq = a.t.Hkv * a.t.G;
+  const int b = row / Hq;
+  const int h = row % Hq;
+  const int g = h / a.t.G;
+  const int j = h % a.t.G;
+  const int unit = b * a.t.Hkv + g;
+  const int tid = threadIdx.x;
+  constexpr int PS = D + 1;
+  float acc = 0.0f;
+  if (tid <= D) {
+    for (int s = 0; s < a.nsp; ++s)
+      acc += a.piv_part[(((int64_t)unit * a.nsp + s) * a.t.G + j) * PS + tid];
+    for (int s = 0; s < a.nsh; ++s)
+      acc += a.host_part[(((int64_t)unit * a.nsh + s) * a.t.G + j) * PS + tid];
+    if (tid == D) s_d = acc;
+  }
+  __syncthreads();
+  const float dh = s_d;
+  if (tid < D) {
+    a.n_hat[(int64_t)row * D + tid] = acc;
+    a.o[(int64_t)row * D + tid] = acc / dh;
+  } else if (tid == D) {
+    a.d_hat[row] = dh;
+    a.lse[row] = (float)(a.m_hat[row] + log((double)dh));
+  }
+
+  const int n = a.t.s[b].n;
+  const double *wcr = a.wc + row_tok_base(a.t, b, h);
+  const double *sc = a.cscale + row_chunk_base(a.t, b, h);
+  const double *rr = a.r + tok_base(a.t, b, g);
+  const uint32_t *fb = a.fbits + word_base(a.t, b, g);
+  const double Bst = a.beta_star[row];
+  const double kappa = a.params[0], l = a.params[1];
+  Cert c{0.0, 0.0, 0.0, 0.0};
+  int cnt = 0;
+  for (int i = tid; i < n; i += DC_NT) {
+    const double ri = rr[i];
+    if (!(ri < 1.0)) continue;
+    if ((fb[i >> 5] >> (i & 31)) & 1) continue;
+    const double wi = wcr[i] * sc[i / SKETCH_CHUNK];
+    const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+    c.beta += x.beta; c.V += x.V; ++cnt;
+    top2_merge(c.b1, c.b2, x.b, 0.0);
+  }
+  const Cert o = block_cert(c, scr);
+  const double tot = block_sum<DC_NT>((double)cnt, scr);
+  if (tid == 0) a.eps_after[row] = tot > 0.0 ? bern_E(o.beta, o.V, o.b1, l) / a.d_sketch[row] : 0.0;
+}
+
+hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_finish, dim3(rows), dim3(DC_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace verkv

@@ -1,0 +1,112 @@
+// Kernel argument blocks and launchers of the VerKV library (internal).
+#pragma once
+#include "common.h"
+
+namespace verkv {
+
+struct CompressArgs {
+  SeqTable t;
+  const float *tau;           // [B][Hkv][n]
+  double eta;
+  uint64_t seed;
+  uint32_t layer;
+  double *r;                  // [B][Hkv][n]
+  uint32_t *resident;         // [B][Hkv][W]
+  int32_t *piv_idx;           // [B][Hkv][cap]
+  int32_t *piv_count;         // [B][Hkv]
+  int32_t cap;
+  uint64_t *keys_a;           // workspace [B][Hkv][n]
+  uint64_t *keys_b;           // workspace [B][Hkv][n]
+  int32_t *status;            // workspace [0]: error bits, [1]: max pivot count
+};
+
+struct GatherArgs {
+  SeqTable t;
+  const uint8_t *K_host, *V_host;   // device-visible pointers to the pinned host cache
+  const int32_t *piv_idx, *piv_count;
+  uint8_t *piv_k, *piv_v;
+  int32_t cap;
+  int32_t row_bytes;
+};
+
+struct SketchArgs {
+  SeqTable t;
+  const uint8_t *sketch;      // [B][Hkv][n][128] kv dtype
+  const float *q;             // [B][Hq][128]
+  double sqrt_d;              // sqrt(128): scores are q.k / sqrt(d)
+  double *wc;                 // [B][Hq][n]
+  double2 *cstat;             // [B][Hq][nchunks]  (m_c, sum_c)
+  uint32_t *fbits;            // [B][Hkv][W]  cleared here
+  int32_t total_blocks;
+};
+
+struct DecideArgs {
+  SeqTable t;
+  const double *wc;          // [B][Hq][n]   exp(s - m_chunk)
+  const double2 *cstat;      // [B][Hq][nch] (m_chunk, sum over chunk)
+  double *cscale;            // [B][Hq][nch] out: exp(m_chunk - m_hat)
+  const double *r;           // [B][Hkv][n]
+  uint32_t *fbits;           // [B][Hkv][W]
+  double kappa, eps, l;
+  double *m_hat, *d_sketch, *beta_star, *eps_hat;
+  uint8_t *certified;
+  int32_t *kstar;
+  int32_t *status;
+  double *params;            // out: kappa, l of this step (read by the finish kernel)
+};
+
+struct UnionArgs {
+  SeqTable t;
+  const uint32_t *fbits, *resident;
+  const int32_t *piv_idx, *piv_count;
+  int32_t cap;
+  const double *r, *wc, *cscale, *beta_star;
+  double kappa;
+  int32_t *fetch_idx;
+  int32_t fetch_cap;
+  int32_t *fetch_count, *h2d_count;
+  int32_t *h2d_idx;          // [B][Hkv][n]
+  float *coef;               // [B][Hq][cap]
+};
+
+struct AttendArgs {
+  SeqTable t;
+  const float *q;            // [B][Hq][128]
+  const double *m_hat;       // [B][Hq]
+  float inv_sqrt_d;
+  const uint8_t *krows;      // pivots [B][Hkv][cap][128] or host cache [B][Hkv][n][128]
+  const uint8_t *vrows;
+  const int32_t *count;      // [B][Hkv] rows in the list
+  const int32_t *list;       // host source: [B][Hkv][n] token ids; pivots: null
+  const float *coef;         // pivots: [B][Hq][cap]; host: null (coefficient 1)
+  int32_t cap;
+  float *part;               // [B][Hkv][nsplit][G][129]
+  int32_t nsplit;
+};
+
+struct FinishArgs {
+  SeqTable t;
+  const float *piv_part;     // [B][Hkv][nsp][G][129]
+  int32_t nsp;
+  const float *host_part;    // [B][Hkv][nsh][G][129]
+  int32_t nsh;
+  const double *wc, *cscale, *r;
+  const uint32_t *fbits;
+  const double *m_hat, *d_sketch, *beta_star;
+  const double *params;      // kappa, l written by the decision kernel
+  double *eps_after;
+  float *n_hat, *d_hat, *o, *lse;
+};
+
+constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
+constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets nsp)
+
+hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
+hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
+hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st);
+hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);
+hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, hipStream_t st);
+hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
+
+}  // namespace verkv

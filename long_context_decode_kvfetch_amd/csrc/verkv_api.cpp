@@ -1,0 +1,503 @@
+// Host runtime of the VerKV C ABI (include/verkv.h): argument checks, workspace
+// layout, launches.  No device or host memory is allocated per call; every buffer is
+// the caller's.  Compiled by hipcc for gfx950 together with the kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace verkv;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+verkv_status hip_fail(hipError_t e, const char *where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return VERKV_EHIP;
+}
+#define HIP_TRY(expr, where)                          \
+  do {                                                \
+    hipError_t _e = (expr);                           \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Build the per-sequence offset table and validate the shape.
+verkv_status make_table(const verkv_shape *s, SeqTable &t) {
+  if (!s || !s->seq_len) return VERKV_EINVAL;
+  if (s->head_dim != VERKV_HEAD_DIM) return VERKV_EUNSUPPORTED;
+  if (s->batch < 1 || s->n_kv_heads < 1 || s->group < 1) return VERKV_EINVAL;
+  if (s->batch > VERKV_MAX_BATCH || s->group > VERKV_MAX_GROUP) return VERKV_EUNSUPPORTED;
+  if (s->n_sink < 0 || s->n_local < 0) return VERKV_EINVAL;
+  if (s->kv_dtype != VERKV_BF16 && s->kv_dtype != VERKV_F32) return VERKV_EINVAL;
+  std::memset(&t, 0, sizeof(t));
+  t.B = s->batch;
+  t.Hkv = s->n_kv_heads;
+  t.G = s->group;
+  t.n_sink = s->n_sink;
+  t.n_local = s->n_local;
+  int64_t tok = 0, words = 0, chunks = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    const int32_t n = s->seq_len[b];
+    if (n < 1) return VERKV_EINVAL;
+    if (n > VERKV_MAX_SEQ_LEN) return VERKV_EUNSUPPORTED;
+    t.s[b].n = n;
+    t.s[b].tok_off = (int32_t)tok;
+    t.s[b].word_off = (int32_t)words;
+    t.s[b].chunk_off = (int32_t)chunks;
+    tok += n;
+    words += words_of(n);
+    chunks += chunks_of(n);
+    t.max_n = std::max(t.max_n, n);
+  }
+  // every flat index below must stay inside int32 element counts per array
+  const int64_t hq = (int64_t)s->n_kv_heads * s->group;
+  if (tok * hq > INT32_MAX || chunks * hq * (int64_t)s->n_kv_heads > INT32_MAX) return VERKV_EUNSUPPORTED;
+  return VERKV_OK;
+}
+
+struct Totals {
+  int64_t tok = 0, words = 0, chunks = 0;
+};
+Totals totals(const SeqTable &t) {
+  Totals r;
+  for (int b = 0; b < t.B; ++b) {
+    r.tok += t.s[b].n;
+    r.words += words_of(t.s[b].n);
+    r.chunks += chunks_of(t.s[b].n);
+  }
+  return r;
+}
+
+int row_bytes(const verkv_shape *s) { return VERKV_HEAD_DIM * (s->kv_dtype == VERKV_BF16 ? 2 : 4); }
+
+int host_splits(int units) { return std::max(4, std::min(64, 512 / std::max(1, units))); }
+int pivot_splits(int cap) { return std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS); }
+
+// Decode workspace layout.
+struct DecodeWs {
+  size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status, total;
+  int nsp, nsh;
+};
+DecodeWs decode_layout(const SeqTable &t, int cap) {
+  const Totals T = totals(t);
+  const int64_t Hq = (int64_t)t.Hkv * t.G;
+  const int units = t.B * t.Hkv;
+  DecodeWs w;
+  w.nsp = pivot_splits(cap);
+  w.nsh = host_splits(units);
+  size_t off = 0;
+  w.wc = off;     off = align_up(off + 8 * (size_t)(Hq * T.tok));
+  w.cstat = off;  off = align_up(off + 16 * (size_t)(Hq * T.chunks));
+  w.cscale = off; off = align_up(off + 8 * (size_t)(Hq * T.chunks));
+  w.fbits = off;  off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
+  w.h2d = off;    off = align_up(off + 4 * (size_t)(t.Hkv * T.tok));
+  w.coef = off;   off = align_up(off + 4 * (size_t)(t.B * Hq * (int64_t)cap));
+  w.ppart = off;  off = align_up(off + 4 * (size_t)units * w.nsp * t.G * (D + 1));
+  w.hpart = off;  off = align_up(off + 4 * (size_t)units * w.nsh * t.G * (D + 1));
+  w.status = off; off = align_up(off + 64);
+  w.total = off;
+  return w;
+}
+
+struct CompressWs {
+  size_t ka, kb, status, total;
+};
+CompressWs compress_layout(const SeqTable &t) {
+  const Totals T = totals(t);
+  CompressWs w;
+  size_t off = 0;
+  w.ka = off;     off = align_up(off + 8 * (size_t)(t.Hkv * T.tok));
+  w.kb = off;     off = align_up(off + 8 * (size_t)(t.Hkv * T.tok));
+  w.status = off; off = align_up(off + 64);
+  w.total = off;
+  return w;
+}
+
+// A host-cache pointer as the kernels must see it: pinned host memory is translated
+// to its device-visible address; device memory is used as is.
+verkv_status device_view(const void *p, const void **out) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    std::snprintf(g_last_error, sizeof(g_last_error), "host cache pointer is not pinned or device memory");
+    return VERKV_EINVAL;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = p;
+    return VERKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void *d = nullptr;
+    e = hipHostGetDevicePointer(&d, const_cast<void *>(p), 0);
+    if (e != hipSuccess || !d) {
+      (void)hipGetLastError();
+      std::snprintf(g_last_error, sizeof(g_last_error), "pinned host cache is not mapped for the device");
+      return VERKV_EINVAL;
+    }
+    *out = d;
+    return VERKV_OK;
+  }
+  std::snprintf(g_last_error, sizeof(g_last_error), "host cache pointer is pageable memory");
+  return VERKV_EINVAL;
+}
+
+// ---------------------------------------------------------------- optional kernel timing
+enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_COUNT };
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> ev;       // pairs
+  std::vector<int> kind;
+  size_t used = 0;
+};
+Profiler g_prof;
+
+struct Timed {
+  hipStream_t st;
+  int slot = -1;
+  Timed(int kid, hipStream_t s) : st(s) {
+    if (g_prof.on && g_prof.used < g_prof.kind.size()) {
+      slot = (int)g_prof.used++;
+      g_prof.kind[slot] = kid;
+      (void)hipEventRecord(g_prof.ev[2 * slot], st);
+    }
+  }
+  ~Timed() {
+    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], st);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t verkv_version(void) { return 100; }
+
+const char *verkv_status_str(int32_t s) {
+  switch (s) {
+    case VERKV_OK: return "ok";
+    case VERKV_EINVAL: return "invalid argument";
+    case VERKV_EBUDGET: return "budget below the forced sink + local tokens";
+    case VERKV_ECAPACITY: return "pivot capacity exceeded";
+    case VERKV_EHIP: return "HIP runtime error";
+    case VERKV_EUNSUPPORTED: return "unsupported shape";
+    case VERKV_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char *verkv_last_error(void) { return g_last_error; }
+
+size_t verkv_compress_workspace_bytes(const verkv_shape *s) {
+  SeqTable t;
+  if (make_table(s, t) != VERKV_OK) return 0;
+  return compress_layout(t).total;
+}
+
+size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap) {
+  SeqTable t;
+  if (cap < 1 || make_table(s, t) != VERKV_OK) return 0;
+  return decode_layout(t, cap).total;
+}
+
+verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *K_host,
+                            const void *V_host, double eta, uint64_t seed, verkv_state *st,
+                            void *workspace, size_t workspace_bytes, int32_t *needed_cap,
+                            verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!tau || !K_host || !V_host || !st || !workspace) return VERKV_EINVAL;
+  if (!st->r || !st->resident || !st->piv_idx || !st->piv_count || !st->piv_k || !st->piv_v ||
+      st->cap < 1)
+    return VERKV_EINVAL;
+  if (!(eta > 0.0 && eta <= 1.0)) return VERKV_EINVAL;
+  for (int b = 0; b < t.B; ++b) {
+    const int n = t.s[b].n;
+    const int forced = std::min(n, s->n_sink + s->n_local);
+    if (eta * (double)n - (double)forced < 0.0) return VERKV_EBUDGET;
+  }
+  const CompressWs L = compress_layout(t);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((rc = device_view(K_host, &Kd)) != VERKV_OK) return rc;
+  if ((rc = device_view(V_host, &Vd)) != VERKV_OK) return rc;
+
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  int32_t *status = reinterpret_cast<int32_t *>(ws + L.status);
+  HIP_TRY(hipMemsetAsync(status, 0, 16, stream), "hipMemsetAsync");
+  CompressArgs a;
+  a.t = t;
+  a.tau = tau;
+  a.eta = eta;
+  a.seed = seed;
+  a.layer = s->layer;
+  a.r = st->r;
+  a.resident = st->resident;
+  a.piv_idx = st->piv_idx;
+  a.piv_count = st->piv_count;
+  a.cap = st->cap;
+  a.keys_a = reinterpret_cast<uint64_t *>(ws + L.ka);
+  a.keys_b = reinterpret_cast<uint64_t *>(ws + L.kb);
+  a.status = status;
+  const int units = t.B * t.Hkv;
+  {
+    Timed tm(K_POISSON, stream);
+    HIP_TRY(launch_poissoncomp(a, units, stream), "poissoncomp launch");
+  }
+  int32_t hstat[2] = {0, 0};
+  HIP_TRY(hipMemcpyAsync(hstat, status, sizeof(hstat), hipMemcpyDeviceToHost, stream), "hipMemcpyAsync");
+  HIP_TRY(hipStreamSynchronize(stream), "hipStreamSynchronize");
+  if (hstat[0] & 1) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "tau outside [0, 1]");
+    return VERKV_EINVAL;
+  }
+  if (hstat[1] > st->cap) {
+    if (needed_cap) *needed_cap = hstat[1];
+    return VERKV_ECAPACITY;
+  }
+  if (needed_cap) *needed_cap = hstat[1];
+  GatherArgs gth;
+  gth.t = t;
+  gth.K_host = static_cast<const uint8_t *>(Kd);
+  gth.V_host = static_cast<const uint8_t *>(Vd);
+  gth.piv_idx = st->piv_idx;
+  gth.piv_count = st->piv_count;
+  gth.piv_k = static_cast<uint8_t *>(st->piv_k);
+  gth.piv_v = static_cast<uint8_t *>(st->piv_v);
+  gth.cap = st->cap;
+  gth.row_bytes = row_bytes(s);
+  {
+    Timed tm(K_GATHER, stream);
+    HIP_TRY(launch_gather_pivots(gth, units, stream), "gather launch");
+  }
+  return VERKV_OK;
+}
+
+static verkv_status check_step(const verkv_shape *s, const verkv_state *st, const float *q,
+                               const verkv_step_out *out, SeqTable &t) {
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!st || !q || !out) return VERKV_EINVAL;
+  if (!st->r || !st->resident || !st->piv_idx || !st->piv_count || !st->piv_k || !st->piv_v ||
+      !st->sketch || st->cap < 1)
+    return VERKV_EINVAL;
+  return VERKV_OK;
+}
+
+verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
+                               double beta, double eps, double delta, verkv_step_out *out,
+                               void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = check_step(s, st, q, out, t);
+  if (rc != VERKV_OK) return rc;
+  if (!(beta >= 0.0) || !(eps > 0.0) || !(delta > 0.0 && delta < 1.0)) return VERKV_EINVAL;
+  if (!out->m_hat || !out->d_sketch || !out->beta_star || !out->eps_hat || !out->certified ||
+      !out->kstar || !out->fetch_count || !out->h2d_count || !workspace)
+    return VERKV_EINVAL;
+  if (out->fetch_idx && out->fetch_cap < 1) return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, st->cap);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const bool bf16 = s->kv_dtype == VERKV_BF16;
+  const Totals T = totals(t);
+  const int units = t.B * t.Hkv;
+  const int rows = units * t.G;
+
+  SketchArgs sk;
+  sk.t = t;
+  sk.sketch = static_cast<const uint8_t *>(st->sketch);
+  sk.q = q;
+  sk.sqrt_d = std::sqrt((double)VERKV_HEAD_DIM);
+  sk.wc = reinterpret_cast<double *>(ws + L.wc);
+  sk.cstat = reinterpret_cast<double2 *>(ws + L.cstat);
+  sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
+  sk.total_blocks = (int32_t)(t.Hkv * T.chunks);
+  {
+    Timed tm(K_SKETCH, stream);
+    HIP_TRY(launch_sketch(sk, bf16, stream), "sketch launch");
+  }
+
+  DecideArgs dc;
+  dc.t = t;
+  dc.wc = sk.wc;
+  dc.cstat = sk.cstat;
+  dc.cscale = reinterpret_cast<double *>(ws + L.cscale);
+  dc.r = st->r;
+  dc.fbits = sk.fbits;
+  dc.kappa = beta;
+  dc.eps = eps;
+  dc.l = std::log(2.0 / delta);
+  dc.m_hat = out->m_hat;
+  dc.d_sketch = out->d_sketch;
+  dc.beta_star = out->beta_star;
+  dc.eps_hat = out->eps_hat;
+  dc.certified = out->certified;
+  dc.kstar = out->kstar;
+  dc.status = reinterpret_cast<int32_t *>(ws + L.status);
+  dc.params = reinterpret_cast<double *>(ws + L.status + 32);
+  {
+    Timed tm(K_DECIDE, stream);
+    HIP_TRY(launch_decide(dc, rows, stream), "decide launch");
+  }
+
+  UnionArgs un;
+  un.t = t;
+  un.fbits = sk.fbits;
+  un.resident = st->resident;
+  un.piv_idx = st->piv_idx;
+  un.piv_count = st->piv_count;
+  un.cap = st->cap;
+  un.r = st->r;
+  un.wc = sk.wc;
+  un.cscale = dc.cscale;
+  un.beta_star = out->beta_star;
+  un.kappa = beta;
+  un.fetch_idx = out->fetch_idx;
+  un.fetch_cap = out->fetch_cap;
+  un.fetch_count = out->fetch_count;
+  un.h2d_count = out->h2d_count;
+  un.h2d_idx = reinterpret_cast<int32_t *>(ws + L.h2d);
+  un.coef = reinterpret_cast<float *>(ws + L.coef);
+  {
+    Timed tm(K_UNION, stream);
+    HIP_TRY(launch_union(un, units, stream), "union launch");
+  }
+
+  AttendArgs at;
+  at.t = t;
+  at.q = q;
+  at.m_hat = out->m_hat;
+  at.inv_sqrt_d = (float)(1.0 / std::sqrt((double)VERKV_HEAD_DIM));
+  at.krows = static_cast<const uint8_t *>(st->piv_k);
+  at.vrows = static_cast<const uint8_t *>(st->piv_v);
+  at.count = st->piv_count;
+  at.list = nullptr;
+  at.coef = un.coef;
+  at.cap = st->cap;
+  at.part = reinterpret_cast<float *>(ws + L.ppart);
+  at.nsplit = L.nsp;
+  {
+    Timed tm(K_PIVOT, stream);
+    HIP_TRY(launch_attend(at, units, bf16, false, stream), "pivot attention launch");
+  }
+  return VERKV_OK;
+}
+
+verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
+                          const void *K_host, const void *V_host, verkv_step_out *out,
+                          void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = check_step(s, st, q, out, t);
+  if (rc != VERKV_OK) return rc;
+  if (!K_host || !V_host || !workspace || !out->eps_after || !out->n_hat || !out->d_hat ||
+      !out->o || !out->lse || !out->m_hat || !out->d_sketch || !out->beta_star || !out->h2d_count)
+    return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, st->cap);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((rc = device_view(K_host, &Kd)) != VERKV_OK) return rc;
+  if ((rc = device_view(V_host, &Vd)) != VERKV_OK) return rc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const bool bf16 = s->kv_dtype == VERKV_BF16;
+  const int units = t.B * t.Hkv;
+  const int rows = units * t.G;
+
+  AttendArgs at;
+  at.t = t;
+  at.q = q;
+  at.m_hat = out->m_hat;
+  at.inv_sqrt_d = (float)(1.0 / std::sqrt((double)VERKV_HEAD_DIM));
+  at.krows = static_cast<const uint8_t *>(Kd);
+  at.vrows = static_cast<const uint8_t *>(Vd);
+  at.count = out->h2d_count;
+  at.list = reinterpret_cast<const int32_t *>(ws + L.h2d);
+  at.coef = nullptr;
+  at.cap = st->cap;
+  at.part = reinterpret_cast<float *>(ws + L.hpart);
+  at.nsplit = L.nsh;
+  {
+    Timed tm(K_HOST, stream);
+    HIP_TRY(launch_attend(at, units, bf16, true, stream), "host attention launch");
+  }
+
+  FinishArgs fi;
+  fi.t = t;
+  fi.piv_part = reinterpret_cast<const float *>(ws + L.ppart);
+  fi.nsp = L.nsp;
+  fi.host_part = at.part;
+  fi.nsh = L.nsh;
+  fi.wc = reinterpret_cast<const double *>(ws + L.wc);
+  fi.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  fi.r = st->r;
+  fi.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  fi.m_hat = out->m_hat;
+  fi.d_sketch = out->d_sketch;
+  fi.beta_star = out->beta_star;
+  fi.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa, l of the step
+  fi.eps_after = out->eps_after;
+  fi.n_hat = out->n_hat;
+  fi.d_hat = out->d_hat;
+  fi.o = out->o;
+  fi.lse = out->lse;
+  {
+    Timed tm(K_FINISH, stream);
+    HIP_TRY(launch_finish(fi, rows, stream), "finish launch");
+  }
+  (void)rows;
+  return VERKV_OK;
+}
+
+int32_t verkv_profile_begin(int32_t max_launches) {
+  verkv_profile_end();
+  if (max_launches < 1) return VERKV_EINVAL;
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  g_prof.kind.assign((size_t)max_launches, -1);
+  for (auto &e : g_prof.ev) {
+    hipError_t rc = hipEventCreate(&e);
+    if (rc != hipSuccess) {
+      verkv_profile_end();
+      return hip_fail(rc, "hipEventCreate");
+    }
+  }
+  g_prof.used = 0;
+  g_prof.on = true;
+  return VERKV_OK;
+}
+
+int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds) {
+  if (!total_ms || !launches || n_kinds < VERKV_PROFILE_KINDS) return VERKV_EINVAL;
+  for (int k = 0; k < VERKV_PROFILE_KINDS; ++k) { total_ms[k] = 0.0; launches[k] = 0; }
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    HIP_TRY(hipEventSynchronize(g_prof.ev[2 * i + 1]), "hipEventSynchronize");
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]), "hipEventElapsedTime");
+    total_ms[g_prof.kind[i]] += ms;
+    launches[g_prof.kind[i]] += 1;
+  }
+  g_prof.used = 0;
+  return VERKV_OK;
+}
+
+void verkv_profile_end(void) {
+  for (auto &e : g_prof.ev)
+    if (e) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kind.clear();
+  g_prof.used = 0;
+  g_prof.on = false;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+"""Runs a synthetic workload through the library: uploads the cache, compresses it
+and executes decode steps.  Used by the tests, the benchmark and the smoke check.
+
+Exact-sketch mode: the device-resident sketch is the key cache itself (the setting of
+Theorem 2 on the picx.dev summary page).  The complete K/V cache lives in pinned host
+memory; only H u S and the sketch are on the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import verkv
+from .synth import Workload
+
+
+def _cat(arrs):
+    return np.concatenate([a.reshape(-1) for a in arrs])
+
+
+class Session:
+    """One layer of a workload, compressed on the GPU, ready for decode steps."""
+
+    def __init__(self, wl: Workload, cap: int | None = None, device: str = "cuda",
+                 host_pinned: bool = True, seed: int | None = None):
+        self.wl = wl
+        self.device = device
+        lens = [s.n for s in wl.seqs]
+        self.shape = verkv.LayerShape(lens, wl.n_kv_heads, wl.group, wl.n_sink, wl.n_local,
+                                      wl.kv_dtype, wl.layer)
+        dt = self.shape.torch_dtype
+        K = torch.from_numpy(_cat([s.K for s in wl.seqs])).to(dt)
+        V = torch.from_numpy(_cat([s.V for s in wl.seqs])).to(dt)
+        if host_pinned:
+            self.K_host = torch.empty(K.shape, dtype=dt, pin_memory=True)
+            self.V_host = torch.empty(V.shape, dtype=dt, pin_memory=True)
+            self.K_host.copy_(K)
+            self.V_host.copy_(V)
+        else:                                   # whole cache on the device (tests only)
+            self.K_host = K.to(device)
+            self.V_host = V.to(device)
+        self.sketch = K.to(device)              # exact sketch: the keys, device resident
+        self.tau = torch.from_numpy(_cat([s.tau for s in wl.seqs]).astype(np.float32)).to(device)
+        self.cap = int(cap) if cap else verkv.default_cap(self.shape, wl.eta)
+        self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device)
+        self.cws = verkv.workspace(self.shape.compress_workspace_bytes(), device)
+        self.dws = verkv.workspace(self.shape.decode_workspace_bytes(self.cap), device)
+        self.out = verkv.StepBuffers(self.shape, device=device)
+        self.seed = wl.seed if seed is None else seed
+        self.max_pivots = None
+
+    def compress(self, stream=None):
+        self.max_pivots = verkv.compress(self.shape, self.tau, self.K_host, self.V_host,
+                                         self.wl.eta, self.seed, self.state, self.cws, stream)
+        return self.max_pivots
+
+    def queries(self, step: int) -> torch.Tensor:
+        """Query rows of one step as a device tensor [B][Hq][128] (float32)."""
+        return torch.from_numpy(np.ascontiguousarray(self.wl.queries[step])).to(self.device)
+
+    def step(self, q: torch.Tensor, kappa=None, eps=None, delta=None, stream=None,
+             out: verkv.StepBuffers | None = None):
+        out = out or self.out
+        wl = self.wl
+        verkv.decode_step(self.shape, self.state, q, wl.kappa if kappa is None else kappa,
+                          wl.eps if eps is None else eps, wl.delta if delta is None else delta,
+                          out, self.dws, stream)
+        verkv.refine(self.shape, self.state, q, self.K_host, self.V_host, out, self.dws, stream)
+        return out
+
+    # ---------------------------------------------------------------- host-side views
+    def state_numpy(self):
+        """r, resident mask, pivot lists per (sequence, KV head)."""
+        torch.cuda.synchronize()
+        r = self.state.r.cpu().numpy()
+        res = self.state.resident.cpu().numpy().view(np.uint32)
+        cnt = self.state.piv_count.cpu().numpy()
+        pidx = self.state.piv_idx.view(-1, self.cap).cpu().numpy()
+        out = []
+        roff, woff = 0, 0
+        for b, n in enumerate(self.shape.seq_lens):
+            W = (n + 31) // 32
+            for g in range(self.shape.n_kv_heads):
+                u = b * self.shape.n_kv_heads + g
+                bits = np.unpackbits(res[woff + g * W: woff + (g + 1) * W].view(np.uint8),
+                                     bitorder="little")[:n].astype(bool)
+                out.append(dict(r=r[roff + g * n: roff + (g + 1) * n], resident=bits,
+                                piv_idx=pidx[u, :min(int(cnt[u]), self.cap)], piv_count=int(cnt[u])))
+            roff += self.shape.n_kv_heads * n
+            woff += self.shape.n_kv_heads * W
+        return out
+
+    def results_numpy(self, out: verkv.StepBuffers | None = None):
+        out = out or self.out
+        torch.cuda.synchronize()
+        rows = self.shape.batch * self.shape.n_q_heads
+        res = {k: getattr(out, k).cpu().numpy() for k in
+               ("m_hat", "d_sketch", "beta_star", "eps_hat", "certified", "kstar", "eps_after",
+                "d_hat", "lse", "fetch_count", "h2d_count")}
+        res["o"] = out.o.view(rows, -1).cpu().numpy()
+        res["n_hat"] = out.n_hat.view(rows, -1).cpu().numpy()
+        res["fetch"] = out.fetch_lists(self.shape)
+        return res

@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every symbol include/verkv.h declares, and rejects
+bad arguments on the host before any GPU work (no compute calls; no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verkv.h")
+
+
+@pytest.fixture(scope="module")
+def vk():
+    from long_context_decode_kvfetch_amd import verkv
+    if not os.path.exists(verkv.LIB_PATH):
+        from long_context_decode_kvfetch_amd import build
+        build.build()
+    return verkv
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("verkv_compress", "verkv_decode_step", "verkv_refine",
+              "verkv_compress_workspace_bytes", "verkv_decode_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(vk):
+    lib = vk.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(vk):
+    lib = vk.lib()
+    assert lib.verkv_version() == 100
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.verkv_status_str(st).decode() not in ("", "unknown status")
+    assert lib.verkv_status_str(7).decode() == "unknown status"
+
+
+def _shape(vk, lens=(4096,), hkv=1, g=8, dtype="f32", n_sink=4, n_local=64, head_dim=None):
+    sh = vk.LayerShape(list(lens), hkv, g, n_sink, n_local, dtype)
+    if head_dim is not None:
+        sh.c.head_dim = head_dim
+    return sh
+
+
+def test_workspace_sizes(vk):
+    a = _shape(vk).decode_workspace_bytes(640)
+    b = _shape(vk, lens=(8192,)).decode_workspace_bytes(640)
+    assert 0 < a < b and a % 256 == 0
+    assert _shape(vk).compress_workspace_bytes() >= 2 * 8 * 4096
+    assert _shape(vk, head_dim=64).decode_workspace_bytes(640) == 0
+    assert _shape(vk, g=9).compress_workspace_bytes() == 0
+    assert _shape(vk).decode_workspace_bytes(0) == 0
+    # ragged batch grows with every sequence
+    r1 = _shape(vk, lens=(1000, 3000), hkv=8, g=4, dtype="bf16").decode_workspace_bytes(512)
+    r2 = _shape(vk, lens=(1000, 3000, 17), hkv=8, g=4, dtype="bf16").decode_workspace_bytes(512)
+    assert r2 > r1
+
+
+FAKE = 4096      # a non-null pointer value the host checks never dereference
+
+
+def _fake_state(vk, cap=640):
+    return vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap, FAKE)
+
+
+def _fake_out(vk):
+    return vk.StepOut(*([FAKE] * 6), FAKE, 16, FAKE, FAKE, *([FAKE] * 5))
+
+
+def test_decode_step_rejects_bad_arguments_on_host(vk):
+    lib = vk.lib()
+    sh = _shape(vk)
+    st = _fake_state(vk)
+    out = _fake_out(vk)
+    big = 1 << 40
+
+    def call(shape=sh, beta=1.0, eps=0.05, delta=0.05, state=st, q=FAKE, ws=FAKE, wsb=big):
+        return lib.verkv_decode_step(C.byref(shape.c), C.byref(state), q, beta, eps, delta,
+                                     C.byref(out), ws, wsb, None)
+
+    assert call(eps=0.0) == vk.EINVAL
+    assert call(eps=-1.0) == vk.EINVAL
+    assert call(delta=0.0) == vk.EINVAL
+    assert call(delta=1.0) == vk.EINVAL
+    assert call(beta=-0.5) == vk.EINVAL
+    assert call(beta=float("nan")) == vk.EINVAL
+    assert call(q=None) == vk.EINVAL
+    assert call(wsb=16) == vk.EWORKSPACE
+    assert call(shape=_shape(vk, head_dim=64)) == vk.EUNSUPPORTED
+    assert call(shape=_shape(vk, g=9)) == vk.EUNSUPPORTED
+    assert call(shape=_shape(vk, lens=(0,))) == vk.EINVAL
+    assert call(shape=_shape(vk, lens=((1 << 20) + 1,))) == vk.EUNSUPPORTED
+    assert call(state=_fake_state(vk, cap=0)) == vk.EINVAL
+    nostate = vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 640, 0)     # no sketch
+    assert call(state=nostate) == vk.EINVAL
+    assert lib.verkv_decode_step(None, C.byref(st), FAKE, 1.0, 0.05, 0.05, C.byref(out), FAKE,
+                                 big, None) == vk.EINVAL
+
+
+def test_compress_rejects_bad_arguments_on_host(vk):
+    lib = vk.lib()
+    st = _fake_state(vk)
+    need = C.c_int32(-7)
+
+    def call(shape, eta=0.125, state=st, wsb=1 << 40, tau=FAKE):
+        return lib.verkv_compress(C.byref(shape.c), tau, FAKE, FAKE, eta, 0, C.byref(state),
+                                  FAKE, wsb, C.byref(need), None)
+
+    sh = _shape(vk)
+    assert call(sh, eta=0.0) == vk.EINVAL
+    assert call(sh, eta=1.5) == vk.EINVAL
+    assert call(sh, eta=float("nan")) == vk.EINVAL
+    assert call(sh, tau=None) == vk.EINVAL
+    # eta * n below the 68 forced tokens
+    assert call(sh, eta=60 / 4096) == vk.EBUDGET
+    # budget check is per sequence of a ragged batch
+    assert call(_shape(vk, lens=(4096, 100), dtype="bf16"), eta=0.5) == vk.EBUDGET
+    assert call(sh, wsb=64) == vk.EWORKSPACE
+    assert call(sh, state=_fake_state(vk, cap=0)) == vk.EINVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from long_context_decode_kvfetch_amd import verkv
+    monkeypatch.setattr(verkv, "_LIB", None)
+    monkeypatch.setattr(verkv, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        verkv.lib()
