@@ -1,0 +1,218 @@
+"""Benchmark: certified KVFetch decode steps/s at 32K context, eta = 1/16, on one MI355X.
+
+Workload (synthetic, seeded): Qwen3-4B-shaped decode, one layer per step: 32 query /
+8 KV heads, head_dim 128, n = 32768, bf16 cache ~ N(0,1) with 1% planted heavy hitters
+per KV head, tau ~ Beta(0.3, 3), eta = 1/16, H = 4 sink + 128 local, eps = 0.05,
+delta = 0.05, one query token per step.  The complete K/V cache of every layer sits in
+pinned host memory; the sketch (exact: the keys) and H u S are GPU resident.
+
+A step is one verkv_decode_step + verkv_refine on one layer: sketch scores, shrinkage
+fixed point, certificate, fetch selection, resident-pivot attention, host fetch of
+F minus S over the host link, and the finished output; after it every query row is
+certified (eps_hat(L minus F) < eps).  Steps run back to back on one stream, as decode
+steps must.  Consecutive steps visit different layers (8 independently generated
+layers, each with its own cache and queries) so that the working set of a step is not
+served from the previous step's Infinity Cache lines.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits with a message: this build measures
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+N_CTX = 32768
+ETA = 1.0 / 16
+N_LAYERS_ROT = 8
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--layers", type=int, default=N_LAYERS_ROT)
+    p.add_argument("--profile-steps", type=int, default=64)
+    p.add_argument("--cpu-steps", type=int, default=8)
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def h2d_bandwidth(torch, nbytes=256 << 20, reps=5):
+    """Pinned host -> device copy bandwidth, GB/s (contiguous)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(steps):
+    """The oracle (as it stands) on the same workload: one layer, `steps` decode steps."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import synth
+    from oracle import api as oapi
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:                                          # pragma: no cover
+        cores = os.cpu_count() or 1
+    wl = synth.gqa_layer(seed=0, n=N_CTX, steps=steps, layer=0)
+    s = wl.seqs[0]
+    comp = oapi.compress_sequence(s.tau, wl.n_sink, wl.n_local, wl.eta, 0, 0, wl.seed)
+    t0 = time.perf_counter()
+    for st in range(steps):
+        oapi.decode_sequence(s.K, s.V, comp, wl.queries[st, 0], wl.group, wl.kappa, wl.eps, wl.delta)
+    dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} decode steps of one layer (32q/8kv, n={N_CTX}, bf16 values in "
+                      f"float64, eta=1/16), prefill excluded; {dt:.1f} s on "
+                      f"{os.cpu_count()} host cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the KVFetch path shards by sequence and KV head with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_decode_kvfetch_amd import synth, verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K, W, L = args.steps, args.warmup, args.layers
+    total = K + W + args.profile_steps
+    per_layer = (total + L - 1) // L
+    log(f"[bench] generating {L} layers (n={N_CTX}, 32q/8kv, bf16)")
+    sessions = []
+    for layer in range(L):
+        wl = synth.gqa_layer(seed=0, n=N_CTX, steps=per_layer, layer=layer)
+        sess = Session(wl)
+        sess.compress()
+        sess.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries[:, :])).to("cuda")
+        sessions.append(sess)
+        log(f"[bench] layer {layer} compressed, max pivots {sess.max_pivots}, cap {sess.cap}")
+    torch.cuda.synchronize()
+
+    def run(step_index):
+        sess = sessions[step_index % L]
+        sess.step(sess.qdev[(step_index // L) % per_layer])
+        return sess
+
+    for i in range(W):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(W, W + K):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1)
+    ms_per_step = ev_ms / K
+    log(f"[bench] {K} steps: {wall * 1e3:.1f} ms wall, {ev_ms:.1f} ms events")
+
+    # per-step statistics over one pass of every layer
+    cert, fetched, h2d, rows, n_tok = 0, 0, 0, 0, 0
+    for sess in sessions:
+        sess.step(sess.qdev[0])
+        r = sess.results_numpy()
+        cert += int(r["certified"].sum())
+        fetched += int(r["fetch_count"].sum())
+        h2d += int(r["h2d_count"].sum())
+        rows += r["certified"].size
+        n_tok += N_CTX * sess.shape.n_kv_heads
+        assert np.all(r["eps_after"] < sess.wl.eps), "a row finished uncertified"
+    # exact sketch: only the value rows of F minus S cross the host link (256 B each)
+    h2d_bytes_step = h2d / L * 128 * 2
+
+    # kernel durations with HIP events around every launch of the profiled steps
+    P = args.profile_steps
+    verkv.profile_begin(8 * P + 16)
+    for i in range(W + K, W + K + P):
+        run(i)
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    piv_bytes = sum(int(s.state.piv_count.sum().item()) for s in sessions) / L * 2 * 128 * 2
+    sketch_bytes = 8 * N_CTX * 128 * 2
+    kern = {}
+    for name, (ms, cnt) in prof.items():
+        if cnt:
+            kern[name] = {"avg_us": ms / cnt * 1e3, "launches": cnt}
+    kern["sketch_scores"]["algorithmic_bytes"] = sketch_bytes
+    kern["sketch_scores"]["GBps"] = sketch_bytes / (kern["sketch_scores"]["avg_us"] * 1e-6) / 1e9
+    kern["attend_pivots"]["algorithmic_bytes"] = piv_bytes
+    kern["attend_pivots"]["GBps"] = piv_bytes / (kern["attend_pivots"]["avg_us"] * 1e-6) / 1e9
+    kern["attend_host"]["host_bytes"] = h2d_bytes_step
+    kern["attend_host"]["GBps"] = h2d_bytes_step / (kern["attend_host"]["avg_us"] * 1e-6) / 1e9
+    # dominant HBM-streaming kernel (the host-row kernel is bound by the host link)
+    hbm_kernels = ("sketch_scores", "attend_pivots")
+    dom = max(hbm_kernels, key=lambda k: kern[k]["avg_us"])
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["GBps"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": None}
+    h2d_peak = h2d_bandwidth(torch)
+
+    out = {
+        "metric": "certified decode steps/s at 32K ctx, eta=1/16; achieved HBM GB/s vs peak",
+        "value": round(K / (ev_ms * 1e-3), 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64+f32",
+        "data": "synthetic",
+        "config": {"workload": "gqa decode layer-step: 32q/8kv heads, d=128, n=32768, bf16 "
+                               "cache in pinned host memory, exact sketch, eta=1/16, "
+                               "H=4 sink+128 local, eps=0.05, delta=0.05, 1% planted heavy "
+                               "hitters, tau~Beta(0.3,3)",
+                   "layers_rotated": L, "seq_len": N_CTX, "batch": 1},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "step_stats": {"rows_certified_without_fetch": cert / rows,
+                       "fetched_fraction_of_cache": fetched / n_tok,
+                       "h2d_fraction_of_cache": h2d / n_tok,
+                       "h2d_bytes_per_step": h2d_bytes_step,
+                       "h2d_GBps_per_step": h2d_bytes_step / (ms_per_step * 1e-3) / 1e9,
+                       "pinned_h2d_copy_GBps": round(h2d_peak, 1),
+                       "wall_ms_per_step": wall * 1e3 / K},
+        "kernels": kern,
+    }
+    if not args.no_cpu:
+        log(f"[bench] cpu baseline: oracle, {args.cpu_steps} steps")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_steps)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -85,6 +85,9 @@ typedef struct {
   int32_t cap;              /* pivot capacity per (sequence, KV head)                  */
   const void *sketch;       /* [B][Hkv][n_b][128] kv_dtype token-level key sketch.     */
                             /* Exact-sketch mode: the keys themselves, on the device.  */
+  int32_t sketch_exact;     /* 1: the sketch rows are the keys, so the host fetch of    */
+                            /* KVFetch step 5 reads only the value rows and takes the  */
+                            /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
 } verkv_state;
 
 /* Per-step results.  Row arrays are [B][Hq]; KV-head arrays are [B][Hkv]. */
@@ -148,8 +151,8 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
                                double beta, double eps, double delta, verkv_step_out *out,
                                void *workspace, size_t workspace_bytes, verkv_stream_t stream);
 
-/* KVFetch step 5: reads the rows F \ S of K and V from the pinned host cache
- * (zero-copy loads issued by the kernels), adds their exact terms, and finishes
+/* KVFetch step 5: reads the rows F \ S of V (and of K unless st->sketch_exact) from the
+ * pinned host cache (zero-copy loads issued by the kernels), adds their exact terms, and finishes
  * every row: o = N_hat / D_hat, lse, n_hat, d_hat and eps_after = eps_hat(L \ F).
  * Must follow verkv_decode_step on the same stream with the same workspace, q, s
  * and st.  Rows whose KV head fetched nothing are finished from the resident
@@ -166,12 +169,18 @@ size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
  * waits for the recorded launches, writes per kernel kind the summed duration in ms
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
- * 7 finish), and clears the record.  verkv_profile_end destroys the events.  Not
+ * 7 finish, 8 eps_after partials), and clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 8
+#define VERKV_PROFILE_KINDS 9
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);
+
+/* Waits for `stream` and reports problems the kernels of the last steps flagged in
+ * `workspace` (a decode workspace): VERKV_OK, or VERKV_EHIP with verkv_last_error()
+ * naming the condition (a team barrier that timed out, a fixed-point iteration that
+ * did not converge).  Clears the flags. */
+verkv_status verkv_check(void *workspace, const verkv_shape *s, int32_t cap, verkv_stream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *verkv_status_str(int32_t status);

@@ -7,7 +7,9 @@
 //   * resident pivots H u S (device rows, coefficient from the decision kernels): the
 //     HBM stream of every decode step;
 //   * rows F \ S read straight from the pinned host cache (zero-copy loads over the
-//     host link, coefficient 1): KVFetch step 5.
+//     host link, coefficient 1): KVFetch step 5.  When the sketch is exact (its rows
+//     are the keys) the weights of these rows are the float64 sketch weights of step 1
+//     and only the value rows cross the host link.
 // Each lane owns a 16-byte slice of a K row and of the matching V row; G query rows
 // stay in registers; scores are reduced across the lanes of a row with DPP; no MFMA
 // (one to eight query rows per KV head is far too thin for a matrix core).  m_hat is
@@ -20,7 +22,7 @@ namespace verkv {
 constexpr int AT_NT = 256;
 constexpr int AT_NW = AT_NT / WAVE;
 
-template <bool BF16, int G, bool HOST>
+template <bool BF16, int G, bool HOST, bool EXACT>
 __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   using RS = RowSlice<BF16>;
   constexpr int EPL = RS::EPL;
@@ -73,18 +75,23 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
 
   const int64_t src_base = HOST ? tok_base(a.t, b, g) : (int64_t)unit * a.cap;
   const int32_t *list = HOST ? a.list + tok_base(a.t, b, g) : nullptr;
+  (void)list;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
 
   for (int base = p0; base < p1; base += STEP * U) {
     uint4 kr[U], vr[U];
     int pp[U];
+    int tk[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
       pp[u] = p;
+      tk[u] = 0;
       if (p < p1) {
-        const int64_t rowi = HOST ? src_base + list[p] : src_base + p;
-        kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+        const int tok = HOST ? list[p] : p;
+        tk[u] = tok;
+        const int64_t rowi = src_base + tok;
+        if (!EXACT) kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
         vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
       } else {
         kr[u] = make_uint4(0, 0, 0, 0);
@@ -93,19 +100,31 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float x[EPL];
-      RS::widen(kr[u], x);
       float w[G];
+      if constexpr (EXACT) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float dot = 0.0f;
+        for (int j = 0; j < G; ++j) {
+          const int h = g * G + j;
+          double wd = 0.0;
+          if (pp[u] < p1)
+            wd = a.wc[row_tok_base(a.t, b, h) + tk[u]] *
+                 a.cscale[row_chunk_base(a.t, b, h) + tk[u] / SKETCH_CHUNK];
+          w[j] = (float)wd;
+        }
+      } else {
+        float x[EPL];
+        RS::widen(kr[u], x);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
-        dot = sum16(dot);
-        if (LPT == 32) dot += shfl_xor_f(dot, 16);
-        float c = 1.0f;
-        if (!HOST && pp[u] < p1) c = a.coef[((int64_t)b * Hq + g * G + j) * a.cap + pp[u]];
-        w[j] = (pp[u] < p1) ? c * __expf(dot - mh[j]) : 0.0f;
+        for (int j = 0; j < G; ++j) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
+          dot = sum16(dot);
+          if (LPT == 32) dot += shfl_xor_f(dot, 16);
+          float c = 1.0f;
+          if (!HOST && pp[u] < p1) c = a.coef[((int64_t)b * Hq + g * G + j) * a.cap + pp[u]];
+          w[j] = (pp[u] < p1) ? c * __expf(dot - mh[j]) : 0.0f;
+        }
       }
       float v[EPL];
       RS::widen(vr[u], v);
@@ -146,20 +165,26 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   }
 }
 
-template <bool BF16, int G, bool HOST>
+template <bool BF16, int G, bool HOST, bool EXACT>
 static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st) {
-  hipLaunchKernelGGL((k_attend<BF16, G, HOST>), dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
+  hipLaunchKernelGGL((k_attend<BF16, G, HOST, EXACT>), dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, hipStream_t st) {
-  const int key = (a.t.G * 2 + (bf16 ? 1 : 0)) * 2 + (host ? 1 : 0);
-  switch (key) {
-#define VERKV_AT_CASE(GG)                                                    \
-  case (GG * 2 + 1) * 2 + 1: return launch_attend_t<true, GG, true>(a, units, st);   \
-  case (GG * 2 + 1) * 2: return launch_attend_t<true, GG, false>(a, units, st);      \
-  case (GG * 2) * 2 + 1: return launch_attend_t<false, GG, true>(a, units, st);      \
-  case (GG * 2) * 2: return launch_attend_t<false, GG, false>(a, units, st);
+template <bool BF16, int G>
+static hipError_t launch_attend_g(const AttendArgs &a, int units, bool host, bool exact,
+                                  hipStream_t st) {
+  if (!host) return launch_attend_t<BF16, G, false, false>(a, units, st);
+  if (exact) return launch_attend_t<BF16, G, true, true>(a, units, st);
+  return launch_attend_t<BF16, G, true, false>(a, units, st);
+}
+
+hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, bool exact,
+                         hipStream_t st) {
+  switch (a.t.G * 2 + (bf16 ? 1 : 0)) {
+#define VERKV_AT_CASE(GG)                                                              \
+  case GG * 2 + 1: return launch_attend_g<true, GG>(a, units, host, exact, st);        \
+  case GG * 2: return launch_attend_g<false, GG>(a, units, host, exact, st);
     VERKV_AT_CASE(1) VERKV_AT_CASE(2) VERKV_AT_CASE(3) VERKV_AT_CASE(4)
     VERKV_AT_CASE(5) VERKV_AT_CASE(6) VERKV_AT_CASE(7) VERKV_AT_CASE(8)
 #undef VERKV_AT_CASE

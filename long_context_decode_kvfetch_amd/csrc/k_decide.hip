@@ -1,5 +1,5 @@
-// KVFetch steps 2-4 for gfx950, one workgroup of 1024 threads per query row, all in
-// float64 ("Verify Before You Fetch", picx.dev summary page, "Methodology"):
+// KVFetch steps 2-4 for gfx950, all in float64 ("Verify Before You Fetch", picx.dev
+// summary page, "Methodology"):
 //   * Definition 2: lambda_i = clip_[r_i,1](beta r_i / (w_i (1 - r_i))) with the bias
 //     beta = sum_L w_i (1 - lambda_i) taken self-consistent.  beta is the unique root
 //     of B = f(B), f piecewise linear and non-increasing; it is found by a safeguarded
@@ -18,14 +18,23 @@
 // into it until at most WIN tokens remain.  Those are sorted in LDS (bitonic) and
 // scanned against a deterministic re-sum of everything below them.  The tokens of F
 // are OR-ed into the KV head's fetch bitmask (the union over the GQA group).
+//
+// Parallel layout: a query row is served by a team of T workgroups of 1024 threads,
+// each owning a contiguous slice of the row's tokens (T = 8 puts the 32 rows of a
+// 32-query-head layer on all 256 CUs).  Every reduction is first done inside the
+// workgroup, then combined across the team in a fixed member order after a barrier
+// on a counter in global memory; histograms are merged by bucket ranges (member m
+// merges buckets [m*NB/T, (m+1)*NB/T)).  Every member therefore sees identical
+// combined values and takes the same path through the phases.  With T > 1 the
+// kernel is launched cooperatively so that the whole team is resident; a barrier
+// wait is bounded and reports a timeout in the status word instead of hanging.
+// With T = 1 the barriers reduce to workgroup barriers and any grid size works.
 #include "kernels.h"
 
 namespace verkv {
 
 constexpr int DC_NT = 1024;
 constexpr int DC_NW = DC_NT / WAVE;
-constexpr int NBUCKET = 1024;
-constexpr int WIN = 1024;
 constexpr int MAX_CHUNKS = VERKV_MAX_SEQ_LEN / SKETCH_CHUNK;
 constexpr uint32_t IDX_MAX = (1u << 20) - 1;
 constexpr int NLEV = 9;
@@ -146,6 +155,37 @@ __device__ __forceinline__ Cert block_cert(Cert v, double *scr /*[4*DC_NW]*/) {
   return o;
 }
 
+// ------------------------------------------------------------------ team barrier
+constexpr uint32_t SPIN_LIMIT = 1u << 24;
+
+// One release add per workgroup (publishes the workgroup's stores, which the
+// workgroup barrier has already completed to L2), a spin on relaxed agent-scope loads
+// (these bypass the non-coherent caches without invalidating them), and one acquire
+// fence once the count is reached.
+__device__ __forceinline__ void team_barrier(uint32_t *ctr, uint32_t target, int32_t *status) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > SPIN_LIMIT) {
+        atomicOr(status, 4);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ Cert cert_combine(Cert a, const Cert &b) {
+  a.beta += b.beta;
+  a.V += b.V;
+  top2_merge(a.b1, a.b2, b.b1, b.b2);
+  return a;
+}
+
 __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   __shared__ double s_scale[MAX_CHUNKS];
   __shared__ double scr[4 * DC_NW];
@@ -155,10 +195,18 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   __shared__ uint64_t h_b[NBUCKET];
   __shared__ uint64_t w_key[WIN];
   __shared__ uint32_t w_lo[WIN];
-  __shared__ uint32_t w_slot[WIN];
   __shared__ int32_t s_int[4];
 
-  const int row = blockIdx.x;
+  const int T = a.team;
+  int row, m;
+  if (a.xcd_map) {                      // members of a team on the same XCD (round-robin dispatch)
+    const int idx = blockIdx.x >> 3;
+    row = (idx / T) * 8 + (blockIdx.x & 7);
+    m = idx % T;
+  } else {
+    row = blockIdx.x / T;
+    m = blockIdx.x % T;
+  }
   const int Hq = a.t.Hkv * a.t.G;
   const int b = row / Hq;
   const int h = row % Hq;
@@ -166,13 +214,24 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   const int n = a.t.s[b].n;
   const int nch = chunks_of(n);
   const int tid = threadIdx.x;
+  const int s0 = (int)((int64_t)n * m / T);
+  const int s1 = (int)((int64_t)n * (m + 1) / T);
   const double *wcr = a.wc + row_tok_base(a.t, b, h);
   const double2 *cs = a.cstat + row_chunk_base(a.t, b, h);
   const double *rr = a.r + tok_base(a.t, b, g);
   uint32_t *fb = a.fbits + word_base(a.t, b, g);
   const double kappa = a.kappa, l = a.l, eps = a.eps;
+  uint32_t *bar = a.bar + row;
+  double *part = a.part + (int64_t)row * 2 * T * 8;          // [2][T][8]
+  uint32_t nbar = 0;
+#define TEAM_SYNC()                                                         \
+  do {                                                                      \
+    if (T > 1) team_barrier(bar, (++nbar) * (uint32_t)T, a.status);         \
+    else __syncthreads();                                                   \
+  } while (0)
+#define SLOT() (part + (int64_t)(nbar & 1) * T * 8)
 
-  // ---- step 1 (finish): m_hat, per-chunk rescale, D = sum of all sketch weights
+  // ---- step 1 (finish): m_hat, per-chunk rescale, D (every member, same order)
   double mloc = -INFINITY;
   for (int c = tid; c < nch; c += DC_NT) mloc = fmax(mloc, cs[c].x);
   const double m_hat = block_max<DC_NT>(mloc, scr);
@@ -180,38 +239,43 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   for (int c = tid; c < nch; c += DC_NT) {
     const double sc = exp(cs[c].x - m_hat);
     s_scale[c] = sc;
-    a.cscale[row_chunk_base(a.t, b, h) + c] = sc;
+    if (m == 0) a.cscale[row_chunk_base(a.t, b, h) + c] = sc;
     dloc += sc * cs[c].y;
   }
   const double Dd = block_sum<DC_NT>(dloc, scr);      // barrier also publishes s_scale
 
 #define FOR_L(body)                                                   \
-  for (int i = tid; i < n; i += DC_NT) {                              \
+  for (int i = s0 + tid; i < s1; i += DC_NT) {                        \
     const double ri = rr[i];                                          \
     if (!(ri < 1.0)) continue;                                        \
     const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];             \
     body                                                              \
   }
 
+  // team-combine helpers: member partials go to SLOT()[m*8 + k]
+  auto combine_sum1 = [&](double v) -> double {
+    if (T == 1) return v;
+    if (tid == 0) SLOT()[m * 8] = v;
+    double *sl = SLOT();
+    TEAM_SYNC();
+    double t = 0.0;
+    for (int k = 0; k < T; ++k) t += sl[k * 8];
+    return t;
+  };
+
   // ---- self-consistent beta (Definition 2)
   double Bst;
-  if (isinf(kappa)) {
+  if (isinf(kappa) || kappa == 0.0) {
     double acc = 0.0;
-    FOR_L(if (ri == 0.0) acc += wi;)
-    Bst = block_sum<DC_NT>(acc, scr);
-  } else if (kappa == 0.0) {
-    double acc = 0.0;
-    FOR_L(acc += wi * (1.0 - ri);)
-    Bst = block_sum<DC_NT>(acc, scr);
+    if (isinf(kappa)) { FOR_L(if (ri == 0.0) acc += wi;) }
+    else { FOR_L(acc += wi * (1.0 - ri);) }
+    Bst = combine_sum1(block_sum<DC_NT>(acc, scr));
   } else {
-    double acc = 0.0;
-    FOR_L(acc += (ri == 0.0) ? wi : wi * (1.0 - ri);)
-    const double f0 = block_sum<DC_NT>(acc, scr);     // f(0): the upper end of the bracket
-    double lo = 0.0, hi = f0, B = f0;
-    Bst = f0;
-    bool done = (f0 == 0.0);
+    double lo = 0.0, hi = INFINITY, B = 0.0;
+    Bst = 0.0;
+    bool done = false;
     int iter = 0;
-    for (; !done && iter < 200; ++iter) {
+    for (; iter < 200; ++iter) {
       Red4 v{0.0, 0.0, 0.0, INFINITY};
       FOR_L(
         if (ri == 0.0) { v.s0 += wi; }
@@ -222,19 +286,30 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
           else if (B >= tt) { v.mx = fmax(v.mx, tt); }
           else { v.s0 += wi; v.s1 += kappa * ri / (1.0 - ri); v.mx = fmax(v.mx, aa); v.mn = fmin(v.mn, tt); }
         })
-      const Red4 o = block_red4(v, scr);
+      Red4 o = block_red4(v, scr);
+      if (T > 1) {
+        double *sl = SLOT();
+        if (tid == 0) { sl[m * 8] = o.s0; sl[m * 8 + 1] = o.s1; sl[m * 8 + 2] = o.mx; sl[m * 8 + 3] = o.mn; }
+        TEAM_SYNC();
+        o = Red4{0.0, 0.0, 0.0, INFINITY};
+        for (int k = 0; k < T; ++k) {
+          o.s0 += sl[k * 8]; o.s1 += sl[k * 8 + 1];
+          o.mx = fmax(o.mx, sl[k * 8 + 2]); o.mn = fmin(o.mn, sl[k * 8 + 3]);
+        }
+      }
       const double hB = B * (1.0 + o.s1) - o.s0;        // B - f(B)
       const double Bn = o.s0 / (1.0 + o.s1);             // root of this linear piece
-      if (Bn >= o.mx && Bn <= o.mn) { Bst = Bn; done = true; break; }
+      Bst = Bn;
+      if (iter == 0 && o.s0 == 0.0) { Bst = 0.0; done = true; break; }   // f(0) = 0: f vanishes
+      if (Bn >= o.mx && Bn <= o.mn) { done = true; break; }
       if (hB == 0.0) { Bst = B; done = true; break; }
       if (hB < 0.0) lo = B; else hi = B;
       double Bnext = Bn;
       if (!(Bnext > lo && Bnext < hi)) Bnext = 0.5 * (lo + hi);
-      if (Bnext == B || !(hi > lo)) { Bst = Bn; done = true; break; }
+      if (Bnext == B || !(hi > lo)) { done = true; break; }
       B = Bnext;
-      Bst = Bn;
     }
-    if (!done && tid == 0) atomicOr(&a.status[0], 2);
+    if (!done && tid == 0 && m == 0) atomicOr(a.status, 2);
   }
 
   // ---- eq. (7) certificate
@@ -244,20 +319,31 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
     cl.beta += x.beta; cl.V += x.V; ++nL;
     top2_merge(cl.b1, cl.b2, x.b, 0.0);)
-  const Cert ct = block_cert(cl, scr);
-  const double E_all = (block_sum<DC_NT>((double)nL, scr) > 0.0) ? bern_E(ct.beta, ct.V, ct.b1, l) : 0.0;
+  Cert ct = block_cert(cl, scr);
+  double nLt = block_sum<DC_NT>((double)nL, scr);
+  if (T > 1) {
+    double *sl = SLOT();
+    if (tid == 0) { sl[m * 8] = ct.beta; sl[m * 8 + 1] = ct.V; sl[m * 8 + 2] = ct.b1; sl[m * 8 + 3] = ct.b2; sl[m * 8 + 4] = nLt; }
+    TEAM_SYNC();
+    ct = Cert{0.0, 0.0, 0.0, 0.0};
+    nLt = 0.0;
+    for (int k = 0; k < T; ++k) {
+      ct = cert_combine(ct, Cert{sl[k * 8], sl[k * 8 + 1], sl[k * 8 + 2], sl[k * 8 + 3]});
+      nLt += sl[k * 8 + 4];
+    }
+  }
+  const double E_all = nLt > 0.0 ? bern_E(ct.beta, ct.V, ct.b1, l) : 0.0;
   const double ehat = E_all / Dd;
   const bool cert = ehat < eps;
-  if (tid == 0) {
+  if (tid == 0 && m == 0) {
     if (row == 0) { a.params[0] = kappa; a.params[1] = l; }
     a.m_hat[row] = m_hat;
     a.d_sketch[row] = Dd;
     a.beta_star[row] = Bst;
     a.eps_hat[row] = ehat;
     a.certified[row] = cert ? 1 : 0;
-    if (cert) a.kstar[row] = 0;
   }
-  if (cert) return;
+  if (cert) return;                                    // kstar was cleared before the kernel
 
   // ---- eqs. (9)-(10): MSD search for the k* cut over the bits of g
   const double thr = eps * Dd;
@@ -266,6 +352,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   uint32_t plo = 0;
   int lev = -1;
   bool above_mode = false;                               // cut above the whole window
+  const int64_t hrow = (int64_t)row * T * NBUCKET;
+  const int64_t mrow = (int64_t)row * NBUCKET;
 #define KEY_OF(wi, ri, x, key, lo)                                             \
   const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));                \
   const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));              \
@@ -286,6 +374,30 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         atomicMax((unsigned long long *)&h_b[dig], (unsigned long long)dbits(x.b));
       })
     __syncthreads();
+    if (T > 1) {
+      // publish this member's histogram, merge a bucket range, read the merged one
+      const int64_t hm = hrow + (int64_t)m * NBUCKET;
+      for (int k = tid; k < NBUCKET; k += DC_NT) {
+        a.hcnt[hm + k] = h_cnt[k]; a.hbeta[hm + k] = h_beta[k]; a.hV[hm + k] = h_V[k]; a.hmax[hm + k] = h_b[k];
+      }
+      TEAM_SYNC();
+      const int k0 = m * NBUCKET / T, k1 = (m + 1) * NBUCKET / T;
+      for (int k = k0 + tid; k < k1; k += DC_NT) {
+        uint32_t c = 0; double sb = 0.0, sv = 0.0; uint64_t mb = 0;
+        for (int q = 0; q < T; ++q) {
+          const int64_t o = hrow + (int64_t)q * NBUCKET + k;
+          c += a.hcnt[o]; sb += a.hbeta[o]; sv += a.hV[o];
+          const uint64_t x = a.hmax[o];
+          mb = x > mb ? x : mb;
+        }
+        a.mcnt[mrow + k] = c; a.mbeta[mrow + k] = sb; a.mV[mrow + k] = sv; a.mmax[mrow + k] = mb;
+      }
+      TEAM_SYNC();
+      for (int k = tid; k < NBUCKET; k += DC_NT) {
+        h_cnt[k] = a.mcnt[mrow + k]; h_beta[k] = a.mbeta[mrow + k]; h_V[k] = a.mV[mrow + k]; h_b[k] = a.mmax[mrow + k];
+      }
+      __syncthreads();
+    }
     // inclusive scan over buckets (thread k owns bucket k): beta, V sums and max b
     double sb = h_beta[tid], sv = h_V[tid], smx = bitsd(h_b[tid]);
     const uint32_t mycnt = h_cnt[tid];
@@ -298,7 +410,6 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       h_beta[tid] = sb; h_V[tid] = sv; h_b[tid] = dbits(smx);
       __syncthreads();
     }
-    // h_* now hold inclusive prefixes; ensure the initial values are loaded before overwrite
     if (tid == 0) s_int[0] = INT32_MAX;
     __syncthreads();
     const bool below_fails = bern_E(bel_beta, bel_V, bel_b, l) >= thr;
@@ -308,7 +419,6 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     __syncthreads();
     const int j = s_int[0];
     if (j == INT32_MAX) { above_mode = true; break; }
-    // exclusive prefix of bucket j
     const double eb = j > 0 ? h_beta[j - 1] : 0.0;
     const double ev = j > 0 ? h_V[j - 1] : 0.0;
     const double em = j > 0 ? bitsd(h_b[j - 1]) : 0.0;
@@ -329,20 +439,39 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   uint32_t tlo = 0;
   if (!above_mode) {
     if (tid == 0) s_int[1] = 0;
-    for (int k = tid; k < WIN; k += DC_NT) { w_key[k] = ~0ull; w_lo[k] = ~0u; w_slot[k] = k; }
+    for (int k = tid; k < WIN; k += DC_NT) { w_key[k] = ~0ull; w_lo[k] = ~0u; }
     __syncthreads();
+    uint64_t *gkey = a.wkey + (int64_t)row * WIN;
+    uint32_t *glo = a.wlo + (int64_t)row * WIN;
     Red4 bel{0.0, 0.0, 0.0, 0.0};
     FOR_L(
       KEY_OF(wi, ri, x, key, lo)
       const int cw = cmp_window(key, lo, lev, pkey, plo);
       if (cw < 0) { bel.s0 += x.beta; bel.s1 += x.V; bel.mx = fmax(bel.mx, x.b); }
       else if (cw == 0) {
-        const int p = atomicAdd(&s_int[1], 1);
-        if (p < WIN) { w_key[p] = key; w_lo[p] = lo; }
+        if (T > 1) {
+          const uint32_t p = atomicAdd(&a.wcount[row], 1u);
+          if (p < (uint32_t)WIN) { gkey[p] = key; glo[p] = lo; }
+        } else {
+          const int p = atomicAdd(&s_int[1], 1);
+          if (p < WIN) { w_key[p] = key; w_lo[p] = lo; }
+        }
       })
-    const Red4 bo = block_red4(bel, scr);
-    const int wcount = min(s_int[1], WIN);
-    // bitonic sort of (key, lo) ascending over WIN slots; w_slot follows
+    Red4 bo = block_red4(bel, scr);
+    int wcount;
+    if (T > 1) {
+      double *sl = SLOT();
+      if (tid == 0) { sl[m * 8] = bo.s0; sl[m * 8 + 1] = bo.s1; sl[m * 8 + 2] = bo.mx; }
+      TEAM_SYNC();
+      bo = Red4{0.0, 0.0, 0.0, 0.0};
+      for (int k = 0; k < T; ++k) { bo.s0 += sl[k * 8]; bo.s1 += sl[k * 8 + 1]; bo.mx = fmax(bo.mx, sl[k * 8 + 2]); }
+      wcount = min((int)__hip_atomic_load(&a.wcount[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), WIN);
+      for (int k = tid; k < wcount; k += DC_NT) { w_key[k] = gkey[k]; w_lo[k] = glo[k]; }
+      __syncthreads();
+    } else {
+      wcount = min(s_int[1], WIN);
+    }
+    // bitonic sort of (key, lo) ascending over WIN slots
     for (int k2 = 2; k2 <= WIN; k2 <<= 1) {
       for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
         const int p = tid ^ j2;
@@ -359,7 +488,6 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         __syncthreads();
       }
     }
-    // terms of the sorted window members (token = IDX_MAX - lo)
     double tb = 0.0, tv = 0.0, tm = 0.0;
     if (tid < wcount) {
       const int i = (int)(IDX_MAX - w_lo[tid]);
@@ -368,7 +496,6 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
       tb = x.beta; tv = x.V; tm = x.b;
     }
-    // inclusive scan in sorted order (reuse the bucket arrays)
     h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
     __syncthreads();
     for (int off = 1; off < WIN; off <<= 1) {
@@ -404,12 +531,18 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     else inF = (key > tkey) || (key == tkey && lo >= tlo);
     if (inF) { atomicOr(&fb[i >> 5], 1u << (i & 31)); ++kc; })
   const int64_t ks = block_sum_i64<DC_NT>(kc, (int64_t *)scr);
-  if (tid == 0) a.kstar[row] = (int32_t)ks;
+  if (tid == 0 && ks) atomicAdd(&a.kstar[row], (int32_t)ks);
 #undef KEY_OF
 #undef FOR_L
+#undef TEAM_SYNC
+#undef SLOT
 }
 
 // ------------------------------------------------------------------ union, lists, pivot coefficients
+// Block 0 of a KV head compacts its fetch bitmask into the ascending list F and the
+// list F \ S of host rows; the other blocks give every resident pivot its estimator
+// coefficient for every query row of the group: 1 on H and on S n F, lambda_i / r_i
+// on S \ F (Definition 2 with the fetched tokens exact).
 constexpr int UN_NT = 1024;
 
 __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
@@ -422,71 +555,100 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
   const int Hq = a.t.Hkv * G;
   const int tid = threadIdx.x;
   const uint32_t *fb = a.fbits + word_base(a.t, b, g);
-  const uint32_t *res = a.resident + word_base(a.t, b, g);
-  const int W = words_of(n);
-  const int wpt = (W + UN_NT - 1) / UN_NT;
-  const int w0 = tid * wpt, w1 = min(W, w0 + wpt);
-  int32_t cf = 0, ch = 0;
-  for (int w = w0; w < w1; ++w) { cf += __popc(fb[w]); ch += __popc(fb[w] & ~res[w]); }
-  int32_t tf, th;
-  int32_t pf = block_excl_scan<UN_NT>(cf, iscr, &tf);
-  int32_t ph = block_excl_scan<UN_NT>(ch, iscr, &th);
-  int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
-  int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = fb[w];
-    const uint32_t rw = res[w];
-    while (bits) {
-      const int j = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int tok = 32 * w + j;
-      if (fl && pf < a.fetch_cap) fl[pf] = tok;
-      ++pf;
-      if (!((rw >> j) & 1)) hl[ph++] = tok;
-    }
-  }
-  if (tid == 0) {
-    a.fetch_count[unit] = tf;
-    a.h2d_count[unit] = th;
-  }
-  // coefficients of the resident pivots: 1 on H and on S n F, lambda_i / r_i on S \ F
-  const int cnt = min(a.piv_count[unit], a.cap);
-  const int32_t *pidx = a.piv_idx + (int64_t)unit * a.cap;
-  const double *rr = a.r + tok_base(a.t, b, g);
-  for (int p = tid; p < cnt; p += UN_NT) {
-    const int tok = pidx[p];
-    const double ri = rr[tok];
-    const bool exact = (ri >= 1.0) || ((fb[tok >> 5] >> (tok & 31)) & 1);
-    for (int j = 0; j < G; ++j) {
-      const int h = g * G + j;
-      float cf32 = 1.0f;
-      if (!exact) {
-        const double wi = a.wc[row_tok_base(a.t, b, h) + tok] *
-                          a.cscale[row_chunk_base(a.t, b, h) + tok / SKETCH_CHUNK];
-        const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], a.kappa);
-        cf32 = (float)(lam / ri);
+  if (blockIdx.y == 0) {
+    const uint32_t *res = a.resident + word_base(a.t, b, g);
+    const int W = words_of(n);
+    const int wpt = (W + UN_NT - 1) / UN_NT;
+    const int w0 = tid * wpt, w1 = min(W, w0 + wpt);
+    int32_t cf = 0, ch = 0;
+    for (int w = w0; w < w1; ++w) { cf += __popc(fb[w]); ch += __popc(fb[w] & ~res[w]); }
+    int32_t tf, th;
+    int32_t pf = block_excl_scan<UN_NT>(cf, iscr, &tf);
+    int32_t ph = block_excl_scan<UN_NT>(ch, iscr, &th);
+    int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
+    int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = fb[w];
+      const uint32_t rw = res[w];
+      while (bits) {
+        const int j = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int tok = 32 * w + j;
+        if (fl && pf < a.fetch_cap) fl[pf] = tok;
+        ++pf;
+        if (!((rw >> j) & 1)) hl[ph++] = tok;
       }
-      a.coef[((int64_t)b * Hq + h) * a.cap + p] = cf32;
     }
+    if (tid == 0) {
+      a.fetch_count[unit] = tf;
+      a.h2d_count[unit] = th;
+    }
+    return;
+  }
+  const int cnt = min(a.piv_count[unit], a.cap);
+  const int p = (blockIdx.y - 1) * UN_NT + tid;
+  if (p >= cnt) return;
+  const int tok = a.piv_idx[(int64_t)unit * a.cap + p];
+  const double ri = a.r[tok_base(a.t, b, g) + tok];
+  const bool exact = (ri >= 1.0) || ((fb[tok >> 5] >> (tok & 31)) & 1);
+  for (int j = 0; j < G; ++j) {
+    const int h = g * G + j;
+    float cf32 = 1.0f;
+    if (!exact) {
+      const double wi = a.wc[row_tok_base(a.t, b, h) + tok] *
+                        a.cscale[row_chunk_base(a.t, b, h) + tok / SKETCH_CHUNK];
+      const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], a.kappa);
+      cf32 = (float)(lam / ri);
+    }
+    a.coef[((int64_t)b * Hq + h) * a.cap + p] = cf32;
   }
 }
 
-hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_decide, dim3(rows), dim3(DC_NT), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
-  hipLaunchKernelGGL(k_union, dim3(units), dim3(UN_NT), 0, st, a);
-  return hipGetLastError();
+// ------------------------------------------------------------------ eps_hat(L \ F)
+// Partial certificate terms of the tokens that stay sampled, per (row, slice); the
+// finishing kernel combines the slices in order (Lemma 1 on L \ F, lambda frozen).
+__global__ __launch_bounds__(DC_NT) void k_after(AfterArgs a) {
+  __shared__ double scr[4 * DC_NW];
+  const int T = a.team;
+  const int row = blockIdx.x / T;
+  const int m = blockIdx.x % T;
+  const int Hq = a.t.Hkv * a.t.G;
+  const int b = row / Hq;
+  const int h = row % Hq;
+  const int g = h / a.t.G;
+  const int n = a.t.s[b].n;
+  const int s0 = (int)((int64_t)n * m / T);
+  const int s1 = (int)((int64_t)n * (m + 1) / T);
+  const double *wcr = a.wc + row_tok_base(a.t, b, h);
+  const double *sc = a.cscale + row_chunk_base(a.t, b, h);
+  const double *rr = a.r + tok_base(a.t, b, g);
+  const uint32_t *fb = a.fbits + word_base(a.t, b, g);
+  const double Bst = a.beta_star[row];
+  const double kappa = a.params[0];
+  Cert c{0.0, 0.0, 0.0, 0.0};
+  int cnt = 0;
+  for (int i = s0 + threadIdx.x; i < s1; i += DC_NT) {
+    const double ri = rr[i];
+    if (!(ri < 1.0)) continue;
+    if ((fb[i >> 5] >> (i & 31)) & 1) continue;
+    const double wi = wcr[i] * sc[i / SKETCH_CHUNK];
+    const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+    c.beta += x.beta; c.V += x.V; ++cnt;
+    top2_merge(c.b1, c.b2, x.b, 0.0);
+  }
+  const Cert o = block_cert(c, scr);
+  const double tot = block_sum<DC_NT>((double)cnt, scr);
+  if (threadIdx.x == 0) {
+    double *p = a.part + ((int64_t)row * T + m) * 8;
+    p[0] = o.beta; p[1] = o.V; p[2] = o.b1; p[3] = o.b2; p[4] = tot;
+  }
 }
 
 // ------------------------------------------------------------------ finish a row
 // N_hat and D_hat are the fixed-order sums of the partials of the resident pivots and
-// of the host rows; o = N_hat / D_hat, lse = m_hat + ln D_hat; eps_after = eps_hat(L \ F)
-// with lambda frozen (Lemma 1 on the tokens that remain sampled).
-__global__ __launch_bounds__(DC_NT) void k_finish(FinishArgs a) {
-  __shared__ double scr[4 * DC_NW];
+// of the host rows; o = N_hat / D_hat, lse = m_hat + ln D_hat; eps_after combines the
+// slices of k_after.
+__global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
   __shared__ float s_d;
   const int row = blockIdx.x;
   const int Hq = a.t.Hkv * a.t.G;
@@ -513,33 +675,47 @@ __global__ __launch_bounds__(DC_NT) void k_finish(FinishArgs a) {
   } else if (tid == D) {
     a.d_hat[row] = dh;
     a.lse[row] = (float)(a.m_hat[row] + log((double)dh));
+  } else if (tid == D + 1) {
+    Cert c{0.0, 0.0, 0.0, 0.0};
+    double tot = 0.0;
+    for (int k = 0; k < a.team; ++k) {
+      const double *p = a.after_part + ((int64_t)row * a.team + k) * 8;
+      c = cert_combine(c, Cert{p[0], p[1], p[2], p[3]});
+      tot += p[4];
+    }
+    a.eps_after[row] = tot > 0.0 ? bern_E(c.beta, c.V, c.b1, a.params[1]) / a.d_sketch[row] : 0.0;
   }
+}
 
-  const int n = a.t.s[b].n;
-  const double *wcr = a.wc + row_tok_base(a.t, b, h);
-  const double *sc = a.cscale + row_chunk_base(a.t, b, h);
-  const double *rr = a.r + tok_base(a.t, b, g);
-  const uint32_t *fb = a.fbits + word_base(a.t, b, g);
-  const double Bst = a.beta_star[row];
-  const double kappa = a.params[0], l = a.params[1];
-  Cert c{0.0, 0.0, 0.0, 0.0};
-  int cnt = 0;
-  for (int i = tid; i < n; i += DC_NT) {
-    const double ri = rr[i];
-    if (!(ri < 1.0)) continue;
-    if ((fb[i >> 5] >> (i & 31)) & 1) continue;
-    const double wi = wcr[i] * sc[i / SKETCH_CHUNK];
-    const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
-    c.beta += x.beta; c.V += x.V; ++cnt;
-    top2_merge(c.b1, c.b2, x.b, 0.0);
+hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st) {
+  const dim3 grid(rows * a.team), block(DC_NT);
+  if (a.team > 1) {
+    void *args[] = {const_cast<DecideArgs *>(&a)};
+    return hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, 0, st);
   }
-  const Cert o = block_cert(c, scr);
-  const double tot = block_sum<DC_NT>((double)cnt, scr);
-  if (tid == 0) a.eps_after[row] = tot > 0.0 ? bern_E(o.beta, o.V, o.b1, l) / a.d_sketch[row] : 0.0;
+  hipLaunchKernelGGL(k_decide, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+int decide_blocks_per_cu() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decide, DC_NT, 0) != hipSuccess) return 1;
+  return nb > 0 ? nb : 1;
+}
+
+hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
+  const int ncoef = (a.cap + UN_NT - 1) / UN_NT;
+  hipLaunchKernelGGL(k_union, dim3(units, 1 + ncoef), dim3(UN_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_after, dim3(rows * a.team), dim3(DC_NT), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_finish, dim3(rows), dim3(DC_NT), 0, st, a);
+  hipLaunchKernelGGL(k_finish, dim3(rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -64,10 +64,17 @@ __global__ __launch_bounds__(SketchCfg<BF16>::NT) void k_sketch(SketchArgs a) {
   const int grp = lane / LPT;               // which of the TPW rows of an instruction
   const int d0 = sub * EPL;
 
-  // clear this chunk's words of the fetch bitmask (SKETCH_CHUNK / 32 words)
+  // clear this chunk's words of the fetch bitmask (SKETCH_CHUNK / 32 words), and on
+  // chunk 0 the per-row counters of the decision kernel for the G rows of this head
   if (threadIdx.x < SKETCH_CHUNK / 32) {
     const int w = c * (SKETCH_CHUNK / 32) + threadIdx.x;
     if (w < words_of(n)) a.fbits[word_base(a.t, b, g) + w] = 0u;
+  }
+  if (c == 0 && threadIdx.x < G) {
+    const int64_t row = (int64_t)b * a.t.Hkv * G + g * G + threadIdx.x;
+    a.bar[row] = 0u;
+    a.wcount[row] = 0u;
+    a.kstar[row] = 0;
   }
 
   // query slices in float64

@@ -37,6 +37,8 @@ struct SketchArgs {
   double *wc;                 // [B][Hq][n]
   double2 *cstat;             // [B][Hq][nchunks]  (m_c, sum_c)
   uint32_t *fbits;            // [B][Hkv][W]  cleared here
+  uint32_t *bar, *wcount;     // [B][Hq] decision-kernel counters, cleared here
+  int32_t *kstar;             // [B][Hq] cleared here
   int32_t total_blocks;
 };
 
@@ -53,6 +55,30 @@ struct DecideArgs {
   int32_t *kstar;
   int32_t *status;
   double *params;            // out: kappa, l of this step (read by the finish kernel)
+  // team workspace (T workgroups per row)
+  int32_t team;
+  int32_t xcd_map;           // 1: map the members of a team to one XCD
+  uint32_t *bar;             // [rows] barrier counters (cleared by the sketch kernel)
+  double *part;              // [rows][2][T][8] member partials
+  uint32_t *hcnt;            // [rows][T][NBUCKET] member histograms
+  double *hbeta, *hV;
+  uint64_t *hmax;
+  uint32_t *mcnt;            // [rows][NBUCKET] merged histograms
+  double *mbeta, *mV;
+  uint64_t *mmax;
+  uint64_t *wkey;            // [rows][WIN] final window
+  uint32_t *wlo;
+  uint32_t *wcount;          // [rows] (cleared by the sketch kernel)
+};
+
+struct AfterArgs {
+  SeqTable t;
+  const double *wc, *cscale, *r;
+  const uint32_t *fbits;
+  const double *beta_star;
+  const double *params;      // kappa, l written by the decision kernel
+  int32_t team;
+  double *part;              // [rows][T][8]
 };
 
 struct UnionArgs {
@@ -82,6 +108,8 @@ struct AttendArgs {
   int32_t cap;
   float *part;               // [B][Hkv][nsplit][G][129]
   int32_t nsplit;
+  const double *wc;          // host source with exact sketch: weights w_hat = wc * cscale
+  const double *cscale;
 };
 
 struct FinishArgs {
@@ -94,10 +122,14 @@ struct FinishArgs {
   const uint32_t *fbits;
   const double *m_hat, *d_sketch, *beta_star;
   const double *params;      // kappa, l written by the decision kernel
+  const double *after_part;  // [rows][T][8] from k_after
+  int32_t team;
   double *eps_after;
   float *n_hat, *d_hat, *o, *lse;
 };
 
+constexpr int NBUCKET = 1024;    // digit buckets of the k* search
+constexpr int WIN = 1024;        // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
 constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets nsp)
 
@@ -106,7 +138,10 @@ hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st);
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);
-hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, hipStream_t st);
+hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, bool exact,
+                         hipStream_t st);
+hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st);
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
+int decide_blocks_per_cu();
 
 }  // namespace verkv

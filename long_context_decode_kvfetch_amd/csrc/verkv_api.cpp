@@ -81,19 +81,49 @@ int row_bytes(const verkv_shape *s) { return VERKV_HEAD_DIM * (s->kv_dtype == VE
 int host_splits(int units) { return std::max(4, std::min(64, 512 / std::max(1, units))); }
 int pivot_splits(int cap) { return std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS); }
 
+// Workgroups per query row in the decision kernel, as sized in the workspace: enough
+// to cover 256 CUs with one workgroup each, at least 4096 tokens per workgroup, at
+// most 16.  At launch it is lowered further if fewer workgroups can be co-resident.
+constexpr int TEAM_MAX = 16;
+int team_size(int rows, int max_n) {
+  const int by_cu = 256 / std::max(1, rows);
+  const int by_len = (max_n + 4095) / 4096;
+  return std::max(1, std::min(TEAM_MAX, std::min(by_cu, by_len)));
+}
+
 // Decode workspace layout.
 struct DecodeWs {
-  size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status, total;
-  int nsp, nsh;
+  size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
+  size_t bar, wcount, part, hcnt, hbeta, hV, hmax, mcnt, mbeta, mV, mmax, wkey, wlo, apart;
+  size_t total;
+  int nsp, nsh, team;
 };
 DecodeWs decode_layout(const SeqTable &t, int cap) {
   const Totals T = totals(t);
   const int64_t Hq = (int64_t)t.Hkv * t.G;
   const int units = t.B * t.Hkv;
+  const int64_t rows = (int64_t)units * t.G;
   DecodeWs w;
   w.nsp = pivot_splits(cap);
   w.nsh = host_splits(units);
+  w.team = team_size((int)rows, t.max_n);
+  const int64_t tm = w.team > 1 ? w.team : 0;       // member histograms only for teams
   size_t off = 0;
+  w.bar = off;    off = align_up(off + 4 * (size_t)rows);
+  w.wcount = off; off = align_up(off + 4 * (size_t)rows);
+  w.part = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team * 8));
+  w.apart = off;  off = align_up(off + 8 * (size_t)(rows * w.team * 8));
+  w.hcnt = off;   off = align_up(off + 4 * (size_t)(rows * tm * NBUCKET));
+  w.hbeta = off;  off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
+  w.hV = off;     off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
+  w.hmax = off;   off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
+  const int64_t mm = w.team > 1 ? 1 : 0;
+  w.mcnt = off;   off = align_up(off + 4 * (size_t)(rows * mm * NBUCKET));
+  w.mbeta = off;  off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
+  w.mV = off;     off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
+  w.mmax = off;   off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
+  w.wkey = off;   off = align_up(off + 8 * (size_t)(rows * mm * WIN));
+  w.wlo = off;    off = align_up(off + 4 * (size_t)(rows * mm * WIN));
   w.wc = off;     off = align_up(off + 8 * (size_t)(Hq * T.tok));
   w.cstat = off;  off = align_up(off + 16 * (size_t)(Hq * T.chunks));
   w.cscale = off; off = align_up(off + 8 * (size_t)(Hq * T.chunks));
@@ -151,8 +181,24 @@ verkv_status device_view(const void *p, const void **out) {
   return VERKV_EINVAL;
 }
 
+// Co-resident decision workgroups on the current device (cached per device).
+int decide_capacity() {
+  static int cache[64];
+  static bool init[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!init[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    cache[dev] = cus * decide_blocks_per_cu();
+    init[dev] = true;
+  }
+  return cache[dev];
+}
+
 // ---------------------------------------------------------------- optional kernel timing
-enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_COUNT };
+enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -180,7 +226,7 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 100; }
+int32_t verkv_version(void) { return 102; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -323,6 +369,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.wc = reinterpret_cast<double *>(ws + L.wc);
   sk.cstat = reinterpret_cast<double2 *>(ws + L.cstat);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
+  sk.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
+  sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
+  sk.kstar = out->kstar;
   sk.total_blocks = (int32_t)(t.Hkv * T.chunks);
   {
     Timed tm(K_SKETCH, stream);
@@ -347,6 +396,23 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.kstar = out->kstar;
   dc.status = reinterpret_cast<int32_t *>(ws + L.status);
   dc.params = reinterpret_cast<double *>(ws + L.status + 32);
+  int team = L.team;
+  if (team > 1) team = std::max(1, std::min(team, decide_capacity() / rows));
+  dc.team = team;
+  dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;
+  dc.bar = sk.bar;
+  dc.part = reinterpret_cast<double *>(ws + L.part);
+  dc.hcnt = reinterpret_cast<uint32_t *>(ws + L.hcnt);
+  dc.hbeta = reinterpret_cast<double *>(ws + L.hbeta);
+  dc.hV = reinterpret_cast<double *>(ws + L.hV);
+  dc.hmax = reinterpret_cast<uint64_t *>(ws + L.hmax);
+  dc.mcnt = reinterpret_cast<uint32_t *>(ws + L.mcnt);
+  dc.mbeta = reinterpret_cast<double *>(ws + L.mbeta);
+  dc.mV = reinterpret_cast<double *>(ws + L.mV);
+  dc.mmax = reinterpret_cast<uint64_t *>(ws + L.mmax);
+  dc.wkey = reinterpret_cast<uint64_t *>(ws + L.wkey);
+  dc.wlo = reinterpret_cast<uint32_t *>(ws + L.wlo);
+  dc.wcount = sk.wcount;
   {
     Timed tm(K_DECIDE, stream);
     HIP_TRY(launch_decide(dc, rows, stream), "decide launch");
@@ -388,9 +454,11 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   at.cap = st->cap;
   at.part = reinterpret_cast<float *>(ws + L.ppart);
   at.nsplit = L.nsp;
+  at.wc = nullptr;
+  at.cscale = nullptr;
   {
     Timed tm(K_PIVOT, stream);
-    HIP_TRY(launch_attend(at, units, bf16, false, stream), "pivot attention launch");
+    HIP_TRY(launch_attend(at, units, bf16, false, false, stream), "pivot attention launch");
   }
   return VERKV_OK;
 }
@@ -428,9 +496,27 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   at.cap = st->cap;
   at.part = reinterpret_cast<float *>(ws + L.hpart);
   at.nsplit = L.nsh;
+  at.wc = reinterpret_cast<const double *>(ws + L.wc);
+  at.cscale = reinterpret_cast<const double *>(ws + L.cscale);
   {
     Timed tm(K_HOST, stream);
-    HIP_TRY(launch_attend(at, units, bf16, true, stream), "host attention launch");
+    HIP_TRY(launch_attend(at, units, bf16, true, st->sketch_exact != 0, stream),
+            "host attention launch");
+  }
+
+  AfterArgs af;
+  af.t = t;
+  af.wc = reinterpret_cast<const double *>(ws + L.wc);
+  af.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  af.r = st->r;
+  af.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  af.beta_star = out->beta_star;
+  af.params = reinterpret_cast<const double *>(ws + L.status + 32);
+  af.team = L.team;
+  af.part = reinterpret_cast<double *>(ws + L.apart);
+  {
+    Timed tm(K_AFTER, stream);
+    HIP_TRY(launch_after(af, rows, stream), "eps_after launch");
   }
 
   FinishArgs fi;
@@ -447,6 +533,8 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   fi.d_sketch = out->d_sketch;
   fi.beta_star = out->beta_star;
   fi.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa, l of the step
+  fi.after_part = af.part;
+  fi.team = L.team;
   fi.eps_after = out->eps_after;
   fi.n_hat = out->n_hat;
   fi.d_hat = out->d_hat;
@@ -458,6 +546,27 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   }
   (void)rows;
   return VERKV_OK;
+}
+
+verkv_status verkv_check(void *workspace, const verkv_shape *s, int32_t cap, verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!workspace || cap < 1) return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, cap);
+  int32_t *status = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + L.status);
+  int32_t h = 0;
+  HIP_TRY(hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, stream), "hipMemcpyAsync");
+  HIP_TRY(hipStreamSynchronize(stream), "hipStreamSynchronize");
+  if (h == 0) return VERKV_OK;
+  const int32_t zero = 0;
+  HIP_TRY(hipMemcpyAsync(status, &zero, sizeof(zero), hipMemcpyHostToDevice, stream), "hipMemcpyAsync");
+  HIP_TRY(hipStreamSynchronize(stream), "hipStreamSynchronize");
+  std::snprintf(g_last_error, sizeof(g_last_error), "kernel flags 0x%x:%s%s", h,
+                (h & 4) ? " team barrier timed out;" : "",
+                (h & 2) ? " fixed point did not converge;" : "");
+  return VERKV_EHIP;
 }
 
 int32_t verkv_profile_begin(int32_t max_launches) {

@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 8
+PROFILE_KINDS = 9
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
-                "attend_pivots", "attend_host", "finish"]
+                "attend_pivots", "attend_host", "finish", "eps_after"]
 
 
 class VerKVError(RuntimeError):
@@ -44,7 +44,7 @@ class Shape(C.Structure):
 class State(C.Structure):
     _fields_ = [("r", C.c_void_p), ("resident", C.c_void_p), ("piv_idx", C.c_void_p),
                 ("piv_count", C.c_void_p), ("piv_k", C.c_void_p), ("piv_v", C.c_void_p),
-                ("cap", C.c_int32), ("sketch", C.c_void_p)]
+                ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32)]
 
 
 class StepOut(C.Structure):
@@ -87,6 +87,8 @@ def _lib():
         lib.verkv_profile_report.restype = i32
         lib.verkv_profile_report.argtypes = [C.POINTER(C.c_double), C.POINTER(i32), i32]
         lib.verkv_profile_end.restype = None
+        lib.verkv_check.restype = i32
+        lib.verkv_check.argtypes = [vp, C.POINTER(Shape), i32, vp]
         _LIB = lib
     return _LIB
 
@@ -165,7 +167,8 @@ def default_cap(shape: LayerShape, eta: float) -> int:
 class LayerState:
     """GPU-resident compressed state of one layer (caller-owned torch buffers)."""
 
-    def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda"):
+    def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda",
+                 sketch_exact: bool = True):
         hkv, tot = shape.n_kv_heads, shape.total_tokens
         words = sum((n + 31) // 32 for n in shape.seq_lens)
         units = shape.batch * hkv
@@ -179,7 +182,8 @@ class LayerState:
         self.piv_v = torch.empty(units * cap * HEAD_DIM, dtype=shape.torch_dtype, device=device)
         self.sketch = sketch
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
-                       _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch))
+                       _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch),
+                       1 if sketch_exact else 0)
 
 
 class StepBuffers:
@@ -252,6 +256,12 @@ def refine(shape: LayerShape, state: LayerState, q: torch.Tensor, K_host: torch.
            "verkv_refine")
 
 
+def check(shape: LayerShape, cap: int, workspace: torch.Tensor, stream=None) -> None:
+    """verkv_check: synchronise and raise if the kernels flagged a problem."""
+    _check(_lib().verkv_check(_ptr(workspace), C.byref(shape.c), int(cap), _stream(stream)),
+           "verkv_check")
+
+
 def profile_begin(max_launches: int) -> None:
     _check(_lib().verkv_profile_begin(int(max_launches)), "verkv_profile_begin")
 
@@ -269,4 +279,4 @@ def profile_end() -> None:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)

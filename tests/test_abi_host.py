@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(vk):
 
 def test_version_and_status_strings(vk):
     lib = vk.lib()
-    assert lib.verkv_version() == 100
+    assert lib.verkv_version() == 101
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.verkv_status_str(st).decode() not in ("", "unknown status")
     assert lib.verkv_status_str(7).decode() == "unknown status"
@@ -71,7 +71,7 @@ FAKE = 4096      # a non-null pointer value the host checks never dereference
 
 
 def _fake_state(vk, cap=640):
-    return vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap, FAKE)
+    return vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap, FAKE, 1)
 
 
 def _fake_out(vk):
@@ -102,7 +102,7 @@ def test_decode_step_rejects_bad_arguments_on_host(vk):
     assert call(shape=_shape(vk, lens=(0,))) == vk.EINVAL
     assert call(shape=_shape(vk, lens=((1 << 20) + 1,))) == vk.EUNSUPPORTED
     assert call(state=_fake_state(vk, cap=0)) == vk.EINVAL
-    nostate = vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 640, 0)     # no sketch
+    nostate = vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 640, 0, 1)  # no sketch
     assert call(state=nostate) == vk.EINVAL
     assert lib.verkv_decode_step(None, C.byref(st), FAKE, 1.0, 0.05, 0.05, C.byref(out), FAKE,
                                  big, None) == vk.EINVAL

@@ -35,6 +35,8 @@ def _run(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, **kw):
         q = sess.queries(st)
         say(f"[parity] {label}: step {st}")
         sess.step(q, kappa=kappa, eps=eps, delta=delta)
+        from long_context_decode_kvfetch_amd import verkv
+        verkv.check(sess.shape, sess.cap, sess.dws)
         oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta)
         summ.append(compare_step(sess, wl, ocomp, oo, st, kappa=kappa, eps=eps, delta=delta))
     say(f"[parity] {label}: {summ}")
@@ -115,3 +117,16 @@ def test_deterministic_repeat():
                 assert np.array_equal(x, y)
         else:
             assert np.array_equal(a[k], b[k]), k
+
+
+def test_host_fetch_reads_keys_when_sketch_not_exact():
+    """With sketch_exact = 0 the refinement scores the fetched rows from the host keys."""
+    _run(synth.single_head(5, n=4096), label="single-head, K from host", sketch_exact=False)
+    _run(synth.gqa_layer(seed=6, n=8192, steps=1, hkv=2), label="gqa, K from host",
+         sketch_exact=False)
+
+
+def test_long_context_131k_eta_1_32():
+    """n = 131072, eta = 1/32 (the long-context shape), two KV heads, full length."""
+    _run(synth.gqa_layer(seed=7, n=131072, steps=1, hkv=2, eta=1.0 / 32, eps=0.1),
+         label="131k")
