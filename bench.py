@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--profile-steps", type=int, default=64)
     p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a 256 MiB elementwise copy kernel (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -121,6 +123,16 @@ def main():
         sess = sessions[step_index % L]
         sess.step(sess.qdev[(step_index // L) % per_layer])
         return sess
+
+    if args.calib_copy:
+        # a kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE: reads and
+        # writes 256 MiB once per launch
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(W):
         run(i)

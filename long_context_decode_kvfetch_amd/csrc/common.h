@@ -109,45 +109,65 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Block-wide reductions in a fixed order (deterministic).  `scratch` must hold one
-// entry per wave; every thread receives the result.  Ends with a barrier so the
+__device__ __forceinline__ double max16(double v) {
+  v = fmax(v, dpp_d<DPP_XOR1>(v));
+  v = fmax(v, dpp_d<DPP_XOR2>(v));
+  v = fmax(v, dpp_d<DPP_HALF_MIRROR>(v));
+  v = fmax(v, dpp_d<DPP_MIRROR>(v));
+  return v;
+}
+__device__ __forceinline__ double min16(double v) {
+  v = fmin(v, dpp_d<DPP_XOR1>(v));
+  v = fmin(v, dpp_d<DPP_XOR2>(v));
+  v = fmin(v, dpp_d<DPP_HALF_MIRROR>(v));
+  v = fmin(v, dpp_d<DPP_MIRROR>(v));
+  return v;
+}
+
+// Block-wide reductions in a fixed order (deterministic): each wave reduces, lane k of
+// every wave then reads wave k's partial and a 16-lane butterfly finishes, so every
+// thread holds the same result and only one partial per quantity is live per lane.
+// `scratch` holds one entry per wave (at most 16 waves).  Ends with a barrier so the
 // scratch may be reused immediately.
 template <int NT>
 __device__ __forceinline__ double block_sum(double v, double *scratch) {
   constexpr int NW = NT / WAVE;
+  static_assert(NW <= 16, "at most 16 waves");
   v = wave_sum(v);
-  const int w = threadIdx.x / WAVE;
-  if ((threadIdx.x & (WAVE - 1)) == 0) scratch[w] = v;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) scratch[threadIdx.x / WAVE] = v;
   __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) t += scratch[i];
+  const int k = lane & 15;
+  double t = k < NW ? scratch[k] : 0.0;
+  t = sum16(t);
   __syncthreads();
   return t;
 }
 template <int NT>
 __device__ __forceinline__ double block_max(double v, double *scratch) {
   constexpr int NW = NT / WAVE;
+  static_assert(NW <= 16, "at most 16 waves");
   v = wave_max(v);
-  const int w = threadIdx.x / WAVE;
-  if ((threadIdx.x & (WAVE - 1)) == 0) scratch[w] = v;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) scratch[threadIdx.x / WAVE] = v;
   __syncthreads();
-  double t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) t = fmax(t, scratch[i]);
+  const int k = lane & 15;
+  double t = k < NW ? scratch[k] : -INFINITY;
+  t = max16(t);
   __syncthreads();
   return t;
 }
 template <int NT>
 __device__ __forceinline__ double block_min(double v, double *scratch) {
   constexpr int NW = NT / WAVE;
+  static_assert(NW <= 16, "at most 16 waves");
   v = wave_min(v);
-  const int w = threadIdx.x / WAVE;
-  if ((threadIdx.x & (WAVE - 1)) == 0) scratch[w] = v;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) scratch[threadIdx.x / WAVE] = v;
   __syncthreads();
-  double t = scratch[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) t = fmin(t, scratch[i]);
+  const int k = lane & 15;
+  double t = k < NW ? scratch[k] : INFINITY;
+  t = min16(t);
   __syncthreads();
   return t;
 }
@@ -159,7 +179,7 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t *scratch) {
   if ((threadIdx.x & (WAVE - 1)) == 0) scratch[w] = v;
   __syncthreads();
   int64_t t = 0;
-#pragma unroll
+#pragma unroll 1
   for (int i = 0; i < NW; ++i) t += scratch[i];
   __syncthreads();
   return t;

@@ -12,16 +12,16 @@
 //     set is the k* tokens of largest g (ties: lower token index first) where k* is
 //     the least k with eps_hat(L_g[k:]) < eps.
 // The k* cut is found without sorting L: a most-significant-digit search over the
-// bits of g (10-bit digits, then the token index for exact ties) keeps per-bucket
+// bits of g (9-bit digits, then the token index for exact ties) keeps per-bucket
 // counts, sums of beta_i and V_i and the maximum b_i in LDS, walks the buckets in
 // ascending g to the first one whose inclusion pushes E(L') to eps*D, and recurses
 // into it until at most WIN tokens remain.  Those are sorted in LDS (bitonic) and
 // scanned against a deterministic re-sum of everything below them.  The tokens of F
 // are OR-ed into the KV head's fetch bitmask (the union over the GQA group).
 //
-// Parallel layout: a query row is served by a team of T workgroups of 1024 threads,
-// each owning a contiguous slice of the row's tokens (T = 8 puts the 32 rows of a
-// 32-query-head layer on all 256 CUs).  Every reduction is first done inside the
+// Parallel layout: a query row is served by a team of T workgroups of 512 threads,
+// each owning a contiguous slice of the row's tokens (T = 16 puts the 32 rows of a
+// 32-query-head layer on all 256 CUs, two workgroups per CU).  Every reduction is first done inside the
 // workgroup, then combined across the team in a fixed member order after a barrier
 // on a counter in global memory; histograms are merged by bucket ranges (member m
 // merges buckets [m*NB/T, (m+1)*NB/T)).  Every member therefore sees identical
@@ -33,14 +33,17 @@
 
 namespace verkv {
 
-constexpr int DC_NT = 1024;
+constexpr int DC_NT = DECIDE_THREADS;
 constexpr int DC_NW = DC_NT / WAVE;
 constexpr int MAX_CHUNKS = VERKV_MAX_SEQ_LEN / SKETCH_CHUNK;
 constexpr uint32_t IDX_MAX = (1u << 20) - 1;
-constexpr int NLEV = 9;
-__device__ __constant__ int c_lev_lo[NLEV] = {0, 0, 0, 0, 0, 0, 0, 1, 1};
-__device__ __constant__ int c_lev_shift[NLEV] = {53, 43, 33, 23, 13, 3, 0, 10, 0};
-__device__ __constant__ int c_lev_width[NLEV] = {10, 10, 10, 10, 10, 10, 3, 10, 10};
+// digit levels: 7 of the 63 bits of g >= 0 (9 bits each), then 3 of the 20-bit
+// tie-breaking token key
+constexpr int NLEV = 10;
+constexpr int FIRST_LO_LEV = 7;
+__device__ __constant__ int c_lev_lo[NLEV] = {0, 0, 0, 0, 0, 0, 0, 1, 1, 1};
+__device__ __constant__ int c_lev_shift[NLEV] = {54, 45, 36, 27, 18, 9, 0, 11, 2, 0};
+__device__ __constant__ int c_lev_width[NLEV] = {9, 9, 9, 9, 9, 9, 9, 9, 9, 2};
 
 __device__ __forceinline__ double lam_of(double w, double r, double B, double kappa) {
   if (r == 0.0) return 0.0;
@@ -100,7 +103,7 @@ __device__ __forceinline__ int cmp_window(uint64_t key, uint32_t lo, int lev, ui
   return lp < plo ? -1 : (lp > plo ? 1 : 0);
 }
 
-// Four fixed-order block reductions in one barrier round.
+// Four fixed-order block reductions in one barrier round (see block_sum).
 struct Red4 { double s0, s1, mx, mn; };
 __device__ __forceinline__ Red4 block_red4(Red4 v, double *scr /*[4*DC_NW]*/) {
   v.s0 = wave_sum(v.s0);
@@ -108,18 +111,18 @@ __device__ __forceinline__ Red4 block_red4(Red4 v, double *scr /*[4*DC_NW]*/) {
   v.mx = wave_max(v.mx);
   v.mn = wave_min(v.mn);
   const int w = threadIdx.x / WAVE;
-  if ((threadIdx.x & (WAVE - 1)) == 0) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) {
     scr[w] = v.s0; scr[DC_NW + w] = v.s1; scr[2 * DC_NW + w] = v.mx; scr[3 * DC_NW + w] = v.mn;
   }
   __syncthreads();
-  Red4 o{0.0, 0.0, scr[2 * DC_NW], scr[3 * DC_NW]};
-#pragma unroll
-  for (int i = 0; i < DC_NW; ++i) {
-    o.s0 += scr[i];
-    o.s1 += scr[DC_NW + i];
-    o.mx = fmax(o.mx, scr[2 * DC_NW + i]);
-    o.mn = fmin(o.mn, scr[3 * DC_NW + i]);
-  }
+  const int k = lane & 15;
+  const bool in = k < DC_NW;
+  Red4 o;
+  o.s0 = sum16(in ? scr[k] : 0.0);
+  o.s1 = sum16(in ? scr[DC_NW + k] : 0.0);
+  o.mx = max16(in ? scr[2 * DC_NW + k] : -INFINITY);
+  o.mn = min16(in ? scr[3 * DC_NW + k] : INFINITY);
   __syncthreads();
   return o;
 }
@@ -132,25 +135,87 @@ __device__ __forceinline__ void top2_merge(double &a1, double &a2, double c1, do
   a1 = hi;
   a2 = lo2;
 }
+template <int CTRL>
+__device__ __forceinline__ void top2_step_dpp(double &a1, double &a2) {
+  const double c1 = dpp_d<CTRL>(a1), c2 = dpp_d<CTRL>(a2);
+  top2_merge(a1, a2, c1, c2);
+}
+__device__ __forceinline__ void top2_16(double &a1, double &a2) {
+  top2_step_dpp<DPP_XOR1>(a1, a2);
+  top2_step_dpp<DPP_XOR2>(a1, a2);
+  top2_step_dpp<DPP_HALF_MIRROR>(a1, a2);
+  top2_step_dpp<DPP_MIRROR>(a1, a2);
+}
 __device__ __forceinline__ Cert block_cert(Cert v, double *scr /*[4*DC_NW]*/) {
   v.beta = wave_sum(v.beta);
   v.V = wave_sum(v.V);
-  for (int m = 1; m < WAVE; m <<= 1) {
+  top2_16(v.b1, v.b2);
+  for (int m = 16; m < WAVE; m <<= 1) {
     const double o1 = shfl_xor_d(v.b1, m), o2 = shfl_xor_d(v.b2, m);
     top2_merge(v.b1, v.b2, o1, o2);
   }
   const int w = threadIdx.x / WAVE;
-  if ((threadIdx.x & (WAVE - 1)) == 0) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) {
     scr[w] = v.beta; scr[DC_NW + w] = v.V; scr[2 * DC_NW + w] = v.b1; scr[3 * DC_NW + w] = v.b2;
   }
   __syncthreads();
-  Cert o{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int i = 0; i < DC_NW; ++i) {
-    o.beta += scr[i];
-    o.V += scr[DC_NW + i];
-    top2_merge(o.b1, o.b2, scr[2 * DC_NW + i], scr[3 * DC_NW + i]);
+  const int k = lane & 15;
+  const bool in = k < DC_NW;
+  Cert o;
+  o.beta = sum16(in ? scr[k] : 0.0);
+  o.V = sum16(in ? scr[DC_NW + k] : 0.0);
+  o.b1 = in ? scr[2 * DC_NW + k] : 0.0;
+  o.b2 = in ? scr[3 * DC_NW + k] : 0.0;
+  top2_16(o.b1, o.b2);
+  __syncthreads();
+  return o;
+}
+
+// Per-pass accumulator of the Newton iteration for the bias: the linear model of f on
+// the piece containing B (C0, C1 and the piece's ends), plus what the certificate
+// needs if the root lies on this piece: on a piece every lambda_i is r_i, 1 or
+// B kappa r_i / (w_i (1 - r_i)), so V(L) = Vc + B^2 Vm and b(L) is the larger of the
+// constant b_i and B times the largest mid-piece coefficient (top two of each kept).
+struct NewtonAcc {
+  double c0, c1, lo, hi;       // model and piece [lo, hi]
+  double vc, vm, cnt;          // V constant part, V coefficient of B^2, |L|
+  double bc1, bc2, bm1, bm2;   // top two constant b, top two mid coefficients
+};
+constexpr int NQ = 11;
+__device__ __forceinline__ NewtonAcc block_newton(NewtonAcc v, double *scr /*[NQ*DC_NW]*/) {
+  v.c0 = wave_sum(v.c0); v.c1 = wave_sum(v.c1);
+  v.vc = wave_sum(v.vc); v.vm = wave_sum(v.vm); v.cnt = wave_sum(v.cnt);
+  v.lo = wave_max(v.lo); v.hi = wave_min(v.hi);
+  top2_16(v.bc1, v.bc2);
+  top2_16(v.bm1, v.bm2);
+  for (int m = 16; m < WAVE; m <<= 1) {
+    double o1 = shfl_xor_d(v.bc1, m), o2 = shfl_xor_d(v.bc2, m);
+    top2_merge(v.bc1, v.bc2, o1, o2);
+    o1 = shfl_xor_d(v.bm1, m); o2 = shfl_xor_d(v.bm2, m);
+    top2_merge(v.bm1, v.bm2, o1, o2);
   }
+  const int w = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) {
+    double *q = scr + w;
+    q[0] = v.c0; q[DC_NW] = v.c1; q[2 * DC_NW] = v.lo; q[3 * DC_NW] = v.hi;
+    q[4 * DC_NW] = v.vc; q[5 * DC_NW] = v.vm; q[6 * DC_NW] = v.cnt;
+    q[7 * DC_NW] = v.bc1; q[8 * DC_NW] = v.bc2; q[9 * DC_NW] = v.bm1; q[10 * DC_NW] = v.bm2;
+  }
+  __syncthreads();
+  const int k = lane & 15;
+  const bool in = k < DC_NW;
+  const double *q = scr + (in ? k : 0);
+  NewtonAcc o;
+  o.c0 = sum16(in ? q[0] : 0.0); o.c1 = sum16(in ? q[DC_NW] : 0.0);
+  o.lo = max16(in ? q[2 * DC_NW] : 0.0); o.hi = min16(in ? q[3 * DC_NW] : INFINITY);
+  o.vc = sum16(in ? q[4 * DC_NW] : 0.0); o.vm = sum16(in ? q[5 * DC_NW] : 0.0);
+  o.cnt = sum16(in ? q[6 * DC_NW] : 0.0);
+  o.bc1 = in ? q[7 * DC_NW] : 0.0; o.bc2 = in ? q[8 * DC_NW] : 0.0;
+  o.bm1 = in ? q[9 * DC_NW] : 0.0; o.bm2 = in ? q[10 * DC_NW] : 0.0;
+  top2_16(o.bc1, o.bc2);
+  top2_16(o.bm1, o.bm2);
   __syncthreads();
   return o;
 }
@@ -186,9 +251,33 @@ __device__ __forceinline__ Cert cert_combine(Cert a, const Cert &b) {
   return a;
 }
 
+// A member keeps its slice's sketch weights and inclusion probabilities in LDS
+// (dynamic shared memory, up to LDS_TOK tokens) for the fixed-point passes, and the
+// selection terms and keys of up to TR tokens per thread in registers (slot k of thread
+// t is token s0 + t + k * DC_NT).  Longer slices are streamed from memory on every pass,
+// four tokens' loads in flight per thread.
+constexpr int TR = 8;
+constexpr int LDS_TOK = 4096;
+constexpr int SB = 4;
+
+// Sort (key, lo) ascending across the 64 lanes of a wave (bitonic, registers only).
+__device__ __forceinline__ void wave_bitonic(uint64_t &key, uint32_t &lo) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  for (int k = 2; k <= WAVE; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t pk = __shfl_xor(key, j, WAVE);
+      const uint32_t pl = __shfl_xor(lo, j, WAVE);
+      const bool keep_min = (((lane & k) == 0) == ((lane & j) == 0));
+      const bool mine_gt = (key > pk) || (key == pk && lo > pl);
+      if (keep_min == mine_gt) { key = pk; lo = pl; }
+    }
+  }
+}
+
 __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
-  __shared__ double s_scale[MAX_CHUNKS];
-  __shared__ double scr[4 * DC_NW];
+  extern __shared__ double s_dyn[];          // [nch] chunk scales, then [2][LDS_TOK] cache
+  __shared__ double scr[NQ * DC_NW];
+  __shared__ double s_part[TEAM_MAX * PART];
   __shared__ uint32_t h_cnt[NBUCKET];
   __shared__ double h_beta[NBUCKET];
   __shared__ double h_V[NBUCKET];
@@ -214,22 +303,48 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   const int n = a.t.s[b].n;
   const int nch = chunks_of(n);
   const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
   const int s0 = (int)((int64_t)n * m / T);
   const int s1 = (int)((int64_t)n * (m + 1) / T);
+  const bool cached = (s1 - s0) <= TR * DC_NT;        // selection terms in registers
+  const bool lcache = (s1 - s0) <= LDS_TOK && a.lds_cache;  // (w, r) in LDS
+  double *s_scale = s_dyn;
+  double *s_w = s_dyn + a.nch_max;
+  double *s_r = s_w + LDS_TOK;
   const double *wcr = a.wc + row_tok_base(a.t, b, h);
   const double2 *cs = a.cstat + row_chunk_base(a.t, b, h);
   const double *rr = a.r + tok_base(a.t, b, g);
   uint32_t *fb = a.fbits + word_base(a.t, b, g);
   const double kappa = a.kappa, l = a.l, eps = a.eps;
   uint32_t *bar = a.bar + row;
-  double *part = a.part + (int64_t)row * 2 * T * 8;          // [2][T][8]
+  double *part = a.part + (int64_t)row * 2 * T * PART;       // [2][T][PART]
   uint32_t nbar = 0;
 #define TEAM_SYNC()                                                         \
   do {                                                                      \
     if (T > 1) team_barrier(bar, (++nbar) * (uint32_t)T, a.status);         \
     else __syncthreads();                                                   \
   } while (0)
-#define SLOT() (part + (int64_t)(nbar & 1) * T * 8)
+#define SLOT() (part + (int64_t)(nbar & 1) * T * PART)
+  // exchange: every member has written its PART values to `sl` (tid 0); after the
+  // barrier the team's partials are staged in LDS with one parallel load
+#define TEAM_STAGE(sl)                                                      \
+  do {                                                                      \
+    TEAM_SYNC();                                                            \
+    for (int j_ = tid; j_ < T * PART; j_ += DC_NT) s_part[j_] = (sl)[j_];   \
+    __syncthreads();                                                        \
+  } while (0)
+#ifdef VERKV_PHASE_TIMING
+  int nstamp = 0;
+#define STAMP()                                                                                  \
+  do {                                                                                           \
+    if (tid == 0 && a.phase_clock && nstamp < 16)                                                \
+      a.phase_clock[((int64_t)row * T + m) * 16 + nstamp] = wall_clock64();                      \
+    ++nstamp;                                                                                    \
+  } while (0)
+#else
+#define STAMP() do {} while (0)
+#endif
+  STAMP();
 
   // ---- step 1 (finish): m_hat, per-chunk rescale, D (every member, same order)
   double mloc = -INFINITY;
@@ -243,66 +358,132 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     dloc += sc * cs[c].y;
   }
   const double Dd = block_sum<DC_NT>(dloc, scr);      // barrier also publishes s_scale
+  const double *cz = a.cf0 + row_chunk_base(a.t, b, h);
+  double zloc = 0.0;
+  for (int c = tid; c < nch; c += DC_NT) zloc += s_scale[c] * cz[c];
+  const double f0 = block_sum<DC_NT>(zloc, scr);      // f(0) = sum_L w (1 - r)
+
+  // (w, r) of the slice in LDS; r >= 1 marks a token of H
+  if (lcache) {
+    for (int i = s0 + tid; i < s1; i += DC_NT) {
+      const double ri = rr[i];
+      s_r[i - s0] = ri;
+      s_w[i - s0] = ri < 1.0 ? wcr[i] * s_scale[i / SKETCH_CHUNK] : 0.0;
+    }
+    __syncthreads();
+  }
+  STAMP();
 
 #define FOR_L(body)                                                   \
-  for (int i = s0 + tid; i < s1; i += DC_NT) {                        \
-    const double ri = rr[i];                                          \
-    if (!(ri < 1.0)) continue;                                        \
-    const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];             \
-    body                                                              \
+  if (lcache) {                                                       \
+    for (int i = s0 + tid; i < s1; i += DC_NT) {                      \
+      const double ri = s_r[i - s0];                                  \
+      if (!(ri < 1.0)) continue;                                      \
+      const double wi = s_w[i - s0];                                  \
+      body                                                            \
+    }                                                                 \
+  } else {                                                            \
+    for (int i0 = s0 + tid; i0 < s1; i0 += SB * DC_NT) {              \
+      double rb[SB], wb[SB];                                          \
+      _Pragma("unroll")                                               \
+      for (int u = 0; u < SB; ++u) {                                  \
+        const int iu = i0 + u * DC_NT;                                \
+        rb[u] = iu < s1 ? rr[iu] : 2.0;                               \
+        wb[u] = iu < s1 ? wcr[iu] : 0.0;                              \
+      }                                                               \
+      _Pragma("unroll")                                               \
+      for (int u = 0; u < SB; ++u) {                                  \
+        const int i = i0 + u * DC_NT;                                 \
+        const double ri = rb[u];                                      \
+        if (!(ri < 1.0)) continue;                                    \
+        const double wi = wb[u] * s_scale[i / SKETCH_CHUNK];          \
+        body                                                          \
+      }                                                               \
+    }                                                                 \
   }
 
-  // team-combine helpers: member partials go to SLOT()[m*8 + k]
   auto combine_sum1 = [&](double v) -> double {
     if (T == 1) return v;
-    if (tid == 0) SLOT()[m * 8] = v;
     double *sl = SLOT();
-    TEAM_SYNC();
+    if (tid == 0) sl[m * PART] = v;
+    TEAM_STAGE(sl);
     double t = 0.0;
-    for (int k = 0; k < T; ++k) t += sl[k * 8];
+    for (int k = 0; k < T; ++k) t += s_part[k * PART];
     return t;
   };
 
-  // ---- self-consistent beta (Definition 2)
-  double Bst;
+  // ---- self-consistent beta (Definition 2) and the eq. (7) totals
+  double Bst = 0.0;
+  Cert ct{0.0, 0.0, 0.0, 0.0};
+  double nLt = 0.0;
+  bool have_cert = false;
   if (isinf(kappa) || kappa == 0.0) {
     double acc = 0.0;
     if (isinf(kappa)) { FOR_L(if (ri == 0.0) acc += wi;) }
     else { FOR_L(acc += wi * (1.0 - ri);) }
     Bst = combine_sum1(block_sum<DC_NT>(acc, scr));
-  } else {
-    double lo = 0.0, hi = INFINITY, B = 0.0;
-    Bst = 0.0;
+  } else if (f0 > 0.0) {
+    // safeguarded Newton from B = f(0), the upper end of the bracket [0, f(0)]
+    double lo = 0.0, hi = INFINITY, B = f0;
     bool done = false;
-    int iter = 0;
-    for (; iter < 200; ++iter) {
-      Red4 v{0.0, 0.0, 0.0, INFINITY};
+    for (int iter = 0; iter < 200; ++iter) {
+      NewtonAcc v{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       FOR_L(
-        if (ri == 0.0) { v.s0 += wi; }
+        v.cnt += 1.0;
+        if (ri == 0.0) { v.c0 += wi; }
         else if (wi != 0.0) {
           const double aa = wi * (1.0 - ri) / kappa;
           const double tt = aa / ri;
-          if (B <= aa) { v.s0 += wi * (1.0 - ri); v.mn = fmin(v.mn, aa); }
-          else if (B >= tt) { v.mx = fmax(v.mx, tt); }
-          else { v.s0 += wi; v.s1 += kappa * ri / (1.0 - ri); v.mx = fmax(v.mx, aa); v.mn = fmin(v.mn, tt); }
+          if (B <= aa) {
+            v.c0 += wi * (1.0 - ri); v.hi = fmin(v.hi, aa);
+            const Terms x = terms_of(wi, ri, ri);
+            v.vc += x.V; top2_merge(v.bc1, v.bc2, x.b, 0.0);
+          } else if (B >= tt) {
+            v.lo = fmax(v.lo, tt);
+            const Terms x = terms_of(wi, ri, 1.0);
+            v.vc += x.V; top2_merge(v.bc1, v.bc2, x.b, 0.0);
+          } else {
+            v.c0 += wi; v.c1 += kappa * ri / (1.0 - ri);
+            v.lo = fmax(v.lo, aa); v.hi = fmin(v.hi, tt);
+            v.vm += kappa * kappa * ri / (1.0 - ri);
+            top2_merge(v.bm1, v.bm2, kappa * fmax(ri, 1.0 - ri) / (1.0 - ri), 0.0);
+          }
         })
-      Red4 o = block_red4(v, scr);
+      NewtonAcc o = block_newton(v, scr);
       if (T > 1) {
         double *sl = SLOT();
-        if (tid == 0) { sl[m * 8] = o.s0; sl[m * 8 + 1] = o.s1; sl[m * 8 + 2] = o.mx; sl[m * 8 + 3] = o.mn; }
-        TEAM_SYNC();
-        o = Red4{0.0, 0.0, 0.0, INFINITY};
+        if (tid == 0) {
+          double *q = sl + m * PART;
+          q[0] = o.c0; q[1] = o.c1; q[2] = o.lo; q[3] = o.hi; q[4] = o.vc; q[5] = o.vm;
+          q[6] = o.cnt; q[7] = o.bc1; q[8] = o.bc2; q[9] = o.bm1; q[10] = o.bm2;
+        }
+        TEAM_STAGE(sl);
+        o = NewtonAcc{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
         for (int k = 0; k < T; ++k) {
-          o.s0 += sl[k * 8]; o.s1 += sl[k * 8 + 1];
-          o.mx = fmax(o.mx, sl[k * 8 + 2]); o.mn = fmin(o.mn, sl[k * 8 + 3]);
+          const double *q = s_part + k * PART;
+          o.c0 += q[0]; o.c1 += q[1]; o.lo = fmax(o.lo, q[2]); o.hi = fmin(o.hi, q[3]);
+          o.vc += q[4]; o.vm += q[5]; o.cnt += q[6];
+          top2_merge(o.bc1, o.bc2, q[7], q[8]);
+          top2_merge(o.bm1, o.bm2, q[9], q[10]);
         }
       }
-      const double hB = B * (1.0 + o.s1) - o.s0;        // B - f(B)
-      const double Bn = o.s0 / (1.0 + o.s1);             // root of this linear piece
+      STAMP();
+      const double hB = B * (1.0 + o.c1) - o.c0;        // B - f(B)
+      const double Bn = o.c0 / (1.0 + o.c1);             // root of this linear piece
       Bst = Bn;
-      if (iter == 0 && o.s0 == 0.0) { Bst = 0.0; done = true; break; }   // f(0) = 0: f vanishes
-      if (Bn >= o.mx && Bn <= o.mn) { done = true; break; }
-      if (hB == 0.0) { Bst = B; done = true; break; }
+      bool on_piece = (Bn >= o.lo && Bn <= o.hi);
+      if (!on_piece && hB == 0.0) { Bst = B; on_piece = true; }
+      if (on_piece) {
+        // the totals of eq. (7) on this piece, at B = Bst
+        ct.beta = o.c0 - Bst * o.c1;
+        ct.V = o.vc + Bst * Bst * o.vm;
+        ct.b1 = o.bc1; ct.b2 = o.bc2;
+        top2_merge(ct.b1, ct.b2, Bst * o.bm1, Bst * o.bm2);
+        nLt = o.cnt;
+        have_cert = true;
+        done = true;
+        break;
+      }
       if (hB < 0.0) lo = B; else hi = B;
       double Bnext = Bn;
       if (!(Bnext > lo && Bnext < hi)) Bnext = 0.5 * (lo + hi);
@@ -312,26 +493,29 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     if (!done && tid == 0 && m == 0) atomicOr(a.status, 2);
   }
 
-  // ---- eq. (7) certificate
-  Cert cl{0.0, 0.0, 0.0, 0.0};
-  int nL = 0;
-  FOR_L(
-    const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
-    cl.beta += x.beta; cl.V += x.V; ++nL;
-    top2_merge(cl.b1, cl.b2, x.b, 0.0);)
-  Cert ct = block_cert(cl, scr);
-  double nLt = block_sum<DC_NT>((double)nL, scr);
-  if (T > 1) {
-    double *sl = SLOT();
-    if (tid == 0) { sl[m * 8] = ct.beta; sl[m * 8 + 1] = ct.V; sl[m * 8 + 2] = ct.b1; sl[m * 8 + 3] = ct.b2; sl[m * 8 + 4] = nLt; }
-    TEAM_SYNC();
-    ct = Cert{0.0, 0.0, 0.0, 0.0};
-    nLt = 0.0;
-    for (int k = 0; k < T; ++k) {
-      ct = cert_combine(ct, Cert{sl[k * 8], sl[k * 8 + 1], sl[k * 8 + 2], sl[k * 8 + 3]});
-      nLt += sl[k * 8 + 4];
+  if (!have_cert) {
+    Cert cl{0.0, 0.0, 0.0, 0.0};
+    int nL = 0;
+    FOR_L(
+      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+      cl.beta += x.beta; cl.V += x.V; ++nL;
+      top2_merge(cl.b1, cl.b2, x.b, 0.0);)
+    ct = block_cert(cl, scr);
+    nLt = block_sum<DC_NT>((double)nL, scr);
+    if (T > 1) {
+      double *sl = SLOT();
+      if (tid == 0) { double *q = sl + m * PART; q[0] = ct.beta; q[1] = ct.V; q[2] = ct.b1; q[3] = ct.b2; q[4] = nLt; }
+      TEAM_STAGE(sl);
+      ct = Cert{0.0, 0.0, 0.0, 0.0};
+      nLt = 0.0;
+      for (int k = 0; k < T; ++k) {
+        const double *q = s_part + k * PART;
+        ct = cert_combine(ct, Cert{q[0], q[1], q[2], q[3]});
+        nLt += q[4];
+      }
     }
   }
+  STAMP();
   const double E_all = nLt > 0.0 ? bern_E(ct.beta, ct.V, ct.b1, l) : 0.0;
   const double ehat = E_all / Dd;
   const bool cert = ehat < eps;
@@ -346,6 +530,48 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   if (cert) return;                                    // kstar was cleared before the kernel
 
   // ---- eqs. (9)-(10): MSD search for the k* cut over the bits of g
+  // per-token terms and keys, cached for the remaining passes
+  uint64_t ckey[TR];
+  double cbeta[TR], cV[TR], cb[TR];
+  bool cin[TR];
+#pragma unroll
+  for (int k = 0; k < TR; ++k) {
+    ckey[k] = 0; cbeta[k] = 0.0; cV[k] = 0.0; cb[k] = 0.0; cin[k] = false;
+    const int i = s0 + tid + k * DC_NT;
+    if (cached && i < s1) {
+      const double ri = lcache ? s_r[i - s0] : rr[i];
+      if (ri < 1.0) {
+        const double wi = lcache ? s_w[i - s0] : wcr[i] * s_scale[i / SKETCH_CHUNK];
+        const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+        cbeta[k] = x.beta; cV[k] = x.V; cb[k] = x.b;
+        ckey[k] = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));
+        cin[k] = true;
+      }
+    }
+  }
+#define FOR_SEL(body)                                                          \
+  if (cached) {                                                                \
+    _Pragma("unroll")                                                          \
+    for (int k = 0; k < TR; ++k) {                                             \
+      if (!cin[k]) continue;                                                   \
+      const int i = s0 + tid + k * DC_NT;                                      \
+      const uint64_t key = ckey[k];                                            \
+      const uint32_t lo = IDX_MAX - (uint32_t)i;                               \
+      const Terms x{cbeta[k], cV[k], cb[k]};                                   \
+      body                                                                     \
+    }                                                                          \
+  } else {                                                                     \
+    for (int i = s0 + tid; i < s1; i += DC_NT) {                               \
+      const double ri = rr[i];                                                 \
+      if (!(ri < 1.0)) continue;                                               \
+      const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];                    \
+      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));            \
+      const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));          \
+      const uint32_t lo = IDX_MAX - (uint32_t)i;                               \
+      body                                                                     \
+    }                                                                          \
+  }
+
   const double thr = eps * Dd;
   double bel_beta = 0.0, bel_V = 0.0, bel_b = 0.0;     // tokens below the window
   uint64_t pkey = 0;
@@ -353,19 +579,13 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   int lev = -1;
   bool above_mode = false;                               // cut above the whole window
   const int64_t hrow = (int64_t)row * T * NBUCKET;
-  const int64_t mrow = (int64_t)row * NBUCKET;
-#define KEY_OF(wi, ri, x, key, lo)                                             \
-  const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));                \
-  const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));              \
-  const uint32_t lo = IDX_MAX - (uint32_t)i;
 
   for (int L = 0; L < NLEV; ++L) {
     for (int k = tid; k < NBUCKET; k += DC_NT) { h_cnt[k] = 0; h_beta[k] = 0.0; h_V[k] = 0.0; h_b[k] = 0; }
     __syncthreads();
     const int sh = c_lev_shift[L];
     const uint32_t dmask = (1u << c_lev_width[L]) - 1u;
-    FOR_L(
-      KEY_OF(wi, ri, x, key, lo)
+    FOR_SEL(
       if (cmp_window(key, lo, lev, pkey, plo) == 0) {
         const uint32_t dig = c_lev_lo[L] ? ((lo >> sh) & dmask) : (uint32_t)((key >> sh) & dmask);
         atomicAdd(&h_cnt[dig], 1u);
@@ -374,27 +594,33 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         atomicMax((unsigned long long *)&h_b[dig], (unsigned long long)dbits(x.b));
       })
     __syncthreads();
+    STAMP();
     if (T > 1) {
-      // publish this member's histogram, merge a bucket range, read the merged one
+      // publish this member's histogram; after the barrier every member sums all of
+      // them in member order, so all hold the same merged histogram
       const int64_t hm = hrow + (int64_t)m * NBUCKET;
       for (int k = tid; k < NBUCKET; k += DC_NT) {
         a.hcnt[hm + k] = h_cnt[k]; a.hbeta[hm + k] = h_beta[k]; a.hV[hm + k] = h_V[k]; a.hmax[hm + k] = h_b[k];
       }
       TEAM_SYNC();
-      const int k0 = m * NBUCKET / T, k1 = (m + 1) * NBUCKET / T;
-      for (int k = k0 + tid; k < k1; k += DC_NT) {
-        uint32_t c = 0; double sb = 0.0, sv = 0.0; uint64_t mb = 0;
-        for (int q = 0; q < T; ++q) {
-          const int64_t o = hrow + (int64_t)q * NBUCKET + k;
-          c += a.hcnt[o]; sb += a.hbeta[o]; sv += a.hV[o];
-          const uint64_t x = a.hmax[o];
-          mb = x > mb ? x : mb;
-        }
-        a.mcnt[mrow + k] = c; a.mbeta[mrow + k] = sb; a.mV[mrow + k] = sv; a.mmax[mrow + k] = mb;
-      }
-      TEAM_SYNC();
       for (int k = tid; k < NBUCKET; k += DC_NT) {
-        h_cnt[k] = a.mcnt[mrow + k]; h_beta[k] = a.mbeta[mrow + k]; h_V[k] = a.mV[mrow + k]; h_b[k] = a.mmax[mrow + k];
+        uint32_t c = 0; double sb = 0.0, sv = 0.0; uint64_t mb = 0;
+        for (int q0 = 0; q0 < T; q0 += 4) {          // four members' loads in flight
+          uint32_t qc[4]; double qb[4], qv[4]; uint64_t qm[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            qc[u] = 0; qb[u] = 0.0; qv[u] = 0.0; qm[u] = 0;
+            if (q0 + u < T) {
+              const int64_t o = hrow + (int64_t)(q0 + u) * NBUCKET + k;
+              qc[u] = a.hcnt[o]; qb[u] = a.hbeta[o]; qv[u] = a.hV[o]; qm[u] = a.hmax[o];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (q0 + u < T) { c += qc[u]; sb += qb[u]; sv += qv[u]; mb = qm[u] > mb ? qm[u] : mb; }
+          }
+        }
+        h_cnt[k] = c; h_beta[k] = sb; h_V[k] = sv; h_b[k] = mb;
       }
       __syncthreads();
     }
@@ -426,7 +652,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     if (!c_lev_lo[L]) {
       pkey = (L == 0) ? (uint64_t)j : ((pkey << c_lev_width[L]) | (uint64_t)j);
     } else {
-      plo = (L == NLEV - 2) ? (uint32_t)j : ((plo << c_lev_width[L]) | (uint32_t)j);
+      plo = (L == FIRST_LO_LEV) ? (uint32_t)j : ((plo << c_lev_width[L]) | (uint32_t)j);
     }
     lev = L;
     const uint32_t cntj = h_cnt[j];
@@ -444,11 +670,10 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     uint64_t *gkey = a.wkey + (int64_t)row * WIN;
     uint32_t *glo = a.wlo + (int64_t)row * WIN;
     Red4 bel{0.0, 0.0, 0.0, 0.0};
-    FOR_L(
-      KEY_OF(wi, ri, x, key, lo)
-      const int cw = cmp_window(key, lo, lev, pkey, plo);
-      if (cw < 0) { bel.s0 += x.beta; bel.s1 += x.V; bel.mx = fmax(bel.mx, x.b); }
-      else if (cw == 0) {
+    FOR_SEL(
+      const int cw2 = cmp_window(key, lo, lev, pkey, plo);
+      if (cw2 < 0) { bel.s0 += x.beta; bel.s1 += x.V; bel.mx = fmax(bel.mx, x.b); }
+      else if (cw2 == 0) {
         if (T > 1) {
           const uint32_t p = atomicAdd(&a.wcount[row], 1u);
           if (p < (uint32_t)WIN) { gkey[p] = key; glo[p] = lo; }
@@ -461,79 +686,119 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     int wcount;
     if (T > 1) {
       double *sl = SLOT();
-      if (tid == 0) { sl[m * 8] = bo.s0; sl[m * 8 + 1] = bo.s1; sl[m * 8 + 2] = bo.mx; }
-      TEAM_SYNC();
+      if (tid == 0) { sl[m * PART] = bo.s0; sl[m * PART + 1] = bo.s1; sl[m * PART + 2] = bo.mx; }
+      TEAM_STAGE(sl);
       bo = Red4{0.0, 0.0, 0.0, 0.0};
-      for (int k = 0; k < T; ++k) { bo.s0 += sl[k * 8]; bo.s1 += sl[k * 8 + 1]; bo.mx = fmax(bo.mx, sl[k * 8 + 2]); }
+      for (int k = 0; k < T; ++k) {
+        bo.s0 += s_part[k * PART]; bo.s1 += s_part[k * PART + 1]; bo.mx = fmax(bo.mx, s_part[k * PART + 2]);
+      }
       wcount = min((int)__hip_atomic_load(&a.wcount[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), WIN);
       for (int k = tid; k < wcount; k += DC_NT) { w_key[k] = gkey[k]; w_lo[k] = glo[k]; }
       __syncthreads();
     } else {
       wcount = min(s_int[1], WIN);
     }
-    // bitonic sort of (key, lo) ascending over WIN slots
-    for (int k2 = 2; k2 <= WIN; k2 <<= 1) {
-      for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
-        const int p = tid ^ j2;
-        if (p > tid) {
-          const uint64_t ka = w_key[tid], kb = w_key[p];
-          const uint32_t la = w_lo[tid], lb = w_lo[p];
-          const bool gt = (ka > kb) || (ka == kb && la > lb);
-          const bool up = (tid & k2) == 0;
-          if (gt == up) {
-            w_key[tid] = kb; w_key[p] = ka;
-            w_lo[tid] = lb; w_lo[p] = la;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    double tb = 0.0, tv = 0.0, tm = 0.0;
-    if (tid < wcount) {
-      const int i = (int)(IDX_MAX - w_lo[tid]);
-      const double ri = rr[i];
-      const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
-      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
-      tb = x.beta; tv = x.V; tm = x.b;
-    }
-    h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
-    __syncthreads();
-    for (int off = 1; off < WIN; off <<= 1) {
-      double ob = 0.0, ov = 0.0, om = 0.0;
-      if (tid >= off) { ob = h_beta[tid - off]; ov = h_V[tid - off]; om = bitsd(h_b[tid - off]); }
-      __syncthreads();
-      if (tid >= off) { tb += ob; tv += ov; tm = fmax(tm, om); }
-      h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
-      __syncthreads();
-    }
+    STAMP();
+    const bool bfail = bern_E(bo.s0, bo.s1, bo.mx, l) >= thr;
     if (tid == 0) s_int[2] = INT32_MAX;
     __syncthreads();
-    const bool bfail = bern_E(bo.s0, bo.s1, bo.mx, l) >= thr;
-    if (tid < wcount && (bfail || bern_E(bo.s0 + tb, bo.s1 + tv, fmax(bo.mx, tm), l) >= thr))
-      atomicMin(&s_int[2], tid);
-    __syncthreads();
-    const int jc = s_int[2];
-    if (jc == INT32_MAX) {
-      above_mode = true;                                 // every window token stays in L'
+    if (wcount <= WAVE) {
+      // one wave sorts and scans the window in registers
+      if (tid < WAVE) {
+        uint64_t key = lane < wcount ? w_key[lane] : ~0ull;
+        uint32_t lo = lane < wcount ? w_lo[lane] : ~0u;
+        wave_bitonic(key, lo);
+        double tb = 0.0, tv = 0.0, tm = 0.0;
+        if (lane < wcount) {
+          const int i = (int)(IDX_MAX - lo);
+          const double ri = rr[i];
+          const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
+          const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+          tb = x.beta; tv = x.V; tm = x.b;
+        }
+        for (int off = 1; off < WAVE; off <<= 1) {
+          const double ob = __shfl_up(tb, off, WAVE), ov = __shfl_up(tv, off, WAVE),
+                       om = __shfl_up(tm, off, WAVE);
+          if (lane >= off) { tb += ob; tv += ov; tm = fmax(tm, om); }
+        }
+        const bool fails = lane < wcount &&
+                           (bfail || bern_E(bo.s0 + tb, bo.s1 + tv, fmax(bo.mx, tm), l) >= thr);
+        const uint64_t fm = __ballot(fails);
+        const int jc = fm ? __ffsll((long long)fm) - 1 : 0;      // uniform in the wave
+        const uint64_t kj = __shfl(key, jc, WAVE);                // whole wave active
+        const uint32_t lj = __shfl(lo, jc, WAVE);
+        if (lane == 0 && fm) {
+          s_int[2] = jc;
+          w_key[0] = kj;
+          w_lo[0] = lj;
+        }
+      }
+      __syncthreads();
+      if (s_int[2] == INT32_MAX) above_mode = true;
+      else { tkey = w_key[0]; tlo = w_lo[0]; }
     } else {
-      tkey = w_key[jc];
-      tlo = w_lo[jc];
+      // bitonic sort of (key, lo) ascending over the next power of two >= wcount
+      int P = 128;
+      while (P < wcount) P <<= 1;     // wcount <= WIN == DC_NT
+      for (int k2 = 2; k2 <= P; k2 <<= 1) {
+        for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+          const int p = tid ^ j2;
+          if (tid < P && p > tid) {
+            const uint64_t ka = w_key[tid], kb = w_key[p];
+            const uint32_t la = w_lo[tid], lb = w_lo[p];
+            const bool gt = (ka > kb) || (ka == kb && la > lb);
+            const bool up = (tid & k2) == 0;
+            if (gt == up) {
+              w_key[tid] = kb; w_key[p] = ka;
+              w_lo[tid] = lb; w_lo[p] = la;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      double tb = 0.0, tv = 0.0, tm = 0.0;
+      if (tid < wcount) {
+        const int i = (int)(IDX_MAX - w_lo[tid]);
+        const double ri = rr[i];
+        const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
+        const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+        tb = x.beta; tv = x.V; tm = x.b;
+      }
+      h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
+      __syncthreads();
+      for (int off = 1; off < P; off <<= 1) {
+        double ob = 0.0, ov = 0.0, om = 0.0;
+        if (tid >= off) { ob = h_beta[tid - off]; ov = h_V[tid - off]; om = bitsd(h_b[tid - off]); }
+        __syncthreads();
+        if (tid >= off) { tb += ob; tv += ov; tm = fmax(tm, om); }
+        h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
+        __syncthreads();
+      }
+      if (tid < wcount && (bfail || bern_E(bo.s0 + tb, bo.s1 + tv, fmax(bo.mx, tm), l) >= thr))
+        atomicMin(&s_int[2], tid);
+      __syncthreads();
+      const int jc = s_int[2];
+      if (jc == INT32_MAX) above_mode = true;
+      else { tkey = w_key[jc]; tlo = w_lo[jc]; }
     }
     __syncthreads();
   }
 
+  STAMP();
   // ---- mark F_h = tokens at or after the cut in g-descending order
   int64_t kc = 0;
-  FOR_L(
-    KEY_OF(wi, ri, x, key, lo)
+  FOR_SEL(
     bool inF;
     if (above_mode) inF = cmp_window(key, lo, lev, pkey, plo) > 0;
     else inF = (key > tkey) || (key == tkey && lo >= tlo);
     if (inF) { atomicOr(&fb[i >> 5], 1u << (i & 31)); ++kc; })
   const int64_t ks = block_sum_i64<DC_NT>(kc, (int64_t *)scr);
   if (tid == 0 && ks) atomicAdd(&a.kstar[row], (int32_t)ks);
-#undef KEY_OF
+  STAMP();
+#undef STAMP
+#undef FOR_SEL
 #undef FOR_L
+#undef TEAM_STAGE
 #undef TEAM_SYNC
 #undef SLOT
 }
@@ -687,19 +952,37 @@ __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
   }
 }
 
-hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st) {
+size_t decide_lds_bytes(int nch_max, bool slice_cache) {
+  return sizeof(double) * ((size_t)nch_max + (slice_cache ? 2 * (size_t)LDS_TOK : 0));
+}
+
+bool decide_slice_cached(int max_n, int team) { return (max_n + team - 1) / team <= LDS_TOK; }
+
+hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    // allow the largest dynamic LDS this kernel asks for (chunk scales + slice cache)
+    hipError_t e = hipFuncSetAttribute((const void *)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)decide_lds_bytes(MAX_CHUNKS, true));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  a.nch_max = chunks_of(a.t.max_n);
+  a.lds_cache = decide_slice_cached(a.t.max_n, a.team) ? 1 : 0;
+  const size_t dyn = decide_lds_bytes(a.nch_max, a.lds_cache != 0);
   const dim3 grid(rows * a.team), block(DC_NT);
   if (a.team > 1) {
-    void *args[] = {const_cast<DecideArgs *>(&a)};
-    return hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, 0, st);
+    void *args[] = {&a};
+    return hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, (unsigned)dyn, st);
   }
-  hipLaunchKernelGGL(k_decide, grid, block, 0, st, a);
+  hipLaunchKernelGGL(k_decide, grid, block, dyn, st, a);
   return hipGetLastError();
 }
 
-int decide_blocks_per_cu() {
+int decide_blocks_per_cu(int max_n, int team) {
+  const size_t dyn = decide_lds_bytes(chunks_of(max_n), decide_slice_cached(max_n, team));
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decide, DC_NT, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decide, DC_NT, dyn) != hipSuccess) return 1;
   return nb > 0 ? nb : 1;
 }
 

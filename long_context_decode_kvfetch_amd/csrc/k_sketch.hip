@@ -53,6 +53,7 @@ __global__ __launch_bounds__(SketchCfg<BF16>::NT) void k_sketch(SketchArgs a) {
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
 
   __shared__ double s_red[SK_NW][G];
+  __shared__ double s_f0[SK_NW][G];
 
   int b, g, c;
   sketch_block(a.t, blockIdx.x, b, g, c);
@@ -137,24 +138,34 @@ __global__ __launch_bounds__(SketchCfg<BF16>::NT) void k_sketch(SketchArgs a) {
   for (int w = 1; w < SK_NW; ++w) mc = fmax(mc, s_red[w][myrow]);
   __syncthreads();
 
-  double sum = 0.0;
+  // exp(s - m_c), their sum D_c, and f(0)_c = sum over L of exp(s - m_c)(1 - r): the
+  // bias of the shrinkage estimator at beta = 0, where every lambda_i equals r_i
+  double sum = 0.0, f0 = 0.0;
   double *wrow = a.wc + row_tok_base(a.t, b, g * G + myrow);
+  const double *rr = a.r + tok_base(a.t, b, g);
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int tok = tok0 + it * TPW + grp;
     const double e = exp(keep[it] - mc);
+    const double ri = tok < n ? rr[tok] : 1.0;
     sum += e;
+    if (ri < 1.0) f0 += e * (1.0 - ri);
     if (sub < G && tok < n) wrow[tok] = e;
   }
-  for (int m = LPT; m < WAVE; m <<= 1) sum += shfl_xor_d(sum, m);
-  if (grp == 0 && sub < G) s_red[wv][sub] = sum;
+  for (int m = LPT; m < WAVE; m <<= 1) {
+    sum += shfl_xor_d(sum, m);
+    f0 += shfl_xor_d(f0, m);
+  }
+  if (grp == 0 && sub < G) { s_red[wv][sub] = sum; s_f0[wv][sub] = f0; }
   __syncthreads();
   if (threadIdx.x < G) {
-    double s = 0.0;
+    double s = 0.0, z = 0.0;
 #pragma unroll
-    for (int w = 0; w < SK_NW; ++w) s += s_red[w][threadIdx.x];
+    for (int w = 0; w < SK_NW; ++w) { s += s_red[w][threadIdx.x]; z += s_f0[w][threadIdx.x]; }
     // thread j is lane j of wave 0, whose `sub` is j, so `mc` is row j's maximum
-    a.cstat[row_chunk_base(a.t, b, g * G + threadIdx.x) + c] = make_double2(mc, s);
+    const int64_t o = row_chunk_base(a.t, b, g * G + threadIdx.x) + c;
+    a.cstat[o] = make_double2(mc, s);
+    a.cf0[o] = z;
   }
 }
 

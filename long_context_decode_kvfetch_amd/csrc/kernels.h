@@ -36,6 +36,8 @@ struct SketchArgs {
   double sqrt_d;              // sqrt(128): scores are q.k / sqrt(d)
   double *wc;                 // [B][Hq][n]
   double2 *cstat;             // [B][Hq][nchunks]  (m_c, sum_c)
+  const double *r;            // [B][Hkv][n] inclusion probabilities
+  double *cf0;                // [B][Hq][nchunks]  sum over L of wc (1 - r): f(0) per chunk
   uint32_t *fbits;            // [B][Hkv][W]  cleared here
   uint32_t *bar, *wcount;     // [B][Hq] decision-kernel counters, cleared here
   int32_t *kstar;             // [B][Hq] cleared here
@@ -46,6 +48,7 @@ struct DecideArgs {
   SeqTable t;
   const double *wc;          // [B][Hq][n]   exp(s - m_chunk)
   const double2 *cstat;      // [B][Hq][nch] (m_chunk, sum over chunk)
+  const double *cf0;         // [B][Hq][nch] f(0) per chunk, relative to m_chunk
   double *cscale;            // [B][Hq][nch] out: exp(m_chunk - m_hat)
   const double *r;           // [B][Hkv][n]
   uint32_t *fbits;           // [B][Hkv][W]
@@ -59,16 +62,16 @@ struct DecideArgs {
   int32_t team;
   int32_t xcd_map;           // 1: map the members of a team to one XCD
   uint32_t *bar;             // [rows] barrier counters (cleared by the sketch kernel)
-  double *part;              // [rows][2][T][8] member partials
+  double *part;              // [rows][2][T][PART] member partials
   uint32_t *hcnt;            // [rows][T][NBUCKET] member histograms
   double *hbeta, *hV;
   uint64_t *hmax;
-  uint32_t *mcnt;            // [rows][NBUCKET] merged histograms
-  double *mbeta, *mV;
-  uint64_t *mmax;
   uint64_t *wkey;            // [rows][WIN] final window
   uint32_t *wlo;
   uint32_t *wcount;          // [rows] (cleared by the sketch kernel)
+  uint64_t *phase_clock;     // [rows][T][16] phase timestamps (VERKV_PHASE_TIMING builds)
+  int32_t nch_max;           // chunk scales held in dynamic LDS
+  int32_t lds_cache;         // 1: the launch reserved LDS for the (w, r) slice cache
 };
 
 struct AfterArgs {
@@ -128,20 +131,24 @@ struct FinishArgs {
   float *n_hat, *d_hat, *o, *lse;
 };
 
-constexpr int NBUCKET = 1024;    // digit buckets of the k* search
-constexpr int WIN = 1024;        // final window of the k* search
+constexpr int NBUCKET = 512;     // digit buckets of the k* search (9-bit digits)
+constexpr int PART = 16;         // doubles per team member in an exchange slot
+constexpr int TEAM_MAX = 16;     // workgroups per query row in the decision kernel
+constexpr int DECIDE_THREADS = 512;
+constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
+constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
 constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets nsp)
 
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);
-hipError_t launch_decide(const DecideArgs &a, int rows, hipStream_t st);
+hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st);
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, bool exact,
                          hipStream_t st);
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st);
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
-int decide_blocks_per_cu();
+int decide_blocks_per_cu(int max_n, int team);
 
 }  // namespace verkv

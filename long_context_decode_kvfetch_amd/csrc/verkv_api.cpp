@@ -82,19 +82,18 @@ int host_splits(int units) { return std::max(4, std::min(64, 512 / std::max(1, u
 int pivot_splits(int cap) { return std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS); }
 
 // Workgroups per query row in the decision kernel, as sized in the workspace: enough
-// to cover 256 CUs with one workgroup each, at least 4096 tokens per workgroup, at
-// most 16.  At launch it is lowered further if fewer workgroups can be co-resident.
-constexpr int TEAM_MAX = 16;
+// to give 256 CUs two workgroups each, at least TEAM_MIN_TOKENS tokens per workgroup,
+// at most TEAM_MAX.  At launch it is lowered further if fewer can be co-resident.
 int team_size(int rows, int max_n) {
-  const int by_cu = 256 / std::max(1, rows);
-  const int by_len = (max_n + 4095) / 4096;
+  const int by_cu = 512 / std::max(1, rows);
+  const int by_len = (max_n + TEAM_MIN_TOKENS - 1) / TEAM_MIN_TOKENS;
   return std::max(1, std::min(TEAM_MAX, std::min(by_cu, by_len)));
 }
 
 // Decode workspace layout.
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
-  size_t bar, wcount, part, hcnt, hbeta, hV, hmax, mcnt, mbeta, mV, mmax, wkey, wlo, apart;
+  size_t bar, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0;
   size_t total;
   int nsp, nsh, team;
 };
@@ -111,21 +110,18 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   size_t off = 0;
   w.bar = off;    off = align_up(off + 4 * (size_t)rows);
   w.wcount = off; off = align_up(off + 4 * (size_t)rows);
-  w.part = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team * 8));
+  w.part = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team * PART));
   w.apart = off;  off = align_up(off + 8 * (size_t)(rows * w.team * 8));
   w.hcnt = off;   off = align_up(off + 4 * (size_t)(rows * tm * NBUCKET));
   w.hbeta = off;  off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
   w.hV = off;     off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
   w.hmax = off;   off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
   const int64_t mm = w.team > 1 ? 1 : 0;
-  w.mcnt = off;   off = align_up(off + 4 * (size_t)(rows * mm * NBUCKET));
-  w.mbeta = off;  off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
-  w.mV = off;     off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
-  w.mmax = off;   off = align_up(off + 8 * (size_t)(rows * mm * NBUCKET));
   w.wkey = off;   off = align_up(off + 8 * (size_t)(rows * mm * WIN));
   w.wlo = off;    off = align_up(off + 4 * (size_t)(rows * mm * WIN));
   w.wc = off;     off = align_up(off + 8 * (size_t)(Hq * T.tok));
   w.cstat = off;  off = align_up(off + 16 * (size_t)(Hq * T.chunks));
+  w.cf0 = off;    off = align_up(off + 8 * (size_t)(Hq * T.chunks));
   w.cscale = off; off = align_up(off + 8 * (size_t)(Hq * T.chunks));
   w.fbits = off;  off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2d = off;    off = align_up(off + 4 * (size_t)(t.Hkv * T.tok));
@@ -181,20 +177,14 @@ verkv_status device_view(const void *p, const void **out) {
   return VERKV_EINVAL;
 }
 
-// Co-resident decision workgroups on the current device (cached per device).
-int decide_capacity() {
-  static int cache[64];
-  static bool init[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!init[dev]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-    cache[dev] = cus * decide_blocks_per_cu();
-    init[dev] = true;
-  }
-  return cache[dev];
+// Co-resident decision workgroups on the current device for a team size (the LDS the
+// kernel reserves depends on the slice each member holds).
+int decide_capacity(int max_n, int team) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return cus * decide_blocks_per_cu(max_n, team);
 }
 
 // ---------------------------------------------------------------- optional kernel timing
@@ -368,6 +358,8 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.sqrt_d = std::sqrt((double)VERKV_HEAD_DIM);
   sk.wc = reinterpret_cast<double *>(ws + L.wc);
   sk.cstat = reinterpret_cast<double2 *>(ws + L.cstat);
+  sk.r = st->r;
+  sk.cf0 = reinterpret_cast<double *>(ws + L.cf0);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
   sk.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
   sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
@@ -382,6 +374,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.t = t;
   dc.wc = sk.wc;
   dc.cstat = sk.cstat;
+  dc.cf0 = sk.cf0;
   dc.cscale = reinterpret_cast<double *>(ws + L.cscale);
   dc.r = st->r;
   dc.fbits = sk.fbits;
@@ -397,7 +390,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.status = reinterpret_cast<int32_t *>(ws + L.status);
   dc.params = reinterpret_cast<double *>(ws + L.status + 32);
   int team = L.team;
-  if (team > 1) team = std::max(1, std::min(team, decide_capacity() / rows));
+  while (team > 1 && team * rows > decide_capacity(t.max_n, team)) --team;
   dc.team = team;
   dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;
   dc.bar = sk.bar;
@@ -406,13 +399,14 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.hbeta = reinterpret_cast<double *>(ws + L.hbeta);
   dc.hV = reinterpret_cast<double *>(ws + L.hV);
   dc.hmax = reinterpret_cast<uint64_t *>(ws + L.hmax);
-  dc.mcnt = reinterpret_cast<uint32_t *>(ws + L.mcnt);
-  dc.mbeta = reinterpret_cast<double *>(ws + L.mbeta);
-  dc.mV = reinterpret_cast<double *>(ws + L.mV);
-  dc.mmax = reinterpret_cast<uint64_t *>(ws + L.mmax);
   dc.wkey = reinterpret_cast<uint64_t *>(ws + L.wkey);
   dc.wlo = reinterpret_cast<uint32_t *>(ws + L.wlo);
   dc.wcount = sk.wcount;
+  dc.phase_clock = nullptr;
+#ifdef VERKV_PHASE_TIMING
+  if (workspace_bytes >= L.total + (size_t)rows * team * 16 * 8)
+    dc.phase_clock = reinterpret_cast<uint64_t *>(ws + L.total);
+#endif
   {
     Timed tm(K_DECIDE, stream);
     HIP_TRY(launch_decide(dc, rows, stream), "decide launch");
