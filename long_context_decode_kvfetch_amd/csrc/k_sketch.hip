@@ -3,33 +3,30 @@
 // "KVFETCH" step 1: estimated weights w_hat_i from the sketch; the decisions of
 // steps 2-4 are made on these weights, so they are kept in float64 end to end).
 //
-// Streaming layout: a workgroup (256 threads for bf16, 512 for float32 rows) owns
-// SKETCH_CHUNK = 256 tokens of one
-// (sequence, KV head).  Each lane loads one 16-byte slice of a key row (8 bf16 or 4
-// float32 elements), so a wave instruction reads 1 KB of contiguous rows; the G query
-// rows stay in registers as float64 and the per-lane partial dot products are summed
-// across the lanes of a row with DPP butterflies.  The chunk keeps its scores in
-// registers, takes the per-row chunk maximum m_c, and writes
-//   wc_i = exp(s_i - m_c)       (float64, [row][token])
-//   (m_c, sum_i wc_i)           per (row, chunk)
-// The decision kernel rescales by exp(m_c - m_hat) once m_hat = max_c m_c is known.
-// The same workgroup clears the chunk's words of the step's fetch bitmask.
+// Streaming layout: one wave owns SKETCH_CHUNK = 256 tokens of one (sequence, KV
+// head).  A key row is split over 8 lanes (16 when the group has more than four query
+// rows), each holding its float64 query elements in registers, so one wave load reads
+// whole rows (1 KB contiguous).  The per-lane partial dot products of four query rows
+// are reduce-scattered over the row's lanes with DPP exchanges (four exchanges over 8
+// lanes instead of three butterfly levels per query row).  Scores wait in LDS for the
+// per-row chunk maximum m_c; the wave writes
+//   wc_i = exp(s_i - m_c)            (float64, [row][token], whole lines)
+//   (m_c, sum_i wc_i), f(0)_c        per (row, chunk)
+// where f(0)_c = sum over the chunk's tokens of L of wc_i (1 - r_i): the bias of the
+// shrinkage estimator at beta = 0.  The decision kernel rescales by exp(m_c - m_hat)
+// once m_hat = max_c m_c is known.  The workgroup also clears the chunk's words of the
+// step's fetch bitmask and, on chunk 0, the decision kernel's per-row counters.
 #include "kernels.h"
 
 namespace verkv {
 
-// bf16 rows: 4 waves of 64 tokens; float32 rows (32 lanes per row): 8 waves of 32
-// tokens, so that every lane keeps 16 scores either way.
-template <bool BF16>
-struct SketchCfg {
-  static constexpr int NT = BF16 ? 256 : 512;
-  static constexpr int NW = NT / WAVE;
-};
+constexpr int SK_WAVES = 4;               // waves per workgroup, one chunk each
+constexpr int DPP_ROR8 = 0x128;          // row_ror:8 -> lane i <-> i ^ 8 within a 16-lane row
 
-// Map a flat block index to (sequence, KV head, chunk).
-__device__ __forceinline__ void sketch_block(const SeqTable &t, int blk, int &b, int &g, int &c) {
+// Map a flat chunk index to (sequence, KV head, chunk).
+__device__ __forceinline__ void sketch_chunk(const SeqTable &t, int blk, int &b, int &g, int &c) {
   int lo = 0, hi = t.B - 1;
-  while (lo < hi) {                       // last sequence whose first block <= blk
+  while (lo < hi) {                       // last sequence whose first chunk <= blk
     const int mid = (lo + hi + 1) >> 1;
     if (t.Hkv * t.s[mid].chunk_off <= blk) lo = mid; else hi = mid - 1;
   }
@@ -40,138 +37,228 @@ __device__ __forceinline__ void sketch_block(const SeqTable &t, int blk, int &b,
   c = rel % nch;
 }
 
+// Reduce-scatters of four per-lane partials v[0..3] over the lanes that share a token.
+// 16 lanes (one DPP row): on return lanes 4r..4r+3 of the row hold the total of v[r].
+__device__ __forceinline__ double reduce_scatter4x16(const double *v, int s) {
+  const bool b3 = (s >> 3) & 1;
+  const bool b2 = (s >> 2) & 1;
+  // lanes i and i^8: bit 3 clear keeps {0,1}, set keeps {2,3}
+  double k0 = b3 ? v[2] : v[0], k1 = b3 ? v[3] : v[1];
+  const double s0 = b3 ? v[0] : v[2], s1 = b3 ? v[1] : v[3];
+  k0 += dpp_d<DPP_ROR8>(s0);
+  k1 += dpp_d<DPP_ROR8>(s1);
+  // lanes i and 7-i of each half row: bit 2 clear keeps the first, set the second
+  double k = b2 ? k1 : k0;
+  const double o = b2 ? k0 : k1;
+  k += dpp_d<DPP_HALF_MIRROR>(o);
+  // the four lanes of the quad now cover all 16 lanes between them
+  k += dpp_d<DPP_XOR1>(k);
+  k += dpp_d<DPP_XOR2>(k);
+  return k;
+}
+// 8 lanes (half a DPP row): on return lanes 2r, 2r+1 of the group hold the total of v[r].
+__device__ __forceinline__ double reduce_scatter4x8(const double *v, int s) {
+  const bool b2 = (s >> 2) & 1;
+  const bool b1 = (s >> 1) & 1;
+  // lanes i and 7-i: lanes 0-3 keep {0,1}, lanes 4-7 keep {2,3}
+  double k0 = b2 ? v[2] : v[0], k1 = b2 ? v[3] : v[1];
+  const double s0 = b2 ? v[0] : v[2], s1 = b2 ? v[1] : v[3];
+  k0 += dpp_d<DPP_HALF_MIRROR>(s0);
+  k1 += dpp_d<DPP_HALF_MIRROR>(s1);
+  // lanes i and i^2: bit 1 clear keeps the first, set the second
+  double k = b1 ? k1 : k0;
+  const double o = b1 ? k0 : k1;
+  k += dpp_d<DPP_XOR2>(o);
+  k += dpp_d<DPP_XOR1>(k);
+  return k;
+}
+
+// One wave streams one chunk of SKETCH_CHUNK tokens.  A token row is split over LPT
+// lanes (8 when G <= 4, else 16, so the float64 query slices of the G rows fit in
+// registers); a load step reads 64 / LPT whole rows with one or more fully used 1 KB
+// wave loads, and batches of 8 loads per lane are kept one batch ahead of the
+// arithmetic.  Scores wait in the wave's own LDS region for the chunk maximum; then
+// each lane takes CH / 64 tokens of every row for exp, the sums and the stores.  Waves
+// never wait for each other.
 template <bool BF16, int G>
-__global__ __launch_bounds__(SketchCfg<BF16>::NT) void k_sketch(SketchArgs a) {
-  constexpr int SK_NW = SketchCfg<BF16>::NW;
+__global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   using RS = RowSlice<BF16>;
-  constexpr int EPL = RS::EPL;              // elements per lane
-  constexpr int LPT = D / EPL;              // lanes per token row (16 or 32)
-  constexpr int TPW = WAVE / LPT;           // token rows per wave instruction (4 or 2)
-  constexpr int TOK_PER_WAVE = SKETCH_CHUNK / SK_NW;
-  constexpr int ITER = TOK_PER_WAVE / TPW;  // 16
-  constexpr int BATCH = 8;                  // loads in flight per lane
+  constexpr int CH = SKETCH_CHUNK;
+  constexpr int EPP = RS::EPL;              // elements per 16-byte piece
+  constexpr int LPT = G <= 4 ? 8 : 16;      // lanes per token row
+  constexpr int TPS = WAVE / LPT;           // tokens per load step
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
+  constexpr int PPL = ROW_BYTES / 16 / LPT; // 16-byte pieces per lane per token
+  constexpr int EPT = PPL * EPP;            // elements per lane per token
+  constexpr int STEPS = CH / TPS;
+  constexpr int SB = 8 / PPL;               // load steps per batch
+  constexpr int NB = STEPS / SB;
+  constexpr int NG4 = (G + 3) / 4;          // groups of four query rows
+  constexpr int TPL = CH / WAVE;            // tokens per lane in the exp phase
+  static_assert(PPL >= 1 && STEPS % SB == 0 && CH % WAVE == 0, "sketch tiling");
 
-  __shared__ double s_red[SK_NW][G];
-  __shared__ double s_f0[SK_NW][G];
+  __shared__ double s_sc[SK_WAVES][G][CH];
 
-  int b, g, c;
-  sketch_block(a.t, blockIdx.x, b, g, c);
-  const int n = a.t.s[b].n;
-  const int Hq = a.t.Hkv * G;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x / WAVE;
-  const int sub = lane % LPT;               // slice of the row this lane owns
-  const int grp = lane / LPT;               // which of the TPW rows of an instruction
-  const int d0 = sub * EPL;
+  const int flat = blockIdx.x * SK_WAVES + wv;
+  if (flat >= a.total_blocks) return;       // whole wave; no block barriers below
+  int b, g, c;
+  sketch_chunk(a.t, flat, b, g, c);
+  const int n = a.t.s[b].n;
+  const int Hq = a.t.Hkv * G;
+  const int sidx = lane & (LPT - 1);        // lane within the token's group
+  const int tsub = lane / LPT;              // token of the load step
+  const int rsel = LPT == 8 ? (sidx >> 1) & 3 : (sidx >> 2) & 3;   // row of four it ends with
+  const bool writer = LPT == 8 ? (sidx & 1) == 0 : (sidx & 3) == 0;
+  const int base = c * CH;
+  double (*sc)[CH] = s_sc[wv];
 
-  // clear this chunk's words of the fetch bitmask (SKETCH_CHUNK / 32 words), and on
-  // chunk 0 the per-row counters of the decision kernel for the G rows of this head
-  if (threadIdx.x < SKETCH_CHUNK / 32) {
-    const int w = c * (SKETCH_CHUNK / 32) + threadIdx.x;
+  // clear this chunk's words of the fetch bitmask, and on chunk 0 the per-row counters
+  // of the decision kernel for the G rows of this head
+  if (lane < CH / 32) {
+    const int w = c * (CH / 32) + lane;
     if (w < words_of(n)) a.fbits[word_base(a.t, b, g) + w] = 0u;
   }
-  if (c == 0 && threadIdx.x < G) {
-    const int64_t row = (int64_t)b * a.t.Hkv * G + g * G + threadIdx.x;
+  if (c == 0 && lane < G) {
+    const int64_t row = (int64_t)b * a.t.Hkv * G + g * G + lane;
     a.bar[row] = 0u;
     a.wcount[row] = 0u;
     a.kstar[row] = 0;
   }
 
-  // query slices in float64
-  double qd[G][EPL];
+  // float64 query elements of the pieces sidx, sidx + LPT, ...
+  double qd[G][EPT];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float *qr = a.q + ((int64_t)b * Hq + g * G + j) * D + d0;
+    const float *qr = a.q + ((int64_t)b * Hq + g * G + j) * D;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qd[j][e] = (double)qr[e];
+    for (int p = 0; p < PPL; ++p)
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) qd[j][p * EPP + e] = (double)qr[(sidx + p * LPT) * EPP + e];
   }
 
-  const int tok0 = c * SKETCH_CHUNK + wv * TOK_PER_WAVE;
-  const uint8_t *rows = a.sketch + tok_base(a.t, b, g) * ROW_BYTES;
-  const int myrow = sub < G ? sub : 0;      // the query row whose scores this lane keeps
-  double keep[ITER];
-
+  // rows past n (the last chunk) re-read row n-1; their scores are replaced by -inf
+  const uint8_t *rows = a.sketch + tok_base(a.t, b, g) * ROW_BYTES + sidx * 16;
+  auto load_batch = [&](int bi, uint4 *raw) {
 #pragma unroll
-  for (int it0 = 0; it0 < ITER; it0 += BATCH) {
-    uint4 raw[BATCH];
+    for (int k = 0; k < SB; ++k) {
+      const int tok = min(base + (bi * SB + k) * TPS + tsub, n - 1);
+      const uint8_t *rp = rows + (int64_t)tok * ROW_BYTES;
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int tok = tok0 + (it0 + k) * TPW + grp;
-      raw[k] = tok < n ? *(const uint4 *)(rows + (int64_t)tok * ROW_BYTES + d0 * (BF16 ? 2 : 4))
-                       : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < PPL; ++p) raw[k * PPL + p] = *(const uint4 *)(rp + p * LPT * 16);
+    }
+  };
+  uint4 cur[SB * PPL], nxt[SB * PPL];
+  double run_max = -INFINITY;               // max of this lane's scores of row rsel
+  load_batch(0, cur);
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi + 1 < NB) load_batch(bi + 1, nxt);
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      double acc[NG4 * 4];
+#pragma unroll
+      for (int j = 0; j < NG4 * 4; ++j) acc[j] = 0.0;
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        float x[EPP];
+        RS::widen(cur[k * PPL + p], x);
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+          const double xe = (double)x[e];
+#pragma unroll
+          for (int j = 0; j < G; ++j) acc[j] = fma(qd[j][p * EPP + e], xe, acc[j]);
+        }
+      }
+      const int tk = (bi * SB + k) * TPS + tsub;        // token within the chunk
+#pragma unroll
+      for (int q4 = 0; q4 < NG4; ++q4) {
+        const double v = LPT == 8 ? reduce_scatter4x8(acc + 4 * q4, sidx)
+                                  : reduce_scatter4x16(acc + 4 * q4, sidx);
+        const int j = 4 * q4 + rsel;
+        const double sv = base + tk < n ? v * a.inv_sqrt_d : -INFINITY;
+        if (writer && j < G) sc[j][tk] = sv;
+        if (NG4 == 1) run_max = fmax(run_max, sv);
+      }
     }
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      float x[EPL];
-      RS::widen(raw[k], x);
-      double acc[G];
+    for (int k = 0; k < SB * PPL; ++k) cur[k] = nxt[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // chunk maxima m_c of the G rows, wave-uniform
+  double mrow[G];
+  if (NG4 == 1) {
+    // lanes with equal rsel differ in bit 0 and bits 3-5 (LPT 8)
+    double m = run_max;
+    m = fmax(m, dpp_d<DPP_XOR1>(m));
+    m = fmax(m, dpp_d<DPP_ROR8>(m));
+    m = fmax(m, shfl_xor_d(m, 16));
+    m = fmax(m, shfl_xor_d(m, 32));
 #pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = 0.0;
+    for (int j = 0; j < G; ++j)
+      mrow[j] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(m), 2 * j),
+                                 __builtin_amdgcn_readlane(__double2loint(m), 2 * j));
+  } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const double xe = (double)x[e];
+    for (int j = 0; j < G; ++j) {
+      double m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < G; ++j) acc[j] = fma(qd[j][e], xe, acc[j]);
-      }
-      double mine = 0.0;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        double v = sum16(acc[j]);
-        if (LPT == 32) v += shfl_xor_d(v, 16);
-        mine = (j == myrow) ? v : mine;
-      }
-      const int tok = tok0 + (it0 + k) * TPW + grp;
-      keep[it0 + k] = tok < n ? mine / a.sqrt_d : -INFINITY;
+      for (int u = 0; u < TPL; ++u) m = fmax(m, sc[j][lane + u * WAVE]);
+      m = max16(m);
+      m = fmax(m, shfl_xor_d(m, 16));
+      mrow[j] = fmax(m, shfl_xor_d(m, 32));
     }
   }
 
-  // per-row chunk maximum: lanes with the same `sub` hold the same row
-  double mx = -INFINITY;
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) mx = fmax(mx, keep[it]);
-  for (int m = LPT; m < WAVE; m <<= 1) mx = fmax(mx, shfl_xor_d(mx, m));
-  if (grp == 0 && sub < G) s_red[wv][sub] = mx;
-  __syncthreads();
-  double mc = s_red[0][myrow];
-#pragma unroll
-  for (int w = 1; w < SK_NW; ++w) mc = fmax(mc, s_red[w][myrow]);
-  __syncthreads();
-
-  // exp(s - m_c), their sum D_c, and f(0)_c = sum over L of exp(s - m_c)(1 - r): the
-  // bias of the shrinkage estimator at beta = 0, where every lambda_i equals r_i
-  double sum = 0.0, f0 = 0.0;
-  double *wrow = a.wc + row_tok_base(a.t, b, g * G + myrow);
+  // wc = exp(s - m_c), D_c = sum of wc, f(0)_c = sum over L of wc (1 - r); the
+  // exponentials of all rows first (independent chains), then sums and stores
   const double *rr = a.r + tok_base(a.t, b, g);
+  double om[TPL];                           // 1 - r on L, 0 on the resident set and past n
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int tok = tok0 + it * TPW + grp;
-    const double e = exp(keep[it] - mc);
-    const double ri = tok < n ? rr[tok] : 1.0;
-    sum += e;
-    if (ri < 1.0) f0 += e * (1.0 - ri);
-    if (sub < G && tok < n) wrow[tok] = e;
+  for (int u = 0; u < TPL; ++u) {
+    const int tok = base + lane + u * WAVE;
+    const double rv = tok < n ? rr[tok] : 1.0;
+    om[u] = rv < 1.0 ? 1.0 - rv : 0.0;
   }
-  for (int m = LPT; m < WAVE; m <<= 1) {
-    sum += shfl_xor_d(sum, m);
-    f0 += shfl_xor_d(f0, m);
-  }
-  if (grp == 0 && sub < G) { s_red[wv][sub] = sum; s_f0[wv][sub] = f0; }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    double s = 0.0, z = 0.0;
+  double ev[G][TPL];
 #pragma unroll
-    for (int w = 0; w < SK_NW; ++w) { s += s_red[w][threadIdx.x]; z += s_f0[w][threadIdx.x]; }
-    // thread j is lane j of wave 0, whose `sub` is j, so `mc` is row j's maximum
-    const int64_t o = row_chunk_base(a.t, b, g * G + threadIdx.x) + c;
-    a.cstat[o] = make_double2(mc, s);
-    a.cf0[o] = z;
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) ev[j][u] = exp(sc[j][lane + u * WAVE] - mrow[j]);
+  double part[2 * G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    double sum = 0.0, f0 = 0.0;
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) { sum += ev[j][u]; f0 += ev[j][u] * om[u]; }
+    part[2 * j] = sum;
+    part[2 * j + 1] = f0;
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    double *wrow = a.wc + row_tok_base(a.t, b, g * G + j) + base;
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+      if (base + lane + u * WAVE < n) wrow[lane + u * WAVE] = ev[j][u];
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * G; ++k) part[k] = wave_sum(part[k]);
+  if (lane < G) {
+    double pm = mrow[0], ps = part[0], pf = part[1];
+#pragma unroll
+    for (int j = 1; j < G; ++j)
+      if (lane == j) { pm = mrow[j]; ps = part[2 * j]; pf = part[2 * j + 1]; }
+    const int64_t o = row_chunk_base(a.t, b, g * G + lane) + c;
+    a.cstat[o] = make_double2(pm, ps);
+    a.cf0[o] = pf;
   }
 }
 
 template <bool BF16, int G>
 static hipError_t launch_sketch_t(const SketchArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_sketch<BF16, G>), dim3(a.total_blocks), dim3(SketchCfg<BF16>::NT), 0, st, a);
+  const int blocks = (a.total_blocks + SK_WAVES - 1) / SK_WAVES;
+  hipLaunchKernelGGL((k_sketch<BF16, G>), dim3(blocks), dim3(SK_WAVES * WAVE), 0, st, a);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ struct SketchArgs {
   SeqTable t;
   const uint8_t *sketch;      // [B][Hkv][n][128] kv dtype
   const float *q;             // [B][Hq][128]
-  double sqrt_d;              // sqrt(128): scores are q.k / sqrt(d)
+  double inv_sqrt_d;          // 1/sqrt(128): scores are q.k / sqrt(d)
   double *wc;                 // [B][Hq][n]
   double2 *cstat;             // [B][Hq][nchunks]  (m_c, sum_c)
   const double *r;            // [B][Hkv][n] inclusion probabilities

@@ -355,7 +355,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.t = t;
   sk.sketch = static_cast<const uint8_t *>(st->sketch);
   sk.q = q;
-  sk.sqrt_d = std::sqrt((double)VERKV_HEAD_DIM);
+  sk.inv_sqrt_d = 1.0 / std::sqrt((double)VERKV_HEAD_DIM);
   sk.wc = reinterpret_cast<double *>(ws + L.wc);
   sk.cstat = reinterpret_cast<double2 *>(ws + L.cstat);
   sk.r = st->r;
