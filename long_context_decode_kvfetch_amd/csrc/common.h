@@ -8,7 +8,7 @@
 namespace verkv {
 
 constexpr int D = VERKV_HEAD_DIM;          // head dimension
-constexpr int SKETCH_CHUNK = 256;          // tokens per sketch-scoring workgroup
+constexpr int SKETCH_CHUNK = 128;          // tokens per sketch-scoring wave
 constexpr int WAVE = 64;
 
 // Per-sequence offsets of a ragged batch, passed by value in kernel arguments.

@@ -167,8 +167,7 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
 
 template <bool BF16, int G, bool HOST, bool EXACT>
 static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st) {
-  hipLaunchKernelGGL((k_attend<BF16, G, HOST, EXACT>), dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_attend<BF16, G, HOST, EXACT>, dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
 }
 
 template <bool BF16, int G>

@@ -240,14 +240,12 @@ __global__ __launch_bounds__(256) void k_gather_pivots(GatherArgs a) {
 }
 
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st) {
-  hipLaunchKernelGGL(k_poissoncomp, dim3(units), dim3(PC_NT), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_poissoncomp, dim3(units), dim3(PC_NT), 0, st, a);
 }
 
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st) {
   const int nblk = (a.cap + GATHER_ROWS - 1) / GATHER_ROWS;
-  hipLaunchKernelGGL(k_gather_pivots, dim3(nblk, units), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_gather_pivots, dim3(nblk, units), dim3(256), 0, st, a);
 }
 
 }  // namespace verkv

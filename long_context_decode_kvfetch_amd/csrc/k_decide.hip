@@ -973,10 +973,16 @@ hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st) {
   const dim3 grid(rows * a.team), block(DC_NT);
   if (a.team > 1) {
     void *args[] = {&a};
+    if (g_launch_ev.start) {
+      (void)hipEventRecord(g_launch_ev.start, st);
+      const hipError_t e = hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, (unsigned)dyn, st);
+      (void)hipEventRecord(g_launch_ev.stop, st);
+      g_launch_ev.used = true;
+      return e;
+    }
     return hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, (unsigned)dyn, st);
   }
-  hipLaunchKernelGGL(k_decide, grid, block, dyn, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_decide, grid, block, (uint32_t)dyn, st, a);
 }
 
 int decide_blocks_per_cu(int max_n, int team) {
@@ -988,18 +994,15 @@ int decide_blocks_per_cu(int max_n, int team) {
 
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
   const int ncoef = (a.cap + UN_NT - 1) / UN_NT;
-  hipLaunchKernelGGL(k_union, dim3(units, 1 + ncoef), dim3(UN_NT), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_union, dim3(units, 1 + ncoef), dim3(UN_NT), 0, st, a);
 }
 
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_after, dim3(rows * a.team), dim3(DC_NT), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_after, dim3(rows * a.team), dim3(DC_NT), 0, st, a);
 }
 
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(k_finish, dim3(rows), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_finish, dim3(rows), dim3(256), 0, st, a);
 }
 
 }  // namespace verkv

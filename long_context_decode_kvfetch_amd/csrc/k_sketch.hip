@@ -3,7 +3,7 @@
 // "KVFETCH" step 1: estimated weights w_hat_i from the sketch; the decisions of
 // steps 2-4 are made on these weights, so they are kept in float64 end to end).
 //
-// Streaming layout: one wave owns SKETCH_CHUNK = 256 tokens of one (sequence, KV
+// Streaming layout: one wave owns SKETCH_CHUNK = 128 tokens of one (sequence, KV
 // head).  A key row is split over 8 lanes (16 when the group has more than four query
 // rows), each holding its float64 query elements in registers, so one wave load reads
 // whole rows (1 KB contiguous).  The per-lane partial dot products of four query rows
@@ -258,8 +258,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
 template <bool BF16, int G>
 static hipError_t launch_sketch_t(const SketchArgs &a, hipStream_t st) {
   const int blocks = (a.total_blocks + SK_WAVES - 1) / SK_WAVES;
-  hipLaunchKernelGGL((k_sketch<BF16, G>), dim3(blocks), dim3(SK_WAVES * WAVE), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_sketch<BF16, G>, dim3(blocks), dim3(SK_WAVES * WAVE), 0, st, a);
 }
 
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st) {

@@ -1,6 +1,7 @@
 // Kernel argument blocks and launchers of the VerKV library (internal).
 #pragma once
 #include "common.h"
+#include <hip/hip_ext.h>
 
 namespace verkv {
 
@@ -139,6 +140,25 @@ constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
 constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
 constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets nsp)
+
+// Timing of the next launch: when `start` is set, the launcher hands the pair to
+// hipExtLaunchKernel, which stamps them from the dispatch packet itself (kernel
+// execution time, without the gap before the dispatch), and marks them used.
+// Cooperative launches record them around the launch instead.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+extern thread_local LaunchEvents g_launch_ev;
+
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                                Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, g_launch_ev.start, g_launch_ev.stop, 0,
+                        args...);
+  if (g_launch_ev.start) g_launch_ev.used = true;
+  return hipGetLastError();
+}
 
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);

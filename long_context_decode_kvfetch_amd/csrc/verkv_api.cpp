@@ -196,19 +196,25 @@ struct Profiler {
   size_t used = 0;
 };
 Profiler g_prof;
+}  // namespace
+namespace verkv {
+thread_local LaunchEvents g_launch_ev;
+}
+namespace {
 
+// Hands the next launch an event pair; the launcher has the dispatch stamp them.
 struct Timed {
-  hipStream_t st;
   int slot = -1;
-  Timed(int kid, hipStream_t s) : st(s) {
+  Timed(int kid, hipStream_t) {
     if (g_prof.on && g_prof.used < g_prof.kind.size()) {
       slot = (int)g_prof.used++;
       g_prof.kind[slot] = kid;
-      (void)hipEventRecord(g_prof.ev[2 * slot], st);
+      g_launch_ev = {g_prof.ev[2 * slot], g_prof.ev[2 * slot + 1], false};
     }
   }
   ~Timed() {
-    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], st);
+    if (slot >= 0 && !g_launch_ev.used) g_prof.kind[slot] = -1;   // the launch failed early
+    g_launch_ev = LaunchEvents{};
   }
 };
 
@@ -569,7 +575,7 @@ int32_t verkv_profile_begin(int32_t max_launches) {
   g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
   g_prof.kind.assign((size_t)max_launches, -1);
   for (auto &e : g_prof.ev) {
-    hipError_t rc = hipEventCreate(&e);
+    hipError_t rc = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (rc != hipSuccess) {
       verkv_profile_end();
       return hip_fail(rc, "hipEventCreate");
@@ -584,6 +590,7 @@ int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kind
   if (!total_ms || !launches || n_kinds < VERKV_PROFILE_KINDS) return VERKV_EINVAL;
   for (int k = 0; k < VERKV_PROFILE_KINDS; ++k) { total_ms[k] = 0.0; launches[k] = 0; }
   for (size_t i = 0; i < g_prof.used; ++i) {
+    if (g_prof.kind[i] < 0) continue;
     HIP_TRY(hipEventSynchronize(g_prof.ev[2 * i + 1]), "hipEventSynchronize");
     float ms = 0.0f;
     HIP_TRY(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]), "hipEventElapsedTime");

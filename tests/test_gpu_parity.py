@@ -59,7 +59,7 @@ def test_gqa_layer_full_size_bf16():
 
 
 def test_ragged_tails_and_small_sequences():
-    """Lengths that are not multiples of the 256-token chunk or of 32-bit words, and
+    """Lengths that are not multiples of the sketch chunk or of 32-bit words, and
     several sequences (independent Philox stream ids)."""
     wl = synth.ragged_batch(seed=5, batch=3, n_min=1000, n_max=5000)
     wl.seqs[0] = synth.gqa_layer(seed=9, n=2333, steps=1).seqs[0]
