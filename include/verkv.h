@@ -133,12 +133,12 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
                             verkv_stream_t stream);
 size_t verkv_compress_workspace_bytes(const verkv_shape *s);
 
-/* KVFetch steps 1-4 and the resident half of step 5 (picx.dev summary, "KVFETCH";
- * Definition 2; Lemma 1): per query row, sketch weights over all n_b tokens, the
- * self-consistent shrinkage bias, eps_hat(L), the certified flag, and when it fails
- * the fetch order g (eq. 9) and k* (eq. 10); per KV head the union F of the
- * group's fetch sets; then attention partials over the resident pivots H u S with
- * coefficient 1 on H u (S n F) and lambda_i / r_i on S \ F.
+/* KVFetch steps 1-4 (picx.dev summary, "KVFETCH"; Definition 2; Lemma 1): per query
+ * row, sketch weights over all n_b tokens, the self-consistent shrinkage bias,
+ * eps_hat(L), the certified flag, and when it fails the fetch order g (eq. 9) and k*
+ * (eq. 10); per KV head the union F of the group's fetch sets, the fetch list and the
+ * estimator coefficients of the resident pivots (1 on H u (S n F), lambda_i / r_i on
+ * S \ F).
  *   q      [B][Hq][128] float32
  *   beta   multiplier kappa of the bias term inside the clip: 1 is the paper's
  *          estimator, +INFINITY gives lambda = 1 (Horvitz-Thompson), 0 gives
@@ -151,12 +151,16 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
                                double beta, double eps, double delta, verkv_step_out *out,
                                void *workspace, size_t workspace_bytes, verkv_stream_t stream);
 
-/* KVFetch step 5: reads the rows F \ S of V (and of K unless st->sketch_exact) from the
- * pinned host cache (zero-copy loads issued by the kernels), adds their exact terms, and finishes
- * every row: o = N_hat / D_hat, lse, n_hat, d_hat and eps_after = eps_hat(L \ F).
+/* KVFetch step 5: attention partials over the resident pivots H u S, the rows F \ S
+ * of V (and of K unless st->sketch_exact) read from the pinned host cache (zero-copy
+ * loads issued by the kernels) with their exact terms, and the finished rows:
+ * o = N_hat / D_hat, lse, n_hat, d_hat and eps_after = eps_hat(L \ F).
  * Must follow verkv_decode_step on the same stream with the same workspace, q, s
- * and st.  Rows whose KV head fetched nothing are finished from the resident
- * partials alone. */
+ * and st.  The resident-pivot and eps_after kernels run on a second stream of the
+ * library (one per device, default priority) while the host rows stream in on
+ * `stream`; the call joins it back into `stream` before the finishing kernel, so
+ * every result is ordered on `stream` as usual.  Rows whose KV head fetched nothing
+ * are finished from the resident partials alone. */
 verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
                           const void *K_host, const void *V_host, verkv_step_out *out,
                           void *workspace, size_t workspace_bytes, verkv_stream_t stream);
@@ -165,13 +169,13 @@ size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
 /* Optional kernel timing (instrumentation).  verkv_profile_begin creates 2*max_launches
  * HIP events (the only allocation the library makes, done here and not per step) and
  * turns recording on: every kernel launched afterwards by this library, up to
- * max_launches, is bracketed by events on the stream it runs on.  verkv_profile_report
+ * max_launches, is timed by an event pair that the dispatch itself stamps.  verkv_profile_report
  * waits for the recorded launches, writes per kernel kind the summed duration in ms
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
- * 7 finish, 8 eps_after partials), and clears the record.  verkv_profile_end destroys the events.  Not
+ * 7 finish, 8 eps_after partials, 9 pivot coefficients), and clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 9
+#define VERKV_PROFILE_KINDS 10
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);

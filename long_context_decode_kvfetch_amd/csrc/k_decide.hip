@@ -23,12 +23,12 @@
 // each owning a contiguous slice of the row's tokens (T = 16 puts the 32 rows of a
 // 32-query-head layer on all 256 CUs, two workgroups per CU).  Every reduction is first done inside the
 // workgroup, then combined across the team in a fixed member order after a barrier
-// on a counter in global memory; histograms are merged by bucket ranges (member m
-// merges buckets [m*NB/T, (m+1)*NB/T)).  Every member therefore sees identical
-// combined values and takes the same path through the phases.  With T > 1 the
-// kernel is launched cooperatively so that the whole team is resident; a barrier
-// wait is bounded and reports a timeout in the status word instead of hanging.
-// With T = 1 the barriers reduce to workgroup barriers and any grid size works.
+// on a counter in global memory; for the histograms every member sums all members'
+// copies in member order.  Every member therefore sees identical
+// combined values and takes the same path through the phases.  With T > 1 the grid
+// never exceeds what the device holds at once, so whole teams are resident; a
+// barrier wait is bounded and reports a timeout in the status word instead of
+// hanging.  With T = 1 the barriers reduce to workgroup barriers and any grid works.
 #include "kernels.h"
 
 namespace verkv {
@@ -220,28 +220,67 @@ __device__ __forceinline__ NewtonAcc block_newton(NewtonAcc v, double *scr /*[NQ
   return o;
 }
 
-// ------------------------------------------------------------------ team barrier
+// ------------------------------------------------------------------ team exchange
 constexpr uint32_t SPIN_LIMIT = 1u << 24;
 
-// One release add per workgroup (publishes the workgroup's stores, which the
-// workgroup barrier has already completed to L2), a spin on relaxed agent-scope loads
-// (these bypass the non-coherent caches without invalidating them), and one acquire
-// fence once the count is reached.
-__device__ __forceinline__ void team_barrier(uint32_t *ctr, uint32_t target, int32_t *status) {
+// Everything members exchange goes through agent-scope atomic stores and loads, which
+// the device keeps coherent across CUs and XCDs without whole-cache write-backs or
+// invalidations.  A member publishes exchange k by waiting until its own stores are
+// complete, then storing k into its sequence word; it proceeds once every member's
+// sequence word reads k.  Sequence words are double-buffered by the parity of k (and
+// cleared by the sketch kernel each step), so a member running one exchange ahead
+// never overwrites a word or a data slot that a slower member still has to read: to
+// write parity p again for exchange k + 2 it must have seen every member publish
+// k + 1, which each does only after reading the data of k.  The spin is bounded and
+// reports a timeout in the status word instead of hanging.
+__device__ __forceinline__ void xput(double *p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xput(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xput(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename X>
+__device__ __forceinline__ X xget(const X *p) {
+  return __hip_atomic_load(const_cast<X *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void team_exchange(double *seq /*[T] of this parity*/, int m, int T,
+                                              uint32_t k, int32_t *status) {
+  __builtin_amdgcn_s_waitcnt(0);          // this thread's exchange stores are complete
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const double kd = (double)k;
+  if (threadIdx.x == 0) xput(seq + m, kd);
+  if (threadIdx.x < (unsigned)T) {
     uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
+    while (xget(seq + threadIdx.x) != kd) {
       if (++spins > SPIN_LIMIT) {
         atomicOr(status, 4);
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   __syncthreads();
+}
+
+// OR the flags of the wave's 64 consecutive tokens base, base+1, ... into the bitmask:
+// one ballot, then lanes 0-2 OR the (at most three) 32-bit words the run touches.
+// Every lane of the wave must call it.
+__device__ __forceinline__ void or_bits_wave(uint32_t *fb, int base, bool flag, int lane) {
+  const uint64_t M = __ballot(flag);
+  if (!M) return;
+  const int sh = base & 31;
+  if (lane < 3) {
+    uint32_t v;
+    if (lane == 0) v = (uint32_t)(M << sh);
+    else if (lane == 1) v = (uint32_t)(M >> (32 - sh));
+    else v = sh ? (uint32_t)(M >> (64 - sh)) : 0u;
+    if (v) atomicOr(&fb[(base >> 5) + lane], v);
+  }
 }
 
 __device__ __forceinline__ Cert cert_combine(Cert a, const Cert &b) {
@@ -316,29 +355,32 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   const double *rr = a.r + tok_base(a.t, b, g);
   uint32_t *fb = a.fbits + word_base(a.t, b, g);
   const double kappa = a.kappa, l = a.l, eps = a.eps;
-  uint32_t *bar = a.bar + row;
-  double *part = a.part + (int64_t)row * 2 * T * PART;       // [2][T][PART]
-  uint32_t nbar = 0;
+  // exchange slots of this row, member stride TW (the workspace's team size)
+  const int TW = a.team_ws;
+  double *xseq = a.xseq + (int64_t)row * 2 * TW;              // [2][TW] sequence words
+  double *part = a.part + (int64_t)row * 2 * TW * PART;       // [2][TW][PART]
+  uint32_t nx = 0;                                             // exchanges done
+#define XPAR() ((int)((nx + 1) & 1))                            // parity of the next exchange
 #define TEAM_SYNC()                                                         \
   do {                                                                      \
-    if (T > 1) team_barrier(bar, (++nbar) * (uint32_t)T, a.status);         \
+    if (T > 1) { ++nx; team_exchange(xseq + (nx & 1) * TW, m, T, nx, a.status); } \
     else __syncthreads();                                                   \
   } while (0)
-#define SLOT() (part + (int64_t)(nbar & 1) * T * PART)
-  // exchange: every member has written its PART values to `sl` (tid 0); after the
-  // barrier the team's partials are staged in LDS with one parallel load
+#define SLOT() (part + (int64_t)XPAR() * TW * PART)
+  // exchange: every member has stored its PART values into `sl` (tid 0); after the
+  // exchange the team's partials are staged in LDS with one parallel load
 #define TEAM_STAGE(sl)                                                      \
   do {                                                                      \
     TEAM_SYNC();                                                            \
-    for (int j_ = tid; j_ < T * PART; j_ += DC_NT) s_part[j_] = (sl)[j_];   \
+    for (int j_ = tid; j_ < T * PART; j_ += DC_NT) s_part[j_] = xget((sl) + j_); \
     __syncthreads();                                                        \
   } while (0)
 #ifdef VERKV_PHASE_TIMING
   int nstamp = 0;
 #define STAMP()                                                                                  \
   do {                                                                                           \
-    if (tid == 0 && a.phase_clock && nstamp < 16)                                                \
-      a.phase_clock[((int64_t)row * T + m) * 16 + nstamp] = wall_clock64();                      \
+    if (tid == 0 && a.phase_clock && nstamp < 32)                                                \
+      a.phase_clock[((int64_t)row * T + m) * 32 + nstamp] = wall_clock64();                      \
     ++nstamp;                                                                                    \
   } while (0)
 #else
@@ -405,7 +447,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   auto combine_sum1 = [&](double v) -> double {
     if (T == 1) return v;
     double *sl = SLOT();
-    if (tid == 0) sl[m * PART] = v;
+    if (tid == 0) xput(sl + m * PART, v);
     TEAM_STAGE(sl);
     double t = 0.0;
     for (int k = 0; k < T; ++k) t += s_part[k * PART];
@@ -428,34 +470,42 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     bool done = false;
     for (int iter = 0; iter < 200; ++iter) {
       NewtonAcc v{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      // per token: lambda = r below aa = w (1 - r) / kappa, 1 above tt = aa / r, linear
+      // in between; two reciprocals, the rest products, no branch on the piece
       FOR_L(
         v.cnt += 1.0;
         if (ri == 0.0) { v.c0 += wi; }
         else if (wi != 0.0) {
-          const double aa = wi * (1.0 - ri) / kappa;
-          const double tt = aa / ri;
-          if (B <= aa) {
-            v.c0 += wi * (1.0 - ri); v.hi = fmin(v.hi, aa);
-            const Terms x = terms_of(wi, ri, ri);
-            v.vc += x.V; top2_merge(v.bc1, v.bc2, x.b, 0.0);
-          } else if (B >= tt) {
-            v.lo = fmax(v.lo, tt);
-            const Terms x = terms_of(wi, ri, 1.0);
-            v.vc += x.V; top2_merge(v.bc1, v.bc2, x.b, 0.0);
-          } else {
-            v.c0 += wi; v.c1 += kappa * ri / (1.0 - ri);
-            v.lo = fmax(v.lo, aa); v.hi = fmin(v.hi, tt);
-            v.vm += kappa * kappa * ri / (1.0 - ri);
-            top2_merge(v.bm1, v.bm2, kappa * fmax(ri, 1.0 - ri) / (1.0 - ri), 0.0);
-          }
+          const double q1 = 1.0 - ri;
+          const double ir = 1.0 / ri;
+          const double iq = 1.0 / q1;
+          const double wq = wi * q1;
+          const double aa = wq / kappa;
+          const double tt = aa * ir;
+          const double mx = fmax(ri, q1);
+          const bool plo = B <= aa;
+          const bool phi = !plo && B >= tt;
+          const bool pmid = !plo && !phi;
+          v.c0 += plo ? wq : (pmid ? wi : 0.0);
+          v.c1 += pmid ? kappa * ri * iq : 0.0;
+          v.vm += pmid ? kappa * kappa * ri * iq : 0.0;
+          v.vc += plo ? ri * wi * wq : (phi ? wi * wq * ir : 0.0);
+          v.lo = fmax(v.lo, plo ? 0.0 : (phi ? tt : aa));
+          v.hi = fmin(v.hi, plo ? aa : (phi ? INFINITY : tt));
+          const double bc = plo ? wi * mx : wi * mx * ir;
+          top2_merge(v.bc1, v.bc2, pmid ? 0.0 : bc, 0.0);
+          top2_merge(v.bm1, v.bm2, pmid ? kappa * mx * iq : 0.0, 0.0);
         })
+      STAMP();
       NewtonAcc o = block_newton(v, scr);
+      STAMP();
       if (T > 1) {
         double *sl = SLOT();
         if (tid == 0) {
           double *q = sl + m * PART;
-          q[0] = o.c0; q[1] = o.c1; q[2] = o.lo; q[3] = o.hi; q[4] = o.vc; q[5] = o.vm;
-          q[6] = o.cnt; q[7] = o.bc1; q[8] = o.bc2; q[9] = o.bm1; q[10] = o.bm2;
+          xput(q + 0, o.c0); xput(q + 1, o.c1); xput(q + 2, o.lo); xput(q + 3, o.hi);
+          xput(q + 4, o.vc); xput(q + 5, o.vm); xput(q + 6, o.cnt); xput(q + 7, o.bc1);
+          xput(q + 8, o.bc2); xput(q + 9, o.bm1); xput(q + 10, o.bm2);
         }
         TEAM_STAGE(sl);
         o = NewtonAcc{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
@@ -504,7 +554,10 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     nLt = block_sum<DC_NT>((double)nL, scr);
     if (T > 1) {
       double *sl = SLOT();
-      if (tid == 0) { double *q = sl + m * PART; q[0] = ct.beta; q[1] = ct.V; q[2] = ct.b1; q[3] = ct.b2; q[4] = nLt; }
+      if (tid == 0) {
+        double *q = sl + m * PART;
+        xput(q + 0, ct.beta); xput(q + 1, ct.V); xput(q + 2, ct.b1); xput(q + 3, ct.b2); xput(q + 4, nLt);
+      }
       TEAM_STAGE(sl);
       ct = Cert{0.0, 0.0, 0.0, 0.0};
       nLt = 0.0;
@@ -578,31 +631,62 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   uint32_t plo = 0;
   int lev = -1;
   bool above_mode = false;                               // cut above the whole window
-  const int64_t hrow = (int64_t)row * T * NBUCKET;
+  const int64_t hrow = (int64_t)row * 2 * TW * NBUCKET;       // [2][TW][NBUCKET] per row
 
   for (int L = 0; L < NLEV; ++L) {
     for (int k = tid; k < NBUCKET; k += DC_NT) { h_cnt[k] = 0; h_beta[k] = 0.0; h_V[k] = 0.0; h_b[k] = 0; }
     __syncthreads();
     const int sh = c_lev_shift[L];
     const uint32_t dmask = (1u << c_lev_width[L]) - 1u;
-    FOR_SEL(
-      if (cmp_window(key, lo, lev, pkey, plo) == 0) {
-        const uint32_t dig = c_lev_lo[L] ? ((lo >> sh) & dmask) : (uint32_t)((key >> sh) & dmask);
+    auto hist_tok = [&](bool act, uint64_t key, uint32_t lo, const Terms &x) {
+      const uint32_t dig = c_lev_lo[L] ? ((lo >> sh) & dmask) : (uint32_t)((key >> sh) & dmask);
+      if (act) {
         atomicAdd(&h_cnt[dig], 1u);
         atomicAdd(&h_beta[dig], x.beta);
         atomicAdd(&h_V[dig], x.V);
         atomicMax((unsigned long long *)&h_b[dig], (unsigned long long)dbits(x.b));
-      })
+      }
+    };
+    if (cached) {
+#pragma unroll
+      for (int k = 0; k < TR; ++k) {
+        const int i = s0 + tid + k * DC_NT;
+        const uint32_t lo = IDX_MAX - (uint32_t)i;
+        const bool act = cin[k] && cmp_window(ckey[k], lo, lev, pkey, plo) == 0;
+        hist_tok(act, ckey[k], lo, Terms{cbeta[k], cV[k], cb[k]});
+      }
+    } else {
+      for (int i0 = s0; i0 < s1; i0 += DC_NT) {
+        const int i = i0 + tid;
+        const uint32_t lo = IDX_MAX - (uint32_t)i;
+        bool act = false;
+        uint64_t key = 0;
+        Terms x{0.0, 0.0, 0.0};
+        if (i < s1) {
+          const double ri = rr[i];
+          if (ri < 1.0) {
+            const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
+            x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+            key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));
+            act = cmp_window(key, lo, lev, pkey, plo) == 0;
+          }
+        }
+        hist_tok(act, key, lo, x);
+      }
+    }
     __syncthreads();
     STAMP();
     if (T > 1) {
       // publish this member's histogram; after the barrier every member sums all of
       // them in member order, so all hold the same merged histogram
-      const int64_t hm = hrow + (int64_t)m * NBUCKET;
+      const int64_t hp = hrow + (int64_t)XPAR() * TW * NBUCKET;   // this exchange's buffer
+      const int64_t hm = hp + (int64_t)m * NBUCKET;
       for (int k = tid; k < NBUCKET; k += DC_NT) {
-        a.hcnt[hm + k] = h_cnt[k]; a.hbeta[hm + k] = h_beta[k]; a.hV[hm + k] = h_V[k]; a.hmax[hm + k] = h_b[k];
+        xput(a.hcnt + hm + k, h_cnt[k]); xput(a.hbeta + hm + k, h_beta[k]);
+        xput(a.hV + hm + k, h_V[k]); xput(a.hmax + hm + k, h_b[k]);
       }
       TEAM_SYNC();
+      STAMP();
       for (int k = tid; k < NBUCKET; k += DC_NT) {
         uint32_t c = 0; double sb = 0.0, sv = 0.0; uint64_t mb = 0;
         for (int q0 = 0; q0 < T; q0 += 4) {          // four members' loads in flight
@@ -611,8 +695,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
           for (int u = 0; u < 4; ++u) {
             qc[u] = 0; qb[u] = 0.0; qv[u] = 0.0; qm[u] = 0;
             if (q0 + u < T) {
-              const int64_t o = hrow + (int64_t)(q0 + u) * NBUCKET + k;
-              qc[u] = a.hcnt[o]; qb[u] = a.hbeta[o]; qv[u] = a.hV[o]; qm[u] = a.hmax[o];
+              const int64_t o = hp + (int64_t)(q0 + u) * NBUCKET + k;
+              qc[u] = xget(a.hcnt + o); qb[u] = xget(a.hbeta + o); qv[u] = xget(a.hV + o); qm[u] = xget(a.hmax + o);
             }
           }
 #pragma unroll
@@ -623,6 +707,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         h_cnt[k] = c; h_beta[k] = sb; h_V[k] = sv; h_b[k] = mb;
       }
       __syncthreads();
+      STAMP();
     }
     // inclusive scan over buckets (thread k owns bucket k): beta, V sums and max b
     double sb = h_beta[tid], sv = h_V[tid], smx = bitsd(h_b[tid]);
@@ -676,7 +761,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       else if (cw2 == 0) {
         if (T > 1) {
           const uint32_t p = atomicAdd(&a.wcount[row], 1u);
-          if (p < (uint32_t)WIN) { gkey[p] = key; glo[p] = lo; }
+          if (p < (uint32_t)WIN) { xput(gkey + p, key); xput(glo + p, lo); }
         } else {
           const int p = atomicAdd(&s_int[1], 1);
           if (p < WIN) { w_key[p] = key; w_lo[p] = lo; }
@@ -686,14 +771,14 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     int wcount;
     if (T > 1) {
       double *sl = SLOT();
-      if (tid == 0) { sl[m * PART] = bo.s0; sl[m * PART + 1] = bo.s1; sl[m * PART + 2] = bo.mx; }
+      if (tid == 0) { xput(sl + m * PART, bo.s0); xput(sl + m * PART + 1, bo.s1); xput(sl + m * PART + 2, bo.mx); }
       TEAM_STAGE(sl);
       bo = Red4{0.0, 0.0, 0.0, 0.0};
       for (int k = 0; k < T; ++k) {
         bo.s0 += s_part[k * PART]; bo.s1 += s_part[k * PART + 1]; bo.mx = fmax(bo.mx, s_part[k * PART + 2]);
       }
       wcount = min((int)__hip_atomic_load(&a.wcount[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), WIN);
-      for (int k = tid; k < wcount; k += DC_NT) { w_key[k] = gkey[k]; w_lo[k] = glo[k]; }
+      for (int k = tid; k < wcount; k += DC_NT) { w_key[k] = xget(gkey + k); w_lo[k] = xget(glo + k); }
       __syncthreads();
     } else {
       wcount = min(s_int[1], WIN);
@@ -786,12 +871,37 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
 
   STAMP();
   // ---- mark F_h = tokens at or after the cut in g-descending order
+  // one ballot per wave and token group; at most three word ORs per wave instead of
+  // one atomic per fetched token
   int64_t kc = 0;
-  FOR_SEL(
-    bool inF;
-    if (above_mode) inF = cmp_window(key, lo, lev, pkey, plo) > 0;
-    else inF = (key > tkey) || (key == tkey && lo >= tlo);
-    if (inF) { atomicOr(&fb[i >> 5], 1u << (i & 31)); ++kc; })
+  auto in_F = [&](uint64_t key, uint32_t lo) -> bool {
+    if (above_mode) return cmp_window(key, lo, lev, pkey, plo) > 0;
+    return (key > tkey) || (key == tkey && lo >= tlo);
+  };
+  if (cached) {
+#pragma unroll
+    for (int k = 0; k < TR; ++k) {
+      const int i = s0 + tid + k * DC_NT;
+      const bool f = cin[k] && in_F(ckey[k], IDX_MAX - (uint32_t)i);
+      kc += f ? 1 : 0;
+      or_bits_wave(fb, i - lane, f, lane);
+    }
+  } else {
+    for (int i0 = s0; i0 < s1; i0 += DC_NT) {
+      const int i = i0 + tid;
+      bool f = false;
+      if (i < s1) {
+        const double ri = rr[i];
+        if (ri < 1.0) {
+          const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
+          const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+          f = in_F(dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd)), IDX_MAX - (uint32_t)i);
+        }
+      }
+      kc += f ? 1 : 0;
+      or_bits_wave(fb, i - lane, f, lane);
+    }
+  }
   const int64_t ks = block_sum_i64<DC_NT>(kc, (int64_t *)scr);
   if (tid == 0 && ks) atomicAdd(&a.kstar[row], (int32_t)ks);
   STAMP();
@@ -804,10 +914,10 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
 }
 
 // ------------------------------------------------------------------ union, lists, pivot coefficients
-// Block 0 of a KV head compacts its fetch bitmask into the ascending list F and the
-// list F \ S of host rows; the other blocks give every resident pivot its estimator
-// coefficient for every query row of the group: 1 on H and on S n F, lambda_i / r_i
-// on S \ F (Definition 2 with the fetched tokens exact).
+// List pass (one block per KV head): compacts the head's fetch bitmask into the
+// ascending list F and the list F \ S of host rows.  Coefficient pass: gives every
+// resident pivot its estimator coefficient for every query row of the group: 1 on H
+// and on S n F, lambda_i / r_i on S \ F (Definition 2 with the fetched tokens exact).
 constexpr int UN_NT = 1024;
 
 __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
@@ -820,28 +930,58 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
   const int Hq = a.t.Hkv * G;
   const int tid = threadIdx.x;
   const uint32_t *fb = a.fbits + word_base(a.t, b, g);
-  if (blockIdx.y == 0) {
+  if (!a.coef_pass) {
+    // Every wave owns a contiguous run of 64-token groups (two bitmask words).  Pass 1
+    // counts each wave's tokens; a block scan gives each wave its first list
+    // position; pass 2 walks the groups in order, one lane per token, and writes the
+    // set bits with a ballot prefix so that consecutive list entries come from
+    // consecutive lanes (whole-line stores).
+    constexpr int NWV = UN_NT / WAVE;
     const uint32_t *res = a.resident + word_base(a.t, b, g);
     const int W = words_of(n);
-    const int wpt = (W + UN_NT - 1) / UN_NT;
-    const int w0 = tid * wpt, w1 = min(W, w0 + wpt);
+    const int ngrp = (W + 1) / 2;
+    const int gpw = (ngrp + NWV - 1) / NWV;
+    const int lane = tid & (WAVE - 1);
+    const int wv = tid / WAVE;
+    const int ga = min(ngrp, wv * gpw), gb = min(ngrp, ga + gpw);
+    auto group_bits = [&](const uint32_t *wd, int gi) -> uint64_t {
+      const uint64_t lo32 = wd[2 * gi];
+      const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
+      return lo32 | (hi32 << 32);
+    };
     int32_t cf = 0, ch = 0;
-    for (int w = w0; w < w1; ++w) { cf += __popc(fb[w]); ch += __popc(fb[w] & ~res[w]); }
+    for (int gi = ga + lane; gi < gb; gi += WAVE) {
+      const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
+      cf += __popcll(f);
+      ch += __popcll(f & ~r);
+    }
+    cf = (int32_t)wave_sum_i64(cf);
+    ch = (int32_t)wave_sum_i64(ch);
     int32_t tf, th;
-    int32_t pf = block_excl_scan<UN_NT>(cf, iscr, &tf);
-    int32_t ph = block_excl_scan<UN_NT>(ch, iscr, &th);
+    int32_t pf = block_excl_scan<UN_NT>(lane == 0 ? cf : 0, iscr, &tf);
+    int32_t ph = block_excl_scan<UN_NT>(lane == 0 ? ch : 0, iscr, &th);
+    pf = __shfl(pf, 0, WAVE);                 // the wave's first positions (lane 0's)
+    ph = __shfl(ph, 0, WAVE);
     int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
     int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = fb[w];
-      const uint32_t rw = res[w];
-      while (bits) {
-        const int j = __ffs(bits) - 1;
-        bits &= bits - 1;
-        const int tok = 32 * w + j;
-        if (fl && pf < a.fetch_cap) fl[pf] = tok;
-        ++pf;
-        if (!((rw >> j) & 1)) hl[ph++] = tok;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int c0 = ga; c0 < gb; c0 += WAVE) {
+      // lane j holds group c0 + j; the walk below takes them in order by shuffle
+      uint64_t fl_l = 0, rl_l = 0;
+      if (c0 + lane < gb) { fl_l = group_bits(fb, c0 + lane); rl_l = group_bits(res, c0 + lane); }
+      const int nj = min(WAVE, gb - c0);
+      for (int jj = 0; jj < nj; ++jj) {
+        const uint64_t f = __shfl(fl_l, jj, WAVE), r = __shfl(rl_l, jj, WAVE);
+        const uint64_t hsel = f & ~r;
+        const bool inf = (f >> lane) & 1ull, inh = (hsel >> lane) & 1ull;
+        const int tok = 64 * (c0 + jj) + lane;
+        if (inf) {
+          const int32_t pos = pf + (int32_t)__popcll(f & below);
+          if (fl && pos < a.fetch_cap) fl[pos] = tok;
+        }
+        if (inh) hl[ph + (int32_t)__popcll(hsel & below)] = tok;
+        pf += (int32_t)__popcll(f);
+        ph += (int32_t)__popcll(hsel);
       }
     }
     if (tid == 0) {
@@ -851,8 +991,9 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
     return;
   }
   const int cnt = min(a.piv_count[unit], a.cap);
-  const int p = (blockIdx.y - 1) * UN_NT + tid;
+  const int p = blockIdx.y * UN_NT + tid;
   if (p >= cnt) return;
+  const double kappa = a.params[0];
   const int tok = a.piv_idx[(int64_t)unit * a.cap + p];
   const double ri = a.r[tok_base(a.t, b, g) + tok];
   const bool exact = (ri >= 1.0) || ((fb[tok >> 5] >> (tok & 31)) & 1);
@@ -862,7 +1003,7 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
     if (!exact) {
       const double wi = a.wc[row_tok_base(a.t, b, h) + tok] *
                         a.cscale[row_chunk_base(a.t, b, h) + tok / SKETCH_CHUNK];
-      const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], a.kappa);
+      const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], kappa);
       cf32 = (float)(lam / ri);
     }
     a.coef[((int64_t)b * Hq + h) * a.cap + p] = cf32;
@@ -924,12 +1065,25 @@ __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
   const int unit = b * a.t.Hkv + g;
   const int tid = threadIdx.x;
   constexpr int PS = D + 1;
+  // partials in split order; 16 loads in flight per batch (the order of the sum is
+  // unchanged, only the loads are issued ahead)
+  constexpr int FB = 16;
+  auto add_parts = [&](const float *base, int ns, float acc) -> float {
+    const int64_t stride = (int64_t)a.t.G * PS;
+    for (int s0 = 0; s0 < ns; s0 += FB) {
+      float v[FB];
+#pragma unroll
+      for (int u = 0; u < FB; ++u) v[u] = s0 + u < ns ? base[(s0 + u) * stride] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < FB; ++u)
+        if (s0 + u < ns) acc += v[u];
+    }
+    return acc;
+  };
   float acc = 0.0f;
   if (tid <= D) {
-    for (int s = 0; s < a.nsp; ++s)
-      acc += a.piv_part[(((int64_t)unit * a.nsp + s) * a.t.G + j) * PS + tid];
-    for (int s = 0; s < a.nsh; ++s)
-      acc += a.host_part[(((int64_t)unit * a.nsh + s) * a.t.G + j) * PS + tid];
+    acc = add_parts(a.piv_part + ((int64_t)unit * a.nsp * a.t.G + j) * PS + tid, a.nsp, acc);
+    acc = add_parts(a.host_part + ((int64_t)unit * a.nsh * a.t.G + j) * PS + tid, a.nsh, acc);
     if (tid == D) s_d = acc;
   }
   __syncthreads();
@@ -971,17 +1125,10 @@ hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st) {
   a.lds_cache = decide_slice_cached(a.t.max_n, a.team) ? 1 : 0;
   const size_t dyn = decide_lds_bytes(a.nch_max, a.lds_cache != 0);
   const dim3 grid(rows * a.team), block(DC_NT);
-  if (a.team > 1) {
-    void *args[] = {&a};
-    if (g_launch_ev.start) {
-      (void)hipEventRecord(g_launch_ev.start, st);
-      const hipError_t e = hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, (unsigned)dyn, st);
-      (void)hipEventRecord(g_launch_ev.stop, st);
-      g_launch_ev.used = true;
-      return e;
-    }
-    return hipLaunchCooperativeKernel((const void *)k_decide, grid, block, args, (unsigned)dyn, st);
-  }
+  // An ordinary launch: the caller sizes the grid to what the device holds at once
+  // (decide_blocks_per_cu x CUs), so every team is co-resident once earlier work on
+  // the stream has drained; a barrier wait that cannot complete still ends (bounded
+  // spin, status bit 4).  This avoids the cooperative launch's fixed cost per step.
   return launch_kernel(k_decide, grid, block, (uint32_t)dyn, st, a);
 }
 
@@ -993,8 +1140,8 @@ int decide_blocks_per_cu(int max_n, int team) {
 }
 
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
-  const int ncoef = (a.cap + UN_NT - 1) / UN_NT;
-  return launch_kernel(k_union, dim3(units, 1 + ncoef), dim3(UN_NT), 0, st, a);
+  const int ny = a.coef_pass ? (a.cap + UN_NT - 1) / UN_NT : 1;
+  return launch_kernel(k_union, dim3(units, ny), dim3(UN_NT), 0, st, a);
 }
 
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {

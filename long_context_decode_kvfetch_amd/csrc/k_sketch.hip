@@ -15,7 +15,8 @@
 // where f(0)_c = sum over the chunk's tokens of L of wc_i (1 - r_i): the bias of the
 // shrinkage estimator at beta = 0.  The decision kernel rescales by exp(m_c - m_hat)
 // once m_hat = max_c m_c is known.  The workgroup also clears the chunk's words of the
-// step's fetch bitmask and, on chunk 0, the decision kernel's per-row counters.
+// step's fetch bitmask and, on chunk 0, the decision kernel's per-row counters and
+// exchange sequence words.
 #include "kernels.h"
 
 namespace verkv {
@@ -120,11 +121,13 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
     const int w = c * (CH / 32) + lane;
     if (w < words_of(n)) a.fbits[word_base(a.t, b, g) + w] = 0u;
   }
-  if (c == 0 && lane < G) {
-    const int64_t row = (int64_t)b * a.t.Hkv * G + g * G + lane;
-    a.bar[row] = 0u;
-    a.wcount[row] = 0u;
-    a.kstar[row] = 0;
+  if (c == 0) {
+    const int64_t row0 = ((int64_t)b * a.t.Hkv + g) * G;
+    if (lane < G) {
+      a.wcount[row0 + lane] = 0u;
+      a.kstar[row0 + lane] = 0;
+    }
+    for (int i = lane; i < G * a.xseq_row; i += WAVE) a.xseq[row0 * a.xseq_row + i] = 0.0;
   }
 
   // float64 query elements of the pieces sidx, sidx + LPT, ...

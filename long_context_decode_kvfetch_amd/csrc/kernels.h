@@ -40,7 +40,9 @@ struct SketchArgs {
   const double *r;            // [B][Hkv][n] inclusion probabilities
   double *cf0;                // [B][Hq][nchunks]  sum over L of wc (1 - r): f(0) per chunk
   uint32_t *fbits;            // [B][Hkv][W]  cleared here
-  uint32_t *bar, *wcount;     // [B][Hq] decision-kernel counters, cleared here
+  uint32_t *wcount;           // [B][Hq] decision-kernel window counters, cleared here
+  double *xseq;               // [B][Hq][xseq_row] team exchange sequence words, cleared here
+  int32_t xseq_row;
   int32_t *kstar;             // [B][Hq] cleared here
   int32_t total_blocks;
 };
@@ -62,15 +64,16 @@ struct DecideArgs {
   // team workspace (T workgroups per row)
   int32_t team;
   int32_t xcd_map;           // 1: map the members of a team to one XCD
-  uint32_t *bar;             // [rows] barrier counters (cleared by the sketch kernel)
-  double *part;              // [rows][2][T][PART] member partials
-  uint32_t *hcnt;            // [rows][T][NBUCKET] member histograms
+  int32_t team_ws;           // member stride TW of the exchange slots (team >= launched T)
+  double *xseq;              // [rows][2][TW] exchange sequence words (cleared by the sketch kernel)
+  double *part;              // [rows][2][TW][PART] member partials
+  uint32_t *hcnt;            // [rows][2][TW][NBUCKET] member histograms
   double *hbeta, *hV;
   uint64_t *hmax;
   uint64_t *wkey;            // [rows][WIN] final window
   uint32_t *wlo;
   uint32_t *wcount;          // [rows] (cleared by the sketch kernel)
-  uint64_t *phase_clock;     // [rows][T][16] phase timestamps (VERKV_PHASE_TIMING builds)
+  uint64_t *phase_clock;     // [rows][T][32] phase timestamps (VERKV_PHASE_TIMING builds)
   int32_t nch_max;           // chunk scales held in dynamic LDS
   int32_t lds_cache;         // 1: the launch reserved LDS for the (w, r) slice cache
 };
@@ -97,6 +100,8 @@ struct UnionArgs {
   int32_t *fetch_count, *h2d_count;
   int32_t *h2d_idx;          // [B][Hkv][n]
   float *coef;               // [B][Hq][cap]
+  int32_t coef_pass;         // 0: fetch lists (grid y = 1); 1: pivot coefficients
+  const double *params;      // coefficient pass: params[0] = kappa of the step (device)
 };
 
 struct AttendArgs {
@@ -144,7 +149,6 @@ constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets ns
 // Timing of the next launch: when `start` is set, the launcher hands the pair to
 // hipExtLaunchKernel, which stamps them from the dispatch packet itself (kernel
 // execution time, without the gap before the dispatch), and marks them used.
-// Cooperative launches record them around the launch instead.
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
   bool used = false;

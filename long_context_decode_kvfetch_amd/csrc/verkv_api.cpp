@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -93,7 +94,7 @@ int team_size(int rows, int max_n) {
 // Decode workspace layout.
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
-  size_t bar, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0;
+  size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0;
   size_t total;
   int nsp, nsh, team;
 };
@@ -108,14 +109,14 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.team = team_size((int)rows, t.max_n);
   const int64_t tm = w.team > 1 ? w.team : 0;       // member histograms only for teams
   size_t off = 0;
-  w.bar = off;    off = align_up(off + 4 * (size_t)rows);
+  w.xseq = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team));
   w.wcount = off; off = align_up(off + 4 * (size_t)rows);
   w.part = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team * PART));
   w.apart = off;  off = align_up(off + 8 * (size_t)(rows * w.team * 8));
-  w.hcnt = off;   off = align_up(off + 4 * (size_t)(rows * tm * NBUCKET));
-  w.hbeta = off;  off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
-  w.hV = off;     off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
-  w.hmax = off;   off = align_up(off + 8 * (size_t)(rows * tm * NBUCKET));
+  w.hcnt = off;   off = align_up(off + 4 * (size_t)(rows * 2 * tm * NBUCKET));   // two buffers
+  w.hbeta = off;  off = align_up(off + 8 * (size_t)(rows * 2 * tm * NBUCKET));
+  w.hV = off;     off = align_up(off + 8 * (size_t)(rows * 2 * tm * NBUCKET));
+  w.hmax = off;   off = align_up(off + 8 * (size_t)(rows * 2 * tm * NBUCKET));
   const int64_t mm = w.team > 1 ? 1 : 0;
   w.wkey = off;   off = align_up(off + 8 * (size_t)(rows * mm * WIN));
   w.wlo = off;    off = align_up(off + 4 * (size_t)(rows * mm * WIN));
@@ -187,8 +188,39 @@ int decide_capacity(int max_n, int team) {
   return cus * decide_blocks_per_cu(max_n, team);
 }
 
+// ---------------------------------------------------------------- side stream
+// verkv_refine runs the resident-pivot attention and the eps_after pass on a second
+// stream of the library (default priority) while the host-row kernel, bound by the host
+// link, runs on the caller's stream; both are joined before the finishing kernel.  One
+// stream and one event pair per device, created on first use; the fork and join of one
+// call are recorded under a per-device lock.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int MAX_DEVICES = 64;
+Side g_side[MAX_DEVICES];
+std::mutex g_side_init;
+
+verkv_status side_for_device(Side **out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return VERKV_EUNSUPPORTED;
+  Side &sd = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (!sd.s) {
+    HIP_TRY(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming), "hipEventCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming), "hipEventCreateWithFlags");
+  }
+  *out = &sd;
+  return VERKV_OK;
+}
+
 // ---------------------------------------------------------------- optional kernel timing
-enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER, K_COUNT };
+enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER,
+                K_COEF, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -222,7 +254,7 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 102; }
+int32_t verkv_version(void) { return 103; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -367,8 +399,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.r = st->r;
   sk.cf0 = reinterpret_cast<double *>(ws + L.cf0);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
-  sk.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
   sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
+  sk.xseq = reinterpret_cast<double *>(ws + L.xseq);
+  sk.xseq_row = 2 * L.team;
   sk.kstar = out->kstar;
   sk.total_blocks = (int32_t)(t.Hkv * T.chunks);
   {
@@ -399,7 +432,8 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   while (team > 1 && team * rows > decide_capacity(t.max_n, team)) --team;
   dc.team = team;
   dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;
-  dc.bar = sk.bar;
+  dc.team_ws = L.team;
+  dc.xseq = sk.xseq;
   dc.part = reinterpret_cast<double *>(ws + L.part);
   dc.hcnt = reinterpret_cast<uint32_t *>(ws + L.hcnt);
   dc.hbeta = reinterpret_cast<double *>(ws + L.hbeta);
@@ -410,7 +444,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.wcount = sk.wcount;
   dc.phase_clock = nullptr;
 #ifdef VERKV_PHASE_TIMING
-  if (workspace_bytes >= L.total + (size_t)rows * team * 16 * 8)
+  if (workspace_bytes >= L.total + (size_t)rows * team * 32 * 8)
     dc.phase_clock = reinterpret_cast<uint64_t *>(ws + L.total);
 #endif
   {
@@ -436,30 +470,13 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   un.h2d_count = out->h2d_count;
   un.h2d_idx = reinterpret_cast<int32_t *>(ws + L.h2d);
   un.coef = reinterpret_cast<float *>(ws + L.coef);
+  un.params = nullptr;
+  un.coef_pass = 0;
   {
     Timed tm(K_UNION, stream);
     HIP_TRY(launch_union(un, units, stream), "union launch");
   }
 
-  AttendArgs at;
-  at.t = t;
-  at.q = q;
-  at.m_hat = out->m_hat;
-  at.inv_sqrt_d = (float)(1.0 / std::sqrt((double)VERKV_HEAD_DIM));
-  at.krows = static_cast<const uint8_t *>(st->piv_k);
-  at.vrows = static_cast<const uint8_t *>(st->piv_v);
-  at.count = st->piv_count;
-  at.list = nullptr;
-  at.coef = un.coef;
-  at.cap = st->cap;
-  at.part = reinterpret_cast<float *>(ws + L.ppart);
-  at.nsplit = L.nsp;
-  at.wc = nullptr;
-  at.cscale = nullptr;
-  {
-    Timed tm(K_PIVOT, stream);
-    HIP_TRY(launch_attend(at, units, bf16, false, false, stream), "pivot attention launch");
-  }
   return VERKV_OK;
 }
 
@@ -483,6 +500,14 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
 
+  Side *sd = nullptr;
+  if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
+  std::lock_guard<std::mutex> lk(sd->mu);
+  // fork: the side stream starts where the caller's stream is now
+  HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
+
+  // caller's stream: rows F \ S from the host cache
   AttendArgs at;
   at.t = t;
   at.q = q;
@@ -504,6 +529,53 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
             "host attention launch");
   }
 
+  // side stream: estimator coefficients of the resident pivots, their attention
+  // partials, then eps_after
+  UnionArgs un;
+  un.t = t;
+  un.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  un.resident = st->resident;
+  un.piv_idx = st->piv_idx;
+  un.piv_count = st->piv_count;
+  un.cap = st->cap;
+  un.r = st->r;
+  un.wc = reinterpret_cast<const double *>(ws + L.wc);
+  un.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  un.beta_star = out->beta_star;
+  un.kappa = 0.0;
+  un.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa of the step
+  un.fetch_idx = nullptr;
+  un.fetch_cap = 0;
+  un.fetch_count = nullptr;
+  un.h2d_count = nullptr;
+  un.h2d_idx = nullptr;
+  un.coef = reinterpret_cast<float *>(ws + L.coef);
+  un.coef_pass = 1;
+  {
+    Timed tm(K_COEF, sd->s);
+    HIP_TRY(launch_union(un, units, sd->s), "pivot coefficient launch");
+  }
+
+  AttendArgs pv;
+  pv.t = t;
+  pv.q = q;
+  pv.m_hat = out->m_hat;
+  pv.inv_sqrt_d = at.inv_sqrt_d;
+  pv.krows = static_cast<const uint8_t *>(st->piv_k);
+  pv.vrows = static_cast<const uint8_t *>(st->piv_v);
+  pv.count = st->piv_count;
+  pv.list = nullptr;
+  pv.coef = reinterpret_cast<const float *>(ws + L.coef);
+  pv.cap = st->cap;
+  pv.part = reinterpret_cast<float *>(ws + L.ppart);
+  pv.nsplit = L.nsp;
+  pv.wc = nullptr;
+  pv.cscale = nullptr;
+  {
+    Timed tm(K_PIVOT, sd->s);
+    HIP_TRY(launch_attend(pv, units, bf16, false, false, sd->s), "pivot attention launch");
+  }
+
   AfterArgs af;
   af.t = t;
   af.wc = reinterpret_cast<const double *>(ws + L.wc);
@@ -515,9 +587,13 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   af.team = L.team;
   af.part = reinterpret_cast<double *>(ws + L.apart);
   {
-    Timed tm(K_AFTER, stream);
-    HIP_TRY(launch_after(af, rows, stream), "eps_after launch");
+    Timed tm(K_AFTER, sd->s);
+    HIP_TRY(launch_after(af, rows, sd->s), "eps_after launch");
   }
+
+  // join before the finishing kernel
+  HIP_TRY(hipEventRecord(sd->join, sd->s), "hipEventRecord");
+  HIP_TRY(hipStreamWaitEvent(stream, sd->join, 0), "hipStreamWaitEvent");
 
   FinishArgs fi;
   fi.t = t;

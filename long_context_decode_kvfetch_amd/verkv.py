@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 9
+PROFILE_KINDS = 10
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
-                "attend_pivots", "attend_host", "finish", "eps_after"]
+                "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef"]
 
 
 class VerKVError(RuntimeError):
