@@ -89,14 +89,7 @@ __device__ __forceinline__ double wave_sum(double v) {
   v += shfl_xor_d(v, 32);
   return v;
 }
-__device__ __forceinline__ double wave_max(double v) {
-  for (int m = 1; m < WAVE; m <<= 1) v = fmax(v, shfl_xor_d(v, m));
-  return v;
-}
-__device__ __forceinline__ double wave_min(double v) {
-  for (int m = 1; m < WAVE; m <<= 1) v = fmin(v, shfl_xor_d(v, m));
-  return v;
-}
+
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
   for (int m = 1; m < WAVE; m <<= 1) v += __shfl_xor(v, m, WAVE);
   return v;
@@ -122,6 +115,18 @@ __device__ __forceinline__ double min16(double v) {
   v = fmin(v, dpp_d<DPP_HALF_MIRROR>(v));
   v = fmin(v, dpp_d<DPP_MIRROR>(v));
   return v;
+}
+
+// wave-wide maximum / minimum: DPP inside each row of 16 lanes, then two shuffles
+__device__ __forceinline__ double wave_max(double v) {
+  v = max16(v);
+  v = fmax(v, shfl_xor_d(v, 16));
+  return fmax(v, shfl_xor_d(v, 32));
+}
+__device__ __forceinline__ double wave_min(double v) {
+  v = min16(v);
+  v = fmin(v, shfl_xor_d(v, 16));
+  return fmin(v, shfl_xor_d(v, 32));
 }
 
 // Block-wide reductions in a fixed order (deterministic): each wave reduces, lane k of

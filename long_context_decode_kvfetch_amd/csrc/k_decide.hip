@@ -31,6 +31,8 @@
 // hanging.  With T = 1 the barriers reduce to workgroup barriers and any grid works.
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace verkv {
 
 constexpr int DC_NT = DECIDE_THREADS;
@@ -67,20 +69,44 @@ __device__ __forceinline__ Terms terms_of(double w, double r, double lam) {
   return t;
 }
 
+// terms_of(w, r, lam_of(w, r, B, kappa)) written with 1/r (ir) and r/(1-r) (rq) at
+// hand: lambda w is kB rq on the middle piece, so every term is a product.
+__device__ __forceinline__ Terms terms_at(double w, double r, double ir, double rq, double kB,
+                                          bool kinf) {
+  Terms t{0.0, 0.0, 0.0};
+  if (r == 0.0) { t.beta = w; return t; }             // lambda = 0
+  if (w == 0.0) return t;                             // lambda = 1, nothing left
+  const double q1 = 1.0 - r, mx = fmax(r, q1);
+  const double num = kinf ? INFINITY : kB * rq;       // lambda w before the clip
+  if (num >= w) {                                     // lambda = 1
+    t.V = w * w * q1 * ir;
+    t.b = w * mx * ir;
+  } else if (num <= r * w) {                          // lambda = r
+    t.beta = w * q1;
+    t.V = r * w * w * q1;
+    t.b = w * mx;
+  } else {                                            // lambda w = kB rq
+    t.beta = w - num;
+    t.V = num * num * q1 * ir;
+    t.b = num * mx * ir;
+  }
+  return t;
+}
+
 __device__ __forceinline__ double bern_E(double beta, double V, double b, double l) {
   const double t = b * l / 3.0;
   return beta + t + sqrt(t * t + 2.0 * V * l);
 }
 
 // g_i of eq. (9), lambda frozen; sqrt(X) - sqrt(Y) evaluated as (X - Y)/(sqrt X + sqrt Y).
+// sqX = sqrt(X) with X = (b1 l/3)^2 + 2 V l is the same for every token of the row.
 __device__ __forceinline__ double g_of(const Terms &x, double V, double b1, double b2, double l,
-                                       double Dd) {
+                                       double Dd, double sqX) {
   const double bm = (x.b == b1) ? b2 : b1;
   const double t1 = b1 * l / 3.0, tm = bm * l / 3.0;
-  const double X = t1 * t1 + 2.0 * V * l;
   const double Y = tm * tm + 2.0 * (V - x.V) * l;
   const double dX = (t1 - tm) * (t1 + tm) + 2.0 * x.V * l;
-  const double den = sqrt(X) + sqrt(Y);
+  const double den = sqX + sqrt(Y);
   const double frac = den > 0.0 ? dX / den : 0.0;
   const double g = (x.beta + (t1 - tm) + frac) / Dd;
   return g > 0.0 ? g : 0.0;                     // maps -0 to +0
@@ -297,6 +323,9 @@ __device__ __forceinline__ Cert cert_combine(Cert a, const Cert &b) {
 // four tokens' loads in flight per thread.
 constexpr int TR = 8;
 constexpr int LDS_TOK = 4096;
+// the slice cache is only used when n <= TEAM_MAX * LDS_TOK, which bounds the chunk
+// scales that share the dynamic LDS with it
+constexpr int MAX_CACHED_CHUNKS = (TEAM_MAX * LDS_TOK + SKETCH_CHUNK - 1) / SKETCH_CHUNK;
 constexpr int SB = 4;
 
 // Sort (key, lo) ascending across the 64 lanes of a wave (bitonic, registers only).
@@ -314,7 +343,7 @@ __device__ __forceinline__ void wave_bitonic(uint64_t &key, uint32_t &lo) {
 }
 
 __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
-  extern __shared__ double s_dyn[];          // [nch] chunk scales, then [2][LDS_TOK] cache
+  extern __shared__ double s_dyn[];          // [nch] chunk scales, then [4][LDS_TOK] cache
   __shared__ double scr[NQ * DC_NW];
   __shared__ double s_part[TEAM_MAX * PART];
   __shared__ uint32_t h_cnt[NBUCKET];
@@ -346,10 +375,12 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   const int s0 = (int)((int64_t)n * m / T);
   const int s1 = (int)((int64_t)n * (m + 1) / T);
   const bool cached = (s1 - s0) <= TR * DC_NT;        // selection terms in registers
-  const bool lcache = (s1 - s0) <= LDS_TOK && a.lds_cache;  // (w, r) in LDS
+  const bool lcache = (s1 - s0) <= LDS_TOK && a.lds_cache;  // (w, r, 1/r, r/(1-r)) in LDS
   double *s_scale = s_dyn;
   double *s_w = s_dyn + a.nch_max;
   double *s_r = s_w + LDS_TOK;
+  double *s_ir = s_r + LDS_TOK;
+  double *s_rq = s_ir + LDS_TOK;
   const double *wcr = a.wc + row_tok_base(a.t, b, h);
   const double2 *cs = a.cstat + row_chunk_base(a.t, b, h);
   const double *rr = a.r + tok_base(a.t, b, g);
@@ -405,12 +436,16 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   for (int c = tid; c < nch; c += DC_NT) zloc += s_scale[c] * cz[c];
   const double f0 = block_sum<DC_NT>(zloc, scr);      // f(0) = sum_L w (1 - r)
 
-  // (w, r) of the slice in LDS; r >= 1 marks a token of H
+  // (w, r) of the slice in LDS, with 1/r and r/(1-r) for the fixed-point passes;
+  // r >= 1 marks a token of H
   if (lcache) {
     for (int i = s0 + tid; i < s1; i += DC_NT) {
       const double ri = rr[i];
+      const bool inL = ri < 1.0;
       s_r[i - s0] = ri;
-      s_w[i - s0] = ri < 1.0 ? wcr[i] * s_scale[i / SKETCH_CHUNK] : 0.0;
+      s_w[i - s0] = inL ? wcr[i] * s_scale[i / SKETCH_CHUNK] : 0.0;
+      s_ir[i - s0] = inL && ri > 0.0 ? 1.0 / ri : 0.0;
+      s_rq[i - s0] = inL ? ri / (1.0 - ri) : 0.0;
     }
     __syncthreads();
   }
@@ -444,6 +479,37 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     }                                                                 \
   }
 
+  // FOR_L with the reciprocals of r: ir = 1/r, rq = r/(1-r) (0 where r = 0)
+#define FOR_LX(body)                                                  \
+  if (lcache) {                                                       \
+    for (int i0 = s0 + tid; i0 < s1; i0 += 4 * DC_NT) {               \
+      double rb[4], wb[4], ib[4], qb[4];                              \
+      _Pragma("unroll")                                               \
+      for (int u = 0; u < 4; ++u) {                                   \
+        const int iu = i0 + u * DC_NT;                                \
+        const bool ok = iu < s1;                                      \
+        rb[u] = ok ? s_r[iu - s0] : 2.0;                              \
+        wb[u] = ok ? s_w[iu - s0] : 0.0;                              \
+        ib[u] = ok ? s_ir[iu - s0] : 0.0;                             \
+        qb[u] = ok ? s_rq[iu - s0] : 0.0;                             \
+      }                                                               \
+      _Pragma("unroll")                                               \
+      for (int u = 0; u < 4; ++u) {                                   \
+        const double ri = rb[u];                                      \
+        if (!(ri < 1.0)) continue;                                    \
+        const double wi = wb[u];                                      \
+        const double ir = ib[u];                                      \
+        const double rq = qb[u];                                      \
+        body                                                          \
+      }                                                               \
+    }                                                                 \
+  } else {                                                            \
+    FOR_L(                                                            \
+      const double ir = ri > 0.0 ? 1.0 / ri : 0.0;                    \
+      const double rq = ri / (1.0 - ri);                              \
+      body)                                                           \
+  }
+
   auto combine_sum1 = [&](double v) -> double {
     if (T == 1) return v;
     double *sl = SLOT();
@@ -467,28 +533,28 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   } else if (f0 > 0.0) {
     // safeguarded Newton from B = f(0), the upper end of the bracket [0, f(0)]
     double lo = 0.0, hi = INFINITY, B = f0;
+    const double inv_kappa = 1.0 / kappa;
     bool done = false;
     for (int iter = 0; iter < 200; ++iter) {
       NewtonAcc v{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       // per token: lambda = r below aa = w (1 - r) / kappa, 1 above tt = aa / r, linear
-      // in between; two reciprocals, the rest products, no branch on the piece
-      FOR_L(
+      // in between; with 1/r and r/(1-r) at hand every term is a product
+      FOR_LX(
         v.cnt += 1.0;
         if (ri == 0.0) { v.c0 += wi; }
         else if (wi != 0.0) {
           const double q1 = 1.0 - ri;
-          const double ir = 1.0 / ri;
-          const double iq = 1.0 / q1;
+          const double iq = 1.0 + rq;                      // 1 / (1 - r)
           const double wq = wi * q1;
-          const double aa = wq / kappa;
+          const double aa = wq * inv_kappa;
           const double tt = aa * ir;
           const double mx = fmax(ri, q1);
           const bool plo = B <= aa;
           const bool phi = !plo && B >= tt;
           const bool pmid = !plo && !phi;
           v.c0 += plo ? wq : (pmid ? wi : 0.0);
-          v.c1 += pmid ? kappa * ri * iq : 0.0;
-          v.vm += pmid ? kappa * kappa * ri * iq : 0.0;
+          v.c1 += pmid ? kappa * rq : 0.0;
+          v.vm += pmid ? kappa * kappa * rq : 0.0;
           v.vc += plo ? ri * wi * wq : (phi ? wi * wq * ir : 0.0);
           v.lo = fmax(v.lo, plo ? 0.0 : (phi ? tt : aa));
           v.hi = fmin(v.hi, plo ? aa : (phi ? INFINITY : tt));
@@ -543,11 +609,23 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     if (!done && tid == 0 && m == 0) atomicOr(a.status, 2);
   }
 
+  // per-token terms at B*: one formula for every pass of this kernel (tokens of this
+  // member's slice take 1/r and r/(1-r) from the LDS cache, others compute them the
+  // same way)
+  const double kB = kappa * Bst;
+  const bool kinf = isinf(kappa);
+  auto tok_terms = [&](int i, double wi, double ri, bool local) -> Terms {
+    double ir, rq;
+    if (local && lcache) { ir = s_ir[i - s0]; rq = s_rq[i - s0]; }
+    else { ir = ri > 0.0 ? 1.0 / ri : 0.0; rq = ri / (1.0 - ri); }
+    return terms_at(wi, ri, ir, rq, kB, kinf);
+  };
+
   if (!have_cert) {
     Cert cl{0.0, 0.0, 0.0, 0.0};
     int nL = 0;
     FOR_L(
-      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+      const Terms x = tok_terms(i, wi, ri, true);
       cl.beta += x.beta; cl.V += x.V; ++nL;
       top2_merge(cl.b1, cl.b2, x.b, 0.0);)
     ct = block_cert(cl, scr);
@@ -581,6 +659,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     a.certified[row] = cert ? 1 : 0;
   }
   if (cert) return;                                    // kstar was cleared before the kernel
+  const double t1x = ct.b1 * l / 3.0;
+  const double sqX = sqrt(t1x * t1x + 2.0 * ct.V * l);   // sqrt(X) of g_of, once per row
 
   // ---- eqs. (9)-(10): MSD search for the k* cut over the bits of g
   // per-token terms and keys, cached for the remaining passes
@@ -595,9 +675,9 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       const double ri = lcache ? s_r[i - s0] : rr[i];
       if (ri < 1.0) {
         const double wi = lcache ? s_w[i - s0] : wcr[i] * s_scale[i / SKETCH_CHUNK];
-        const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+        const Terms x = tok_terms(i, wi, ri, true);
         cbeta[k] = x.beta; cV[k] = x.V; cb[k] = x.b;
-        ckey[k] = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));
+        ckey[k] = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd, sqX));
         cin[k] = true;
       }
     }
@@ -618,8 +698,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       const double ri = rr[i];                                                 \
       if (!(ri < 1.0)) continue;                                               \
       const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];                    \
-      const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));            \
-      const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));          \
+      const Terms x = tok_terms(i, wi, ri, true);                              \
+      const uint64_t key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd, sqX));     \
       const uint32_t lo = IDX_MAX - (uint32_t)i;                               \
       body                                                                     \
     }                                                                          \
@@ -648,12 +728,40 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
       }
     };
     if (cached) {
+      // A thread first merges its own TR tokens that share a bucket (the first digit
+      // holds exponent bits of g, so a few buckets take most tokens and the LDS
+      // atomics on them serialise); then one update per distinct bucket.
+      uint32_t dg[TR], cn[TR];
+      double sbeta[TR], sV[TR], smb[TR];
 #pragma unroll
       for (int k = 0; k < TR; ++k) {
         const int i = s0 + tid + k * DC_NT;
         const uint32_t lo = IDX_MAX - (uint32_t)i;
         const bool act = cin[k] && cmp_window(ckey[k], lo, lev, pkey, plo) == 0;
-        hist_tok(act, ckey[k], lo, Terms{cbeta[k], cV[k], cb[k]});
+        dg[k] = c_lev_lo[L] ? ((lo >> sh) & dmask) : (uint32_t)((ckey[k] >> sh) & dmask);
+        cn[k] = act ? 1u : 0u;
+        sbeta[k] = act ? cbeta[k] : 0.0;
+        sV[k] = act ? cV[k] : 0.0;
+        smb[k] = act ? cb[k] : 0.0;
+      }
+#pragma unroll
+      for (int k = 1; k < TR; ++k) {
+#pragma unroll
+        for (int j = 0; j < k; ++j) {
+          if (cn[k] && cn[j] && dg[j] == dg[k]) {
+            cn[j] += cn[k]; sbeta[j] += sbeta[k]; sV[j] += sV[k]; smb[j] = fmax(smb[j], smb[k]);
+            cn[k] = 0;
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < TR; ++k) {
+        if (cn[k]) {
+          atomicAdd(&h_cnt[dg[k]], cn[k]);
+          atomicAdd(&h_beta[dg[k]], sbeta[k]);
+          atomicAdd(&h_V[dg[k]], sV[k]);
+          atomicMax((unsigned long long *)&h_b[dg[k]], (unsigned long long)dbits(smb[k]));
+        }
       }
     } else {
       for (int i0 = s0; i0 < s1; i0 += DC_NT) {
@@ -666,8 +774,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
           const double ri = rr[i];
           if (ri < 1.0) {
             const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
-            x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
-            key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd));
+            x = tok_terms(i, wi, ri, true);
+            key = dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd, sqX));
             act = cmp_window(key, lo, lev, pkey, plo) == 0;
           }
         }
@@ -798,7 +906,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
           const int i = (int)(IDX_MAX - lo);
           const double ri = rr[i];
           const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
-          const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+          const Terms x = tok_terms(i, wi, ri, false);
           tb = x.beta; tv = x.V; tm = x.b;
         }
         for (int off = 1; off < WAVE; off <<= 1) {
@@ -846,7 +954,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         const int i = (int)(IDX_MAX - w_lo[tid]);
         const double ri = rr[i];
         const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
-        const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
+        const Terms x = tok_terms(i, wi, ri, false);
         tb = x.beta; tv = x.V; tm = x.b;
       }
       h_beta[tid] = tb; h_V[tid] = tv; h_b[tid] = dbits(tm);
@@ -894,8 +1002,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
         const double ri = rr[i];
         if (ri < 1.0) {
           const double wi = wcr[i] * s_scale[i / SKETCH_CHUNK];
-          const Terms x = terms_of(wi, ri, lam_of(wi, ri, Bst, kappa));
-          f = in_F(dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd)), IDX_MAX - (uint32_t)i);
+          const Terms x = tok_terms(i, wi, ri, true);
+          f = in_F(dbits(g_of(x, ct.V, ct.b1, ct.b2, l, Dd, sqX)), IDX_MAX - (uint32_t)i);
         }
       }
       kc += f ? 1 : 0;
@@ -907,6 +1015,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   STAMP();
 #undef STAMP
 #undef FOR_SEL
+#undef FOR_LX
 #undef FOR_L
 #undef TEAM_STAGE
 #undef TEAM_SYNC
@@ -1107,7 +1216,7 @@ __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
 }
 
 size_t decide_lds_bytes(int nch_max, bool slice_cache) {
-  return sizeof(double) * ((size_t)nch_max + (slice_cache ? 2 * (size_t)LDS_TOK : 0));
+  return sizeof(double) * ((size_t)nch_max + (slice_cache ? 4 * (size_t)LDS_TOK : 0));
 }
 
 bool decide_slice_cached(int max_n, int team) { return (max_n + team - 1) / team <= LDS_TOK; }
@@ -1117,7 +1226,8 @@ hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st) {
   if (!attr_set) {
     // allow the largest dynamic LDS this kernel asks for (chunk scales + slice cache)
     hipError_t e = hipFuncSetAttribute((const void *)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)decide_lds_bytes(MAX_CHUNKS, true));
+                                       (int)std::max(decide_lds_bytes(MAX_CHUNKS, false),
+                                                     decide_lds_bytes(MAX_CACHED_CHUNKS, true)));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
