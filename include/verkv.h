@@ -145,7 +145,10 @@ size_t verkv_compress_workspace_bytes(const verkv_shape *s);
  *          lambda = r; must be >= 0
  *   eps    tolerance > 0;  delta  confidence parameter in (0, 1)
  *   workspace at least verkv_decode_workspace_bytes(s, st->cap); pass the same
- *          workspace to verkv_refine for this step.
+ *          workspace to verkv_refine for this step.  Between steps it keeps each
+ *          row's B*, which the next step on it takes as the starting point of its
+ *          fixed-point search (results do not depend on it; zero-filled or foreign
+ *          contents only cost iterations).
  * No host synchronisation and no host-memory traffic. */
 verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
                                double beta, double eps, double delta, verkv_step_out *out,

@@ -410,14 +410,19 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
   int nstamp = 0;
 #define STAMP()                                                                                  \
   do {                                                                                           \
-    if (tid == 0 && a.phase_clock && nstamp < 32)                                                \
-      a.phase_clock[((int64_t)row * T + m) * 32 + nstamp] = wall_clock64();                      \
+    if (tid == 0 && a.phase_clock && nstamp < 32) {                                              \
+      a.phase_clock[((int64_t)row * T + m) * 64 + nstamp] = wall_clock64();                      \
+      a.phase_clock[((int64_t)row * T + m) * 64 + 32 + nstamp] = clock64();                      \
+    }                                                                                            \
     ++nstamp;                                                                                    \
   } while (0)
 #else
 #define STAMP() do {} while (0)
 #endif
   STAMP();
+
+  // read before the first team exchange; member 0 overwrites it at the end
+  const double bwarm = a.bprev ? a.bprev[row] : 0.0;
 
   // ---- step 1 (finish): m_hat, per-chunk rescale, D (every member, same order)
   double mloc = -INFINITY;
@@ -531,8 +536,10 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     else { FOR_L(acc += wi * (1.0 - ri);) }
     Bst = combine_sum1(block_sum<DC_NT>(acc, scr));
   } else if (f0 > 0.0) {
-    // safeguarded Newton from B = f(0), the upper end of the bracket [0, f(0)]
-    double lo = 0.0, hi = INFINITY, B = f0;
+    // safeguarded Newton inside the bracket [0, f(0)], from this row's B* of the last
+    // step when the workspace holds one in the bracket (the result is the root of the
+    // final linear piece, whatever the start), else from f(0)
+    double lo = 0.0, hi = f0, B = (bwarm > 0.0 && bwarm < f0) ? bwarm : f0;
     const double inv_kappa = 1.0 / kappa;
     bool done = false;
     for (int iter = 0; iter < 200; ++iter) {
@@ -655,6 +662,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     a.m_hat[row] = m_hat;
     a.d_sketch[row] = Dd;
     a.beta_star[row] = Bst;
+    if (a.bprev) a.bprev[row] = Bst;
     a.eps_hat[row] = ehat;
     a.certified[row] = cert ? 1 : 0;
   }
@@ -1022,83 +1030,107 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
 #undef SLOT
 }
 
-// ------------------------------------------------------------------ union, lists, pivot coefficients
-// List pass (one block per KV head): compacts the head's fetch bitmask into the
-// ascending list F and the list F \ S of host rows.  Coefficient pass: gives every
-// resident pivot its estimator coefficient for every query row of the group: 1 on H
-// and on S n F, lambda_i / r_i on S \ F (Definition 2 with the fetched tokens exact).
-constexpr int UN_NT = 1024;
+// ------------------------------------------------------------------ fetch lists
+// LS_NB blocks per KV head, each owning a contiguous run of 64-token groups (two
+// bitmask words).  A block first counts the tokens of all groups before its run (a
+// re-read of at most the head's whole bitmask), so no second launch is needed for the
+// prefix.  Inside the block every wave owns a sub-run: pass 1 counts, a block scan
+// gives each wave its first list position, pass 2 walks the groups in order, one lane
+// per token, and writes the set bits with a ballot prefix so that consecutive list
+// entries come from consecutive lanes (whole-line stores).  Lists are ascending.
+constexpr int LS_NT = 256;
+constexpr int LS_NB = 32;
 
-__global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
-  __shared__ int32_t iscr[UN_NT / WAVE];
-  const int unit = blockIdx.x;
+__global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
+  __shared__ int32_t iscr[LS_NT / WAVE];
+  constexpr int NWV = LS_NT / WAVE;
+  const int unit = blockIdx.y;
   const int b = unit / a.t.Hkv;
   const int g = unit % a.t.Hkv;
   const int n = a.t.s[b].n;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid / WAVE;
+  const uint32_t *fb = a.fbits + word_base(a.t, b, g);
+  const uint32_t *res = a.resident + word_base(a.t, b, g);
+  const int W = words_of(n);
+  const int ngrp = (W + 1) / 2;
+  const int per = (ngrp + LS_NB - 1) / LS_NB;
+  const int B0 = min(ngrp, (int)blockIdx.x * per), B1 = min(ngrp, B0 + per);
+  auto group_bits = [&](const uint32_t *wd, int gi) -> uint64_t {
+    const uint64_t lo32 = wd[2 * gi];
+    const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
+    return lo32 | (hi32 << 32);
+  };
+  // tokens of F and of F \ S before this block's run
+  int32_t cf = 0, ch = 0;
+  for (int gi = tid; gi < B0; gi += LS_NT) {
+    const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
+    cf += __popcll(f);
+    ch += __popcll(f & ~r);
+  }
+  int32_t bf, bh;
+  (void)block_excl_scan<LS_NT>(cf, iscr, &bf);
+  (void)block_excl_scan<LS_NT>(ch, iscr, &bh);
+  // this block's run, split over its waves
+  const int gpw = (B1 - B0 + NWV - 1) / NWV;
+  const int ga = min(B1, B0 + wv * gpw), gb = min(B1, ga + gpw);
+  cf = 0;
+  ch = 0;
+  for (int gi = ga + lane; gi < gb; gi += WAVE) {
+    const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
+    cf += __popcll(f);
+    ch += __popcll(f & ~r);
+  }
+  cf = (int32_t)wave_sum_i64(cf);
+  ch = (int32_t)wave_sum_i64(ch);
+  int32_t tf, th;
+  int32_t pf = block_excl_scan<LS_NT>(lane == 0 ? cf : 0, iscr, &tf);
+  int32_t ph = block_excl_scan<LS_NT>(lane == 0 ? ch : 0, iscr, &th);
+  pf = bf + __shfl(pf, 0, WAVE);            // the wave's first positions (lane 0's)
+  ph = bh + __shfl(ph, 0, WAVE);
+  int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
+  int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int c0 = ga; c0 < gb; c0 += WAVE) {
+    // lane j holds group c0 + j; the walk below takes them in order by shuffle
+    uint64_t fl_l = 0, rl_l = 0;
+    if (c0 + lane < gb) { fl_l = group_bits(fb, c0 + lane); rl_l = group_bits(res, c0 + lane); }
+    const int nj = min(WAVE, gb - c0);
+    for (int jj = 0; jj < nj; ++jj) {
+      const uint64_t f = __shfl(fl_l, jj, WAVE), r = __shfl(rl_l, jj, WAVE);
+      const uint64_t hsel = f & ~r;
+      const bool inf = (f >> lane) & 1ull, inh = (hsel >> lane) & 1ull;
+      const int tok = 64 * (c0 + jj) + lane;
+      if (inf) {
+        const int32_t pos = pf + (int32_t)__popcll(f & below);
+        if (fl && pos < a.fetch_cap) fl[pos] = tok;
+      }
+      if (inh) hl[ph + (int32_t)__popcll(hsel & below)] = tok;
+      pf += (int32_t)__popcll(f);
+      ph += (int32_t)__popcll(hsel);
+    }
+  }
+  if (blockIdx.x == LS_NB - 1 && tid == 0) {
+    a.fetch_count[unit] = bf + tf;
+    a.h2d_count[unit] = bh + th;
+  }
+}
+
+// ------------------------------------------------------------------ pivot coefficients
+// Every resident pivot gets its estimator coefficient for every query row of the
+// group: 1 on H and on S n F, lambda_i / r_i on S \ F (Definition 2 with the fetched
+// tokens exact).
+constexpr int UN_NT = 1024;
+
+__global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
+  const int unit = blockIdx.x;
+  const int b = unit / a.t.Hkv;
+  const int g = unit % a.t.Hkv;
   const int G = a.t.G;
   const int Hq = a.t.Hkv * G;
   const int tid = threadIdx.x;
   const uint32_t *fb = a.fbits + word_base(a.t, b, g);
-  if (!a.coef_pass) {
-    // Every wave owns a contiguous run of 64-token groups (two bitmask words).  Pass 1
-    // counts each wave's tokens; a block scan gives each wave its first list
-    // position; pass 2 walks the groups in order, one lane per token, and writes the
-    // set bits with a ballot prefix so that consecutive list entries come from
-    // consecutive lanes (whole-line stores).
-    constexpr int NWV = UN_NT / WAVE;
-    const uint32_t *res = a.resident + word_base(a.t, b, g);
-    const int W = words_of(n);
-    const int ngrp = (W + 1) / 2;
-    const int gpw = (ngrp + NWV - 1) / NWV;
-    const int lane = tid & (WAVE - 1);
-    const int wv = tid / WAVE;
-    const int ga = min(ngrp, wv * gpw), gb = min(ngrp, ga + gpw);
-    auto group_bits = [&](const uint32_t *wd, int gi) -> uint64_t {
-      const uint64_t lo32 = wd[2 * gi];
-      const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
-      return lo32 | (hi32 << 32);
-    };
-    int32_t cf = 0, ch = 0;
-    for (int gi = ga + lane; gi < gb; gi += WAVE) {
-      const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
-      cf += __popcll(f);
-      ch += __popcll(f & ~r);
-    }
-    cf = (int32_t)wave_sum_i64(cf);
-    ch = (int32_t)wave_sum_i64(ch);
-    int32_t tf, th;
-    int32_t pf = block_excl_scan<UN_NT>(lane == 0 ? cf : 0, iscr, &tf);
-    int32_t ph = block_excl_scan<UN_NT>(lane == 0 ? ch : 0, iscr, &th);
-    pf = __shfl(pf, 0, WAVE);                 // the wave's first positions (lane 0's)
-    ph = __shfl(ph, 0, WAVE);
-    int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
-    int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int c0 = ga; c0 < gb; c0 += WAVE) {
-      // lane j holds group c0 + j; the walk below takes them in order by shuffle
-      uint64_t fl_l = 0, rl_l = 0;
-      if (c0 + lane < gb) { fl_l = group_bits(fb, c0 + lane); rl_l = group_bits(res, c0 + lane); }
-      const int nj = min(WAVE, gb - c0);
-      for (int jj = 0; jj < nj; ++jj) {
-        const uint64_t f = __shfl(fl_l, jj, WAVE), r = __shfl(rl_l, jj, WAVE);
-        const uint64_t hsel = f & ~r;
-        const bool inf = (f >> lane) & 1ull, inh = (hsel >> lane) & 1ull;
-        const int tok = 64 * (c0 + jj) + lane;
-        if (inf) {
-          const int32_t pos = pf + (int32_t)__popcll(f & below);
-          if (fl && pos < a.fetch_cap) fl[pos] = tok;
-        }
-        if (inh) hl[ph + (int32_t)__popcll(hsel & below)] = tok;
-        pf += (int32_t)__popcll(f);
-        ph += (int32_t)__popcll(hsel);
-      }
-    }
-    if (tid == 0) {
-      a.fetch_count[unit] = tf;
-      a.h2d_count[unit] = th;
-    }
-    return;
-  }
   const int cnt = min(a.piv_count[unit], a.cap);
   const int p = blockIdx.y * UN_NT + tid;
   if (p >= cnt) return;
@@ -1163,7 +1195,11 @@ __global__ __launch_bounds__(DC_NT) void k_after(AfterArgs a) {
 // N_hat and D_hat are the fixed-order sums of the partials of the resident pivots and
 // of the host rows; o = N_hat / D_hat, lse = m_hat + ln D_hat; eps_after combines the
 // slices of k_after.
-__global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
+constexpr int FI_GRP = 4;                  // split groups summed in parallel
+constexpr int FI_NT = 576;                 // FI_GRP x (D + 1) = 516 active threads
+
+__global__ __launch_bounds__(FI_NT) void k_finish(FinishArgs a) {
+  __shared__ float s_acc[FI_GRP][D + 1];
   __shared__ float s_d;
   const int row = blockIdx.x;
   const int Hq = a.t.Hkv * a.t.G;
@@ -1174,25 +1210,35 @@ __global__ __launch_bounds__(256) void k_finish(FinishArgs a) {
   const int unit = b * a.t.Hkv + g;
   const int tid = threadIdx.x;
   constexpr int PS = D + 1;
-  // partials in split order; 16 loads in flight per batch (the order of the sum is
-  // unchanged, only the loads are issued ahead)
+  // group q sums the pivot splits [q nsp/4, (q+1) nsp/4) and likewise the host splits,
+  // 16 loads in flight; the groups are then added in order q = 0..3
   constexpr int FB = 16;
-  auto add_parts = [&](const float *base, int ns, float acc) -> float {
+  auto add_parts = [&](const float *base, int s0, int s1, float acc) -> float {
     const int64_t stride = (int64_t)a.t.G * PS;
-    for (int s0 = 0; s0 < ns; s0 += FB) {
+    for (int sa = s0; sa < s1; sa += FB) {
       float v[FB];
 #pragma unroll
-      for (int u = 0; u < FB; ++u) v[u] = s0 + u < ns ? base[(s0 + u) * stride] : 0.0f;
+      for (int u = 0; u < FB; ++u) v[u] = sa + u < s1 ? base[(sa + u) * stride] : 0.0f;
 #pragma unroll
       for (int u = 0; u < FB; ++u)
-        if (s0 + u < ns) acc += v[u];
+        if (sa + u < s1) acc += v[u];
     }
     return acc;
   };
+  if (tid < FI_GRP * PS) {
+    const int q = tid / PS, col = tid % PS;
+    float part = 0.0f;
+    part = add_parts(a.piv_part + ((int64_t)unit * a.nsp * a.t.G + j) * PS + col,
+                     a.nsp * q / FI_GRP, a.nsp * (q + 1) / FI_GRP, part);
+    part = add_parts(a.host_part + ((int64_t)unit * a.nsh * a.t.G + j) * PS + col,
+                     a.nsh * q / FI_GRP, a.nsh * (q + 1) / FI_GRP, part);
+    s_acc[q][col] = part;
+  }
+  __syncthreads();
   float acc = 0.0f;
   if (tid <= D) {
-    acc = add_parts(a.piv_part + ((int64_t)unit * a.nsp * a.t.G + j) * PS + tid, a.nsp, acc);
-    acc = add_parts(a.host_part + ((int64_t)unit * a.nsh * a.t.G + j) * PS + tid, a.nsh, acc);
+#pragma unroll
+    for (int q = 0; q < FI_GRP; ++q) acc += s_acc[q][tid];
     if (tid == D) s_d = acc;
   }
   __syncthreads();
@@ -1250,8 +1296,8 @@ int decide_blocks_per_cu(int max_n, int team) {
 }
 
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
-  const int ny = a.coef_pass ? (a.cap + UN_NT - 1) / UN_NT : 1;
-  return launch_kernel(k_union, dim3(units, ny), dim3(UN_NT), 0, st, a);
+  if (!a.coef_pass) return launch_kernel(k_lists, dim3(LS_NB, units), dim3(LS_NT), 0, st, a);
+  return launch_kernel(k_union, dim3(units, (a.cap + UN_NT - 1) / UN_NT), dim3(UN_NT), 0, st, a);
 }
 
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {
@@ -1259,7 +1305,7 @@ hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {
 }
 
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st) {
-  return launch_kernel(k_finish, dim3(rows), dim3(256), 0, st, a);
+  return launch_kernel(k_finish, dim3(rows), dim3(FI_NT), 0, st, a);
 }
 
 }  // namespace verkv

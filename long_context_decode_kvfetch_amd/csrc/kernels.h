@@ -73,7 +73,9 @@ struct DecideArgs {
   uint64_t *wkey;            // [rows][WIN] final window
   uint32_t *wlo;
   uint32_t *wcount;          // [rows] (cleared by the sketch kernel)
-  uint64_t *phase_clock;     // [rows][T][32] phase timestamps (VERKV_PHASE_TIMING builds)
+  uint64_t *phase_clock;     // [rows][T][64] phase timestamps: 32 wall clock, 32 shader clock
+                             // (VERKV_PHASE_TIMING builds)
+  double *bprev;             // [rows] B* of the last step (Newton start), kept in the workspace
   int32_t nch_max;           // chunk scales held in dynamic LDS
   int32_t lds_cache;         // 1: the launch reserved LDS for the (w, r) slice cache
 };

@@ -94,7 +94,7 @@ int team_size(int rows, int max_n) {
 // Decode workspace layout.
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
-  size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0;
+  size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
   size_t total;
   int nsp, nsh, team;
 };
@@ -130,6 +130,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.ppart = off;  off = align_up(off + 4 * (size_t)units * w.nsp * t.G * (D + 1));
   w.hpart = off;  off = align_up(off + 4 * (size_t)units * w.nsh * t.G * (D + 1));
   w.status = off; off = align_up(off + 64);
+  w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
   w.total = off;
   return w;
 }
@@ -433,6 +434,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.team = team;
   dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;
   dc.team_ws = L.team;
+  dc.bprev = reinterpret_cast<double *>(ws + L.bprev);
   dc.xseq = sk.xseq;
   dc.part = reinterpret_cast<double *>(ws + L.part);
   dc.hcnt = reinterpret_cast<uint32_t *>(ws + L.hcnt);
@@ -444,7 +446,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.wcount = sk.wcount;
   dc.phase_clock = nullptr;
 #ifdef VERKV_PHASE_TIMING
-  if (workspace_bytes >= L.total + (size_t)rows * team * 32 * 8)
+  if (workspace_bytes >= L.total + (size_t)rows * team * 64 * 8)
     dc.phase_clock = reinterpret_cast<uint64_t *>(ws + L.total);
 #endif
   {
