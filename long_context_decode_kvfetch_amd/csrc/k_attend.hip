@@ -121,10 +121,30 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
           for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
           dot = sum16(dot);
           if (LPT == 32) dot += shfl_xor_f(dot, 16);
-          float c = 1.0f;
-          if (!HOST && pp[u] < p1) c = a.coef[((int64_t)b * Hq + g * G + j) * a.cap + pp[u]];
-          w[j] = (pp[u] < p1) ? c * __expf(dot - mh[j]) : 0.0f;
+          w[j] = (pp[u] < p1) ? __expf(dot - mh[j]) : 0.0f;
         }
+      }
+      if constexpr (!HOST) {
+        // the row's G coefficients are contiguous ([unit][cap][G]): one vector load
+        float c[G];
+        if (pp[u] < p1) {
+          const float *cp = a.coef + ((int64_t)unit * a.cap + pp[u]) * G;
+          if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int j4 = 0; j4 < G; j4 += 4) {
+              const float4 c4 = *(const float4 *)(cp + j4);
+              c[j4] = c4.x; c[j4 + 1] = c4.y; c[j4 + 2] = c4.z; c[j4 + 3] = c4.w;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) c[j] = cp[j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < G; ++j) c[j] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) w[j] *= c[j];
       }
       float v[EPL];
       RS::widen(vr[u], v);

@@ -1147,7 +1147,7 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
       const double lam = lam_of(wi, ri, a.beta_star[(int64_t)b * Hq + h], kappa);
       cf32 = (float)(lam / ri);
     }
-    a.coef[((int64_t)b * Hq + h) * a.cap + p] = cf32;
+    a.coef[((int64_t)unit * a.cap + p) * G + j] = cf32;
   }
 }
 

@@ -101,7 +101,7 @@ struct UnionArgs {
   int32_t fetch_cap;
   int32_t *fetch_count, *h2d_count;
   int32_t *h2d_idx;          // [B][Hkv][n]
-  float *coef;               // [B][Hq][cap]
+  float *coef;               // [B][Hkv][cap][G]
   int32_t coef_pass;         // 0: fetch lists (grid y = 1); 1: pivot coefficients
   const double *params;      // coefficient pass: params[0] = kappa of the step (device)
 };
@@ -115,7 +115,7 @@ struct AttendArgs {
   const uint8_t *vrows;
   const int32_t *count;      // [B][Hkv] rows in the list
   const int32_t *list;       // host source: [B][Hkv][n] token ids; pivots: null
-  const float *coef;         // pivots: [B][Hq][cap]; host: null (coefficient 1)
+  const float *coef;         // pivots: [B][Hkv][cap][G]; host: null (coefficient 1)
   int32_t cap;
   float *part;               // [B][Hkv][nsplit][G][129]
   int32_t nsplit;
@@ -146,7 +146,8 @@ constexpr int DECIDE_THREADS = 512;
 constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
 constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
-constexpr int PIVOT_TOKENS = 64;  // pivot rows per attention workgroup (sets nsp)
+constexpr int PIVOT_TOKENS = 64;  // fewest pivot rows per attention workgroup
+constexpr int PIVOT_WGS = 2048;   // attention workgroups aimed at per launch (8 per CU)
 
 // Timing of the next launch: when `start` is set, the launcher hands the pair to
 // hipExtLaunchKernel, which stamps them from the dispatch packet itself (kernel

@@ -80,7 +80,13 @@ Totals totals(const SeqTable &t) {
 int row_bytes(const verkv_shape *s) { return VERKV_HEAD_DIM * (s->kv_dtype == VERKV_BF16 ? 2 : 4); }
 
 int host_splits(int units) { return std::max(4, std::min(64, 512 / std::max(1, units))); }
-int pivot_splits(int cap) { return std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS); }
+// Splits of a KV head's pivot list: about PIVOT_WGS workgroups per launch, none with
+// fewer than PIVOT_TOKENS rows (more splits cost partial writes and a longer finish).
+int pivot_splits(int cap, int units) {
+  const int by_len = std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS);
+  const int by_wgs = std::max(1, (PIVOT_WGS + std::max(1, units) - 1) / std::max(1, units));
+  return std::min(by_len, by_wgs);
+}
 
 // Workgroups per query row in the decision kernel, as sized in the workspace: enough
 // to give 256 CUs two workgroups each, at least TEAM_MIN_TOKENS tokens per workgroup,
@@ -104,7 +110,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   const int units = t.B * t.Hkv;
   const int64_t rows = (int64_t)units * t.G;
   DecodeWs w;
-  w.nsp = pivot_splits(cap);
+  w.nsp = pivot_splits(cap, units);
   w.nsh = host_splits(units);
   w.team = team_size((int)rows, t.max_n);
   const int64_t tm = w.team > 1 ? w.team : 0;       // member histograms only for teams
