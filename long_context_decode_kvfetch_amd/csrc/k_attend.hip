@@ -29,12 +29,12 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   constexpr int LPT = D / EPL;
   constexpr int TPW = WAVE / LPT;
   constexpr int STEP = AT_NW * TPW;          // rows per workgroup iteration
-  constexpr int U = 4;                       // iterations whose loads are in flight together
+  constexpr int U = 2;                       // row groups per batch (two batches in flight)
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
   constexpr int PS = D + 1;
 
-  __shared__ float s_acc[AT_NW][G][D];
-  __shared__ float s_den[AT_NW][G];
+  __shared__ float s_acc[AT_NW][TPW][G][D];
+  __shared__ float s_den[AT_NW][TPW][G];
 
   const int unit = blockIdx.y;
   const int split = blockIdx.x;
@@ -78,26 +78,49 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   (void)list;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
 
-  for (int base = p0; base < p1; base += STEP * U) {
+  // Rows go in batches of STEP * U; the loads of the next batch (and, for pivots, its
+  // coefficients) are issued before the current batch is reduced, so every wave keeps
+  // a batch in flight while it computes.
+  struct Batch {
     uint4 kr[U], vr[U];
-    int pp[U];
-    int tk[U];
+    int pp[U], tk[U];
+    float cc[U][G];
+  };
+  auto issue = [&](int base, Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
-      pp[u] = p;
-      tk[u] = 0;
+      bt.pp[u] = p;
+      bt.tk[u] = 0;
       if (p < p1) {
         const int tok = HOST ? list[p] : p;
-        tk[u] = tok;
+        bt.tk[u] = tok;
         const int64_t rowi = src_base + tok;
-        if (!EXACT) kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
-        vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+        if (!EXACT) bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+        bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+        if constexpr (!HOST) {
+          // the row's G coefficients are contiguous ([unit][cap][G]): vector loads
+          const float *cp = a.coef + ((int64_t)unit * a.cap + p) * G;
+          if constexpr (G % 4 == 0) {
+#pragma unroll
+            for (int j4 = 0; j4 < G; j4 += 4) {
+              const float4 c4 = *(const float4 *)(cp + j4);
+              bt.cc[u][j4] = c4.x; bt.cc[u][j4 + 1] = c4.y; bt.cc[u][j4 + 2] = c4.z; bt.cc[u][j4 + 3] = c4.w;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) bt.cc[u][j] = cp[j];
+          }
+        }
       } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
+        bt.kr[u] = make_uint4(0, 0, 0, 0);
+        bt.vr[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < G; ++j) bt.cc[u][j] = 0.0f;
       }
     }
+  };
+  auto consume = [&](const Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float w[G];
@@ -106,14 +129,14 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
         for (int j = 0; j < G; ++j) {
           const int h = g * G + j;
           double wd = 0.0;
-          if (pp[u] < p1)
-            wd = a.wc[row_tok_base(a.t, b, h) + tk[u]] *
-                 a.cscale[row_chunk_base(a.t, b, h) + tk[u] / SKETCH_CHUNK];
+          if (bt.pp[u] < p1)
+            wd = a.wc[row_tok_base(a.t, b, h) + bt.tk[u]] *
+                 a.cscale[row_chunk_base(a.t, b, h) + bt.tk[u] / SKETCH_CHUNK];
           w[j] = (float)wd;
         }
       } else {
         float x[EPL];
-        RS::widen(kr[u], x);
+        RS::widen(bt.kr[u], x);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           float dot = 0.0f;
@@ -121,33 +144,12 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
           for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
           dot = sum16(dot);
           if (LPT == 32) dot += shfl_xor_f(dot, 16);
-          w[j] = (pp[u] < p1) ? __expf(dot - mh[j]) : 0.0f;
+          w[j] = (bt.pp[u] < p1) ? __expf(dot - mh[j]) : 0.0f;
+          if constexpr (!HOST) w[j] *= bt.cc[u][j];
         }
-      }
-      if constexpr (!HOST) {
-        // the row's G coefficients are contiguous ([unit][cap][G]): one vector load
-        float c[G];
-        if (pp[u] < p1) {
-          const float *cp = a.coef + ((int64_t)unit * a.cap + pp[u]) * G;
-          if constexpr (G % 4 == 0) {
-#pragma unroll
-            for (int j4 = 0; j4 < G; j4 += 4) {
-              const float4 c4 = *(const float4 *)(cp + j4);
-              c[j4] = c4.x; c[j4 + 1] = c4.y; c[j4 + 2] = c4.z; c[j4 + 3] = c4.w;
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < G; ++j) c[j] = cp[j];
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < G; ++j) c[j] = 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) w[j] *= c[j];
       }
       float v[EPL];
-      RS::widen(vr[u], v);
+      RS::widen(bt.vr[u], v);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         den[j] += w[j];
@@ -155,24 +157,31 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
         for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(w[j], v[e], acc[j][e]);
       }
     }
+  };
+  constexpr int SU = STEP * U;
+  Batch A, B;
+  int base = p0;
+  if (base < p1) issue(base, A);
+  while (base < p1) {
+    if (base + SU < p1) issue(base + SU, B);
+    consume(A);
+    base += SU;
+    if (base >= p1) break;
+    if (base + SU < p1) issue(base + SU, A);
+    consume(B);
+    base += SU;
   }
 
-  // reduce over the row groups of the wave, then over waves
+  // every row group of every wave leaves its partial in LDS; each output element is
+  // then summed over the AT_NW x TPW groups in a fixed order
+  if (sub == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) s_den[wv][grp][j] = den[j];
+  }
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    for (int m = LPT; m < WAVE; m <<= 1) {
-      den[j] += shfl_xor_f(den[j], m);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] += shfl_xor_f(acc[j][e], m);
-    }
-  }
-  if (grp == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wv][j][d0 + e] = acc[j][e];
-      if (sub == 0) s_den[wv][j] = den[j];
-    }
+    for (int e = 0; e < EPL; ++e) s_acc[wv][grp][j][d0 + e] = acc[j][e];
   }
   __syncthreads();
   float *out = a.part + ((int64_t)unit * a.nsplit + split) * G * PS;
@@ -180,7 +189,9 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
     const int j = t / PS, d = t % PS;
     float s = 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < AT_NW; ++w2) s += (d < D) ? s_acc[w2][j][d] : s_den[w2][j];
+    for (int w2 = 0; w2 < AT_NW; ++w2)
+#pragma unroll
+      for (int r2 = 0; r2 < TPW; ++r2) s += (d < D) ? s_acc[w2][r2][j][d] : s_den[w2][r2][j];
     out[t] = s;
   }
 }
