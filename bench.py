@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--profile-steps", type=int, default=64)
     p.add_argument("--cpu-steps", type=int, default=32)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-pivot-batch", action="store_true",
+                   help="skip the pivotal-stream measurement at the 16-sequence batch")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 256 MiB elementwise copy kernel (HBM counter calibration)")
     return p.parse_args()
@@ -98,6 +100,39 @@ def profiled_traffic(kernel):
         if kv.get("kernel") == kernel and kv.get("sources_sha256") == sources_sha256(kernel):
             return int(float(kv["traffic_bytes"]))
     return None
+
+
+def pivotal_stream(torch, steps=8):
+    """The resident-pivot attention (the pivotal-KV stream) timed on its own: a ragged
+    batch of 16 sequences (lengths uniform in [8K, 64K], 32q/8kv, bf16, eta = 1/16) with
+    eps large enough that every row certifies, so no host rows share the step.  Returns
+    bytes, microseconds and GB/s per launch (dispatch-stamped events)."""
+    from long_context_decode_kvfetch_amd import synth, verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+    wl = synth.ragged_batch(seed=0, batch=16, steps=steps + 2)
+    sess = Session(wl)
+    sess.compress()
+    qs = [sess.queries(i) for i in range(steps + 2)]
+    for i in range(2):
+        sess.step(qs[i], eps=1e9)
+    torch.cuda.synchronize()
+    verkv.profile_begin(16 * steps + 16)
+    for i in range(2, steps + 2):
+        sess.step(qs[i], eps=1e9)
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    ms, cnt = prof["attend_pivots"]
+    us = ms / cnt * 1e3
+    rows = int(sess.state.piv_count.sum().item())
+    nbytes = rows * 2 * 128 * 2
+    del sess
+    torch.cuda.empty_cache()
+    return {"workload": "16 sequences, n ~ U[8K, 64K], 32q/8kv, d=128, bf16, eta=1/16, "
+                        "every row certified (pivots only)",
+            "pivot_rows": rows, "bytes": nbytes, "avg_us": round(us, 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(steps):
@@ -231,6 +266,10 @@ def main():
             "traffic": profiled_traffic(dom) if dom in KERNEL_SOURCES else None,
             "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}
     h2d_peak = h2d_bandwidth(torch)
+    piv = None
+    if not args.no_pivot_batch:
+        log("[bench] pivotal stream at the 16-sequence batch")
+        piv = pivotal_stream(torch)
 
     out = {
         "metric": "certified decode steps/s at 32K ctx, eta=1/16; achieved HBM GB/s vs peak",
@@ -251,6 +290,7 @@ def main():
                                "hitters, tau~Beta(0.3,3)",
                    "layers_rotated": L, "seq_len": N_CTX, "batch": 1},
         "roofline": roof,
+        "pivotal_stream": piv,
         "cpu_baseline": None,
         "step_stats": {"rows_certified_without_fetch": cert / rows,
                        "fetched_fraction_of_cache": fetched / n_tok,
