@@ -88,6 +88,13 @@ typedef struct {
   int32_t sketch_exact;     /* 1: the sketch rows are the keys, so the host fetch of    */
                             /* KVFetch step 5 reads only the value rows and takes the  */
                             /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
+  const void *v_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the value     */
+                            /* cache verkv_refine reads (may be NULL).  With it and    */
+                            /* sketch_exact, verkv_decode_step copies value rows that  */
+                            /* the previous step on the same workspace read from the   */
+                            /* host into the workspace while the sketch and decision   */
+                            /* kernels run; verkv_refine then takes the rows it needs  */
+                            /* from there.  Results do not depend on it.               */
 } verkv_state;
 
 /* Per-step results.  Row arrays are [B][Hq]; KV-head arrays are [B][Hkv]. */
@@ -147,8 +154,9 @@ size_t verkv_compress_workspace_bytes(const verkv_shape *s);
  *   workspace at least verkv_decode_workspace_bytes(s, st->cap); pass the same
  *          workspace to verkv_refine for this step.  Between steps it keeps each
  *          row's B*, which the next step on it takes as the starting point of its
- *          fixed-point search (results do not depend on it; zero-filled or foreign
- *          contents only cost iterations).
+ *          fixed-point search, and the list of host rows the step read, which the next
+ *          step prefetches (see verkv_state.v_host).  Results do not depend on either:
+ *          zero-filled or foreign contents only cost time.
  * No host synchronisation and no host-memory traffic. */
 verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
                                double beta, double eps, double delta, verkv_step_out *out,
@@ -176,9 +184,10 @@ size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
  * waits for the recorded launches, writes per kernel kind the summed duration in ms
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
- * 7 finish, 8 eps_after partials, 9 pivot coefficients), and clears the record.  verkv_profile_end destroys the events.  Not
+ * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 host-row prefetch), and
+ * clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 10
+#define VERKV_PROFILE_KINDS 11
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);

@@ -93,11 +93,22 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
       bt.pp[u] = p;
       bt.tk[u] = 0;
       if (p < p1) {
-        const int tok = HOST ? list[p] : p;
+        int tok = p;
+        const uint8_t *vsrc = nullptr;
+        if constexpr (HOST) {
+          // a list entry is token | (prefetch slot + 1) << TOKEN_BITS; the slot's row is
+          // used when the slot still holds this token
+          const int32_t e = list[p];
+          tok = e & TOKEN_MASK;
+          const int slot = (int)((uint32_t)e >> TOKEN_BITS) - 1;
+          if (slot >= 0 && a.stage_tok[(int64_t)unit * a.stage_rows + slot] == tok)
+            vsrc = a.stage + ((int64_t)unit * a.stage_rows + slot) * ROW_BYTES + slice;
+        }
         bt.tk[u] = tok;
         const int64_t rowi = src_base + tok;
         if (!EXACT) bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
-        bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+        if (!vsrc) vsrc = a.vrows + rowi * ROW_BYTES + slice;
+        bt.vr[u] = *(const uint4 *)vsrc;
         if constexpr (!HOST) {
           // the row's G coefficients are contiguous ([unit][cap][G]): vector loads
           const float *cp = a.coef + ((int64_t)unit * a.cap + p) * G;

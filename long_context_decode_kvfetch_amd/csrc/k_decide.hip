@@ -1037,7 +1037,9 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
 // prefix.  Inside the block every wave owns a sub-run: pass 1 counts, a block scan
 // gives each wave its first list position, pass 2 walks the groups in order, one lane
 // per token, and writes the set bits with a ballot prefix so that consecutive list
-// entries come from consecutive lanes (whole-line stores).  Lists are ascending.
+// entries come from consecutive lanes (whole-line stores).  Lists are ascending.  A
+// host-row entry also carries the token's prefetch slot + 1 (its rank among the
+// prefetched tokens of the head) above TOKEN_BITS, 0 when it was not prefetched.
 constexpr int LS_NT = 256;
 constexpr int LS_NB = 32;
 
@@ -1062,43 +1064,58 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
     const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
     return lo32 | (hi32 << 32);
   };
-  // tokens of F and of F \ S before this block's run
-  int32_t cf = 0, ch = 0;
+  // prefetched tokens (their rank is the prefetch slot)
+  const uint32_t *sbw = a.sbits ? a.sbits + word_base(a.t, b, g) : nullptr;
+  auto staged_bits = [&](int gi) -> uint64_t { return sbw ? group_bits(sbw, gi) : 0ull; };
+  // tokens of F, of F \ S and prefetched tokens before this block's run
+  int32_t cf = 0, ch = 0, cs = 0;
   for (int gi = tid; gi < B0; gi += LS_NT) {
     const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
     cf += __popcll(f);
     ch += __popcll(f & ~r);
+    cs += __popcll(staged_bits(gi));
   }
-  int32_t bf, bh;
+  int32_t bf, bh, bs;
   (void)block_excl_scan<LS_NT>(cf, iscr, &bf);
   (void)block_excl_scan<LS_NT>(ch, iscr, &bh);
+  (void)block_excl_scan<LS_NT>(cs, iscr, &bs);
   // this block's run, split over its waves
   const int gpw = (B1 - B0 + NWV - 1) / NWV;
   const int ga = min(B1, B0 + wv * gpw), gb = min(B1, ga + gpw);
   cf = 0;
   ch = 0;
+  cs = 0;
   for (int gi = ga + lane; gi < gb; gi += WAVE) {
     const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
     cf += __popcll(f);
     ch += __popcll(f & ~r);
+    cs += __popcll(staged_bits(gi));
   }
   cf = (int32_t)wave_sum_i64(cf);
   ch = (int32_t)wave_sum_i64(ch);
-  int32_t tf, th;
+  cs = (int32_t)wave_sum_i64(cs);
+  int32_t tf, th, ts;
   int32_t pf = block_excl_scan<LS_NT>(lane == 0 ? cf : 0, iscr, &tf);
   int32_t ph = block_excl_scan<LS_NT>(lane == 0 ? ch : 0, iscr, &th);
+  int32_t ps = block_excl_scan<LS_NT>(lane == 0 ? cs : 0, iscr, &ts);
   pf = bf + __shfl(pf, 0, WAVE);            // the wave's first positions (lane 0's)
   ph = bh + __shfl(ph, 0, WAVE);
+  ps = bs + __shfl(ps, 0, WAVE);
   int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
   int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
   const uint64_t below = (1ull << lane) - 1ull;
   for (int c0 = ga; c0 < gb; c0 += WAVE) {
     // lane j holds group c0 + j; the walk below takes them in order by shuffle
-    uint64_t fl_l = 0, rl_l = 0;
-    if (c0 + lane < gb) { fl_l = group_bits(fb, c0 + lane); rl_l = group_bits(res, c0 + lane); }
+    uint64_t fl_l = 0, rl_l = 0, sl_l = 0;
+    if (c0 + lane < gb) {
+      fl_l = group_bits(fb, c0 + lane);
+      rl_l = group_bits(res, c0 + lane);
+      sl_l = staged_bits(c0 + lane);
+    }
     const int nj = min(WAVE, gb - c0);
     for (int jj = 0; jj < nj; ++jj) {
       const uint64_t f = __shfl(fl_l, jj, WAVE), r = __shfl(rl_l, jj, WAVE);
+      const uint64_t sg = __shfl(sl_l, jj, WAVE);
       const uint64_t hsel = f & ~r;
       const bool inf = (f >> lane) & 1ull, inh = (hsel >> lane) & 1ull;
       const int tok = 64 * (c0 + jj) + lane;
@@ -1106,14 +1123,20 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
         const int32_t pos = pf + (int32_t)__popcll(f & below);
         if (fl && pos < a.fetch_cap) fl[pos] = tok;
       }
-      if (inh) hl[ph + (int32_t)__popcll(hsel & below)] = tok;
+      if (inh) {
+        // host-row entry: the token, and its prefetch slot + 1 when it was prefetched
+        const int32_t slot1 = ((sg >> lane) & 1ull) ? ps + (int32_t)__popcll(sg & below) + 1 : 0;
+        hl[ph + (int32_t)__popcll(hsel & below)] = tok | (slot1 << TOKEN_BITS);
+      }
       pf += (int32_t)__popcll(f);
       ph += (int32_t)__popcll(hsel);
+      ps += (int32_t)__popcll(sg);
     }
   }
   if (blockIdx.x == LS_NB - 1 && tid == 0) {
     a.fetch_count[unit] = bf + tf;
     a.h2d_count[unit] = bh + th;
+    if (a.h2d_count_ws) a.h2d_count_ws[unit] = bh + th;
   }
 }
 

@@ -1,0 +1,94 @@
+// Host-row prefetch for gfx950: between two decode steps of a layer the fetch sets
+// overlap heavily, so the value rows the previous step read from the host (KVFetch
+// step 5, "Verify Before You Fetch", picx.dev summary page) are copied into the
+// workspace while the current step's decision kernel runs; the host-row kernel of the
+// current step takes those it needs from there instead of the host link.  The values
+// are the same rows of the same cache, so results do not change.
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace verkv {
+
+// ------------------------------------------------------------------ host-row prefetch
+// Copies, per KV head, the value rows of the first stage_rows entries of the previous
+// step's host-row list from the pinned host cache into the workspace (zero-copy loads,
+// two rows in flight per lane group), records each slot's token, and rebuilds the
+// head's bitmask of prefetched tokens (block 0 of the head).  Entries are validated
+// (token < n), so a list left by another shape only costs useless copies.  The kernel
+// runs beside the decision kernel (one 256-thread block per CU fits next to it: no
+// LDS, at most 32 VGPRs), so it lives in a file of its own.
+constexpr int PF_NT = 256;
+constexpr int PF_GRID = 64;                // blocks per launch: at most one per CU, so each
+                                           // fits beside a decision-kernel workgroup
+
+template <bool BF16>
+__global__ __launch_bounds__(PF_NT) void k_prefetch(PrefetchArgs a) {
+  using RS = RowSlice<BF16>;
+  constexpr int LPR = D / RS::EPL;         // lanes per row (16 or 32)
+  constexpr int RPI = PF_NT / LPR;         // rows per block iteration
+  constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
+  const int unit = blockIdx.y;
+  const int b = unit / a.t.Hkv;
+  const int g = unit % a.t.Hkv;
+  const int n = a.t.s[b].n;
+  const int tid = threadIdx.x;
+  const int cnt = min(max(a.prev_count[unit], 0), n);
+  const int ns = min(cnt, a.stage_rows);
+  const int32_t *pl = a.prev_list + tok_base(a.t, b, g);
+  if (blockIdx.x == 0) {
+    uint32_t *sb = a.sbits + word_base(a.t, b, g);
+    const int W = words_of(n);
+    for (int w = tid; w < W; w += PF_NT) sb[w] = 0u;
+    __syncthreads();
+    // the list is ascending, so the tokens of one bitmask word are consecutive entries:
+    // the first entry of each word gathers the word's bits and stores it (no atomics)
+    for (int p = tid; p < ns; p += PF_NT) {
+      const int tok = pl[p] & TOKEN_MASK;
+      if (tok >= n) continue;
+      const int w = tok >> 5;
+      if (p > 0 && ((pl[p - 1] & TOKEN_MASK) >> 5) == w) continue;
+      uint32_t bits = 0u;
+      for (int q = p; q < ns && q < p + 32; ++q) {
+        const int t2 = pl[q] & TOKEN_MASK;
+        if (t2 >= n || (t2 >> 5) != w) break;
+        bits |= 1u << (t2 & 31);
+      }
+      sb[w] = bits;
+    }
+  }
+  const int sub = tid % LPR;
+  const int64_t src = tok_base(a.t, b, g);
+  uint8_t *dst = a.stage + (int64_t)unit * a.stage_rows * ROW_BYTES;
+  int32_t *dtok = a.stage_tok + (int64_t)unit * a.stage_rows;
+  // two rows per lane group in flight (named registers: an indexed array here would be
+  // placed in LDS, which must stay free for the decision kernel beside this one)
+  auto fetch = [&](int p, uint4 &v) -> int {
+    if (p >= ns) return -1;
+    const int tok = pl[p] & TOKEN_MASK;
+    if (tok >= n) return -1;
+    v = *(const uint4 *)(a.vrows + (src + tok) * ROW_BYTES + sub * 16);
+    return tok;
+  };
+  auto put = [&](int p, int tok, const uint4 &v) {
+    if (p >= a.stage_rows) return;
+    if (tok >= 0) *(uint4 *)(dst + (int64_t)p * ROW_BYTES + sub * 16) = v;
+    if (sub == 0) dtok[p] = tok;
+  };
+  for (int p0 = blockIdx.x * RPI * 2; p0 < a.stage_rows; p0 += gridDim.x * RPI * 2) {
+    const int pa = p0 + tid / LPR, pb = pa + RPI;
+    uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+    const int ta = fetch(pa, va);
+    const int tb = fetch(pb, vb);
+    put(pa, ta, va);
+    put(pb, tb, vb);
+  }
+}
+
+hipError_t launch_prefetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st) {
+  const int per_unit = std::max(1, PF_GRID / std::max(1, units));
+  if (bf16) return launch_kernel(k_prefetch<true>, dim3(per_unit, units), dim3(PF_NT), 0, st, a);
+  return launch_kernel(k_prefetch<false>, dim3(per_unit, units), dim3(PF_NT), 0, st, a);
+}
+
+}  // namespace verkv

@@ -104,6 +104,21 @@ struct UnionArgs {
   float *coef;               // [B][Hkv][cap][G]
   int32_t coef_pass;         // 0: fetch lists (grid y = 1); 1: pivot coefficients
   const double *params;      // coefficient pass: params[0] = kappa of the step (device)
+  const uint32_t *sbits;     // lists: [B][Hkv][W] prefetched tokens, or null
+  int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
+};
+
+// Host-row prefetch: the first stage_rows entries of the previous step's host-row list
+// of each KV head are copied into the workspace (value rows only, exact sketch).
+struct PrefetchArgs {
+  SeqTable t;
+  const int32_t *prev_list;  // [B][Hkv][n] entries of the previous list (token | slot << 20)
+  const int32_t *prev_count; // [B][Hkv]
+  const uint8_t *vrows;      // host value cache (device view) [B][Hkv][n][128]
+  uint8_t *stage;            // [B*Hkv][stage_rows][128] kv dtype
+  int32_t *stage_tok;        // [B*Hkv][stage_rows] token of each slot, -1 if none
+  uint32_t *sbits;           // [B][Hkv][W] bit per prefetched token
+  int32_t stage_rows;
 };
 
 struct AttendArgs {
@@ -121,6 +136,9 @@ struct AttendArgs {
   int32_t nsplit;
   const double *wc;          // host source with exact sketch: weights w_hat = wc * cscale
   const double *cscale;
+  const uint8_t *stage;      // host source: prefetched value rows [B*Hkv][stage_rows][128]
+  const int32_t *stage_tok;  //   and their tokens (a list entry's slot is checked against it)
+  int32_t stage_rows;
 };
 
 struct FinishArgs {
@@ -146,6 +164,10 @@ constexpr int DECIDE_THREADS = 512;
 constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
 constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
+constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot + 1) << 20
+constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
+constexpr int STAGE_SLOTS_MAX = 2047;    // slot + 1 fits the 11 bits above the token
+constexpr int STAGE_ROWS_TOTAL = 20480;  // prefetched rows per call, over all KV heads
 constexpr int PIVOT_TOKENS = 64;  // fewest pivot rows per attention workgroup
 constexpr int PIVOT_WGS = 2048;   // attention workgroups aimed at per launch (8 per CU)
 
@@ -176,6 +198,7 @@ hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, b
                          hipStream_t st);
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st);
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
+hipError_t launch_prefetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st);
 int decide_blocks_per_cu(int max_n, int team);
 
 }  // namespace verkv

@@ -101,6 +101,8 @@ int team_size(int rows, int max_n) {
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
+  size_t stage, stage_tok, sbits, h2dc;
+  int srows;
   size_t total;
   int nsp, nsh, team;
 };
@@ -137,6 +139,12 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.hpart = off;  off = align_up(off + 4 * (size_t)units * w.nsh * t.G * (D + 1));
   w.status = off; off = align_up(off + 64);
   w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
+  // host-row prefetch: value rows staged per KV head (sized for float32 rows)
+  w.srows = std::min(STAGE_SLOTS_MAX, STAGE_ROWS_TOTAL / std::max(1, units));
+  w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * 4);
+  w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
+  w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
+  w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
   w.total = off;
   return w;
 }
@@ -203,7 +211,7 @@ int decide_capacity(int max_n, int team) {
 // call are recorded under a per-device lock.
 struct Side {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, pref = nullptr;
   std::mutex mu;
 };
 constexpr int MAX_DEVICES = 64;
@@ -220,6 +228,7 @@ verkv_status side_for_device(Side **out) {
     HIP_TRY(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking), "hipStreamCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming), "hipEventCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming), "hipEventCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&sd.pref, hipEventDisableTiming), "hipEventCreateWithFlags");
   }
   *out = &sd;
   return VERKV_OK;
@@ -227,7 +236,7 @@ verkv_status side_for_device(Side **out) {
 
 // ---------------------------------------------------------------- optional kernel timing
 enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER,
-                K_COEF, K_COUNT };
+                K_COEF, K_PREFETCH, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -261,7 +270,7 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 103; }
+int32_t verkv_version(void) { return 104; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -416,6 +425,34 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
     HIP_TRY(launch_sketch(sk, bf16, stream), "sketch launch");
   }
 
+  // host-row prefetch on the library's second stream, beside the decision kernel (it
+  // starts after the sketch kernel, which needs every register of the CUs): rows the
+  // previous step on this workspace read from the host
+  Side *sd = nullptr;
+  if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
+  std::unique_lock<std::mutex> lk(sd->mu);
+  const bool prefetch = st->v_host && st->sketch_exact && L.srows > 0;
+  if (prefetch) {
+    const void *Vd = nullptr;
+    if ((rc = device_view(st->v_host, &Vd)) != VERKV_OK) return rc;
+    HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
+    HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
+    PrefetchArgs pa;
+    pa.t = t;
+    pa.prev_list = reinterpret_cast<const int32_t *>(ws + L.h2d);
+    pa.prev_count = reinterpret_cast<const int32_t *>(ws + L.h2dc);
+    pa.vrows = static_cast<const uint8_t *>(Vd);
+    pa.stage = ws + L.stage;
+    pa.stage_tok = reinterpret_cast<int32_t *>(ws + L.stage_tok);
+    pa.sbits = reinterpret_cast<uint32_t *>(ws + L.sbits);
+    pa.stage_rows = L.srows;
+    {
+      Timed tm(K_PREFETCH, sd->s);
+      HIP_TRY(launch_prefetch(pa, units, bf16, sd->s), "prefetch launch");
+    }
+    HIP_TRY(hipEventRecord(sd->pref, sd->s), "hipEventRecord");
+  }
+
   DecideArgs dc;
   dc.t = t;
   dc.wc = sk.wc;
@@ -480,6 +517,11 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   un.coef = reinterpret_cast<float *>(ws + L.coef);
   un.params = nullptr;
   un.coef_pass = 0;
+  un.sbits = prefetch ? reinterpret_cast<const uint32_t *>(ws + L.sbits) : nullptr;
+  un.h2d_count_ws = reinterpret_cast<int32_t *>(ws + L.h2dc);
+  // the list is rewritten here: the prefetch must have read it
+  if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
+  lk.unlock();
   {
     Timed tm(K_UNION, stream);
     HIP_TRY(launch_union(un, units, stream), "union launch");
@@ -531,6 +573,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   at.nsplit = L.nsh;
   at.wc = reinterpret_cast<const double *>(ws + L.wc);
   at.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  at.stage = ws + L.stage;
+  at.stage_tok = reinterpret_cast<const int32_t *>(ws + L.stage_tok);
+  at.stage_rows = L.srows;
   {
     Timed tm(K_HOST, stream);
     HIP_TRY(launch_attend(at, units, bf16, true, st->sketch_exact != 0, stream),
@@ -559,6 +604,8 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   un.h2d_idx = nullptr;
   un.coef = reinterpret_cast<float *>(ws + L.coef);
   un.coef_pass = 1;
+  un.sbits = nullptr;
+  un.h2d_count_ws = nullptr;
   {
     Timed tm(K_COEF, sd->s);
     HIP_TRY(launch_union(un, units, sd->s), "pivot coefficient launch");
@@ -579,6 +626,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   pv.nsplit = L.nsp;
   pv.wc = nullptr;
   pv.cscale = nullptr;
+  pv.stage = nullptr;
+  pv.stage_tok = nullptr;
+  pv.stage_rows = 0;
   {
     Timed tm(K_PIVOT, sd->s);
     HIP_TRY(launch_attend(pv, units, bf16, false, false, sd->s), "pivot attention launch");

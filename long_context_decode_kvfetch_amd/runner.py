@@ -22,7 +22,8 @@ class Session:
     """One layer of a workload, compressed on the GPU, ready for decode steps."""
 
     def __init__(self, wl: Workload, cap: int | None = None, device: str = "cuda",
-                 host_pinned: bool = True, seed: int | None = None, sketch_exact: bool = True):
+                 host_pinned: bool = True, seed: int | None = None, sketch_exact: bool = True,
+                 prefetch: bool = True):
         self.wl = wl
         self.device = device
         lens = [s.n for s in wl.seqs]
@@ -42,7 +43,8 @@ class Session:
         self.sketch = K.to(device)              # exact sketch: the keys, device resident
         self.tau = torch.from_numpy(_cat([s.tau for s in wl.seqs]).astype(np.float32)).to(device)
         self.cap = int(cap) if cap else verkv.default_cap(self.shape, wl.eta)
-        self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device, sketch_exact)
+        self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device, sketch_exact,
+                                      v_host=self.V_host if (host_pinned and prefetch) else None)
         self.cws = verkv.workspace(self.shape.compress_workspace_bytes(), device)
         self.dws = verkv.workspace(self.shape.decode_workspace_bytes(self.cap), device)
         self.out = verkv.StepBuffers(self.shape, device=device)

@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 10
+PROFILE_KINDS = 11
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
-                "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef"]
+                "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef", "prefetch"]
 
 
 class VerKVError(RuntimeError):
@@ -44,7 +44,8 @@ class Shape(C.Structure):
 class State(C.Structure):
     _fields_ = [("r", C.c_void_p), ("resident", C.c_void_p), ("piv_idx", C.c_void_p),
                 ("piv_count", C.c_void_p), ("piv_k", C.c_void_p), ("piv_v", C.c_void_p),
-                ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32)]
+                ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32),
+                ("v_host", C.c_void_p)]
 
 
 class StepOut(C.Structure):
@@ -168,7 +169,7 @@ class LayerState:
     """GPU-resident compressed state of one layer (caller-owned torch buffers)."""
 
     def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda",
-                 sketch_exact: bool = True):
+                 sketch_exact: bool = True, v_host: torch.Tensor | None = None):
         hkv, tot = shape.n_kv_heads, shape.total_tokens
         words = sum((n + 31) // 32 for n in shape.seq_lens)
         units = shape.batch * hkv
@@ -181,9 +182,10 @@ class LayerState:
         self.piv_k = torch.empty(units * cap * HEAD_DIM, dtype=shape.torch_dtype, device=device)
         self.piv_v = torch.empty(units * cap * HEAD_DIM, dtype=shape.torch_dtype, device=device)
         self.sketch = sketch
+        self.v_host = v_host                    # kept alive with the state
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
                        _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch),
-                       1 if sketch_exact else 0)
+                       1 if sketch_exact else 0, _ptr(v_host) if v_host is not None else None)
 
 
 class StepBuffers:
