@@ -130,3 +130,39 @@ def test_long_context_131k_eta_1_32():
     """n = 131072, eta = 1/32 (the long-context shape), two KV heads, full length."""
     _run(synth.gqa_layer(seed=7, n=131072, steps=1, hkv=2, eta=1.0 / 32, eps=0.1),
          label="131k")
+
+
+def test_prefetch_and_workspace_history_do_not_change_results():
+    """Three steps on one layer with the host-row prefetch on, off, and on with a
+    workspace that starts out as random bytes: every output is bit-identical (the
+    prefetched rows are the same host rows; a foreign workspace only costs time)."""
+    from long_context_decode_kvfetch_amd import verkv
+    wl = synth.gqa_layer(seed=2, n=8192, steps=3, hkv=2)
+    keys = ("o", "lse", "n_hat", "d_hat", "beta_star", "eps_hat", "kstar", "certified",
+            "fetch_count", "h2d_count", "eps_after")
+    runs = []
+    for label, kw, scramble in (("prefetch", {}, False), ("no prefetch", {"prefetch": False}, False),
+                                ("random workspace", {}, True)):
+        say(f"[parity] history: {label}")
+        sess = _session(wl, **kw)
+        sess.compress()
+        if scramble:
+            g = torch.Generator(device="cuda").manual_seed(7)
+            sess.dws.copy_(torch.randint(0, 256, sess.dws.shape, dtype=torch.uint8, device="cuda",
+                                         generator=g).view(sess.dws.dtype))
+            torch.cuda.synchronize()
+            try:
+                verkv.check(sess.shape, sess.cap, sess.dws)      # clears random kernel flags
+            except Exception:
+                pass
+        steps = []
+        for st in range(3):
+            sess.step(sess.queries(st))
+            verkv.check(sess.shape, sess.cap, sess.dws)
+            r = sess.results_numpy()
+            steps.append({k: np.array(r[k]) for k in keys})
+        runs.append(steps)
+    for label, other in (("no prefetch", runs[1]), ("random workspace", runs[2])):
+        for st in range(3):
+            for k in keys:
+                assert np.array_equal(runs[0][st][k], other[st][k]), (label, st, k)
