@@ -1125,8 +1125,8 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
       }
       if (inh) {
         // host-row entry: the token, and its prefetch slot + 1 when it was prefetched
-        const int32_t slot1 = ((sg >> lane) & 1ull) ? ps + (int32_t)__popcll(sg & below) + 1 : 0;
-        hl[ph + (int32_t)__popcll(hsel & below)] = tok | (slot1 << TOKEN_BITS);
+        const uint32_t slot1 = ((sg >> lane) & 1ull) ? (uint32_t)(ps + __popcll(sg & below) + 1) : 0u;
+        hl[ph + (int32_t)__popcll(hsel & below)] = (int32_t)((uint32_t)tok | (slot1 << TOKEN_BITS));
       }
       pf += (int32_t)__popcll(f);
       ph += (int32_t)__popcll(hsel);

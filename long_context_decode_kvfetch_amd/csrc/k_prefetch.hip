@@ -13,7 +13,7 @@ namespace verkv {
 // ------------------------------------------------------------------ host-row prefetch
 // Copies, per KV head, the value rows of the first stage_rows entries of the previous
 // step's host-row list from the pinned host cache into the workspace (zero-copy loads,
-// two rows in flight per lane group), records each slot's token, and rebuilds the
+// three rows in flight per lane group), records each slot's token, and rebuilds the
 // head's bitmask of prefetched tokens (block 0 of the head).  Entries are validated
 // (token < n), so a list left by another shape only costs useless copies.  The kernel
 // runs beside the decision kernel (one 256-thread block per CU fits next to it: no
@@ -23,7 +23,7 @@ constexpr int PF_GRID = 64;                // blocks per launch: at most one per
                                            // fits beside a decision-kernel workgroup
 
 template <bool BF16>
-__global__ __launch_bounds__(PF_NT) void k_prefetch(PrefetchArgs a) {
+__global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_prefetch(PrefetchArgs a) {
   using RS = RowSlice<BF16>;
   constexpr int LPR = D / RS::EPL;         // lanes per row (16 or 32)
   constexpr int RPI = PF_NT / LPR;         // rows per block iteration
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(PF_NT) void k_prefetch(PrefetchArgs a) {
   const int64_t src = tok_base(a.t, b, g);
   uint8_t *dst = a.stage + (int64_t)unit * a.stage_rows * ROW_BYTES;
   int32_t *dtok = a.stage_tok + (int64_t)unit * a.stage_rows;
-  // two rows per lane group in flight (named registers: an indexed array here would be
+  // three rows per lane group in flight (named registers: an indexed array here would be
   // placed in LDS, which must stay free for the decision kernel beside this one)
   auto fetch = [&](int p, uint4 &v) -> int {
     if (p >= ns) return -1;
@@ -75,13 +75,15 @@ __global__ __launch_bounds__(PF_NT) void k_prefetch(PrefetchArgs a) {
     if (tok >= 0) *(uint4 *)(dst + (int64_t)p * ROW_BYTES + sub * 16) = v;
     if (sub == 0) dtok[p] = tok;
   };
-  for (int p0 = blockIdx.x * RPI * 2; p0 < a.stage_rows; p0 += gridDim.x * RPI * 2) {
-    const int pa = p0 + tid / LPR, pb = pa + RPI;
-    uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+  for (int p0 = blockIdx.x * RPI * 3; p0 < a.stage_rows; p0 += gridDim.x * RPI * 3) {
+    const int pa = p0 + tid / LPR, pb = pa + RPI, pc = pb + RPI;
+    uint4 va = make_uint4(0, 0, 0, 0), vb = va, vc = va;
     const int ta = fetch(pa, va);
     const int tb = fetch(pb, vb);
+    const int tc = fetch(pc, vc);
     put(pa, ta, va);
     put(pb, tb, vb);
+    put(pc, tc, vc);
   }
 }
 

@@ -166,8 +166,8 @@ constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
 constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot + 1) << 20
 constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
-constexpr int STAGE_SLOTS_MAX = 2047;    // slot + 1 fits the 11 bits above the token
-constexpr int STAGE_ROWS_TOTAL = 20480;  // prefetched rows per call, over all KV heads
+constexpr int STAGE_SLOTS_MAX = 4095;    // slot + 1 fits the 12 bits above the token
+constexpr int STAGE_ROWS_TOTAL = 16384;  // prefetched rows per call, over all KV heads
 constexpr int PIVOT_TOKENS = 64;  // fewest pivot rows per attention workgroup
 constexpr int PIVOT_WGS = 2048;   // attention workgroups aimed at per launch (8 per CU)
 
