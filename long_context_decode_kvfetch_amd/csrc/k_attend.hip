@@ -17,6 +17,8 @@
 // its partial (N[G][128], D[G]) so the finishing kernel sums a fixed set in a fixed order.
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace verkv {
 
 constexpr int AT_NT = 256;
@@ -212,10 +214,188 @@ static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st
   return launch_kernel(k_attend<BF16, G, HOST, EXACT>, dim3(a.nsplit, units), dim3(AT_NT), 0, st, a);
 }
 
+// ------------------------------------------------------------------ resident pivots, persistent
+// The same partials as k_attend over the resident pivots, from workgroups that stay
+// resident: workgroup w takes splits w, w + gridDim.x, ... (split j is split j % nsplit
+// of KV head j / nsplit) and streams their batches back to back, the next batch's
+// loads issued before the current batch is reduced, also across the end of a split,
+// so the loads stay in flight while a split's partial is reduced and written.
+template <bool BF16, int G>
+__global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
+  using RS = RowSlice<BF16>;
+  constexpr int EPL = RS::EPL;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = WAVE / LPT;
+  constexpr int STEP = AT_NW * TPW;
+  constexpr int U = 2;
+  constexpr int SU = STEP * U;
+  constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
+  constexpr int PS = D + 1;
+
+  __shared__ float s_acc[AT_NW][TPW][G][D];
+  __shared__ float s_den[AT_NW][TPW][G];
+
+  const int Hq = a.t.Hkv * G;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wv = threadIdx.x / WAVE;
+  const int sub = lane % LPT;
+  const int grp = lane / LPT;
+  const int d0 = sub * EPL;
+  const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
+  const int nsplit = a.nsplit;
+  const int total = a.t.B * a.t.Hkv * nsplit;
+
+  // the row range of split j
+  auto range = [&](int j, int &unit, int &p0, int &p1) {
+    unit = j / nsplit;
+    const int sp = j % nsplit;
+    const int cnt = min(a.count[unit], a.cap);
+    int per = (cnt + nsplit - 1) / nsplit;
+    per = ((per + STEP - 1) / STEP) * STEP;
+    p0 = sp * per;
+    p1 = min(cnt, p0 + per);
+  };
+
+  struct Batch {
+    uint4 kr[U], vr[U];
+    int pp[U];
+    float cc[U][G];
+  };
+  auto issue = [&](int unit, int base, int p1, Batch &bt) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + u * STEP + wv * TPW + grp;
+      bt.pp[u] = p < p1 ? p : -1;
+      if (p < p1) {
+        const int64_t rowi = (int64_t)unit * a.cap + p;
+        bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+        bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+        const float *cp = a.coef + rowi * G;
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int j4 = 0; j4 < G; j4 += 4) {
+            const float4 c4 = *(const float4 *)(cp + j4);
+            bt.cc[u][j4] = c4.x; bt.cc[u][j4 + 1] = c4.y; bt.cc[u][j4 + 2] = c4.z; bt.cc[u][j4 + 3] = c4.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < G; ++j) bt.cc[u][j] = cp[j];
+        }
+      } else {
+        bt.kr[u] = make_uint4(0, 0, 0, 0);
+        bt.vr[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < G; ++j) bt.cc[u][j] = 0.0f;
+      }
+    }
+  };
+
+  float qf[G][EPL], mh[G];
+  float acc[G][EPL], den[G];
+  auto setup = [&](int unit) {
+    const int b = unit / a.t.Hkv, g = unit % a.t.Hkv;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int64_t qrow = (int64_t)b * Hq + g * G + j;
+      const float *qr = a.q + qrow * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * a.inv_sqrt_d;
+      mh[j] = (float)a.m_hat[qrow];
+      den[j] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
+    }
+  };
+  auto consume = [&](const Batch &bt) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[EPL], v[EPL], w[G];
+      RS::widen(bt.kr[u], x);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
+        dot = sum16(dot);
+        if (LPT == 32) dot += shfl_xor_f(dot, 16);
+        w[j] = bt.pp[u] >= 0 ? __expf(dot - mh[j]) * bt.cc[u][j] : 0.0f;
+      }
+      RS::widen(bt.vr[u], v);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        den[j] += w[j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(w[j], v[e], acc[j][e]);
+      }
+    }
+  };
+  auto epilogue = [&](int j) {
+    if (sub == 0) {
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) s_den[wv][grp][jj] = den[jj];
+    }
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wv][grp][jj][d0 + e] = acc[jj][e];
+    }
+    __syncthreads();
+    float *out = a.part + (int64_t)j * G * PS;
+    for (int t = threadIdx.x; t < G * PS; t += AT_NT) {
+      const int jj = t / PS, d = t % PS;
+      float sm = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < AT_NW; ++w2)
+#pragma unroll
+        for (int r2 = 0; r2 < TPW; ++r2) sm += (d < D) ? s_acc[w2][r2][jj][d] : s_den[w2][r2][jj];
+      out[t] = sm;
+    }
+    __syncthreads();
+  };
+
+  int j = blockIdx.x;
+  if (j >= total) return;
+  int unit, p0, p1;
+  range(j, unit, p0, p1);
+  setup(unit);
+  int base = p0;
+  Batch A, B;
+  issue(unit, base, p1, A);
+  while (true) {
+    // the batch after A: the rest of this split, else the first batch of the next one
+    int nj = j, nunit = unit, nbase = base + SU, np1 = p1;
+    if (nbase >= p1) {
+      nj = j + gridDim.x;
+      if (nj < total) {
+        int q0;
+        range(nj, nunit, q0, np1);
+        nbase = q0;
+      }
+    }
+    const bool more = nj < total;
+    if (more) issue(nunit, nbase, np1, B);
+    consume(A);
+    if (nj != j) {                                   // split j is complete
+      epilogue(j);
+      if (!more) break;
+      j = nj;
+      unit = nunit;
+      p1 = np1;
+      setup(unit);
+    }
+    base = nbase;
+    A = B;
+  }
+}
+
 template <bool BF16, int G>
 static hipError_t launch_attend_g(const AttendArgs &a, int units, bool host, bool exact,
                                   hipStream_t st) {
-  if (!host) return launch_attend_t<BF16, G, false, false>(a, units, st);
+  if (!host) {
+    // persistent workgroups: three per CU, never more than there are splits
+    const int total = units * a.nsplit;
+    return launch_kernel(k_attend_piv<BF16, G>, dim3(std::min(total, 3 * 256)), dim3(AT_NT), 0, st, a);
+  }
   if (exact) return launch_attend_t<BF16, G, true, true>(a, units, st);
   return launch_attend_t<BF16, G, true, false>(a, units, st);
 }
