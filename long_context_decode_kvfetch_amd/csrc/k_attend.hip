@@ -216,18 +216,22 @@ static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st
 
 // ------------------------------------------------------------------ resident pivots, persistent
 // The same partials as k_attend over the resident pivots, from workgroups that stay
-// resident: workgroup w takes splits w, w + gridDim.x, ... (split j is split j % nsplit
-// of KV head j / nsplit) and streams their batches back to back, the next batch's
-// loads issued before the current batch is reduced, also across the end of a split,
-// so the loads stay in flight while a split's partial is reduced and written.
+// resident and share the rows evenly: worker w takes the chunks the coefficient pass
+// scheduled for it (consecutive chunks of PIVOT_CHUNK rows, possibly over several KV
+// heads) and streams their batches back to back, the next batch's loads issued before
+// the current batch is reduced, also across the end of a run, so the loads stay in
+// flight while a run's partial is reduced and written.  A run is the worker's rows of
+// one KV head; its partial goes to the slot the schedule gives it.
+constexpr int PIV_U = 2;           // row groups per batch of a pivot worker
+
 template <bool BF16, int G>
-__global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
+__global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_attend_piv(AttendArgs a) {
   using RS = RowSlice<BF16>;
   constexpr int EPL = RS::EPL;
   constexpr int LPT = D / EPL;
   constexpr int TPW = WAVE / LPT;
   constexpr int STEP = AT_NW * TPW;
-  constexpr int U = 2;
+  constexpr int U = PIV_U;
   constexpr int SU = STEP * U;
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
   constexpr int PS = D + 1;
@@ -236,56 +240,41 @@ __global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
   __shared__ float s_den[AT_NW][TPW][G];
 
   const int Hq = a.t.Hkv * G;
+  const int units = a.t.B * a.t.Hkv;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x / WAVE;
   const int sub = lane % LPT;
   const int grp = lane / LPT;
   const int d0 = sub * EPL;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
-  const int nsplit = a.nsplit;
-  const int total = a.t.B * a.t.Hkv * nsplit;
-
-  // the row range of split j
-  auto range = [&](int j, int &unit, int &p0, int &p1) {
-    unit = j / nsplit;
-    const int sp = j % nsplit;
-    const int cnt = min(a.count[unit], a.cap);
-    int per = (cnt + nsplit - 1) / nsplit;
-    per = ((per + STEP - 1) / STEP) * STEP;
-    p0 = sp * per;
-    p1 = min(cnt, p0 + per);
-  };
+  constexpr int R = PIVOT_CHUNK;
 
   struct Batch {
     uint4 kr[U], vr[U];
     int pp[U];
     float cc[U][G];
   };
+  // every lane loads a row (rows past the run's end repeat an in-bounds row and get
+  // weight 0), so no register is written while a load into it may be in flight
   auto issue = [&](int unit, int base, int p1, Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
       bt.pp[u] = p < p1 ? p : -1;
-      if (p < p1) {
-        const int64_t rowi = (int64_t)unit * a.cap + p;
-        bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
-        bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
-        const float *cp = a.coef + rowi * G;
-        if constexpr (G % 4 == 0) {
+      const int pc = min(max(min(p, p1 - 1), 0), a.cap - 1);
+      const int64_t rowi = (int64_t)unit * a.cap + pc;
+      bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+      bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
+      const float *cp = a.coef + rowi * G;
+      if constexpr (G % 4 == 0) {
 #pragma unroll
-          for (int j4 = 0; j4 < G; j4 += 4) {
-            const float4 c4 = *(const float4 *)(cp + j4);
-            bt.cc[u][j4] = c4.x; bt.cc[u][j4 + 1] = c4.y; bt.cc[u][j4 + 2] = c4.z; bt.cc[u][j4 + 3] = c4.w;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < G; ++j) bt.cc[u][j] = cp[j];
+        for (int j4 = 0; j4 < G; j4 += 4) {
+          const float4 c4 = *(const float4 *)(cp + j4);
+          bt.cc[u][j4] = c4.x; bt.cc[u][j4 + 1] = c4.y; bt.cc[u][j4 + 2] = c4.z; bt.cc[u][j4 + 3] = c4.w;
         }
       } else {
-        bt.kr[u] = make_uint4(0, 0, 0, 0);
-        bt.vr[u] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < G; ++j) bt.cc[u][j] = 0.0f;
+        for (int j = 0; j < G; ++j) bt.cc[u][j] = cp[j];
       }
     }
   };
@@ -329,7 +318,7 @@ __global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
       }
     }
   };
-  auto epilogue = [&](int j) {
+  auto epilogue = [&](int slot) {
     if (sub == 0) {
 #pragma unroll
       for (int jj = 0; jj < G; ++jj) s_den[wv][grp][jj] = den[jj];
@@ -340,7 +329,7 @@ __global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
       for (int e = 0; e < EPL; ++e) s_acc[wv][grp][jj][d0 + e] = acc[jj][e];
     }
     __syncthreads();
-    float *out = a.part + (int64_t)j * G * PS;
+    float *out = a.part + (int64_t)slot * G * PS;
     for (int t = threadIdx.x; t < G * PS; t += AT_NT) {
       const int jj = t / PS, d = t % PS;
       float sm = 0.0f;
@@ -353,38 +342,64 @@ __global__ __launch_bounds__(AT_NT) void k_attend_piv(AttendArgs a) {
     __syncthreads();
   };
 
-  int j = blockIdx.x;
-  if (j >= total) return;
-  int unit, p0, p1;
-  range(j, unit, p0, p1);
+  // this worker's schedule: KV head, first chunk in it, partial slot, chunks in all
+  const int nslots = a.nsplit + units;
+  const int4 sc = a.sched[blockIdx.x];
+  int left = sc.w;
+  if (left <= 0 || sc.x < 0 || sc.x >= units || sc.z < 0 || sc.z >= nslots) return;
+  int unit = sc.x, slot = sc.z;
+  int p1;
+  int base;
+  {
+    const int cnt = min(a.count[unit], a.cap);
+    const int take = min((cnt + R - 1) / R - sc.y, left);
+    base = sc.y * R;
+    p1 = min(cnt, base + take * R);
+    left -= max(take, 0);
+  }
   setup(unit);
-  int base = p0;
-  Batch A, B;
-  issue(unit, base, p1, A);
-  while (true) {
-    // the batch after A: the rest of this split, else the first batch of the next one
-    int nj = j, nunit = unit, nbase = base + SU, np1 = p1;
-    if (nbase >= p1) {
-      nj = j + gridDim.x;
-      if (nj < total) {
-        int q0;
-        range(nj, nunit, q0, np1);
-        nbase = q0;
+  // one step: plan the batch after `cur` (the rest of this run, else the first batch
+  // of the worker's next KV head with pivots), issue it into `nxt`, reduce `cur`, and
+  // close the run if `cur` was its last batch; false once the worker is done.  The two
+  // batches swap roles from step to step, so no register copy waits on loads in flight.
+  auto step = [&](Batch &cur, Batch &nxt) -> bool {
+    int nunit = unit, nbase = base + SU, np1 = p1, nslot = slot;
+    bool more = true;
+    const bool ends = nbase >= p1;
+    if (ends) {
+      more = false;
+      while (left > 0 && nunit + 1 < units) {
+        ++nunit;
+        const int c = min(a.count[nunit], a.cap);
+        if (c <= 0) continue;
+        const int take = min((c + R - 1) / R, left);
+        left -= take;
+        nbase = 0;
+        np1 = min(c, take * R);
+        nslot = a.runs[nunit].x;
+        more = nslot >= 0 && nslot < nslots;
+        break;
       }
     }
-    const bool more = nj < total;
-    if (more) issue(nunit, nbase, np1, B);
-    consume(A);
-    if (nj != j) {                                   // split j is complete
-      epilogue(j);
-      if (!more) break;
-      j = nj;
+    // issued on every path (past the worker's last row it is a batch of weight-0
+    // rows), so the waits for `cur` never have to cover `nxt`
+    issue(nunit, nbase, np1, nxt);
+    __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the reduction
+    consume(cur);
+    if (ends) {
+      epilogue(slot);
+      if (!more) return false;
       unit = nunit;
+      slot = nslot;
       p1 = np1;
       setup(unit);
     }
     base = nbase;
-    A = B;
+    return true;
+  };
+  Batch A, B;
+  issue(unit, base, p1, A);
+  while (step(A, B) && step(B, A)) {
   }
 }
 
@@ -392,9 +407,8 @@ template <bool BF16, int G>
 static hipError_t launch_attend_g(const AttendArgs &a, int units, bool host, bool exact,
                                   hipStream_t st) {
   if (!host) {
-    // persistent workgroups: three per CU, never more than there are splits
-    const int total = units * a.nsplit;
-    return launch_kernel(k_attend_piv<BF16, G>, dim3(std::min(total, 3 * 256)), dim3(AT_NT), 0, st, a);
+    // persistent workers, as many as the schedule was made for (nsplit)
+    return launch_kernel(k_attend_piv<BF16, G>, dim3(a.nsplit), dim3(AT_NT), 0, st, a);
   }
   if (exact) return launch_attend_t<BF16, G, true, true>(a, units, st);
   return launch_attend_t<BF16, G, true, false>(a, units, st);

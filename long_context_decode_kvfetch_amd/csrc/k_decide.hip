@@ -1146,7 +1146,61 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
 // tokens exact).
 constexpr int UN_NT = 1024;
 
+// The work schedule of the pivot attention, computed by one workgroup.  The pivots of
+// KV head u fall into nc_u = ceil(cnt_u / PIVOT_CHUNK) chunks; the chunks of all heads,
+// head after head, form one sequence of NC chunks, and worker w of P = min(workers, NC)
+// takes chunks [floor(w NC / P), floor((w + 1) NC / P)): every worker gets the same
+// number of rows to within a chunk, however ragged the heads are.  A worker sums its
+// chunks of one head into one partial (a run); the runs of head u take the partial
+// slots S_u .. S_u + runs_u - 1 in row order, S_u being the runs of the heads before u.
+__device__ void pivot_schedule(const UnionArgs &a) {
+  __shared__ int32_t s_scan[UN_NT / WAVE];
+  __shared__ int64_t s_sum[UN_NT / WAVE];
+  const int units = a.t.B * a.t.Hkv;
+  auto nc_of = [&](int u) -> int {
+    const int c = min(max(a.piv_count[u], 0), a.cap);
+    return (c + PIVOT_CHUNK - 1) / PIVOT_CHUNK;
+  };
+  int64_t mine = 0;
+  for (int u = threadIdx.x; u < units; u += UN_NT) mine += nc_of(u);
+  const int64_t NC = block_sum_i64<UN_NT>(mine, s_sum);
+  const int64_t P = min((int64_t)a.piv_workers, NC);
+  for (int w = (int)P + threadIdx.x; w < a.piv_workers; w += UN_NT) a.piv_sched[w] = make_int4(0, 0, 0, 0);
+  if (threadIdx.x == 0) a.piv_sched[a.piv_workers] = make_int4((int)NC, (int)P, 0, 0);
+  int64_t carry = 0, slot_carry = 0;
+  for (int t0 = 0; t0 < units; t0 += UN_NT) {
+    const int u = t0 + threadIdx.x;
+    const int ncu = u < units ? nc_of(u) : 0;
+    int32_t tile = 0;
+    const int64_t Cu = carry + block_excl_scan<UN_NT>(ncu, s_scan, &tile);
+    carry += tile;
+    // workers whose first chunk lies in [Cu, Cu + nc_u); run 0 belongs to an earlier
+    // worker unless one of them starts exactly at Cu
+    int64_t wlo = 0, whi = 0;
+    int extra = 0, runs = 0;
+    if (ncu > 0) {
+      wlo = (Cu * P + NC - 1) / NC;
+      whi = ((Cu + ncu) * P + NC - 1) / NC;
+      extra = (wlo < whi && wlo * NC / P == Cu) ? 0 : 1;
+      runs = (int)(whi - wlo) + extra;
+    }
+    int32_t tile_runs = 0;
+    const int64_t Su = slot_carry + block_excl_scan<UN_NT>(runs, s_scan, &tile_runs);
+    slot_carry += tile_runs;
+    if (u >= units) continue;
+    for (int64_t w = wlo; w < whi; ++w) {
+      const int64_t c0 = w * NC / P, c1 = (w + 1) * NC / P;
+      a.piv_sched[w] = make_int4(u, (int)(c0 - Cu), (int)(Su + (w - wlo) + extra), (int)(c1 - c0));
+    }
+    a.piv_runs[u] = make_int2((int)Su, runs);
+  }
+}
+
 __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
+  if (blockIdx.x == a.t.B * a.t.Hkv) {          // the extra column: the schedule
+    if (blockIdx.y == 0) pivot_schedule(a);
+    return;
+  }
   const int unit = blockIdx.x;
   const int b = unit / a.t.Hkv;
   const int g = unit % a.t.Hkv;
@@ -1233,8 +1287,8 @@ __global__ __launch_bounds__(FI_NT) void k_finish(FinishArgs a) {
   const int unit = b * a.t.Hkv + g;
   const int tid = threadIdx.x;
   constexpr int PS = D + 1;
-  // group q sums the pivot splits [q nsp/4, (q+1) nsp/4) and likewise the host splits,
-  // 16 loads in flight; the groups are then added in order q = 0..3
+  // group q sums the pivot partials [S + q runs/4, S + (q+1) runs/4) and the host
+  // splits [q nsh/4, (q+1) nsh/4), 16 loads in flight; the groups are then added in order
   constexpr int FB = 16;
   auto add_parts = [&](const float *base, int s0, int s1, float acc) -> float {
     const int64_t stride = (int64_t)a.t.G * PS;
@@ -1251,8 +1305,9 @@ __global__ __launch_bounds__(FI_NT) void k_finish(FinishArgs a) {
   if (tid < FI_GRP * PS) {
     const int q = tid / PS, col = tid % PS;
     float part = 0.0f;
-    part = add_parts(a.piv_part + ((int64_t)unit * a.nsp * a.t.G + j) * PS + col,
-                     a.nsp * q / FI_GRP, a.nsp * (q + 1) / FI_GRP, part);
+    const int2 rn = a.piv_runs[unit];
+    part = add_parts(a.piv_part + ((int64_t)rn.x * a.t.G + j) * PS + col,
+                     rn.y * q / FI_GRP, rn.y * (q + 1) / FI_GRP, part);
     part = add_parts(a.host_part + ((int64_t)unit * a.nsh * a.t.G + j) * PS + col,
                      a.nsh * q / FI_GRP, a.nsh * (q + 1) / FI_GRP, part);
     s_acc[q][col] = part;
@@ -1320,7 +1375,8 @@ int decide_blocks_per_cu(int max_n, int team) {
 
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
   if (!a.coef_pass) return launch_kernel(k_lists, dim3(LS_NB, units), dim3(LS_NT), 0, st, a);
-  return launch_kernel(k_union, dim3(units, (a.cap + UN_NT - 1) / UN_NT), dim3(UN_NT), 0, st, a);
+  return launch_kernel(k_union, dim3(units + (a.piv_sched ? 1 : 0), (a.cap + UN_NT - 1) / UN_NT),
+                       dim3(UN_NT), 0, st, a);
 }
 
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {

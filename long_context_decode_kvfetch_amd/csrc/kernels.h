@@ -106,6 +106,10 @@ struct UnionArgs {
   const double *params;      // coefficient pass: params[0] = kappa of the step (device)
   const uint32_t *sbits;     // lists: [B][Hkv][W] prefetched tokens, or null
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
+  // coefficient pass: the work schedule of the pivot attention (one extra workgroup)
+  int4 *piv_sched;           // [PIVOT_WORKERS] per worker: KV head, first chunk, slot, chunks
+  int2 *piv_runs;            // [B][Hkv] first partial slot and number of partials
+  int32_t piv_workers;       // workers the pivot attention launches
 };
 
 // Host-row prefetch: the first stage_rows entries of the previous step's host-row list
@@ -132,8 +136,10 @@ struct AttendArgs {
   const int32_t *list;       // host source: [B][Hkv][n] token ids; pivots: null
   const float *coef;         // pivots: [B][Hkv][cap][G]; host: null (coefficient 1)
   int32_t cap;
-  float *part;               // [B][Hkv][nsplit][G][129]
-  int32_t nsplit;
+  float *part;               // host: [B][Hkv][nsplit][G][129]; pivots: [slots][G][129]
+  int32_t nsplit;            // host: splits per KV head
+  const int4 *sched;         // pivots: per-worker schedule from the coefficient pass
+  const int2 *runs;          // pivots: per KV head first slot, number of partials
   const double *wc;          // host source with exact sketch: weights w_hat = wc * cscale
   const double *cscale;
   const uint8_t *stage;      // host source: prefetched value rows [B*Hkv][stage_rows][128]
@@ -143,8 +149,8 @@ struct AttendArgs {
 
 struct FinishArgs {
   SeqTable t;
-  const float *piv_part;     // [B][Hkv][nsp][G][129]
-  int32_t nsp;
+  const float *piv_part;     // [slots][G][129] partials of the resident pivots
+  const int2 *piv_runs;      // [B][Hkv] first slot and number of pivot partials
   const float *host_part;    // [B][Hkv][nsh][G][129]
   int32_t nsh;
   const double *wc, *cscale, *r;
@@ -168,8 +174,8 @@ constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot
 constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
 constexpr int STAGE_SLOTS_MAX = 4095;    // slot + 1 fits the 12 bits above the token
 constexpr int STAGE_ROWS_TOTAL = 16384;  // prefetched rows per call, over all KV heads
-constexpr int PIVOT_TOKENS = 64;  // fewest pivot rows per attention workgroup
-constexpr int PIVOT_WGS = 2048;   // attention workgroups aimed at per launch (8 per CU)
+constexpr int PIVOT_CHUNK = 32;   // pivot rows per schedule chunk (whole row batches)
+constexpr int PIVOT_WORKERS = 768;  // persistent pivot-attention workgroups (3 per CU)
 
 // Timing of the next launch: when `start` is set, the launcher hands the pair to
 // hipExtLaunchKernel, which stamps them from the dispatch packet itself (kernel

@@ -80,13 +80,15 @@ Totals totals(const SeqTable &t) {
 int row_bytes(const verkv_shape *s) { return VERKV_HEAD_DIM * (s->kv_dtype == VERKV_BF16 ? 2 : 4); }
 
 int host_splits(int units) { return std::max(4, std::min(64, 512 / std::max(1, units))); }
-// Splits of a KV head's pivot list: about PIVOT_WGS workgroups per launch, none with
-// fewer than PIVOT_TOKENS rows (more splits cost partial writes and a longer finish).
-int pivot_splits(int cap, int units) {
-  const int by_len = std::max(1, (cap + PIVOT_TOKENS - 1) / PIVOT_TOKENS);
-  const int by_wgs = std::max(1, (PIVOT_WGS + std::max(1, units) - 1) / std::max(1, units));
-  return std::min(by_len, by_wgs);
+// Persistent workers of the pivot attention: PIVOT_WORKERS, or one per schedule chunk
+// when there are fewer chunks at most.  Each worker leaves at most one partial per KV
+// head it touches, and only its first run can start inside a head, so the partials of a
+// step number at most workers + KV heads.
+int pivot_workers(int cap, int units) {
+  const int64_t chunks = (int64_t)units * ((cap + PIVOT_CHUNK - 1) / PIVOT_CHUNK);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(PIVOT_WORKERS, chunks));
 }
+int pivot_slots(int cap, int units) { return pivot_workers(cap, units) + units; }
 
 // Workgroups per query row in the decision kernel, as sized in the workspace: enough
 // to give 256 CUs two workgroups each, at least TEAM_MIN_TOKENS tokens per workgroup,
@@ -101,10 +103,10 @@ int team_size(int rows, int max_n) {
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
-  size_t stage, stage_tok, sbits, h2dc;
+  size_t stage, stage_tok, sbits, h2dc, psched, pruns;
   int srows;
   size_t total;
-  int nsp, nsh, team;
+  int nsp, nsh, team;      // nsp: pivot partial slots
 };
 DecodeWs decode_layout(const SeqTable &t, int cap) {
   const Totals T = totals(t);
@@ -112,7 +114,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   const int units = t.B * t.Hkv;
   const int64_t rows = (int64_t)units * t.G;
   DecodeWs w;
-  w.nsp = pivot_splits(cap, units);
+  w.nsp = pivot_slots(cap, units);
   w.nsh = host_splits(units);
   w.team = team_size((int)rows, t.max_n);
   const int64_t tm = w.team > 1 ? w.team : 0;       // member histograms only for teams
@@ -135,7 +137,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.fbits = off;  off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2d = off;    off = align_up(off + 4 * (size_t)(t.Hkv * T.tok));
   w.coef = off;   off = align_up(off + 4 * (size_t)(t.B * Hq * (int64_t)cap));
-  w.ppart = off;  off = align_up(off + 4 * (size_t)units * w.nsp * t.G * (D + 1));
+  w.ppart = off;  off = align_up(off + 4 * (size_t)w.nsp * t.G * (D + 1));
   w.hpart = off;  off = align_up(off + 4 * (size_t)units * w.nsh * t.G * (D + 1));
   w.status = off; off = align_up(off + 64);
   w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
@@ -145,6 +147,8 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
   w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
+  w.psched = off;    off = align_up(off + 16 * (size_t)(PIVOT_WORKERS + 1));
+  w.pruns = off;     off = align_up(off + 8 * (size_t)units);
   w.total = off;
   return w;
 }
@@ -519,6 +523,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   un.coef_pass = 0;
   un.sbits = prefetch ? reinterpret_cast<const uint32_t *>(ws + L.sbits) : nullptr;
   un.h2d_count_ws = reinterpret_cast<int32_t *>(ws + L.h2dc);
+  un.piv_sched = nullptr;
+  un.piv_runs = nullptr;
+  un.piv_workers = 0;
   // the list is rewritten here: the prefetch must have read it
   if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
   lk.unlock();
@@ -571,6 +578,8 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   at.cap = st->cap;
   at.part = reinterpret_cast<float *>(ws + L.hpart);
   at.nsplit = L.nsh;
+  at.sched = nullptr;
+  at.runs = nullptr;
   at.wc = reinterpret_cast<const double *>(ws + L.wc);
   at.cscale = reinterpret_cast<const double *>(ws + L.cscale);
   at.stage = ws + L.stage;
@@ -606,6 +615,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   un.coef_pass = 1;
   un.sbits = nullptr;
   un.h2d_count_ws = nullptr;
+  un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
+  un.piv_runs = reinterpret_cast<int2 *>(ws + L.pruns);
+  un.piv_workers = pivot_workers(st->cap, units);
   {
     Timed tm(K_COEF, sd->s);
     HIP_TRY(launch_union(un, units, sd->s), "pivot coefficient launch");
@@ -623,7 +635,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   pv.coef = reinterpret_cast<const float *>(ws + L.coef);
   pv.cap = st->cap;
   pv.part = reinterpret_cast<float *>(ws + L.ppart);
-  pv.nsplit = L.nsp;
+  pv.nsplit = un.piv_workers;
+  pv.sched = un.piv_sched;
+  pv.runs = un.piv_runs;
   pv.wc = nullptr;
   pv.cscale = nullptr;
   pv.stage = nullptr;
@@ -656,7 +670,7 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   FinishArgs fi;
   fi.t = t;
   fi.piv_part = reinterpret_cast<const float *>(ws + L.ppart);
-  fi.nsp = L.nsp;
+  fi.piv_runs = un.piv_runs;
   fi.host_part = at.part;
   fi.nsh = L.nsh;
   fi.wc = reinterpret_cast<const double *>(ws + L.wc);
