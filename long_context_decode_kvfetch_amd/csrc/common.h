@@ -51,6 +51,8 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each half row
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within the row
+constexpr int DPP_ROR8 = 0x128;        // row_ror:8 -> lane i <-> i ^ 8 within a 16-lane row
+constexpr int DPP_ROW_BCAST0 = 0x150;  // row_newbcast:n (+ n): lane n of each row to the whole row
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

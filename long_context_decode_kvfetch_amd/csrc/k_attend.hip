@@ -221,7 +221,12 @@ static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st
 // heads) and streams their batches back to back, the next batch's loads issued before
 // the current batch is reduced, also across the end of a run, so the loads stay in
 // flight while a run's partial is reduced and written.  A run is the worker's rows of
-// one KV head; its partial goes to the slot the schedule gives it.
+// one KV head; its partial goes to the slot the schedule gives it.  The schedule names
+// the first run outright, so the first loads leave after one dependent read.
+//
+// With four query rows and 16 lanes per key row (bf16) the scores are reduce-scattered:
+// after five DPP adds lane s of a row holds the full q.k of query row 2 s[3] + s[2], each
+// lane takes exp for that one row and the four weights are broadcast back over the row.
 constexpr int PIV_U = 2;           // row groups per batch of a pivot worker
 
 template <bool BF16, int G>
@@ -235,6 +240,10 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   constexpr int SU = STEP * U;
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
   constexpr int PS = D + 1;
+  constexpr int R = PIVOT_CHUNK;
+  constexpr bool RS4 = (G == 4 && LPT == 16);    // reduce-scattered scores
+  constexpr int NC = RS4 ? 1 : G;                // coefficients held per lane and row
+  constexpr float LOG2E = 1.4426950408889634f;
 
   __shared__ float s_acc[AT_NW][TPW][G][D];
   __shared__ float s_den[AT_NW][TPW][G];
@@ -247,12 +256,13 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int grp = lane / LPT;
   const int d0 = sub * EPL;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
-  constexpr int R = PIVOT_CHUNK;
+  const int myrow = RS4 ? 2 * ((sub >> 3) & 1) + ((sub >> 2) & 1) : 0;   // query row of this lane
+  const int nslots = a.nsplit + units;
 
   struct Batch {
     uint4 kr[U], vr[U];
     int pp[U];
-    float cc[U][G];
+    float cc[U][NC];
   };
   // every lane loads a row (rows past the run's end repeat an in-bounds row and get
   // weight 0), so no register is written while a load into it may be in flight
@@ -266,7 +276,9 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
       bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
       const float *cp = a.coef + rowi * G;
-      if constexpr (G % 4 == 0) {
+      if constexpr (RS4) {
+        bt.cc[u][0] = cp[myrow];
+      } else if constexpr (G % 4 == 0) {
 #pragma unroll
         for (int j4 = 0; j4 < G; j4 += 4) {
           const float4 c4 = *(const float4 *)(cp + j4);
@@ -279,7 +291,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     }
   };
 
-  float qf[G][EPL], mh[G];
+  // query slices pre-scaled by log2(e) / sqrt(d), so a weight is exp2(q.k - m_hat log2 e)
+  float qf[G][EPL], mh[G], mh_mine = 0.0f;
   float acc[G][EPL], den[G];
   auto setup = [&](int unit) {
     const int b = unit / a.t.Hkv, g = unit % a.t.Hkv;
@@ -288,26 +301,52 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       const int64_t qrow = (int64_t)b * Hq + g * G + j;
       const float *qr = a.q + qrow * D + d0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * a.inv_sqrt_d;
-      mh[j] = (float)a.m_hat[qrow];
+      for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * (a.inv_sqrt_d * LOG2E);
+      mh[j] = (float)(a.m_hat[qrow] * (double)LOG2E);
       den[j] = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
     }
+    if constexpr (RS4) mh_mine = myrow == 0 ? mh[0] : myrow == 1 ? mh[1] : myrow == 2 ? mh[2] : mh[3];
   };
   auto consume = [&](const Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float x[EPL], v[EPL], w[G];
       RS::widen(bt.kr[u], x);
+      float dp[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float dot = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = fmaf(qf[j][e], x[e], dot);
-        dot = sum16(dot);
-        if (LPT == 32) dot += shfl_xor_f(dot, 16);
-        w[j] = bt.pp[u] >= 0 ? __expf(dot - mh[j]) * bt.cc[u][j] : 0.0f;
+        dp[j] = dot;
+      }
+      if constexpr (RS4) {
+        const bool b3 = (sub >> 3) & 1, b2 = (sub >> 2) & 1;
+        float k0 = b3 ? dp[2] : dp[0], k1 = b3 ? dp[3] : dp[1];
+        const float s0 = b3 ? dp[0] : dp[2], s1 = b3 ? dp[1] : dp[3];
+        k0 += dpp_f<DPP_ROR8>(s0);
+        k1 += dpp_f<DPP_ROR8>(s1);
+        float k = b2 ? k1 : k0;
+        const float o = b2 ? k0 : k1;
+        k += dpp_f<DPP_HALF_MIRROR>(o);
+        k += dpp_f<DPP_XOR1>(k);
+        k += dpp_f<DPP_XOR2>(k);
+        float wm = exp2f(k - mh_mine) * bt.cc[u][0];
+        wm = bt.pp[u] >= 0 ? wm : 0.0f;
+        // query row j is held by lane 4 j of the row
+        w[0] = dpp_f<DPP_ROW_BCAST0 + 0>(wm);
+        w[1] = dpp_f<DPP_ROW_BCAST0 + 4>(wm);
+        w[2] = dpp_f<DPP_ROW_BCAST0 + 8>(wm);
+        w[3] = dpp_f<DPP_ROW_BCAST0 + 12>(wm);
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float dot = sum16(dp[j]);
+          if (LPT == 32) dot += shfl_xor_f(dot, 16);
+          w[j] = bt.pp[u] >= 0 ? exp2f(dot - mh[j]) * bt.cc[u][j] : 0.0f;
+        }
       }
       RS::widen(bt.vr[u], v);
 #pragma unroll
@@ -342,43 +381,58 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     __syncthreads();
   };
 
-  // this worker's schedule: KV head, first chunk in it, partial slot, chunks in all
-  const int nslots = a.nsplit + units;
-  const int4 sc = a.sched[blockIdx.x];
-  int left = sc.w;
-  if (left <= 0 || sc.x < 0 || sc.x >= units || sc.z < 0 || sc.z >= nslots) return;
-  int unit = sc.x, slot = sc.z;
-  int p1;
-  int base;
-  {
-    const int cnt = min(a.count[unit], a.cap);
-    const int take = min((cnt + R - 1) / R - sc.y, left);
-    base = sc.y * R;
-    p1 = min(cnt, base + take * R);
-    left -= max(take, 0);
+  // this worker's first run {head, first row, end row, slot} and, queued, its second
+  // one {head, end row, slot, chunks left after it}
+  const int4 f0 = a.sched[2 * blockIdx.x];
+  const int4 f1 = a.sched[2 * blockIdx.x + 1];
+  int unit = f0.x, base = f0.y, p1 = f0.z, slot = f0.w, left = 0;
+  if (!(unit >= 0 && unit < units && base >= 0 && base < p1 && p1 <= a.cap && slot >= 0 && slot < nslots))
+    return;                                        // no rows for this worker
+  int q_unit = f1.x, q_p1 = f1.y, q_slot = f1.z, q_left = f1.w;
+  if (q_unit < 0) {
+    left = q_left;                                 // chunks after the first run, heads unknown
+  } else if (!(q_unit < units && q_p1 > 0 && q_p1 <= a.cap && q_slot >= 0 && q_slot < nslots)) {
+    q_unit = -1;
+    q_left = 0;
   }
+  Batch A, B;
+  issue(unit, base, p1, A);
   setup(unit);
   // one step: plan the batch after `cur` (the rest of this run, else the first batch
-  // of the worker's next KV head with pivots), issue it into `nxt`, reduce `cur`, and
-  // close the run if `cur` was its last batch; false once the worker is done.  The two
-  // batches swap roles from step to step, so no register copy waits on loads in flight.
+  // of the worker's next run), issue it into `nxt`, reduce `cur`, and close the run if
+  // `cur` was its last batch; false once the worker is done.  The two batches swap
+  // roles from step to step, so no register copy waits on loads in flight.
   auto step = [&](Batch &cur, Batch &nxt) -> bool {
     int nunit = unit, nbase = base + SU, np1 = p1, nslot = slot;
     bool more = true;
     const bool ends = nbase >= p1;
     if (ends) {
       more = false;
-      while (left > 0 && nunit + 1 < units) {
-        ++nunit;
-        const int c = min(a.count[nunit], a.cap);
-        if (c <= 0) continue;
-        const int take = min((c + R - 1) / R, left);
-        left -= take;
+      if (q_unit >= 0) {                           // the queued second run
+        nunit = q_unit;
         nbase = 0;
-        np1 = min(c, take * R);
-        nslot = a.runs[nunit].x;
-        more = nslot >= 0 && nslot < nslots;
-        break;
+        np1 = q_p1;
+        nslot = q_slot;
+        left = q_left;
+        q_unit = -1;
+        more = true;
+      } else if (left > 0) {
+        // a third run or later, or a head without pivots in between: read the heads
+        for (int u2 = unit + 1; u2 < units; ++u2) {
+          const int c = min(a.count[u2], a.cap);
+          if (c <= 0) continue;
+          const int sl = a.runs[u2].x;
+          if (sl >= 0 && sl < nslots) {
+            const int take = min((c + R - 1) / R, left);
+            left -= take;
+            nunit = u2;
+            nbase = 0;
+            np1 = min(c, take * R);
+            nslot = sl;
+            more = true;
+          }
+          break;
+        }
       }
     }
     // issued on every path (past the worker's last row it is a batch of weight-0
@@ -397,8 +451,6 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     base = nbase;
     return true;
   };
-  Batch A, B;
-  issue(unit, base, p1, A);
   while (step(A, B) && step(B, A)) {
   }
 }

@@ -1153,6 +1153,10 @@ constexpr int UN_NT = 1024;
 // number of rows to within a chunk, however ragged the heads are.  A worker sums its
 // chunks of one head into one partial (a run); the runs of head u take the partial
 // slots S_u .. S_u + runs_u - 1 in row order, S_u being the runs of the heads before u.
+// Worker w's entry is a pair: {head, first row, end row, slot} of its first run, then
+// {head, end row, slot, chunks left after it} of the second run when that is the next
+// head's (head -1 otherwise, with the chunks left after the first run); {NC, P}
+// follows the last pair.
 __device__ void pivot_schedule(const UnionArgs &a) {
   __shared__ int32_t s_scan[UN_NT / WAVE];
   __shared__ int64_t s_sum[UN_NT / WAVE];
@@ -1165,8 +1169,11 @@ __device__ void pivot_schedule(const UnionArgs &a) {
   for (int u = threadIdx.x; u < units; u += UN_NT) mine += nc_of(u);
   const int64_t NC = block_sum_i64<UN_NT>(mine, s_sum);
   const int64_t P = min((int64_t)a.piv_workers, NC);
-  for (int w = (int)P + threadIdx.x; w < a.piv_workers; w += UN_NT) a.piv_sched[w] = make_int4(0, 0, 0, 0);
-  if (threadIdx.x == 0) a.piv_sched[a.piv_workers] = make_int4((int)NC, (int)P, 0, 0);
+  for (int w = (int)P + threadIdx.x; w < a.piv_workers; w += UN_NT) {
+    a.piv_sched[2 * w] = make_int4(0, 0, 0, 0);
+    a.piv_sched[2 * w + 1] = make_int4(0, 0, 0, 0);
+  }
+  if (threadIdx.x == 0) a.piv_sched[2 * a.piv_workers] = make_int4((int)NC, (int)P, 0, 0);
   int64_t carry = 0, slot_carry = 0;
   for (int t0 = 0; t0 < units; t0 += UN_NT) {
     const int u = t0 + threadIdx.x;
@@ -1188,9 +1195,22 @@ __device__ void pivot_schedule(const UnionArgs &a) {
     const int64_t Su = slot_carry + block_excl_scan<UN_NT>(runs, s_scan, &tile_runs);
     slot_carry += tile_runs;
     if (u >= units) continue;
+    const int cnt = min(max(a.piv_count[u], 0), a.cap);
     for (int64_t w = wlo; w < whi; ++w) {
       const int64_t c0 = w * NC / P, c1 = (w + 1) * NC / P;
-      a.piv_sched[w] = make_int4(u, (int)(c0 - Cu), (int)(Su + (w - wlo) + extra), (int)(c1 - c0));
+      const int k0 = (int)(c0 - Cu);
+      const int take = (int)min((int64_t)(ncu - k0), c1 - c0);
+      const int p0 = k0 * PIVOT_CHUNK;
+      const int left = (int)(c1 - c0) - take;
+      a.piv_sched[2 * w] = make_int4(u, p0, min(cnt, p0 + take * PIVOT_CHUNK), (int)(Su + (w - wlo) + extra));
+      // the second run, when it is the next head's (which then starts at slot S_u + runs_u)
+      int4 second = make_int4(-1, 0, 0, left);
+      if (left > 0 && u + 1 < units) {
+        const int cn = min(max(a.piv_count[u + 1], 0), a.cap);
+        const int t2 = min((cn + PIVOT_CHUNK - 1) / PIVOT_CHUNK, left);
+        if (t2 > 0) second = make_int4(u + 1, min(cn, t2 * PIVOT_CHUNK), (int)Su + runs, left - t2);
+      }
+      a.piv_sched[2 * w + 1] = second;
     }
     a.piv_runs[u] = make_int2((int)Su, runs);
   }

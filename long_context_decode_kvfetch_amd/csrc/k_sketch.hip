@@ -22,7 +22,6 @@
 namespace verkv {
 
 constexpr int SK_WAVES = 4;               // waves per workgroup, one chunk each
-constexpr int DPP_ROR8 = 0x128;          // row_ror:8 -> lane i <-> i ^ 8 within a 16-lane row
 
 // Map a flat chunk index to (sequence, KV head, chunk).
 __device__ __forceinline__ void sketch_chunk(const SeqTable &t, int blk, int &b, int &g, int &c) {

@@ -107,7 +107,7 @@ struct UnionArgs {
   const uint32_t *sbits;     // lists: [B][Hkv][W] prefetched tokens, or null
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
   // coefficient pass: the work schedule of the pivot attention (one extra workgroup)
-  int4 *piv_sched;           // [PIVOT_WORKERS] per worker: KV head, first chunk, slot, chunks
+  int4 *piv_sched;           // [2 PIVOT_WORKERS + 1] per worker: first run, chunks after it
   int2 *piv_runs;            // [B][Hkv] first partial slot and number of partials
   int32_t piv_workers;       // workers the pivot attention launches
 };

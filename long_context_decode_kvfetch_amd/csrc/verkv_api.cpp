@@ -147,7 +147,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
   w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
-  w.psched = off;    off = align_up(off + 16 * (size_t)(PIVOT_WORKERS + 1));
+  w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
   w.pruns = off;     off = align_up(off + 8 * (size_t)units);
   w.total = off;
   return w;
