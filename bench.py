@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-pivot-batch", action="store_true",
                    help="skip the pivotal-stream measurement at the 16-sequence batch")
+    p.add_argument("--pivot-only", action="store_true",
+                   help="time only the resident-pivot attention at the 16-sequence batch "
+                        "and print its figures as one JSON line")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 256 MiB elementwise copy kernel (HBM counter calibration)")
     return p.parse_args()
@@ -135,6 +138,17 @@ def pivotal_stream(torch, steps=8):
             "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def calib_copy(torch):
+    """A kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE: an elementwise copy
+    that reads and writes 256 MiB once per launch, three launches."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(steps):
     """The oracle (as it stands) on the same workload: one layer, `steps` decode steps."""
     import numpy as np
@@ -172,6 +186,12 @@ def main():
     from long_context_decode_kvfetch_amd.runner import Session
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.pivot_only:
+        if args.calib_copy:
+            calib_copy(torch)
+        log("[bench] pivotal stream at the 16-sequence batch")
+        print(json.dumps({"pivotal_stream": pivotal_stream(torch)}))
+        return
     K, W, L = args.steps, args.warmup, args.layers
     total = K + W + args.profile_steps
     per_layer = (total + L - 1) // L
@@ -192,14 +212,7 @@ def main():
         return sess
 
     if args.calib_copy:
-        # a kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE: reads and
-        # writes 256 MiB once per launch
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(torch)
 
     for i in range(W):
         run(i)
