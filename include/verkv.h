@@ -30,7 +30,9 @@
  *  - cache rows        [B][Hkv][n_b][128]      kv_dtype elements
  *  - query rows        [B][Hq][128] float32    Hq = Hkv * G; row h uses KV head h / G
  *  - per-row outputs   [B][Hq]
- *  - pivot arrays      [B][Hkv][cap] and [B][Hkv][cap][128]
+ *  - pivot ids         [B][Hkv][cap]
+ *  - pivot K/V rows    [verkv_pivot_rows(s, cap)][128], in the order the pivot-attention
+ *                      kernel reads them (written by verkv_compress; opaque to callers)
  */
 #ifndef VERKV_H
 #define VERKV_H
@@ -80,8 +82,8 @@ typedef struct {
   uint32_t *resident;       /* [B][Hkv][ceil(n_b/32)] bit set for tokens of H u S      */
   int32_t *piv_idx;         /* [B][Hkv][cap] ascending token ids of H u S              */
   int32_t *piv_count;       /* [B][Hkv] |H u S|                                        */
-  void *piv_k;              /* [B][Hkv][cap][128] kv_dtype: keys of H u S              */
-  void *piv_v;              /* [B][Hkv][cap][128] kv_dtype: values of H u S            */
+  void *piv_k;              /* [verkv_pivot_rows(s, cap)][128] kv_dtype: keys of H u S  */
+  void *piv_v;              /* same for the values; row order set by verkv_compress    */
   int32_t cap;              /* pivot capacity per (sequence, KV head)                  */
   const void *sketch;       /* [B][Hkv][n_b][128] kv_dtype token-level key sketch.     */
                             /* Exact-sketch mode: the keys themselves, on the device.  */
@@ -139,6 +141,15 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
                             void *workspace, size_t workspace_bytes, int32_t *needed_cap,
                             verkv_stream_t stream);
 size_t verkv_compress_workspace_bytes(const verkv_shape *s);
+
+/* Rows of 128 kv_dtype elements that st->piv_k and st->piv_v must each hold for pivot
+ * capacity `cap` (0 for an invalid shape or cap < 1).  verkv_compress stores the pivot
+ * rows in the order in which the resident-pivot attention's persistent workers read
+ * them: the pivots of all KV heads, head after head, cut into 32-row chunks and shared
+ * evenly among the workers, worker w's i-th chunk at block i * P + w (P workers), so
+ * the workers read one moving window of memory together.  The count is
+ * (B * Hkv * ceil(cap / 32) + 768) * 32, a little more than B * Hkv * cap. */
+size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
 
 /* KVFetch steps 1-4 (picx.dev summary, "KVFETCH"; Definition 2; Lemma 1): per query
  * row, sketch weights over all n_b tokens, the self-consistent shrinkage bias,

@@ -258,6 +258,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
   const int myrow = RS4 ? 2 * ((sub >> 3) & 1) + ((sub >> 2) & 1) : 0;   // query row of this lane
   const int nslots = a.nsplit + units;
+  const int PW = a.sched[2 * a.nsplit].y;          // workers P the rows were stored for
 
   struct Batch {
     uint4 kr[U], vr[U];
@@ -265,17 +266,21 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     float cc[U][NC];
   };
   // every lane loads a row (rows past the run's end repeat an in-bounds row and get
-  // weight 0), so no register is written while a load into it may be in flight
-  auto issue = [&](int unit, int base, int p1, Batch &bt) {
+  // weight 0), so no register is written while a load into it may be in flight.  K and V
+  // rows are stored in schedule order: row p of a run that starts at row q0 and at the
+  // worker's i0-th chunk is in block (i0 + (p - q0) / PIVOT_CHUNK) P + w; the
+  // coefficients keep the [head][cap] order.
+  auto issue = [&](int unit, int base, int p1, int i0, int q0, Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
       bt.pp[u] = p < p1 ? p : -1;
       const int pc = min(max(min(p, p1 - 1), 0), a.cap - 1);
-      const int64_t rowi = (int64_t)unit * a.cap + pc;
-      bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
-      bt.vr[u] = *(const uint4 *)(a.vrows + rowi * ROW_BYTES + slice);
-      const float *cp = a.coef + rowi * G;
+      const int64_t ich = i0 + (pc - q0) / PIVOT_CHUNK;
+      const int64_t srow = (ich * PW + blockIdx.x) * PIVOT_CHUNK + (pc & (PIVOT_CHUNK - 1));
+      bt.kr[u] = *(const uint4 *)(a.krows + srow * ROW_BYTES + slice);
+      bt.vr[u] = *(const uint4 *)(a.vrows + srow * ROW_BYTES + slice);
+      const float *cp = a.coef + ((int64_t)unit * a.cap + pc) * G;
       if constexpr (RS4) {
         bt.cc[u][0] = cp[myrow];
       } else if constexpr (G % 4 == 0) {
@@ -386,8 +391,11 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int4 f0 = a.sched[2 * blockIdx.x];
   const int4 f1 = a.sched[2 * blockIdx.x + 1];
   int unit = f0.x, base = f0.y, p1 = f0.z, slot = f0.w, left = 0;
-  if (!(unit >= 0 && unit < units && base >= 0 && base < p1 && p1 <= a.cap && slot >= 0 && slot < nslots))
+  if (!(unit >= 0 && unit < units && base >= 0 && base < p1 && p1 <= a.cap && slot >= 0 && slot < nslots &&
+        PW > (int)blockIdx.x && PW <= a.nsplit))
     return;                                        // no rows for this worker
+  // the current run's first worker-local chunk and first row
+  int ci0 = 0, cq0 = base;
   int q_unit = f1.x, q_p1 = f1.y, q_slot = f1.z, q_left = f1.w;
   if (q_unit < 0) {
     left = q_left;                                 // chunks after the first run, heads unknown
@@ -396,16 +404,18 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     q_left = 0;
   }
   Batch A, B;
-  issue(unit, base, p1, A);
+  issue(unit, base, p1, ci0, cq0, A);
   setup(unit);
   // one step: plan the batch after `cur` (the rest of this run, else the first batch
   // of the worker's next run), issue it into `nxt`, reduce `cur`, and close the run if
   // `cur` was its last batch; false once the worker is done.  The two batches swap
   // roles from step to step, so no register copy waits on loads in flight.
   auto step = [&](Batch &cur, Batch &nxt) -> bool {
-    int nunit = unit, nbase = base + SU, np1 = p1, nslot = slot;
+    int nunit = unit, nbase = base + SU, np1 = p1, nslot = slot, ni0 = ci0, nq0 = cq0;
     bool more = true;
     const bool ends = nbase >= p1;
+    // where the worker's next run starts in its chunks
+    const int run_end_i0 = ci0 + (p1 - cq0 + PIVOT_CHUNK - 1) / PIVOT_CHUNK;
     if (ends) {
       more = false;
       if (q_unit >= 0) {                           // the queued second run
@@ -415,6 +425,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         nslot = q_slot;
         left = q_left;
         q_unit = -1;
+        ni0 = run_end_i0;
+        nq0 = 0;
         more = true;
       } else if (left > 0) {
         // a third run or later, or a head without pivots in between: read the heads
@@ -429,6 +441,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
             nbase = 0;
             np1 = min(c, take * R);
             nslot = sl;
+            ni0 = run_end_i0;
+            nq0 = 0;
             more = true;
           }
           break;
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     }
     // issued on every path (past the worker's last row it is a batch of weight-0
     // rows), so the waits for `cur` never have to cover `nxt`
-    issue(nunit, nbase, np1, nxt);
+    issue(nunit, nbase, np1, ni0, nq0, nxt);
     __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the reduction
     consume(cur);
     if (ends) {
@@ -446,6 +460,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
       unit = nunit;
       slot = nslot;
       p1 = np1;
+      ci0 = ni0;
+      cq0 = nq0;
       setup(unit);
     }
     base = nbase;

@@ -217,7 +217,8 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   }
 }
 
-// Copy the K/V rows of the pivots from the pinned host cache (zero-copy reads).
+// Copy the K/V rows of the pivots from the pinned host cache (zero-copy reads) to the
+// places the pivot-attention schedule reads them from (pivot_store_row).
 __global__ __launch_bounds__(256) void k_gather_pivots(GatherArgs a) {
   const int unit = blockIdx.y;
   const int b = unit / a.t.Hkv;
@@ -225,6 +226,10 @@ __global__ __launch_bounds__(256) void k_gather_pivots(GatherArgs a) {
   const int cnt = min(a.piv_count[unit], a.cap);
   const int p0 = blockIdx.x * GATHER_ROWS;
   if (p0 >= cnt) return;
+  const int4 hdr = a.sched[2 * a.workers];
+  const int64_t NC = hdr.x, P = hdr.y;
+  if (NC <= 0 || P <= 0) return;
+  const int64_t c_u = a.runs[unit].z;
   const int per_row = a.row_bytes / 16;                // 16-byte pieces per row
   const int64_t src_row0 = tok_base(a.t, b, g);
   const int nrow = min(GATHER_ROWS, cnt - p0);
@@ -232,8 +237,10 @@ __global__ __launch_bounds__(256) void k_gather_pivots(GatherArgs a) {
     const int p = p0 + e / per_row;
     const int piece = e % per_row;
     const int64_t tok = a.piv_idx[(int64_t)unit * a.cap + p];
+    const int64_t row = pivot_store_row(c_u, p, NC, P);
+    if (row < 0 || row >= a.rows) continue;            // never, for a schedule of these counts
     const int64_t so = (src_row0 + tok) * a.row_bytes + (int64_t)piece * 16;
-    const int64_t dof = ((int64_t)unit * a.cap + p) * a.row_bytes + (int64_t)piece * 16;
+    const int64_t dof = row * a.row_bytes + (int64_t)piece * 16;
     *(uint4 *)(a.piv_k + dof) = *(const uint4 *)(a.K_host + so);
     *(uint4 *)(a.piv_v + dof) = *(const uint4 *)(a.V_host + so);
   }

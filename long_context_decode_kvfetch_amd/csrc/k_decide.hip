@@ -1152,12 +1152,13 @@ constexpr int UN_NT = 1024;
 // takes chunks [floor(w NC / P), floor((w + 1) NC / P)): every worker gets the same
 // number of rows to within a chunk, however ragged the heads are.  A worker sums its
 // chunks of one head into one partial (a run); the runs of head u take the partial
-// slots S_u .. S_u + runs_u - 1 in row order, S_u being the runs of the heads before u.
+// slots S_u .. S_u + runs_u - 1 in row order, S_u being the runs of the heads before u;
+// runs[u] = {S_u, runs_u, C_u (the head's first chunk), 0}.
 // Worker w's entry is a pair: {head, first row, end row, slot} of its first run, then
 // {head, end row, slot, chunks left after it} of the second run when that is the next
 // head's (head -1 otherwise, with the chunks left after the first run); {NC, P}
 // follows the last pair.
-__device__ void pivot_schedule(const UnionArgs &a) {
+__device__ void pivot_schedule(const PlanArgs &a) {
   __shared__ int32_t s_scan[UN_NT / WAVE];
   __shared__ int64_t s_sum[UN_NT / WAVE];
   const int units = a.t.B * a.t.Hkv;
@@ -1168,12 +1169,12 @@ __device__ void pivot_schedule(const UnionArgs &a) {
   int64_t mine = 0;
   for (int u = threadIdx.x; u < units; u += UN_NT) mine += nc_of(u);
   const int64_t NC = block_sum_i64<UN_NT>(mine, s_sum);
-  const int64_t P = min((int64_t)a.piv_workers, NC);
-  for (int w = (int)P + threadIdx.x; w < a.piv_workers; w += UN_NT) {
-    a.piv_sched[2 * w] = make_int4(0, 0, 0, 0);
-    a.piv_sched[2 * w + 1] = make_int4(0, 0, 0, 0);
+  const int64_t P = min((int64_t)a.workers, NC);
+  for (int w = (int)P + threadIdx.x; w < a.workers; w += UN_NT) {
+    a.sched[2 * w] = make_int4(0, 0, 0, 0);
+    a.sched[2 * w + 1] = make_int4(0, 0, 0, 0);
   }
-  if (threadIdx.x == 0) a.piv_sched[2 * a.piv_workers] = make_int4((int)NC, (int)P, 0, 0);
+  if (threadIdx.x == 0) a.sched[2 * a.workers] = make_int4((int)NC, (int)P, 0, 0);
   int64_t carry = 0, slot_carry = 0;
   for (int t0 = 0; t0 < units; t0 += UN_NT) {
     const int u = t0 + threadIdx.x;
@@ -1202,7 +1203,7 @@ __device__ void pivot_schedule(const UnionArgs &a) {
       const int take = (int)min((int64_t)(ncu - k0), c1 - c0);
       const int p0 = k0 * PIVOT_CHUNK;
       const int left = (int)(c1 - c0) - take;
-      a.piv_sched[2 * w] = make_int4(u, p0, min(cnt, p0 + take * PIVOT_CHUNK), (int)(Su + (w - wlo) + extra));
+      a.sched[2 * w] = make_int4(u, p0, min(cnt, p0 + take * PIVOT_CHUNK), (int)(Su + (w - wlo) + extra));
       // the second run, when it is the next head's (which then starts at slot S_u + runs_u)
       int4 second = make_int4(-1, 0, 0, left);
       if (left > 0 && u + 1 < units) {
@@ -1210,15 +1211,26 @@ __device__ void pivot_schedule(const UnionArgs &a) {
         const int t2 = min((cn + PIVOT_CHUNK - 1) / PIVOT_CHUNK, left);
         if (t2 > 0) second = make_int4(u + 1, min(cn, t2 * PIVOT_CHUNK), (int)Su + runs, left - t2);
       }
-      a.piv_sched[2 * w + 1] = second;
+      a.sched[2 * w + 1] = second;
     }
-    a.piv_runs[u] = make_int2((int)Su, runs);
+    a.runs[u] = make_int4((int)Su, runs, (int)Cu, 0);
   }
 }
 
+__global__ __launch_bounds__(UN_NT) void k_piv_schedule(PlanArgs a) { pivot_schedule(a); }
+
 __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
   if (blockIdx.x == a.t.B * a.t.Hkv) {          // the extra column: the schedule
-    if (blockIdx.y == 0) pivot_schedule(a);
+    if (blockIdx.y == 0) {
+      PlanArgs pa;
+      pa.t = a.t;
+      pa.piv_count = a.piv_count;
+      pa.cap = a.cap;
+      pa.workers = a.piv_workers;
+      pa.sched = a.piv_sched;
+      pa.runs = a.piv_runs;
+      pivot_schedule(pa);
+    }
     return;
   }
   const int unit = blockIdx.x;
@@ -1325,7 +1337,7 @@ __global__ __launch_bounds__(FI_NT) void k_finish(FinishArgs a) {
   if (tid < FI_GRP * PS) {
     const int q = tid / PS, col = tid % PS;
     float part = 0.0f;
-    const int2 rn = a.piv_runs[unit];
+    const int4 rn = a.piv_runs[unit];
     part = add_parts(a.piv_part + ((int64_t)rn.x * a.t.G + j) * PS + col,
                      rn.y * q / FI_GRP, rn.y * (q + 1) / FI_GRP, part);
     part = add_parts(a.host_part + ((int64_t)unit * a.nsh * a.t.G + j) * PS + col,
@@ -1397,6 +1409,10 @@ hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st) {
   if (!a.coef_pass) return launch_kernel(k_lists, dim3(LS_NB, units), dim3(LS_NT), 0, st, a);
   return launch_kernel(k_union, dim3(units + (a.piv_sched ? 1 : 0), (a.cap + UN_NT - 1) / UN_NT),
                        dim3(UN_NT), 0, st, a);
+}
+
+hipError_t launch_pivot_schedule(const PlanArgs &a, hipStream_t st) {
+  return launch_kernel(k_piv_schedule, dim3(1), dim3(UN_NT), 0, st, a);
 }
 
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st) {

@@ -25,9 +25,23 @@ struct GatherArgs {
   SeqTable t;
   const uint8_t *K_host, *V_host;   // device-visible pointers to the pinned host cache
   const int32_t *piv_idx, *piv_count;
-  uint8_t *piv_k, *piv_v;
+  uint8_t *piv_k, *piv_v;           // [pivot rows][128], rows in the pivot schedule's order
   int32_t cap;
   int32_t row_bytes;
+  const int4 *sched;                // pivot schedule (header {NC, P} after the worker pairs)
+  const int4 *runs;                 // per KV head {first slot, runs, first chunk, 0}
+  int32_t workers;                  // worker pairs in `sched`
+  int64_t rows;                     // rows allocated in piv_k / piv_v
+};
+
+// The pivot-attention schedule (computed by one workgroup).
+struct PlanArgs {
+  SeqTable t;
+  const int32_t *piv_count;
+  int32_t cap;
+  int32_t workers;
+  int4 *sched;               // [2 workers + 1]
+  int4 *runs;                // [B][Hkv]
 };
 
 struct SketchArgs {
@@ -108,7 +122,7 @@ struct UnionArgs {
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
   // coefficient pass: the work schedule of the pivot attention (one extra workgroup)
   int4 *piv_sched;           // [2 PIVOT_WORKERS + 1] per worker: first run, chunks after it
-  int2 *piv_runs;            // [B][Hkv] first partial slot and number of partials
+  int4 *piv_runs;            // [B][Hkv] first partial slot, partials, first chunk, 0
   int32_t piv_workers;       // workers the pivot attention launches
 };
 
@@ -130,7 +144,7 @@ struct AttendArgs {
   const float *q;            // [B][Hq][128]
   const double *m_hat;       // [B][Hq]
   float inv_sqrt_d;
-  const uint8_t *krows;      // pivots [B][Hkv][cap][128] or host cache [B][Hkv][n][128]
+  const uint8_t *krows;      // pivots [rows][128] in schedule order, or host cache [B][Hkv][n][128]
   const uint8_t *vrows;
   const int32_t *count;      // [B][Hkv] rows in the list
   const int32_t *list;       // host source: [B][Hkv][n] token ids; pivots: null
@@ -139,7 +153,7 @@ struct AttendArgs {
   float *part;               // host: [B][Hkv][nsplit][G][129]; pivots: [slots][G][129]
   int32_t nsplit;            // host: splits per KV head
   const int4 *sched;         // pivots: per-worker schedule from the coefficient pass
-  const int2 *runs;          // pivots: per KV head first slot, number of partials
+  const int4 *runs;          // pivots: per KV head first slot, partials, first chunk
   const double *wc;          // host source with exact sketch: weights w_hat = wc * cscale
   const double *cscale;
   const uint8_t *stage;      // host source: prefetched value rows [B*Hkv][stage_rows][128]
@@ -150,7 +164,7 @@ struct AttendArgs {
 struct FinishArgs {
   SeqTable t;
   const float *piv_part;     // [slots][G][129] partials of the resident pivots
-  const int2 *piv_runs;      // [B][Hkv] first slot and number of pivot partials
+  const int4 *piv_runs;      // [B][Hkv] first slot and number of pivot partials (.x, .y)
   const float *host_part;    // [B][Hkv][nsh][G][129]
   int32_t nsh;
   const double *wc, *cscale, *r;
@@ -177,6 +191,17 @@ constexpr int STAGE_ROWS_TOTAL = 16384;  // prefetched rows per call, over all K
 constexpr int PIVOT_CHUNK = 32;   // pivot rows per schedule chunk (whole row batches)
 constexpr int PIVOT_WORKERS = 768;  // persistent pivot-attention workgroups (3 per CU)
 
+// Where pivot row p of KV head u is stored: the schedule gives worker w of P the global
+// chunks [floor(w NC / P), floor((w + 1) NC / P)); the i-th of them is stored as block
+// i P + w (PIVOT_CHUNK rows), so the workers, which advance through their chunks at the
+// same pace, read one moving window of memory together.  c_u is the head's first chunk.
+__host__ __device__ inline int64_t pivot_store_row(int64_t c_u, int p, int64_t NC, int64_t P) {
+  const int64_t c = c_u + p / PIVOT_CHUNK;
+  const int64_t w = ((c + 1) * P - 1) / NC;
+  const int64_t i = c - w * NC / P;
+  return (i * P + w) * PIVOT_CHUNK + p % PIVOT_CHUNK;
+}
+
 // Timing of the next launch: when `start` is set, the launcher hands the pair to
 // hipExtLaunchKernel, which stamps them from the dispatch packet itself (kernel
 // execution time, without the gap before the dispatch), and marks them used.
@@ -197,6 +222,7 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem,
 
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
+hipError_t launch_pivot_schedule(const PlanArgs &a, hipStream_t st);
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st);
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);

@@ -89,6 +89,12 @@ int pivot_workers(int cap, int units) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(PIVOT_WORKERS, chunks));
 }
 int pivot_slots(int cap, int units) { return pivot_workers(cap, units) + units; }
+// Rows of piv_k / piv_v: the schedule stores worker w's i-th chunk as block i P + w, and
+// the workers' chunk counts differ by at most one, so ceil(NC / P) P <= NC + P - 1 blocks.
+int64_t pivot_rows(int cap, int units) {
+  const int64_t nc_max = (int64_t)units * ((cap + PIVOT_CHUNK - 1) / PIVOT_CHUNK);
+  return (nc_max + PIVOT_WORKERS) * PIVOT_CHUNK;
+}
 
 // Workgroups per query row in the decision kernel, as sized in the workspace: enough
 // to give 256 CUs two workgroups each, at least TEAM_MIN_TOKENS tokens per workgroup,
@@ -148,13 +154,13 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
   w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
-  w.pruns = off;     off = align_up(off + 8 * (size_t)units);
+  w.pruns = off;     off = align_up(off + 16 * (size_t)units);
   w.total = off;
   return w;
 }
 
 struct CompressWs {
-  size_t ka, kb, status, total;
+  size_t ka, kb, status, psched, pruns, total;
 };
 CompressWs compress_layout(const SeqTable &t) {
   const Totals T = totals(t);
@@ -163,6 +169,8 @@ CompressWs compress_layout(const SeqTable &t) {
   w.ka = off;     off = align_up(off + 8 * (size_t)(t.Hkv * T.tok));
   w.kb = off;     off = align_up(off + 8 * (size_t)(t.Hkv * T.tok));
   w.status = off; off = align_up(off + 64);
+  w.psched = off; off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
+  w.pruns = off;  off = align_up(off + 16 * (size_t)(t.B * t.Hkv));
   w.total = off;
   return w;
 }
@@ -274,7 +282,7 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 104; }
+int32_t verkv_version(void) { return 105; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -295,6 +303,12 @@ size_t verkv_compress_workspace_bytes(const verkv_shape *s) {
   SeqTable t;
   if (make_table(s, t) != VERKV_OK) return 0;
   return compress_layout(t).total;
+}
+
+size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap) {
+  SeqTable t;
+  if (make_table(s, t) != VERKV_OK || cap < 1) return 0;
+  return (size_t)pivot_rows(cap, t.B * t.Hkv);
 }
 
 size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap) {
@@ -361,6 +375,16 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
     return VERKV_ECAPACITY;
   }
   if (needed_cap) *needed_cap = hstat[1];
+  // the pivot-attention schedule of these pivot counts: the gather stores the rows in
+  // the order the attention kernel's workers read them
+  PlanArgs pl;
+  pl.t = t;
+  pl.piv_count = st->piv_count;
+  pl.cap = st->cap;
+  pl.workers = pivot_workers(st->cap, units);
+  pl.sched = reinterpret_cast<int4 *>(ws + L.psched);
+  pl.runs = reinterpret_cast<int4 *>(ws + L.pruns);
+  HIP_TRY(launch_pivot_schedule(pl, stream), "pivot schedule launch");
   GatherArgs gth;
   gth.t = t;
   gth.K_host = static_cast<const uint8_t *>(Kd);
@@ -371,6 +395,10 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
   gth.piv_v = static_cast<uint8_t *>(st->piv_v);
   gth.cap = st->cap;
   gth.row_bytes = row_bytes(s);
+  gth.sched = pl.sched;
+  gth.runs = pl.runs;
+  gth.workers = pl.workers;
+  gth.rows = pivot_rows(st->cap, units);
   {
     Timed tm(K_GATHER, stream);
     HIP_TRY(launch_gather_pivots(gth, units, stream), "gather launch");
@@ -616,7 +644,7 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   un.sbits = nullptr;
   un.h2d_count_ws = nullptr;
   un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
-  un.piv_runs = reinterpret_cast<int2 *>(ws + L.pruns);
+  un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
   un.piv_workers = pivot_workers(st->cap, units);
   {
     Timed tm(K_COEF, sd->s);

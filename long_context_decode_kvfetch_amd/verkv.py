@@ -74,6 +74,8 @@ def _lib():
         lib.verkv_compress_workspace_bytes.argtypes = [C.POINTER(Shape)]
         lib.verkv_decode_workspace_bytes.restype = sz
         lib.verkv_decode_workspace_bytes.argtypes = [C.POINTER(Shape), i32]
+        lib.verkv_pivot_rows.restype = sz
+        lib.verkv_pivot_rows.argtypes = [C.POINTER(Shape), i32]
         lib.verkv_compress.restype = i32
         lib.verkv_compress.argtypes = [C.POINTER(Shape), vp, vp, vp, C.c_double, C.c_uint64,
                                        C.POINTER(State), vp, sz, C.POINTER(i32), vp]
@@ -154,6 +156,9 @@ class LayerShape:
     def decode_workspace_bytes(self, cap: int) -> int:
         return int(_lib().verkv_decode_workspace_bytes(C.byref(self.c), int(cap)))
 
+    def pivot_rows(self, cap: int) -> int:
+        return int(_lib().verkv_pivot_rows(C.byref(self.c), int(cap)))
+
 
 def default_cap(shape: LayerShape, eta: float) -> int:
     """A pivot capacity that holds H u S with overwhelming probability: the forced
@@ -179,8 +184,9 @@ class LayerState:
         self.resident = torch.empty(hkv * words, dtype=torch.int32, device=device)
         self.piv_idx = torch.empty(units * cap, dtype=torch.int32, device=device)
         self.piv_count = torch.empty(units, dtype=torch.int32, device=device)
-        self.piv_k = torch.empty(units * cap * HEAD_DIM, dtype=shape.torch_dtype, device=device)
-        self.piv_v = torch.empty(units * cap * HEAD_DIM, dtype=shape.torch_dtype, device=device)
+        prow = shape.pivot_rows(cap)            # pivot K/V rows, stored in schedule order
+        self.piv_k = torch.empty(prow * HEAD_DIM, dtype=shape.torch_dtype, device=device)
+        self.piv_v = torch.empty(prow * HEAD_DIM, dtype=shape.torch_dtype, device=device)
         self.sketch = sketch
         self.v_host = v_host                    # kept alive with the state
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
