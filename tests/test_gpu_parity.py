@@ -66,6 +66,15 @@ def test_ragged_tails_and_small_sequences():
     _run(wl, label="ragged")
 
 
+def test_many_small_heads_pivot_runs_span_heads():
+    """128 short sequences x 10 KV heads = 1280 heads of one or two 32-row pivot chunks
+    each: the resident-pivot workers (768) each take chunks of two or three heads, so the
+    kernel follows a head change inside a worker, including the third head it finds
+    itself, and the finishing kernel sums several partial slots per head."""
+    wl = synth.ragged_batch(seed=11, batch=128, n_min=400, n_max=700, n_local=16, hkv=10)
+    _run(wl, label="many small heads")
+
+
 def test_uniform_tau_no_heavy_hitters_certifies():
     """Uniform scores and no planted keys: eps_hat(L) is about 0.14 at eta = 1/16, so at
     eps = 0.2 every row certifies and nothing is fetched (the no-fetch path)."""
