@@ -85,8 +85,9 @@ typedef struct {
   void *piv_k;              /* [verkv_pivot_rows(s, cap)][128] kv_dtype: keys of H u S  */
   void *piv_v;              /* same for the values; row order set by verkv_compress    */
   int32_t cap;              /* pivot capacity per (sequence, KV head)                  */
-  const void *sketch;       /* [B][Hkv][n_b][128] kv_dtype token-level key sketch.     */
-                            /* Exact-sketch mode: the keys themselves, on the device.  */
+  const void *sketch;       /* [B][Hkv][n_b][128] kv_dtype token-level key sketch      */
+                            /* (or 2-bit rows, see sketch_format), on the device.      */
+                            /* Exact-sketch mode: the keys themselves.                 */
   int32_t sketch_exact;     /* 1: the sketch rows are the keys, so the host fetch of    */
                             /* KVFetch step 5 reads only the value rows and takes the  */
                             /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
@@ -97,7 +98,30 @@ typedef struct {
                             /* host into the workspace while the sketch and decision   */
                             /* kernels run; verkv_refine then takes the rows it needs  */
                             /* from there.  Results do not depend on it.               */
+  int32_t sketch_format;    /* VERKV_SKETCH_ROWS (0): `sketch` holds kv_dtype rows as   */
+                            /* above; VERKV_SKETCH_2BIT (1): `sketch` holds 64-byte     */
+                            /* rows written by verkv_quantize_sketch (needs            */
+                            /* sketch_exact = 0: fetched rows are scored from the host */
+                            /* keys).                                                   */
 } verkv_state;
+
+#define VERKV_SKETCH_ROWS 0
+#define VERKV_SKETCH_2BIT 1
+#define VERKV_SKETCH2_ROW_BYTES 64
+
+/* The 2-bit key sketch (the pages evaluate one but give no quantiser; this one is
+ * asymmetric uniform quantisation per token row in groups of 32 dimensions): for each
+ * group, mn = min, sc = (max - min) / 3 in float32, code_j = the number of midpoints
+ * mn + (c + 1/2) sc, c = 0, 1, 2, that x_j reaches (float64), and the sketch key is
+ * x_hat_j = mn + code_j sc (float64).  Row layout, 64 bytes per (sequence, KV head,
+ * token): bytes 0-31 eight 32-bit words, word w holding the codes of dimensions
+ * 8w..8w+7 in bits 0-15 and of 8(w+8)..8(w+8)+7 in bits 16-31, two bits per dimension
+ * in order; bytes 32-63 eight float32: mn, sc of groups 0, 2, 1, 3.
+ *   K       [B][Hkv][n_b][128] kv_dtype key cache, device memory or pinned host memory
+ *   sketch  [B][Hkv][n_b][64] bytes (device), written
+ * Asynchronous on `stream`. */
+verkv_status verkv_quantize_sketch(const verkv_shape *s, const void *K, void *sketch,
+                                   verkv_stream_t stream);
 
 /* Per-step results.  Row arrays are [B][Hq]; KV-head arrays are [B][Hkv]. */
 typedef struct {
@@ -195,10 +219,11 @@ size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
  * waits for the recorded launches, writes per kernel kind the summed duration in ms
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
- * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 host-row prefetch), and
+ * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 host-row prefetch, 11 2-bit
+ * sketch quantiser), and
  * clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 11
+#define VERKV_PROFILE_KINDS 12
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);

@@ -17,6 +17,11 @@
 // once m_hat = max_c m_c is known.  The workgroup also clears the chunk's words of the
 // step's fetch bitmask and, on chunk 0, the decision kernel's per-row counters and
 // exchange sequence words.
+//
+// With a 2-bit sketch (Q2) a row is 64 bytes of codes and group parameters (the layout
+// k_quant_sketch writes); a lane reads the code word and the (mn, sc) pairs of its two
+// 8-dimension pieces and forms x_hat = mn + code * sc in float64 before the same dot
+// products, so the sketch keys are bit-identical to the quantiser's definition.
 #include "kernels.h"
 
 namespace verkv {
@@ -80,15 +85,15 @@ __device__ __forceinline__ double reduce_scatter4x8(const double *v, int s) {
 // arithmetic.  Scores wait in the wave's own LDS region for the chunk maximum; then
 // each lane takes CH / 64 tokens of every row for exp, the sums and the stores.  Waves
 // never wait for each other.
-template <bool BF16, int G>
+template <bool BF16, int G, bool Q2 = false>
 __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
-  using RS = RowSlice<BF16>;
+  using RS = RowSlice<BF16 || Q2>;          // Q2: pieces of 8 dimensions, as bf16 rows
   constexpr int CH = SKETCH_CHUNK;
   constexpr int EPP = RS::EPL;              // elements per 16-byte piece
   constexpr int LPT = G <= 4 ? 8 : 16;      // lanes per token row
   constexpr int TPS = WAVE / LPT;           // tokens per load step
-  constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
-  constexpr int PPL = ROW_BYTES / 16 / LPT; // 16-byte pieces per lane per token
+  constexpr int ROW_BYTES = Q2 ? SKETCH2_ROW_BYTES : D * (BF16 ? 2 : 4);
+  constexpr int PPL = D * ((BF16 || Q2) ? 2 : 4) / 16 / LPT;   // pieces per lane per token
   constexpr int EPT = PPL * EPP;            // elements per lane per token
   constexpr int STEPS = CH / TPS;
   constexpr int SB = 8 / PPL;               // load steps per batch
@@ -141,14 +146,31 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   }
 
   // rows past n (the last chunk) re-read row n-1; their scores are replaced by -inf
-  const uint8_t *rows = a.sketch + tok_base(a.t, b, g) * ROW_BYTES + sidx * 16;
+  const uint8_t *rows = a.sketch + tok_base(a.t, b, g) * ROW_BYTES + (Q2 ? 0 : sidx * 16);
   auto load_batch = [&](int bi, uint4 *raw) {
 #pragma unroll
     for (int k = 0; k < SB; ++k) {
       const int tok = min(base + (bi * SB + k) * TPS + tsub, n - 1);
       const uint8_t *rp = rows + (int64_t)tok * ROW_BYTES;
+      if constexpr (Q2) {
+        // .x: the code word of pieces (sidx & 7) and (sidx & 7) + 8; .y-.w: parameters.
+        // LPT 8: pieces sidx, sidx + 8 -> (mn, sc) of groups sidx/4 and sidx/4 + 2, one
+        // 16-byte read; LPT 16: piece sidx -> (mn, sc) of group sidx/4
+        uint4 r;
+        r.x = *(const uint32_t *)(rp + 4 * (sidx & 7));
+        if constexpr (LPT == 8) {
+          const uint4 pm = *(const uint4 *)(rp + 32 + 16 * ((sidx >> 2) & 1));
+          raw[2 * k] = make_uint4(r.x, pm.x, pm.y, 0u);
+          raw[2 * k + 1] = make_uint4(r.x >> 16, pm.z, pm.w, 0u);
+        } else {
+          const int gq = sidx >> 2;
+          const uint2 pm = *(const uint2 *)(rp + 32 + 4 * ((gq & 1) * 4 + (gq >> 1) * 2));
+          raw[k] = make_uint4(r.x >> (16 * (sidx >> 3)), pm.x, pm.y, 0u);
+        }
+      } else {
 #pragma unroll
-      for (int p = 0; p < PPL; ++p) raw[k * PPL + p] = *(const uint4 *)(rp + p * LPT * 16);
+        for (int p = 0; p < PPL; ++p) raw[k * PPL + p] = *(const uint4 *)(rp + p * LPT * 16);
+      }
     }
   };
   uint4 cur[SB * PPL], nxt[SB * PPL];
@@ -163,13 +185,25 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
       for (int j = 0; j < NG4 * 4; ++j) acc[j] = 0.0;
 #pragma unroll
       for (int p = 0; p < PPL; ++p) {
-        float x[EPP];
-        RS::widen(cur[k * PPL + p], x);
+        if constexpr (Q2) {
+          // piece codes in bits 0-15 of .x, (mn, sc) in .y, .z
+          const uint4 r = cur[k * PPL + p];
+          const double mn = (double)__uint_as_float(r.y), scl = (double)__uint_as_float(r.z);
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) {
-          const double xe = (double)x[e];
+          for (int e = 0; e < EPP; ++e) {
+            const double xe = fma((double)((r.x >> (2 * e)) & 3u), scl, mn);
 #pragma unroll
-          for (int j = 0; j < G; ++j) acc[j] = fma(qd[j][p * EPP + e], xe, acc[j]);
+            for (int j = 0; j < G; ++j) acc[j] = fma(qd[j][p * EPP + e], xe, acc[j]);
+          }
+        } else {
+          float x[EPP];
+          RS::widen(cur[k * PPL + p], x);
+#pragma unroll
+          for (int e = 0; e < EPP; ++e) {
+            const double xe = (double)x[e];
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j] = fma(qd[j][p * EPP + e], xe, acc[j]);
+          }
         }
       }
       const int tk = (bi * SB + k) * TPS + tsub;        // token within the chunk
@@ -260,6 +294,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
 template <bool BF16, int G>
 static hipError_t launch_sketch_t(const SketchArgs &a, hipStream_t st) {
   const int blocks = (a.total_blocks + SK_WAVES - 1) / SK_WAVES;
+  if (a.q2) return launch_kernel(k_sketch<false, G, true>, dim3(blocks), dim3(SK_WAVES * WAVE), 0, st, a);
   return launch_kernel(k_sketch<BF16, G>, dim3(blocks), dim3(SK_WAVES * WAVE), 0, st, a);
 }
 

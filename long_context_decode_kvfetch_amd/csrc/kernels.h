@@ -44,6 +44,13 @@ struct PlanArgs {
   int4 *runs;                // [B][Hkv]
 };
 
+// The 2-bit sketch rows of a key cache.
+struct QuantArgs {
+  const uint8_t *K;          // [rows][128] kv dtype (device-visible)
+  uint8_t *out;              // [rows][SKETCH2_ROW_BYTES]
+  int64_t rows;              // Hkv * total tokens
+};
+
 struct SketchArgs {
   SeqTable t;
   const uint8_t *sketch;      // [B][Hkv][n][128] kv dtype
@@ -59,6 +66,7 @@ struct SketchArgs {
   int32_t xseq_row;
   int32_t *kstar;             // [B][Hq] cleared here
   int32_t total_blocks;
+  int32_t q2;                 // 1: `sketch` holds 2-bit rows (SKETCH2_ROW_BYTES each)
 };
 
 struct DecideArgs {
@@ -188,6 +196,7 @@ constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot
 constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
 constexpr int STAGE_SLOTS_MAX = 4095;    // slot + 1 fits the 12 bits above the token
 constexpr int STAGE_ROWS_TOTAL = 16384;  // prefetched rows per call, over all KV heads
+constexpr int SKETCH2_ROW_BYTES = 64;   // a 2-bit sketch row: 32 B of codes, 8 float32
 constexpr int PIVOT_CHUNK = 32;   // pivot rows per schedule chunk (whole row batches)
 constexpr int PIVOT_WORKERS = 768;  // persistent pivot-attention workgroups (3 per CU)
 
@@ -224,6 +233,7 @@ hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
 hipError_t launch_pivot_schedule(const PlanArgs &a, hipStream_t st);
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_quant_sketch(const QuantArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st);
 hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, bool exact,

@@ -248,7 +248,7 @@ verkv_status side_for_device(Side **out) {
 
 // ---------------------------------------------------------------- optional kernel timing
 enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER,
-                K_COEF, K_PREFETCH, K_COUNT };
+                K_COEF, K_PREFETCH, K_QUANT, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -282,7 +282,7 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 105; }
+int32_t verkv_version(void) { return 106; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -303,6 +303,26 @@ size_t verkv_compress_workspace_bytes(const verkv_shape *s) {
   SeqTable t;
   if (make_table(s, t) != VERKV_OK) return 0;
   return compress_layout(t).total;
+}
+
+verkv_status verkv_quantize_sketch(const verkv_shape *s, const void *K, void *sketch,
+                                   verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!K || !sketch) return VERKV_EINVAL;
+  const void *Kd = nullptr;
+  if ((rc = device_view(K, &Kd)) != VERKV_OK) return rc;
+  QuantArgs qa;
+  qa.K = static_cast<const uint8_t *>(Kd);
+  qa.out = static_cast<uint8_t *>(sketch);
+  qa.rows = (int64_t)t.Hkv * totals(t).tok;
+  {
+    Timed tm(K_QUANT, stream);
+    HIP_TRY(launch_quant_sketch(qa, s->kv_dtype == VERKV_BF16, stream), "quantise launch");
+  }
+  return VERKV_OK;
 }
 
 size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap) {
@@ -414,6 +434,11 @@ static verkv_status check_step(const verkv_shape *s, const verkv_state *st, cons
   if (!st->r || !st->resident || !st->piv_idx || !st->piv_count || !st->piv_k || !st->piv_v ||
       !st->sketch || st->cap < 1)
     return VERKV_EINVAL;
+  if (st->sketch_format != VERKV_SKETCH_ROWS && st->sketch_format != VERKV_SKETCH_2BIT) return VERKV_EINVAL;
+  if (st->sketch_format == VERKV_SKETCH_2BIT && st->sketch_exact) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "a 2-bit sketch is not exact (sketch_exact must be 0)");
+    return VERKV_EINVAL;
+  }
   return VERKV_OK;
 }
 
@@ -440,6 +465,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   SketchArgs sk;
   sk.t = t;
   sk.sketch = static_cast<const uint8_t *>(st->sketch);
+  sk.q2 = st->sketch_format == VERKV_SKETCH_2BIT ? 1 : 0;
   sk.q = q;
   sk.inv_sqrt_d = 1.0 / std::sqrt((double)VERKV_HEAD_DIM);
   sk.wc = reinterpret_cast<double *>(ws + L.wc);

@@ -23,7 +23,7 @@ class Session:
 
     def __init__(self, wl: Workload, cap: int | None = None, device: str = "cuda",
                  host_pinned: bool = True, seed: int | None = None, sketch_exact: bool = True,
-                 prefetch: bool = True):
+                 prefetch: bool = True, sketch_2bit: bool = False):
         self.wl = wl
         self.device = device
         lens = [s.n for s in wl.seqs]
@@ -40,11 +40,20 @@ class Session:
         else:                                   # whole cache on the device (tests only)
             self.K_host = K.to(device)
             self.V_host = V.to(device)
-        self.sketch = K.to(device)              # exact sketch: the keys, device resident
+        if sketch_2bit:
+            # the 2-bit sketch of the keys (64 B per token row), quantised on the device
+            # from the host cache; fetched rows are then scored from the host keys
+            nbytes = self.shape.total_tokens * self.shape.n_kv_heads * verkv.SKETCH2_ROW_BYTES
+            self.sketch = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            verkv.quantize_sketch(self.shape, self.K_host, self.sketch)
+            sketch_exact = False
+        else:
+            self.sketch = K.to(device)          # exact sketch: the keys, device resident
         self.tau = torch.from_numpy(_cat([s.tau for s in wl.seqs]).astype(np.float32)).to(device)
         self.cap = int(cap) if cap else verkv.default_cap(self.shape, wl.eta)
         self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device, sketch_exact,
-                                      v_host=self.V_host if (host_pinned and prefetch) else None)
+                                      v_host=self.V_host if (host_pinned and prefetch) else None,
+                                      sketch_format=verkv.SKETCH_2BIT if sketch_2bit else verkv.SKETCH_ROWS)
         self.cws = verkv.workspace(self.shape.compress_workspace_bytes(), device)
         self.dws = verkv.workspace(self.shape.decode_workspace_bytes(self.cap), device)
         self.out = verkv.StepBuffers(self.shape, device=device)

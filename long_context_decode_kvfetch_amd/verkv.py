@@ -20,9 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 11
+PROFILE_KINDS = 12
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
-                "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef", "prefetch"]
+                "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef", "prefetch",
+                "quantize_sketch"]
 
 
 class VerKVError(RuntimeError):
@@ -45,7 +46,10 @@ class State(C.Structure):
     _fields_ = [("r", C.c_void_p), ("resident", C.c_void_p), ("piv_idx", C.c_void_p),
                 ("piv_count", C.c_void_p), ("piv_k", C.c_void_p), ("piv_v", C.c_void_p),
                 ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32),
-                ("v_host", C.c_void_p)]
+                ("v_host", C.c_void_p), ("sketch_format", C.c_int32)]
+
+
+SKETCH_ROWS, SKETCH_2BIT, SKETCH2_ROW_BYTES = 0, 1, 64
 
 
 class StepOut(C.Structure):
@@ -76,6 +80,8 @@ def _lib():
         lib.verkv_decode_workspace_bytes.argtypes = [C.POINTER(Shape), i32]
         lib.verkv_pivot_rows.restype = sz
         lib.verkv_pivot_rows.argtypes = [C.POINTER(Shape), i32]
+        lib.verkv_quantize_sketch.restype = i32
+        lib.verkv_quantize_sketch.argtypes = [C.POINTER(Shape), vp, vp, vp]
         lib.verkv_compress.restype = i32
         lib.verkv_compress.argtypes = [C.POINTER(Shape), vp, vp, vp, C.c_double, C.c_uint64,
                                        C.POINTER(State), vp, sz, C.POINTER(i32), vp]
@@ -174,7 +180,8 @@ class LayerState:
     """GPU-resident compressed state of one layer (caller-owned torch buffers)."""
 
     def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda",
-                 sketch_exact: bool = True, v_host: torch.Tensor | None = None):
+                 sketch_exact: bool = True, v_host: torch.Tensor | None = None,
+                 sketch_format: int = SKETCH_ROWS):
         hkv, tot = shape.n_kv_heads, shape.total_tokens
         words = sum((n + 31) // 32 for n in shape.seq_lens)
         units = shape.batch * hkv
@@ -191,7 +198,8 @@ class LayerState:
         self.v_host = v_host                    # kept alive with the state
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
                        _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch),
-                       1 if sketch_exact else 0, _ptr(v_host) if v_host is not None else None)
+                       1 if sketch_exact else 0, _ptr(v_host) if v_host is not None else None,
+                       int(sketch_format))
 
 
 class StepBuffers:
@@ -244,6 +252,15 @@ def compress(shape: LayerShape, tau: torch.Tensor, K_host: torch.Tensor, V_host:
         raise VerKVError(st, "verkv_compress", f"needed cap {need.value} > {state.cap}")
     _check(st, "verkv_compress")
     return need.value
+
+
+def quantize_sketch(shape: LayerShape, K: torch.Tensor, sketch: torch.Tensor, stream=None) -> None:
+    """verkv_quantize_sketch: the 2-bit sketch rows of K (asynchronous on `stream`)."""
+    need = shape.total_tokens * shape.n_kv_heads * SKETCH2_ROW_BYTES
+    if sketch.numel() * sketch.element_size() < need:
+        raise ValueError(f"sketch buffer holds {sketch.numel() * sketch.element_size()} B, needs {need}")
+    _check(_lib().verkv_quantize_sketch(C.byref(shape.c), _ptr(K), _ptr(sketch), _stream(stream)),
+           "verkv_quantize_sketch")
 
 
 def decode_step(shape: LayerShape, state: LayerState, q: torch.Tensor, beta: float, eps: float,

@@ -33,14 +33,17 @@ def oracle_compress(wl):
             for b, s in enumerate(wl.seqs)]
 
 
-def oracle_step(wl, comp, step, kappa=None, eps=None, delta=None):
+def oracle_step(wl, comp, step, kappa=None, eps=None, delta=None, sketch_of=None):
+    """The oracle's step for every sequence; `sketch_of` maps a KV head's key rows to the
+    sketch keys its weights come from (None: the keys themselves)."""
     kappa = wl.kappa if kappa is None else kappa
     eps = wl.eps if eps is None else eps
     delta = wl.delta if delta is None else delta
     outs = []
     for b, s in enumerate(wl.seqs):
+        Ks = None if sketch_of is None else np.stack([sketch_of(s.K[g]) for g in range(s.K.shape[0])])
         outs.append(oapi.decode_sequence(s.K, s.V, comp[b], wl.queries[step, b], wl.group,
-                                         kappa, eps, delta))
+                                         kappa, eps, delta, K_sketch=Ks))
     return outs
 
 
@@ -82,7 +85,8 @@ def rel_l2(a, b):
     return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None, tol=2e-3):
+def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None, tol=2e-3,
+                 sketch_of=None):
     """Compare one step; returns a dict of summary numbers."""
     kappa = wl.kappa if kappa is None else kappa
     eps = wl.eps if eps is None else eps
@@ -105,8 +109,9 @@ def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None,
             near = None
             if bool(res["certified"][row]) != bool(oo["certified"][h]) or \
                     int(res["kstar"][row]) != int(oo["kstar"][h]):
+                Kd = s.K[g] if sketch_of is None else sketch_of(s.K[g])
                 near = cut_near_threshold(wl, ocomp[b][g], wl.queries[step, b, h], kappa, eps,
-                                          delta, s.K[g])
+                                          delta, Kd)
                 assert near, (b, h, "decision", res["certified"][row], oo["certified"][h],
                               res["kstar"][row], oo["kstar"][h], res["eps_hat"][row])
                 exempt_units.add((b, g))

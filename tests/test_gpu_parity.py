@@ -24,7 +24,7 @@ def _session(wl, **kw):
     return Session(wl, **kw)
 
 
-def _run(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, **kw):
+def _run(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, sketch_of=None, **kw):
     say(f"[parity] {label}: {wl.name}")
     sess = _session(wl, **kw)
     sess.compress()
@@ -37,8 +37,9 @@ def _run(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, **kw):
         sess.step(q, kappa=kappa, eps=eps, delta=delta)
         from long_context_decode_kvfetch_amd import verkv
         verkv.check(sess.shape, sess.cap, sess.dws)
-        oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta)
-        summ.append(compare_step(sess, wl, ocomp, oo, st, kappa=kappa, eps=eps, delta=delta))
+        oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta, sketch_of=sketch_of)
+        summ.append(compare_step(sess, wl, ocomp, oo, st, kappa=kappa, eps=eps, delta=delta,
+                                 sketch_of=sketch_of))
     say(f"[parity] {label}: {summ}")
     return sess, summ
 
@@ -175,3 +176,61 @@ def test_prefetch_and_workspace_history_do_not_change_results():
         for st in range(3):
             for k in keys:
                 assert np.array_equal(runs[0][st][k], other[st][k]), (label, st, k)
+
+
+# ------------------------------------------------------------------ the 2-bit sketch
+def _sketch2_of(K):
+    """The oracle's 2-bit sketch of key rows exactly as the device holds them."""
+    from oracle import sketch2
+    return sketch2.sketch_of(K)
+
+
+def _unpack_sketch2(raw):
+    """Codes [rows][128], mn, sc [rows][4] from 64-byte rows (layout in include/verkv.h:
+    word w = codes of dimensions 8w.. | codes of 8(w+8).. << 16; then (mn, sc) of groups
+    0, 2, 1, 3 as float32)."""
+    words = np.ascontiguousarray(raw[:, :32]).view("<u4")
+    prm = np.ascontiguousarray(raw[:, 32:]).view("<f4")
+    rows = raw.shape[0]
+    codes = np.zeros((rows, 128), dtype=np.uint8)
+    for piece in range(16):
+        w = words[:, piece % 8] >> np.uint32(16 * (piece // 8))
+        for e in range(8):
+            codes[:, piece * 8 + e] = (w >> np.uint32(2 * e)) & np.uint32(3)
+    pos = {0: 0, 2: 1, 1: 2, 3: 3}
+    mn = np.stack([prm[:, 2 * pos[g]] for g in range(4)], axis=1)
+    sc = np.stack([prm[:, 2 * pos[g] + 1] for g in range(4)], axis=1)
+    return codes, mn, sc
+
+
+def test_2bit_sketch_codes_match_the_oracle():
+    """verkv_quantize_sketch against the oracle's quantiser, bf16 and float32 keys:
+    every code and every float32 group parameter bit for bit."""
+    from oracle import sketch2
+    for wl in (synth.gqa_layer(seed=3, n=5000, steps=1, hkv=2),
+               synth.single_head(6, n=3000)):
+        say(f"[parity] 2-bit sketch codes: {wl.name}")
+        sess = _session(wl, sketch_2bit=True)
+        torch.cuda.synchronize()
+        raw = sess.sketch.cpu().numpy().reshape(-1, 64)
+        codes, mn, sc = _unpack_sketch2(raw)
+        r = 0
+        for s in wl.seqs:
+            for g in range(wl.n_kv_heads):
+                oc, om, osc = sketch2.quantize_rows(s.K[g])
+                n = s.n
+                assert np.array_equal(codes[r:r + n], oc), (g, "codes")
+                assert np.array_equal(mn[r:r + n].view(np.uint32), om.view(np.uint32)), (g, "mn")
+                assert np.array_equal(sc[r:r + n].view(np.uint32), osc.view(np.uint32)), (g, "sc")
+                r += n
+        assert r == raw.shape[0]
+
+
+def test_decode_with_2bit_sketch():
+    """Steps 1-5 with the 2-bit sketch (weights from x_hat, fetched rows scored from the
+    host keys) against the oracle run on the same sketch keys: 8 query rows per KV head
+    on float32 keys (16 lanes per row) and the GQA shape on bf16 keys (8 lanes)."""
+    _run(synth.single_head(2, n=4096), label="single-head, 2-bit sketch", sketch_2bit=True,
+         sketch_of=_sketch2_of)
+    _run(synth.gqa_layer(seed=8, n=8192, steps=2, hkv=2), steps=(0, 1), label="gqa, 2-bit sketch",
+         sketch_2bit=True, sketch_of=_sketch2_of)
