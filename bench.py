@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-pivot-batch", action="store_true",
                    help="skip the pivotal-stream measurement at the 16-sequence batch")
+    p.add_argument("--no-2bit", action="store_true",
+                   help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--pivot-only", action="store_true",
                    help="time only the resident-pivot attention at the 16-sequence batch "
                         "and print its figures as one JSON line")
@@ -136,6 +138,63 @@ def pivotal_stream(torch, steps=8):
             "pivot_rows": rows, "bytes": nbytes, "avg_us": round(us, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
             "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def sketch2_leg(torch, wls, qdevs, K2, W2):
+    """The layer-step with the 2-bit key sketch (64 B per token row instead of 256 B;
+    fetched rows are scored from the host keys, so K and V rows cross the host link):
+    steps/s over the same rotated layers and the sketch kernel's rate on its own bytes."""
+    from long_context_decode_kvfetch_amd import verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+    L = len(wls)
+    sess2 = []
+    for wl, qd in zip(wls, qdevs):
+        s2 = Session(wl, sketch_2bit=True)
+        s2.compress()
+        s2.qdev = qd
+        sess2.append(s2)
+    per_layer = qdevs[0].shape[0]
+
+    def run(i):
+        s2 = sess2[i % L]
+        s2.step(s2.qdev[(i // L) % per_layer])
+
+    for i in range(W2):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(W2, W2 + K2):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    verkv.profile_begin(8 * 16 + 16)
+    for i in range(W2 + K2, W2 + K2 + 16):
+        run(i)
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    h2d = 0
+    for s2 in sess2:
+        s2.step(s2.qdev[0])
+        h2d += int(s2.results_numpy()["h2d_count"].sum())
+    sk_ms, sk_n = prof["sketch_scores"]
+    sk_us = sk_ms / sk_n * 1e3
+    # per (KV head, token): the 64 B sketch row and r_i (8 B) read, 4 x 8 B weights written
+    sk_bytes = 8 * N_CTX * (64 + 8 + 4 * 8)
+    host_us = prof["attend_host"][0] / prof["attend_host"][1] * 1e3
+    out = {"value": round(K2 / (ms * 1e-3), 2), "unit": "steps/s", "steps": K2,
+           "ms_per_step": round(ms / K2, 4),
+           "sketch_bytes_per_token_head": 64,
+           "sketch_kernel": {"avg_us": round(sk_us, 2), "algorithmic_bytes": sk_bytes,
+                             "GBps": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1)},
+           "h2d_bytes_per_step": h2d / L * 2 * 128 * 2,
+           "host_kernel_avg_us": round(host_us, 1),
+           "note": "K and V rows of F minus S cross the host link (the sketch is not exact)"}
+    del sess2
+    torch.cuda.empty_cache()
+    return out
 
 
 def calib_copy(torch):
@@ -279,6 +338,14 @@ def main():
             "traffic": profiled_traffic(dom) if dom in KERNEL_SOURCES else None,
             "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}
     h2d_peak = h2d_bandwidth(torch)
+    sk2 = None
+    if not args.no_2bit:
+        log("[bench] 2-bit sketch: the same layers, rebuilt")
+        wls = [sess.wl for sess in sessions]
+        qdevs = [sess.qdev for sess in sessions]
+        sessions.clear()
+        torch.cuda.empty_cache()
+        sk2 = sketch2_leg(torch, wls, qdevs, K2=min(K, 64), W2=min(W, 8))
     piv = None
     if not args.no_pivot_batch:
         log("[bench] pivotal stream at the 16-sequence batch")
@@ -304,6 +371,7 @@ def main():
                    "layers_rotated": L, "seq_len": N_CTX, "batch": 1},
         "roofline": roof,
         "pivotal_stream": piv,
+        "sketch_2bit": sk2,
         "cpu_baseline": None,
         "step_stats": {"rows_certified_without_fetch": cert / rows,
                        "fetched_fraction_of_cache": fetched / n_tok,
