@@ -48,6 +48,9 @@ def parse():
                    help="skip the pivotal-stream measurement at the 16-sequence batch")
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
+    p.add_argument("--sweep", action="store_true",
+                   help="eta in {1/8, 1/16, 1/32} x eps in {0.02, 0.05, 0.1} over the rotated "
+                        "32K layers: steps/s and host traffic per setting, one JSON line")
     p.add_argument("--pivot-only", action="store_true",
                    help="time only the resident-pivot attention at the 16-sequence batch "
                         "and print its figures as one JSON line")
@@ -197,6 +200,62 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
     return out
 
 
+def eta_eps_sweep(torch, L, K=32, W=8):
+    """The 32K GQA layer-step at resident fractions eta = 1/8, 1/16, 1/32 and tolerances
+    eps = 0.02, 0.05, 0.1 (delta = 0.05): steps/s and what crosses the host link."""
+    import copy
+    import numpy as np
+    from long_context_decode_kvfetch_amd import synth
+    from long_context_decode_kvfetch_amd.runner import Session
+    base = [synth.gqa_layer(seed=0, n=N_CTX, steps=(K + W + 1 + L - 1) // L + 1, layer=layer)
+            for layer in range(L)]
+    rows = []
+    for eta in (1.0 / 8, 1.0 / 16, 1.0 / 32):
+        sess = []
+        for wl0 in base:
+            wl = copy.copy(wl0)
+            wl.eta = eta
+            s2 = Session(wl)
+            s2.compress()
+            s2.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
+            sess.append(s2)
+        per_layer = sess[0].qdev.shape[0]
+        for eps in (0.02, 0.05, 0.1):
+            def run(i):
+                s2 = sess[i % L]
+                s2.step(s2.qdev[(i // L) % per_layer], eps=eps)
+            for i in range(W):
+                run(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(W, W + K):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            cert = fetched = h2d = nrow = 0
+            for s2 in sess:
+                s2.step(s2.qdev[0], eps=eps)
+                r = s2.results_numpy()
+                cert += int(r["certified"].sum())
+                fetched += int(r["fetch_count"].sum())
+                h2d += int(r["h2d_count"].sum())
+                nrow += r["certified"].size
+            ntok = L * N_CTX * 8
+            rows.append({"eta": eta, "eps": eps, "steps_per_s": round(K / (ms * 1e-3), 1),
+                         "rows_certified_without_fetch": cert / nrow,
+                         "fetched_fraction_of_cache": fetched / ntok,
+                         "h2d_fraction_of_cache": h2d / ntok,
+                         "h2d_bytes_per_step": h2d / L * 128 * 2})
+            log(f"[bench] sweep eta=1/{round(1 / eta)} eps={eps}: {rows[-1]['steps_per_s']} steps/s, "
+                f"F/n {rows[-1]['fetched_fraction_of_cache']:.3f}")
+        del sess
+        torch.cuda.empty_cache()
+    return {"workload": "gqa decode layer-step: 32q/8kv, d=128, n=32768, bf16, exact sketch, "
+                        "delta=0.05, layers rotated", "layers": L, "steps": K, "settings": rows}
+
+
 def calib_copy(torch):
     """A kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE: an elementwise copy
     that reads and writes 256 MiB once per launch, three launches."""
@@ -245,6 +304,9 @@ def main():
     from long_context_decode_kvfetch_amd.runner import Session
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        print(json.dumps({"sweep": eta_eps_sweep(torch, args.layers)}))
+        return
     if args.pivot_only:
         if args.calib_copy:
             calib_copy(torch)
