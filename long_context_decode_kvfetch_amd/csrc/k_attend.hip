@@ -18,6 +18,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace verkv {
 
@@ -218,16 +219,20 @@ static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st
 // The same partials as k_attend over the resident pivots, from workgroups that stay
 // resident and share the rows evenly: worker w takes the chunks the coefficient pass
 // scheduled for it (consecutive chunks of PIVOT_CHUNK rows, possibly over several KV
-// heads) and streams their batches back to back, the next batch's loads issued before
-// the current batch is reduced, also across the end of a run, so the loads stay in
-// flight while a run's partial is reduced and written.  A run is the worker's rows of
-// one KV head; its partial goes to the slot the schedule gives it.  The schedule names
-// the first run outright, so the first loads leave after one dependent read.
+// heads) and streams them through two alternating row batches: while one batch is
+// reduced, the loads of the next are in flight, also across the end of a run (the
+// worker's rows of one KV head), whose partial goes to the slot the schedule gives it.
+// An issue cursor walks the runs one batch ahead of the reduction; each batch carries
+// its run's head, slot and first/last flags.  The query rows of the first run are
+// loaded before the first rows, those of the second run (named in the schedule) are
+// staged in LDS at the start, so a run change does not wait behind rows in flight.  One row group per batch (a quarter of
+// a 32-row chunk per workgroup): on MI355X more rows in flight per wave (two or four
+// row groups, or three batches in the ring) made the stream slower, not faster.
 //
 // With four query rows and 16 lanes per key row (bf16) the scores are reduce-scattered:
 // after five DPP adds lane s of a row holds the full q.k of query row 2 s[3] + s[2], each
 // lane takes exp for that one row and the four weights are broadcast back over the row.
-constexpr int PIV_U = 2;           // row groups per batch of a pivot worker
+constexpr int PIV_U = 1;           // row groups per batch of a pivot worker
 
 template <bool BF16, int G>
 __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_attend_piv(AttendArgs a) {
@@ -247,6 +252,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 
   __shared__ float s_acc[AT_NW][TPW][G][D];
   __shared__ float s_den[AT_NW][TPW][G];
+  __shared__ float s_q2[G][D];                   // second run: scaled query rows
+  __shared__ float s_m2[G];                      //   and m_hat log2(e)
 
   const int Hq = a.t.Hkv * G;
   const int units = a.t.B * a.t.Hkv;
@@ -259,11 +266,15 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   const int myrow = RS4 ? 2 * ((sub >> 3) & 1) + ((sub >> 2) & 1) : 0;   // query row of this lane
   const int nslots = a.nsplit + units;
   const int PW = a.sched[2 * a.nsplit].y;          // workers P the rows were stored for
+  const float qscale = a.inv_sqrt_d * LOG2E;
 
+  // a batch: the loads of SU rows of one run and what the reduction needs to place them
   struct Batch {
     uint4 kr[U], vr[U];
-    int pp[U];
     float cc[U][NC];
+    int base, p1;                // first row of the batch, end row of its run
+    int unit, slot, run;         // run's KV head, partial slot, index among the worker's runs
+    bool first, last, live;      // first / last batch of its run; false past the worker's rows
   };
   // every lane loads a row (rows past the run's end repeat an in-bounds row and get
   // weight 0), so no register is written while a load into it may be in flight.  K and V
@@ -274,7 +285,6 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
-      bt.pp[u] = p < p1 ? p : -1;
       const int pc = min(max(min(p, p1 - 1), 0), a.cap - 1);
       const int64_t ich = i0 + (pc - q0) / PIVOT_CHUNK;
       const int64_t srow = (ich * PW + blockIdx.x) * PIVOT_CHUNK + (pc & (PIVOT_CHUNK - 1));
@@ -294,20 +304,35 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         for (int j = 0; j < G; ++j) bt.cc[u][j] = cp[j];
       }
     }
+    bt.base = base;
+    bt.p1 = p1;
   };
 
   // query slices pre-scaled by log2(e) / sqrt(d), so a weight is exp2(q.k - m_hat log2 e)
   float qf[G][EPL], mh[G], mh_mine = 0.0f;
   float acc[G][EPL], den[G];
-  auto setup = [&](int unit) {
+  auto load_q = [&](int unit) {                    // from memory
     const int b = unit / a.t.Hkv, g = unit % a.t.Hkv;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int64_t qrow = (int64_t)b * Hq + g * G + j;
       const float *qr = a.q + qrow * D + d0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * (a.inv_sqrt_d * LOG2E);
+      for (int e = 0; e < EPL; ++e) qf[j][e] = qr[e] * qscale;
       mh[j] = (float)(a.m_hat[qrow] * (double)LOG2E);
+    }
+  };
+  auto load_q_lds = [&]() {                        // the second run's, staged at the start
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[j][e] = s_q2[j][d0 + e];
+      mh[j] = s_m2[j];
+    }
+  };
+  auto reset = [&]() {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
       den[j] = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
@@ -317,6 +342,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   auto consume = [&](const Batch &bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const bool valid = bt.base + u * STEP + wv * TPW + grp < bt.p1;
       float x[EPL], v[EPL], w[G];
       RS::widen(bt.kr[u], x);
       float dp[G];
@@ -339,7 +365,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         k += dpp_f<DPP_XOR1>(k);
         k += dpp_f<DPP_XOR2>(k);
         float wm = exp2f(k - mh_mine) * bt.cc[u][0];
-        wm = bt.pp[u] >= 0 ? wm : 0.0f;
+        wm = valid ? wm : 0.0f;
         // query row j is held by lane 4 j of the row
         w[0] = dpp_f<DPP_ROW_BCAST0 + 0>(wm);
         w[1] = dpp_f<DPP_ROW_BCAST0 + 4>(wm);
@@ -350,7 +376,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         for (int j = 0; j < G; ++j) {
           float dot = sum16(dp[j]);
           if (LPT == 32) dot += shfl_xor_f(dot, 16);
-          w[j] = bt.pp[u] >= 0 ? exp2f(dot - mh[j]) * bt.cc[u][j] : 0.0f;
+          w[j] = valid ? exp2f(dot - mh[j]) * bt.cc[u][j] : 0.0f;
         }
       }
       RS::widen(bt.vr[u], v);
@@ -390,84 +416,120 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   // one {head, end row, slot, chunks left after it}
   const int4 f0 = a.sched[2 * blockIdx.x];
   const int4 f1 = a.sched[2 * blockIdx.x + 1];
-  int unit = f0.x, base = f0.y, p1 = f0.z, slot = f0.w, left = 0;
-  if (!(unit >= 0 && unit < units && base >= 0 && base < p1 && p1 <= a.cap && slot >= 0 && slot < nslots &&
-        PW > (int)blockIdx.x && PW <= a.nsplit))
+  if (!(f0.x >= 0 && f0.x < units && f0.y >= 0 && f0.y < f0.z && f0.z <= a.cap && f0.w >= 0 &&
+        f0.w < nslots && PW > (int)blockIdx.x && PW <= a.nsplit))
     return;                                        // no rows for this worker
-  // the current run's first worker-local chunk and first row
-  int ci0 = 0, cq0 = base;
-  int q_unit = f1.x, q_p1 = f1.y, q_slot = f1.z, q_left = f1.w;
+  int q_unit = f1.x, q_p1 = f1.y, q_slot = f1.z, q_left = f1.w, left = 0;
   if (q_unit < 0) {
     left = q_left;                                 // chunks after the first run, heads unknown
   } else if (!(q_unit < units && q_p1 > 0 && q_p1 <= a.cap && q_slot >= 0 && q_slot < nslots)) {
     q_unit = -1;
     q_left = 0;
   }
-  Batch A, B;
-  issue(unit, base, p1, ci0, cq0, A);
-  setup(unit);
-  // one step: plan the batch after `cur` (the rest of this run, else the first batch
-  // of the worker's next run), issue it into `nxt`, reduce `cur`, and close the run if
-  // `cur` was its last batch; false once the worker is done.  The two batches swap
-  // roles from step to step, so no register copy waits on loads in flight.
-  auto step = [&](Batch &cur, Batch &nxt) -> bool {
-    int nunit = unit, nbase = base + SU, np1 = p1, nslot = slot, ni0 = ci0, nq0 = cq0;
-    bool more = true;
-    const bool ends = nbase >= p1;
-    // where the worker's next run starts in its chunks
-    const int run_end_i0 = ci0 + (p1 - cq0 + PIVOT_CHUNK - 1) / PIVOT_CHUNK;
-    if (ends) {
-      more = false;
-      if (q_unit >= 0) {                           // the queued second run
-        nunit = q_unit;
-        nbase = 0;
-        np1 = q_p1;
-        nslot = q_slot;
-        left = q_left;
-        q_unit = -1;
-        ni0 = run_end_i0;
-        nq0 = 0;
-        more = true;
-      } else if (left > 0) {
-        // a third run or later, or a head without pivots in between: read the heads
-        for (int u2 = unit + 1; u2 < units; ++u2) {
-          const int c = min(a.count[u2], a.cap);
-          if (c <= 0) continue;
-          const int sl = a.runs[u2].x;
-          if (sl >= 0 && sl < nslots) {
-            const int take = min((c + R - 1) / R, left);
-            left -= take;
-            nunit = u2;
-            nbase = 0;
-            np1 = min(c, take * R);
-            nslot = sl;
-            ni0 = run_end_i0;
-            nq0 = 0;
-            more = true;
-          }
-          break;
+  const bool staged = q_unit >= 0;                 // run 1's queries come from LDS
+
+  // the issue cursor: the run and row of the next batch to load
+  int iu = f0.x, ib = f0.y, ip1 = f0.z, isl = f0.w, ii0 = 0, iq0 = f0.y, irun = 0;
+  bool ifirst = true, idone = false;
+  auto issue_next = [&](Batch &bt) {
+    issue(iu, ib, ip1, ii0, iq0, bt);              // weight-0 rows once the worker is done
+    bt.unit = iu;
+    bt.slot = isl;
+    bt.run = irun;
+    bt.first = ifirst;
+    bt.last = ib + SU >= ip1;
+    bt.live = !idone;
+    ifirst = false;
+    if (idone) return;
+    ib += SU;
+    if (ib < ip1) return;
+    const int run_end_i0 = ii0 + (ip1 - iq0 + R - 1) / R;
+    bool more = false;
+    if (q_unit >= 0) {                             // the queued second run
+      iu = q_unit;
+      ip1 = q_p1;
+      isl = q_slot;
+      left = q_left;
+      q_unit = -1;
+      more = true;
+    } else if (left > 0) {
+      // a third run or later, or a head without pivots in between: read the heads
+      for (int u2 = iu + 1; u2 < units; ++u2) {
+        const int c = min(a.count[u2], a.cap);
+        if (c <= 0) continue;
+        const int sl = a.runs[u2].x;
+        if (sl >= 0 && sl < nslots) {
+          const int take = min((c + R - 1) / R, left);
+          left -= take;
+          iu = u2;
+          ip1 = min(c, take * R);
+          isl = sl;
+          more = true;
         }
+        break;
       }
     }
-    // issued on every path (past the worker's last row it is a batch of weight-0
-    // rows), so the waits for `cur` never have to cover `nxt`
-    issue(nunit, nbase, np1, ni0, nq0, nxt);
-    __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of the reduction
-    consume(cur);
-    if (ends) {
-      epilogue(slot);
-      if (!more) return false;
-      unit = nunit;
-      slot = nslot;
-      p1 = np1;
-      ci0 = ni0;
-      cq0 = nq0;
-      setup(unit);
+    if (!more) {
+      idone = true;
+      ib = ip1;                                    // later batches: weight-0 rows of this run
+      return;
     }
-    base = nbase;
+    ib = 0;
+    ii0 = run_end_i0;
+    iq0 = 0;
+    ++irun;
+    ifirst = true;
+  };
+
+  // the queries of the first run, and those of the second run (staged in LDS), are
+  // loaded before the first rows: a wait for them then never covers rows in flight
+  constexpr int Q2N = (G * D + AT_NT - 1) / AT_NT;
+  float q2v[Q2N];
+  double m2v = 0.0;
+  if (staged) {
+    const int b2 = f1.x / a.t.Hkv, g2 = f1.x % a.t.Hkv;
+#pragma unroll
+    for (int k = 0; k < Q2N; ++k) {
+      const int t = threadIdx.x + k * AT_NT;
+      q2v[k] = t < G * D ? a.q[((int64_t)b2 * Hq + g2 * G + t / D) * D + t % D] : 0.0f;
+    }
+    if (threadIdx.x < G) m2v = a.m_hat[(int64_t)b2 * Hq + g2 * G + threadIdx.x];
+  }
+  load_q(f0.x);
+  Batch A, B;
+  issue_next(A);
+  if (staged) {                                    // visible after the first run's barrier
+#pragma unroll
+    for (int k = 0; k < Q2N; ++k) {
+      const int t = threadIdx.x + k * AT_NT;
+      if (t < G * D) s_q2[t / D][t % D] = q2v[k] * qscale;
+    }
+    if (threadIdx.x < G) s_m2[threadIdx.x] = (float)(m2v * (double)LOG2E);
+  }
+  reset();
+
+  // one step: issue the next batch into `nxt`, reduce `cur`, close its run if it was
+  // the run's last batch; false once the worker is done.  The two steps of the ring are
+  // separate instances (the markers keep the compiler from folding them into one body,
+  // which would reuse registers still being loaded and wait for them).
+  auto step = [&](auto id, Batch &cur, Batch &nxt) -> bool {
+    asm volatile("; pivot ring step %0" ::"n"(decltype(id)::value));
+    if (!cur.live) return false;
+    if (cur.first && cur.run > 0) {                // a new run: its queries, zero partials
+      if (cur.run == 1 && staged)
+        load_q_lds();
+      else
+        load_q(cur.unit);
+      reset();
+    }
+    issue_next(nxt);
+    __builtin_amdgcn_sched_barrier(0);             // keep the loads ahead of the reduction
+    consume(cur);
+    if (cur.last) epilogue(cur.slot);
+    asm volatile("; pivot ring step end %0" ::"n"(decltype(id)::value));
     return true;
   };
-  while (step(A, B) && step(B, A)) {
+  while (step(std::integral_constant<int, 0>{}, A, B) && step(std::integral_constant<int, 1>{}, B, A)) {
   }
 }
 
