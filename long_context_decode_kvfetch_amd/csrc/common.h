@@ -220,6 +220,14 @@ __device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t *scratch, 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
+// A 16-byte load with the streaming (non-temporal) cache policy, for data read once
+// per step: the lines are not kept in the caches for reuse.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Load the 16-byte slice of a cache row that a lane owns and widen it to float.
 // bf16 rows: 8 elements per lane; f32 rows: 4 elements per lane.
 template <bool BF16>

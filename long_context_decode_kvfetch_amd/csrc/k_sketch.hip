@@ -169,7 +169,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
         }
       } else {
 #pragma unroll
-        for (int p = 0; p < PPL; ++p) raw[k * PPL + p] = *(const uint4 *)(rp + p * LPT * 16);
+        for (int p = 0; p < PPL; ++p) raw[k * PPL + p] = load_stream16(rp + p * LPT * 16);
       }
     }
   };
