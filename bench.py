@@ -54,6 +54,12 @@ def parse():
     p.add_argument("--pivot-only", action="store_true",
                    help="time only the resident-pivot attention at the 16-sequence batch "
                         "and print its figures as one JSON line")
+    p.add_argument("--decode36", action="store_true",
+                   help="36 independent 32K layers decoded one after another per token "
+                        "(eta=1/16, eps=0.05): tokens/s and host bytes per token, one JSON line")
+    p.add_argument("--long-context", action="store_true",
+                   help="one 131072-token sequence, eta=1/32, keys planted on non-resident "
+                        "tokens, eps in {0.05, 0.1, 0.2, 0.3, 0.5}: steps/s and fetched share, one JSON line")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a 256 MiB elementwise copy kernel (HBM counter calibration)")
     return p.parse_args()
@@ -82,15 +88,20 @@ def h2d_bandwidth(torch, nbytes=256 << 20, reps=5):
 # runs (FETCH_SIZE, WRITE_SIZE) scaled by a copy kernel of known size.  The record
 # carries a hash of the kernel's sources; once they change the figure no longer
 # describes the kernel and traffic is reported as null.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "sketch_scores_gqa32k_traffic.md")
-KERNEL_SOURCES = {"sketch_scores": ("long_context_decode_kvfetch_amd/csrc/k_sketch.hip",
-                                    "long_context_decode_kvfetch_amd/csrc/common.h")}
+KERNEL_SOURCES = {
+    "sketch_scores": ("profiles/sketch_scores_gqa32k_traffic.md",
+                      ("long_context_decode_kvfetch_amd/csrc/k_sketch.hip",
+                       "long_context_decode_kvfetch_amd/csrc/common.h")),
+    "attend_pivots": ("profiles/attend_pivots_ragged16_kernel_trace.md",
+                      ("long_context_decode_kvfetch_amd/csrc/k_attend.hip",
+                       "long_context_decode_kvfetch_amd/csrc/common.h")),
+}
 
 
 def sources_sha256(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
+    for rel in KERNEL_SOURCES[kernel][1]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -99,7 +110,7 @@ def sources_sha256(kernel):
 def profiled_traffic(kernel):
     """Bytes per launch from the committed counter summary, or None if stale/absent."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(os.path.join(ROOT, KERNEL_SOURCES[kernel][0])) as f:
             lines = [l for l in f if l.startswith("traffic-record:")]
     except OSError:
         return None
@@ -140,7 +151,8 @@ def pivotal_stream(torch, steps=8):
                         "every row certified (pivots only)",
             "pivot_rows": rows, "bytes": nbytes, "avg_us": round(us, 2),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
-            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": profiled_traffic("attend_pivots")}
 
 
 def sketch2_leg(torch, wls, qdevs, K2, W2):
@@ -256,6 +268,125 @@ def eta_eps_sweep(torch, L, K=32, W=8):
                         "delta=0.05, layers rotated", "layers": L, "steps": K, "settings": rows}
 
 
+def decode_36_layers(torch, tokens=16, warm=2, n_layers=36):
+    """A full decode of one sequence through 36 layers shaped like the 32K GQA layer
+    (independent caches, Philox layer word = layer index): every generated token runs
+    the 36 layer-steps back to back on one stream, each with its own query rows.  Reports
+    tokens/s, milliseconds per layer-step and the bytes that crossed the host link per
+    token against the full cache (K and V of 36 layers)."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import synth
+    from long_context_decode_kvfetch_amd.runner import Session
+    sess = []
+    for layer in range(n_layers):
+        wl = synth.gqa_layer(seed=0, n=N_CTX, steps=tokens + warm + 1, layer=layer)
+        s2 = Session(wl)
+        s2.compress()
+        s2.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
+        for sq in wl.seqs:                        # the host copy is pinned; free the arrays
+            sq.K = sq.V = None
+        sess.append(s2)
+        if layer % 6 == 5:
+            log(f"[bench] decode36: {layer + 1} layers compressed")
+    torch.cuda.synchronize()
+
+    def token(t):
+        for s2 in sess:
+            s2.step(s2.qdev[t])
+
+    for t in range(warm):
+        token(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warm, warm + tokens):
+        token(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    cert = fetched = h2d = nrow = 0
+    for s2 in sess:
+        s2.step(s2.qdev[warm + tokens])
+        r = s2.results_numpy()
+        assert np.all(r["eps_after"] < s2.wl.eps), "a row finished uncertified"
+        cert += int(r["certified"].sum())
+        fetched += int(r["fetch_count"].sum())
+        h2d += int(r["h2d_count"].sum())
+        nrow += r["certified"].size
+    ntok = n_layers * N_CTX * 8
+    full = n_layers * 8 * N_CTX * 128 * 2 * 2                # K and V, bf16, all layers
+    resident = sum(int(s2.state.piv_count.sum().item()) for s2 in sess)
+    out = {"workload": f"{n_layers} layers x (32q/8kv, d=128, n={N_CTX}, bf16, exact sketch), "
+                       "eta=1/16, eps=0.05, delta=0.05, one sequence",
+           "layers": n_layers, "tokens": tokens, "tokens_per_s": round(tokens / (ms * 1e-3), 2),
+           "ms_per_token": round(ms / tokens, 3),
+           "ms_per_layer_step": round(ms / tokens / n_layers, 4),
+           "rows_certified_without_fetch": cert / nrow,
+           "fetched_fraction_of_cache": fetched / ntok,
+           "h2d_bytes_per_token": h2d * 128 * 2,
+           "h2d_fraction_of_full_cache_bytes": h2d * 128 * 2 / full,
+           "full_cache_bytes": full,
+           "resident_pivot_fraction": resident / ntok}
+    del sess
+    torch.cuda.empty_cache()
+    return out
+
+
+def long_context_stress(torch, steps=16, warm=2, planted=2048):
+    """One 131072-token sequence (32q/8kv, d=128, bf16, eta = 1/32) whose queries align
+    with keys planted on tokens the sampler did not keep: PoissonComp runs once, then
+    `planted` non-resident tokens per KV head get the heavy-hitter direction and the
+    layer is rebuilt (the sample depends only on tau and the seed, so it is the same).
+    Steps/s, fetched share and host traffic at eps = 0.05, 0.1, 0.2, 0.3, 0.5."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import synth
+    from long_context_decode_kvfetch_amd.runner import Session
+    n = 131072
+    wl = synth.long_context(seed=0, n=n, steps=steps + warm + 1)
+    s0 = Session(wl)
+    s0.compress()
+    resident = np.stack([h["resident"] for h in s0.state_numpy()])
+    del s0
+    torch.cuda.empty_cache()
+    synth.plant_adversarial(wl, resident, planted)
+    sess = Session(wl)
+    sess.compress()
+    qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
+    for sq in wl.seqs:
+        sq.K = sq.V = None
+    rows = []
+    for eps in (0.05, 0.1, 0.2, 0.3, 0.5):
+        for t in range(warm):
+            sess.step(qdev[t], eps=eps)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warm, warm + steps):
+            sess.step(qdev[t], eps=eps)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        sess.step(qdev[warm + steps], eps=eps)
+        r = sess.results_numpy()
+        assert np.all(r["eps_after"] < eps), "a row finished uncertified"
+        ntok = n * 8
+        rows.append({"eps": eps, "steps_per_s": round(steps / (ms * 1e-3), 2),
+                     "ms_per_step": round(ms / steps, 3),
+                     "rows_certified_without_fetch": float(r["certified"].mean()),
+                     "fetched_fraction_of_cache": int(r["fetch_count"].sum()) / ntok,
+                     "h2d_fraction_of_cache": int(r["h2d_count"].sum()) / ntok,
+                     "h2d_bytes_per_step": int(r["h2d_count"].sum()) * 128 * 2})
+        log(f"[bench] long context eps={eps}: {rows[-1]['steps_per_s']} steps/s, "
+            f"F-S/n {rows[-1]['h2d_fraction_of_cache']:.3f}")
+    piv = int(sess.state.piv_count.sum().item())
+    del sess
+    torch.cuda.empty_cache()
+    return {"workload": f"one sequence n={n}, 32q/8kv, d=128, bf16, exact sketch, eta=1/32, "
+                        f"H=4 sink+128 local, {planted} keys per KV head planted on non-resident "
+                        "tokens, delta=0.05", "pivot_rows": piv,
+            "pivot_bytes_per_step": piv * 128 * 2 * 2, "steps": steps, "settings": rows}
+
+
 def calib_copy(torch):
     """A kernel of known traffic for scaling FETCH_SIZE / WRITE_SIZE: an elementwise copy
     that reads and writes 256 MiB once per launch, three launches."""
@@ -306,6 +437,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sweep:
         print(json.dumps({"sweep": eta_eps_sweep(torch, args.layers)}))
+        return
+    if args.decode36:
+        print(json.dumps({"decode_36_layers": decode_36_layers(torch)}))
+        return
+    if args.long_context:
+        print(json.dumps({"long_context": long_context_stress(torch)}))
         return
     if args.pivot_only:
         if args.calib_copy:
