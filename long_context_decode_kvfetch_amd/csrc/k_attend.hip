@@ -283,15 +283,17 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   // rows are stored in schedule order: row p of a run that starts at row q0 and at the
   // worker's i0-th chunk is in block (i0 + (p - q0) / PIVOT_CHUNK) P + w; the
   // coefficients keep the [head][cap] order.
-  auto issue = [&](int unit, int base, int p1, int i0, int q0, Batch &bt) {
+  auto issue = [&](int unit, int base, int p1, int i0, int q0, Batch &bt, bool kv) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * STEP + wv * TPW + grp;
       const int pc = min(max(min(p, p1 - 1), 0), a.cap - 1);
-      const int64_t ich = i0 + (pc - q0) / PIVOT_CHUNK;
-      const int64_t srow = (ich * PW + blockIdx.x) * PIVOT_CHUNK + (pc & (PIVOT_CHUNK - 1));
-      bt.kr[u] = load_stream16(a.krows + srow * ROW_BYTES + slice);
-      bt.vr[u] = load_stream16(a.vrows + srow * ROW_BYTES + slice);
+      if (kv) {
+        const int64_t ich = i0 + (pc - q0) / PIVOT_CHUNK;
+        const int64_t srow = (ich * PW + blockIdx.x) * PIVOT_CHUNK + (pc & (PIVOT_CHUNK - 1));
+        bt.kr[u] = load_stream16(a.krows + srow * ROW_BYTES + slice);
+        bt.vr[u] = load_stream16(a.vrows + srow * ROW_BYTES + slice);
+      }
       const float *cp = a.coef + ((int64_t)unit * a.cap + pc) * G;
       if constexpr (RS4) {
         bt.cc[u][0] = cp[myrow];
@@ -414,6 +416,20 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     __syncthreads();
   };
 
+  // The first batch is the first rows of the worker's first chunk, stored as block
+  // blockIdx.x (schedule order, i = 0): its K/V loads leave before the schedule is read.
+  // Rows past a head's last pivot in its last chunk hold zeros (written by the gather),
+  // so a row of weight 0 there adds nothing.  Block blockIdx.x < nsplit <= the workers
+  // the rows are sized for, so the loads stay inside the buffers for any schedule.
+  Batch A, B;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t srow = (int64_t)blockIdx.x * PIVOT_CHUNK + u * STEP + wv * TPW + grp;
+    A.kr[u] = load_stream16(a.krows + srow * ROW_BYTES + slice);
+    A.vr[u] = load_stream16(a.vrows + srow * ROW_BYTES + slice);
+  }
+  asm volatile("" ::: "memory");                   // keep them ahead of the schedule read
+
   // this worker's first run {head, first row, end row, slot} and, queued, its second
   // one {head, end row, slot, chunks left after it}
   const int4 f0 = a.sched[2 * blockIdx.x];
@@ -433,8 +449,8 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
   // the issue cursor: the run and row of the next batch to load
   int iu = f0.x, ib = f0.y, ip1 = f0.z, isl = f0.w, ii0 = 0, iq0 = f0.y, irun = 0;
   bool ifirst = true, idone = false;
-  auto issue_next = [&](Batch &bt) {
-    issue(iu, ib, ip1, ii0, iq0, bt);              // weight-0 rows once the worker is done
+  auto issue_next = [&](Batch &bt, bool kv) {
+    issue(iu, ib, ip1, ii0, iq0, bt, kv);          // weight-0 rows once the worker is done
     bt.unit = iu;
     bt.slot = isl;
     bt.run = irun;
@@ -498,8 +514,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     if (threadIdx.x < G) m2v = a.m_hat[(int64_t)b2 * Hq + g2 * G + threadIdx.x];
   }
   load_q(f0.x);
-  Batch A, B;
-  issue_next(A);
+  issue_next(A, false);                            // its K/V rows are already on the way
   if (staged) {                                    // visible after the first run's barrier
 #pragma unroll
     for (int k = 0; k < Q2N; ++k) {
@@ -524,7 +539,7 @@ __global__ __launch_bounds__(AT_NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         load_q(cur.unit);
       reset();
     }
-    issue_next(nxt);
+    issue_next(nxt, true);
     __builtin_amdgcn_sched_barrier(0);             // keep the loads ahead of the reduction
     consume(cur);
     if (cur.last) epilogue(cur.slot);

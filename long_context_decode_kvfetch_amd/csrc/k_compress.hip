@@ -225,24 +225,32 @@ __global__ __launch_bounds__(256) void k_gather_pivots(GatherArgs a) {
   const int g = unit % a.t.Hkv;
   const int cnt = min(a.piv_count[unit], a.cap);
   const int p0 = blockIdx.x * GATHER_ROWS;
-  if (p0 >= cnt) return;
+  // rows [cnt, whole chunks) of the head's last chunk are written as zeros: the pivot
+  // attention may load them (with weight 0) before it knows where the head ends
+  const int cntp = (cnt + PIVOT_CHUNK - 1) / PIVOT_CHUNK * PIVOT_CHUNK;
+  if (p0 >= cntp) return;
   const int4 hdr = a.sched[2 * a.workers];
   const int64_t NC = hdr.x, P = hdr.y;
   if (NC <= 0 || P <= 0) return;
   const int64_t c_u = a.runs[unit].z;
   const int per_row = a.row_bytes / 16;                // 16-byte pieces per row
   const int64_t src_row0 = tok_base(a.t, b, g);
-  const int nrow = min(GATHER_ROWS, cnt - p0);
+  const int nrow = min(GATHER_ROWS, cntp - p0);
   for (int e = threadIdx.x; e < nrow * per_row; e += blockDim.x) {
     const int p = p0 + e / per_row;
     const int piece = e % per_row;
-    const int64_t tok = a.piv_idx[(int64_t)unit * a.cap + p];
     const int64_t row = pivot_store_row(c_u, p, NC, P);
     if (row < 0 || row >= a.rows) continue;            // never, for a schedule of these counts
-    const int64_t so = (src_row0 + tok) * a.row_bytes + (int64_t)piece * 16;
     const int64_t dof = row * a.row_bytes + (int64_t)piece * 16;
-    *(uint4 *)(a.piv_k + dof) = *(const uint4 *)(a.K_host + so);
-    *(uint4 *)(a.piv_v + dof) = *(const uint4 *)(a.V_host + so);
+    uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = kk;
+    if (p < cnt) {
+      const int64_t tok = a.piv_idx[(int64_t)unit * a.cap + p];
+      const int64_t so = (src_row0 + tok) * a.row_bytes + (int64_t)piece * 16;
+      kk = *(const uint4 *)(a.K_host + so);
+      vv = *(const uint4 *)(a.V_host + so);
+    }
+    *(uint4 *)(a.piv_k + dof) = kk;
+    *(uint4 *)(a.piv_v + dof) = vv;
   }
 }
 

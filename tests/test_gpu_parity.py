@@ -76,6 +76,15 @@ def test_many_small_heads_pivot_runs_span_heads():
     _run(wl, label="many small heads")
 
 
+def test_ragged_16_sequences_full_size_pivots_only():
+    """The workload the pivotal-KV stream is timed on: 16 sequences with lengths uniform
+    in [8K, 64K] (32q/8kv, bf16, eta = 1/16), eps large enough that every row certifies,
+    so the estimator is the resident pivots alone, through the same persistent-worker
+    launch (768 workers, runs spanning KV heads and sequences)."""
+    wl = synth.ragged_batch(seed=0, batch=16, steps=3)
+    _run(wl, steps=(2,), eps=1e9, label="ragged-16 pivots only")
+
+
 def test_uniform_tau_no_heavy_hitters_certifies():
     """Uniform scores and no planted keys: eps_hat(L) is about 0.14 at eta = 1/16, so at
     eps = 0.2 every row certifies and nothing is fetched (the no-fetch path)."""
