@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--sweep", action="store_true",
-                   help="eta in {1/8, 1/16, 1/32} x eps in {0.02, 0.05, 0.1} over the rotated "
+                   help="eta in {1/8, 1/16, 1/32} x eps in {0.01, 0.02, 0.05, 0.1, 0.3, 0.5} over the rotated "
                         "32K layers: steps/s and host traffic per setting, one JSON line")
     p.add_argument("--pivot-only", action="store_true",
                    help="time only the resident-pivot attention at the 16-sequence batch "
@@ -212,9 +212,13 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
     return out
 
 
+EPS_GRID = (0.01, 0.02, 0.05, 0.1, 0.3, 0.5)
+
+
 def eta_eps_sweep(torch, L, K=32, W=8):
     """The 32K GQA layer-step at resident fractions eta = 1/8, 1/16, 1/32 and tolerances
-    eps = 0.02, 0.05, 0.1 (delta = 0.05): steps/s and what crosses the host link."""
+    eps = 0.01 ... 0.5 (delta = 0.05): steps/s and what crosses the host link, the
+    traffic-against-tolerance curve."""
     import copy
     import numpy as np
     from long_context_decode_kvfetch_amd import synth
@@ -232,7 +236,7 @@ def eta_eps_sweep(torch, L, K=32, W=8):
             s2.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
             sess.append(s2)
         per_layer = sess[0].qdev.shape[0]
-        for eps in (0.02, 0.05, 0.1):
+        for eps in EPS_GRID:
             def run(i):
                 s2 = sess[i % L]
                 s2.step(s2.qdev[(i // L) % per_layer], eps=eps)
