@@ -173,11 +173,11 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
       }
     }
   };
-  uint4 cur[SB * PPL], nxt[SB * PPL];
+  // two batch buffers alternate; the batch loop is unrolled so each buffer keeps its
+  // registers (a copy from the buffer in flight would wait for its loads)
+  uint4 bufA[SB * PPL], bufB[SB * PPL];
   double run_max = -INFINITY;               // max of this lane's scores of row rsel
-  load_batch(0, cur);
-  for (int bi = 0; bi < NB; ++bi) {
-    if (bi + 1 < NB) load_batch(bi + 1, nxt);
+  auto compute = [&](int bi, const uint4 *cur) {
 #pragma unroll
     for (int k = 0; k < SB; ++k) {
       double acc[NG4 * 4];
@@ -217,8 +217,12 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
         if (NG4 == 1) run_max = fmax(run_max, sv);
       }
     }
+  };
+  load_batch(0, bufA);
 #pragma unroll
-    for (int k = 0; k < SB * PPL; ++k) cur[k] = nxt[k];
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi + 1 < NB) load_batch(bi + 1, (bi & 1) ? bufA : bufB);
+    compute(bi, (bi & 1) ? bufB : bufA);
   }
   __builtin_amdgcn_wave_barrier();
 
