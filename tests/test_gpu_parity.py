@@ -151,6 +151,22 @@ def test_long_context_131k_eta_1_32():
          label="131k")
 
 
+def test_long_context_keys_planted_on_non_resident_tokens():
+    """The long-context stress workload at full shape (n = 131072, 8 KV heads, eta = 1/32):
+    2048 keys per KV head get the heavy-hitter direction on tokens the sampler did not keep
+    (the resident mask comes from the oracle's PoissonComp, which the GPU reproduces bit for
+    bit), so most of the attention mass sits on host-only tokens; eps = 0.3."""
+    wl = synth.long_context(seed=0, n=131072, steps=1, eps=0.3)
+    resident = np.stack([c.resident for c in oracle_compress(wl)[0]])
+    synth.plant_adversarial(wl, resident, 2048)
+    _run(wl, label="131k planted")
+
+
+def test_philox_layer_word():
+    """A later layer of a multi-layer decode (layer word 35 of the Philox counter)."""
+    _run(synth.gqa_layer(seed=3, n=8192, steps=1, layer=35), label="layer 35")
+
+
 def test_prefetch_and_workspace_history_do_not_change_results():
     """Three steps on one layer with the host-row prefetch on, off, and on with a
     workspace that starts out as random bytes: every output is bit-identical (the
