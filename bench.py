@@ -14,7 +14,7 @@ steps must.  Consecutive steps visit different layers (8 independently generated
 layers, each with its own cache and queries) so that the working set of a step is not
 served from the previous step's Infinity Cache lines.
 
-Prints ONE JSON line.  --gpus N with N > 1 exits with a message: this build measures
+Prints ONE JSON line.  --gpus N with N > 1 exits with a message: the benchmark measures
 one GPU.
 """
 from __future__ import annotations
