@@ -223,11 +223,13 @@ static hipError_t launch_attend_t(const AttendArgs &a, int units, hipStream_t st
 // reduced, the loads of the next are in flight, also across the end of a run (the
 // worker's rows of one KV head), whose partial goes to the slot the schedule gives it.
 // An issue cursor walks the runs one batch ahead of the reduction; each batch carries
-// its run's head, slot and first/last flags.  The query rows of the first run are
-// loaded before the first rows, those of the second run (named in the schedule) are
-// staged in LDS at the start, so a run change does not wait behind rows in flight.  One row group per batch (a quarter of
-// a 32-row chunk per workgroup): on MI355X more rows in flight per wave (two or four
-// row groups, or three batches in the ring) made the stream slower, not faster.  The
+// its run's head, slot and first/last flags.  The worker's first chunk is stored as
+// block w, so its first batch is loaded before the schedule is read.  The query rows of
+// the first run are loaded before the first rows' coefficients, those of the second run
+// (named in the schedule) are staged in LDS at the start, so a run change does not wait
+// behind rows in flight.  One row group per batch (a quarter of a 32-row chunk per
+// workgroup): on MI355X more rows in flight per wave (two or four row groups, three
+// batches in the ring, or four workers per CU) made the stream slower, not faster.  The
 // K/V rows are read once per step, so they are loaded non-temporally (streaming cache
 // policy): 30.7 -> 28.2 us on the 16-sequence batch.
 //
