@@ -162,6 +162,21 @@ def test_long_context_keys_planted_on_non_resident_tokens():
     _run(wl, label="131k planted")
 
 
+def test_tau_exactly_zero_on_part_of_the_cache():
+    """Scores that are exactly 0 on about 30% of the tokens: those get r = 0, are never
+    drawn and stay in L with lambda = 0 (pure bias, fetch candidates)."""
+    wl = synth.gqa_layer(seed=21, n=8192, steps=1, hkv=2)
+    tau = wl.seqs[0].tau
+    tau[np.random.default_rng(99).random(tau.shape) < 0.3] = 0.0
+    _run(wl, label="tau zeros")
+
+
+def test_maximum_sequence_length():
+    """n = 2^20 tokens, the longest sequence the library accepts (token ids fill the 20
+    bits of a host-row list entry), one KV head of four query rows."""
+    _run(synth.gqa_layer(seed=5, n=1 << 20, steps=1, hkv=1, eta=1.0 / 32, eps=0.1), label="n=2^20")
+
+
 def test_philox_layer_word():
     """A later layer of a multi-layer decode (layer word 35 of the Philox counter)."""
     _run(synth.gqa_layer(seed=3, n=8192, steps=1, layer=35), label="layer 35")
