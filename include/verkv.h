@@ -93,11 +93,15 @@ typedef struct {
                             /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
   const void *v_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the value     */
                             /* cache verkv_refine reads (may be NULL).  With it and    */
-                            /* sketch_exact, verkv_decode_step copies value rows that  */
+                            /* sketch_exact, verkv_decode_step stages value rows that  */
                             /* the previous step on the same workspace read from the   */
-                            /* host into the workspace while the sketch and decision   */
-                            /* kernels run; verkv_refine then takes the rows it needs  */
-                            /* from there.  Results do not depend on it.               */
+                            /* host in the workspace while the decision kernel runs    */
+                            /* (rows it staged the step before are copied within the   */
+                            /* workspace, the others read from v_host); verkv_refine   */
+                            /* then takes the rows it needs from there.  Staged rows   */
+                            /* are reused only for the same v_host address and shape,  */
+                            /* so the rows of v_host must not change between the steps */
+                            /* that share a workspace.  Results do not depend on it.   */
   int32_t sketch_format;    /* VERKV_SKETCH_ROWS (0): `sketch` holds kv_dtype rows as   */
                             /* above; VERKV_SKETCH_2BIT (1): `sketch` holds 64-byte     */
                             /* rows written by verkv_quantize_sketch (needs            */
@@ -189,9 +193,10 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
  *   workspace at least verkv_decode_workspace_bytes(s, st->cap); pass the same
  *          workspace to verkv_refine for this step.  Between steps it keeps each
  *          row's B*, which the next step on it takes as the starting point of its
- *          fixed-point search, and the list of host rows the step read, which the next
- *          step prefetches (see verkv_state.v_host).  Results do not depend on either:
- *          zero-filled or foreign contents only cost time.
+ *          fixed-point search, the list of host rows the step read, which the next
+ *          step prefetches, and the rows staged for it (see verkv_state.v_host).
+ *          Results do not depend on these: zero-filled or foreign contents only cost
+ *          time (staged rows carry the identity of the cache they came from).
  * No host synchronisation and no host-memory traffic. */
 verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
                                double beta, double eps, double delta, verkv_step_out *out,

@@ -79,6 +79,12 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   const int64_t src_base = HOST ? tok_base(a.t, b, g) : (int64_t)unit * a.cap;
   const int32_t *list = HOST ? a.list + tok_base(a.t, b, g) : nullptr;
   (void)list;
+  // the staging buffer this step's prefetch wrote
+  const bool alt = HOST && a.shdr && a.shdr[4] == 1;
+  const uint8_t *stage = alt ? a.stage_alt : a.stage;
+  const int32_t *stage_tok = alt ? a.stage_tok_alt : a.stage_tok;
+  (void)stage;
+  (void)stage_tok;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
 
   // Rows go in batches of STEP * U; the loads of the next batch (and, for pivots, its
@@ -104,8 +110,8 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
           const int32_t e = list[p];
           tok = e & TOKEN_MASK;
           const int slot = (int)((uint32_t)e >> TOKEN_BITS) - 1;
-          if (slot >= 0 && a.stage_tok[(int64_t)unit * a.stage_rows + slot] == tok)
-            vsrc = a.stage + ((int64_t)unit * a.stage_rows + slot) * ROW_BYTES + slice;
+          if (slot >= 0 && slot < a.stage_rows && stage_tok[(int64_t)unit * a.stage_rows + slot] == tok)
+            vsrc = stage + ((int64_t)unit * a.stage_rows + slot) * ROW_BYTES + slice;
         }
         bt.tk[u] = tok;
         const int64_t rowi = src_base + tok;

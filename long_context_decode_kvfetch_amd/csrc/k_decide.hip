@@ -1064,6 +1064,14 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
     const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
     return lo32 | (hi32 << 32);
   };
+  // the prefetch of this step has finished (it runs before this kernel): publish which
+  // buffer it staged and for which cache, for the next step's prefetch
+  if (a.shdr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    a.shdr[3] = a.shdr[4];
+    a.shdr[1] = a.ident_ptr;
+    a.shdr[2] = a.ident_shape;
+    a.shdr[0] = STAGE_MAGIC;
+  }
   // prefetched tokens (their rank is the prefetch slot)
   const uint32_t *sbw = a.sbits ? a.sbits + word_base(a.t, b, g) : nullptr;
   auto staged_bits = [&](int gi) -> uint64_t { return sbw ? group_bits(sbw, gi) : 0ull; };

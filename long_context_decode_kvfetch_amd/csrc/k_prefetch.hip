@@ -11,15 +11,21 @@
 namespace verkv {
 
 // ------------------------------------------------------------------ host-row prefetch
-// Copies, per KV head, the value rows of the first stage_rows entries of the previous
-// step's host-row list from the pinned host cache into the workspace (zero-copy loads,
-// three rows in flight per lane group), records each slot's token, and rebuilds the
-// head's bitmask of prefetched tokens (block 0 of the head).  Entries are validated
-// (token < n), so a list left by another shape only costs useless copies.  The kernel
-// runs beside the decision kernel (one 256-thread block per CU fits next to it: no
-// LDS, at most 32 VGPRs), so it lives in a file of its own.
+// Stages, per KV head, the value rows of the first stage_rows entries of the previous
+// step's host-row list in the workspace (three rows in flight per lane group), records
+// each slot's token, and rebuilds the head's bitmask of prefetched tokens (block 0 of
+// the head).  Two staging buffers alternate: a row the previous step staged is copied
+// from the other buffer (device memory; the list entry carries its slot there), only the
+// others are read from the pinned host cache (zero-copy loads), so the host link carries
+// the rows that are new to the list.
+// The other buffer is trusted only when the staging header names this cache (its
+// device address and a hash of the shape, published by the list kernel of the previous
+// step); otherwise every row comes from the host.  Entries are validated (token < n),
+// so a list left by another shape only costs useless copies.  The kernel runs beside
+// the decision kernel (one 256-thread block per CU fits next to it: no LDS, at most 32
+// VGPRs), so it lives in a file of its own.
 constexpr int PF_NT = 256;
-constexpr int PF_GRID = 64;                // blocks per launch: at most one per CU, so each
+constexpr int PF_GRID = 256;               // blocks per launch: at most one per CU, so each
                                            // fits beside a decision-kernel workgroup
 
 template <bool BF16>
@@ -59,15 +65,31 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   }
   const int sub = tid % LPR;
   const int64_t src = tok_base(a.t, b, g);
-  uint8_t *dst = a.stage + (int64_t)unit * a.stage_rows * ROW_BYTES;
-  int32_t *dtok = a.stage_tok + (int64_t)unit * a.stage_rows;
+  // which buffer to write, and whether the other one holds rows of this cache
+  const uint64_t *h = a.shdr;
+  const bool have_old = h && h[0] == STAGE_MAGIC && h[1] == a.ident_ptr &&
+                        h[2] == a.ident_shape && h[3] <= 1;
+  const int cur = have_old ? 1 - (int)h[3] : 0;
+  if (h && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.shdr[4] = (uint64_t)cur;
+  const int64_t ubase = (int64_t)unit * a.stage_rows;
+  uint8_t *dst = (cur ? a.stage_alt : a.stage) + ubase * ROW_BYTES;
+  int32_t *dtok = (cur ? a.stage_tok_alt : a.stage_tok) + ubase;
+  const uint8_t *osrc = (cur ? a.stage : a.stage_alt) + ubase * ROW_BYTES;
+  const uint32_t *otok = reinterpret_cast<const uint32_t *>((cur ? a.stage_tok : a.stage_tok_alt) + ubase);
   // three rows per lane group in flight (named registers: an indexed array here would be
   // placed in LDS, which must stay free for the decision kernel beside this one)
+  // an entry of the previous list carries the slot its token had in the buffer the
+  // previous step staged (the other buffer now), checked against that slot's token
   auto fetch = [&](int p, uint4 &v) -> int {
     if (p >= ns) return -1;
-    const int tok = pl[p] & TOKEN_MASK;
+    const int32_t e = pl[p];
+    const int tok = e & TOKEN_MASK;
     if (tok >= n) return -1;
-    v = *(const uint4 *)(a.vrows + (src + tok) * ROW_BYTES + sub * 16);
+    const int j = (int)((uint32_t)e >> TOKEN_BITS) - 1;
+    if (have_old && j >= 0 && j < a.stage_rows && otok[j] == (uint32_t)tok)
+      v = *(const uint4 *)(osrc + (int64_t)j * ROW_BYTES + sub * 16);
+    else
+      v = *(const uint4 *)(a.vrows + (src + tok) * ROW_BYTES + sub * 16);
     return tok;
   };
   auto put = [&](int p, int tok, const uint4 &v) {

@@ -127,6 +127,8 @@ struct UnionArgs {
   int32_t coef_pass;         // 0: fetch lists (grid y = 1); 1: pivot coefficients
   const double *params;      // coefficient pass: params[0] = kappa of the step (device)
   const uint32_t *sbits;     // lists: [B][Hkv][W] prefetched tokens, or null
+  uint64_t *shdr;            // lists: staging header to publish (null without a prefetch)
+  uint64_t ident_ptr, ident_shape;
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
   // coefficient pass: the work schedule of the pivot attention (one extra workgroup)
   int4 *piv_sched;           // [2 PIVOT_WORKERS + 1] per worker: first run, chunks after it
@@ -141,8 +143,13 @@ struct PrefetchArgs {
   const int32_t *prev_list;  // [B][Hkv][n] entries of the previous list (token | slot << 20)
   const int32_t *prev_count; // [B][Hkv]
   const uint8_t *vrows;      // host value cache (device view) [B][Hkv][n][128]
-  uint8_t *stage;            // [B*Hkv][stage_rows][128] kv dtype
+  uint8_t *stage;            // [B*Hkv][stage_rows][128] kv dtype: staging buffer 0
   int32_t *stage_tok;        // [B*Hkv][stage_rows] token of each slot, -1 if none
+  uint8_t *stage_alt;        // staging buffer 1 (the buffers alternate from step to step)
+  int32_t *stage_tok_alt;
+  uint64_t *shdr;            // staging header (STAGE_HDR_WORDS), see k_prefetch
+  uint64_t ident_ptr;        // identity of the cache the staged rows come from: the host
+  uint64_t ident_shape;      //   value cache's device address and a hash of the shape
   uint32_t *sbits;           // [B][Hkv][W] bit per prefetched token
   int32_t stage_rows;
 };
@@ -166,6 +173,9 @@ struct AttendArgs {
   const double *cscale;
   const uint8_t *stage;      // host source: prefetched value rows [B*Hkv][stage_rows][128]
   const int32_t *stage_tok;  //   and their tokens (a list entry's slot is checked against it)
+  const uint8_t *stage_alt;  //   the second staging buffer and its tokens; shdr names the
+  const int32_t *stage_tok_alt;  // buffer this step's prefetch wrote (null: buffer 0)
+  const uint64_t *shdr;
   int32_t stage_rows;
 };
 
@@ -195,7 +205,11 @@ constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
 constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot + 1) << 20
 constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
 constexpr int STAGE_SLOTS_MAX = 4095;    // slot + 1 fits the 12 bits above the token
-constexpr int STAGE_ROWS_TOTAL = 16384;  // prefetched rows per call, over all KV heads
+constexpr int STAGE_ROWS_TOTAL = 32768;  // prefetched rows per call, over all KV heads
+// Staging header words: [0] magic, [1] [2] identity of the staged rows' cache, [3] the
+// buffer the last published step staged, [4] the buffer this step's prefetch writes.
+constexpr int STAGE_HDR_WORDS = 8;
+constexpr uint64_t STAGE_MAGIC = 0x7665726b76535447ull;
 constexpr int SKETCH2_ROW_BYTES = 64;   // a 2-bit sketch row: 32 B of codes, 8 float32
 constexpr int PIVOT_CHUNK = 32;   // pivot rows per schedule chunk (whole row batches)
 constexpr int PIVOT_WORKERS = 768;  // persistent pivot-attention workgroups (3 per CU)

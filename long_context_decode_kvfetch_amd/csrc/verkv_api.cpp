@@ -30,6 +30,18 @@ verkv_status hip_fail(hipError_t e, const char *where) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// FNV-1a over the shape of a layer: with the host cache's address it names the rows a
+// workspace's staging buffers hold
+uint64_t shape_ident(const SeqTable &t, bool bf16) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](uint64_t v) {
+    for (int k = 0; k < 8; ++k) { h ^= (v >> (8 * k)) & 0xFF; h *= 1099511628211ull; }
+  };
+  mix((uint64_t)t.B); mix((uint64_t)t.Hkv); mix((uint64_t)t.G); mix(bf16 ? 1 : 0);
+  for (int b = 0; b < t.B; ++b) mix((uint64_t)t.s[b].n);
+  return h;
+}
+
 // Build the per-sequence offset table and validate the shape.
 verkv_status make_table(const verkv_shape *s, SeqTable &t) {
   if (!s || !s->seq_len) return VERKV_EINVAL;
@@ -109,7 +121,7 @@ int team_size(int rows, int max_n) {
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
-  size_t stage, stage_tok, sbits, h2dc, psched, pruns;
+  size_t stage, stage_tok, stage_alt, stage_tok_alt, shdr, sbits, h2dc, psched, pruns;
   int srows;
   size_t total;
   int nsp, nsh, team;      // nsp: pivot partial slots
@@ -151,6 +163,9 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.srows = std::min(STAGE_SLOTS_MAX, STAGE_ROWS_TOTAL / std::max(1, units));
   w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * 4);
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
+  w.stage_alt = off; off = align_up(off + (size_t)units * w.srows * D * 4);
+  w.stage_tok_alt = off; off = align_up(off + 4 * (size_t)units * w.srows);
+  w.shdr = off;      off = align_up(off + 8 * (size_t)STAGE_HDR_WORDS);
   w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
   w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
@@ -490,8 +505,8 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
   std::unique_lock<std::mutex> lk(sd->mu);
   const bool prefetch = st->v_host && st->sketch_exact && L.srows > 0;
+  const void *Vd = nullptr;
   if (prefetch) {
-    const void *Vd = nullptr;
     if ((rc = device_view(st->v_host, &Vd)) != VERKV_OK) return rc;
     HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
     HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
@@ -502,6 +517,11 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
     pa.vrows = static_cast<const uint8_t *>(Vd);
     pa.stage = ws + L.stage;
     pa.stage_tok = reinterpret_cast<int32_t *>(ws + L.stage_tok);
+    pa.stage_alt = ws + L.stage_alt;
+    pa.stage_tok_alt = reinterpret_cast<int32_t *>(ws + L.stage_tok_alt);
+    pa.shdr = reinterpret_cast<uint64_t *>(ws + L.shdr);
+    pa.ident_ptr = reinterpret_cast<uint64_t>(Vd);
+    pa.ident_shape = shape_ident(t, bf16);
     pa.sbits = reinterpret_cast<uint32_t *>(ws + L.sbits);
     pa.stage_rows = L.srows;
     {
@@ -576,6 +596,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   un.params = nullptr;
   un.coef_pass = 0;
   un.sbits = prefetch ? reinterpret_cast<const uint32_t *>(ws + L.sbits) : nullptr;
+  un.shdr = prefetch ? reinterpret_cast<uint64_t *>(ws + L.shdr) : nullptr;
+  un.ident_ptr = reinterpret_cast<uint64_t>(Vd);
+  un.ident_shape = shape_ident(t, bf16);
   un.h2d_count_ws = reinterpret_cast<int32_t *>(ws + L.h2dc);
   un.piv_sched = nullptr;
   un.piv_runs = nullptr;
@@ -638,6 +661,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   at.cscale = reinterpret_cast<const double *>(ws + L.cscale);
   at.stage = ws + L.stage;
   at.stage_tok = reinterpret_cast<const int32_t *>(ws + L.stage_tok);
+  at.stage_alt = ws + L.stage_alt;
+  at.stage_tok_alt = reinterpret_cast<const int32_t *>(ws + L.stage_tok_alt);
+  at.shdr = reinterpret_cast<const uint64_t *>(ws + L.shdr);
   at.stage_rows = L.srows;
   {
     Timed tm(K_HOST, stream);
@@ -668,6 +694,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   un.coef = reinterpret_cast<float *>(ws + L.coef);
   un.coef_pass = 1;
   un.sbits = nullptr;
+  un.shdr = nullptr;
+  un.ident_ptr = 0;
+  un.ident_shape = 0;
   un.h2d_count_ws = nullptr;
   un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
   un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
@@ -696,6 +725,9 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   pv.cscale = nullptr;
   pv.stage = nullptr;
   pv.stage_tok = nullptr;
+  pv.stage_alt = nullptr;
+  pv.stage_tok_alt = nullptr;
+  pv.shdr = nullptr;
   pv.stage_rows = 0;
   {
     Timed tm(K_PIVOT, sd->s);
