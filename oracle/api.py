@@ -2,6 +2,7 @@
 Test infrastructure for the oracle only.
 
 compress_sequence  PoissonComp for every KV head of one sequence (prefill)
+append_sequence    one decode-time token appended to every KV head (growing cache)
 decode_sequence    KVFetch steps 1-5 for every query row of one sequence
 
 A sequence's KV head g uses Philox counter (token, g, layer, stream) with the
@@ -18,6 +19,13 @@ def compress_sequence(tau, n_sink, n_local, eta, layer, stream, seed):
     """tau: [Hkv][n] float32 -> list of poissoncomp.Compressed, one per KV head."""
     return [poissoncomp.compress_head(tau[g], n_sink, n_local, eta, g, layer, stream, seed)
             for g in range(tau.shape[0])]
+
+
+def append_sequence(comp, tau_new, n_sink, n_local, layer, stream, seed):
+    """One decode-time token appended to every KV head of one sequence: comp is the list
+    of poissoncomp.Compressed, tau_new [Hkv] the new token's scores."""
+    return [poissoncomp.append_token(comp[g], float(tau_new[g]), n_sink, n_local, g, layer,
+                                     stream, seed) for g in range(len(comp))]
 
 
 def decode_sequence(K, V, comp, q_rows, group, kappa, eps, delta, K_sketch=None):

@@ -47,6 +47,8 @@ class Compressed:
     piv_idx: np.ndarray    # ascending int64 token ids of H union S
     m_star: int            # saturated non-forced tokens (-1: none qualified)
     c: float               # water level (0 when unused)
+    rule: str = "water"    # how the prefill set r on non-forced tokens (see level_rule)
+    tau: np.ndarray = None # [n] float32 scores (kept for tokens leaving the local window)
 
 
 def forced_mask(n: int, n_sink: int, n_local: int) -> np.ndarray:
@@ -123,8 +125,72 @@ def draw(r: np.ndarray, kv_head: int, layer: int, stream: int, seed: int) -> np.
     return resident
 
 
+def level_rule(n, n_sink, n_local, eta, m_star):
+    """Which branch of the water-filling set r on the non-forced tokens:
+    "all" (the budget covers them all: r = 1), "none" (no budget left: r = 0),
+    "saturated" (no water level qualified: r = 1 where tau > 0, else 0) or "water"
+    (r = min(1, c Q) with the level c)."""
+    forced = int(forced_mask(n, n_sink, n_local).sum())
+    free = n - forced
+    b_rem = float(eta) * float(n) - float(forced)
+    if free == 0 or b_rem >= float(free):
+        return "all"
+    if b_rem == 0.0:
+        return "none"
+    return "saturated" if m_star < 0 else "water"
+
+
 def compress_head(tau, n_sink, n_local, eta, kv_head, layer, stream, seed) -> Compressed:
     r, m_star, c = inclusion_probabilities(tau, n_sink, n_local, eta)
     resident = draw(r, kv_head, layer, stream, seed)
     return Compressed(r=r, resident=resident, piv_idx=np.flatnonzero(resident),
-                      m_star=m_star, c=c)
+                      m_star=m_star, c=c, rule=level_rule(len(r), n_sink, n_local, eta, m_star),
+                      tau=np.asarray(tau, dtype=np.float32).copy())
+
+
+# ------------------------------------------------------------------ a growing cache
+# The pages compress the cache once, at prefill, and say nothing about the tokens decode
+# appends.  Reading taken here (parity unpinned against the pages; pinned by the
+# properties in tests/test_oracle_append.py):
+#   * the appended token n joins the local window: r_n = 1, resident;
+#   * the token leaving the window, t = n - n_local, becomes an ordinary token unless it
+#     is a sink token: it gets the prefill's rule with the prefill's water level,
+#     r_t = min(1, fl(c Q_t)) (or 1 / 0 / 1-if-tau>0 for the "all" / "none" /
+#     "saturated" branches), and if 0 < r_t < 1 it is drawn with the Philox counter
+#     (t, kv_head, layer, stream) it would have had at prefill;
+#   * without a local window (n_local = 0) the appended token itself is the one that
+#     gets the rule and the draw;
+#   * the level is not re-solved, so the resident budget grows by r_t per token.
+def departing_probability(comp: Compressed, tau_t: float) -> float:
+    """r of a token that leaves the forced set, under the prefill's rule."""
+    q = quantize(np.array([tau_t], dtype=np.float32))[0]
+    if comp.rule == "all":
+        return 1.0
+    if comp.rule == "none":
+        return 0.0
+    if comp.rule == "saturated":
+        return 1.0 if q > 0 else 0.0
+    x = comp.c * float(q)
+    return 1.0 if x >= 1.0 else x
+
+
+def append_token(comp: Compressed, tau_new: float, n_sink: int, n_local: int,
+                 kv_head: int, layer: int, stream: int, seed: int) -> Compressed:
+    """The compressed state of one KV head after token n = len(comp.r) is appended."""
+    n = len(comp.r)
+    r = np.concatenate([comp.r, [1.0]])
+    resident = np.concatenate([comp.resident, [True]])
+    tau = np.concatenate([comp.tau, np.array([tau_new], dtype=np.float32)])
+    t = n - n_local                       # the token leaving the window (n itself when n_local = 0)
+    if n_local >= 0 and n_sink <= t <= n:
+        rt = departing_probability(comp, float(tau[t]))
+        r[t] = rt
+        if rt >= 1.0:
+            resident[t] = True
+        elif rt > 0.0:
+            u = philox.uniform53(np.array([t]), kv_head, layer, stream, seed)
+            resident[t] = bool(u[0] < rt)
+        else:
+            resident[t] = False
+    return Compressed(r=r, resident=resident, piv_idx=np.flatnonzero(resident),
+                      m_star=comp.m_star, c=comp.c, rule=comp.rule, tau=tau)
