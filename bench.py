@@ -54,6 +54,10 @@ def parse():
     p.add_argument("--pivot-only", action="store_true",
                    help="time only the resident-pivot attention at the 16-sequence batch "
                         "and print its figures as one JSON line")
+    p.add_argument("--no-decode36", action="store_true",
+                   help="skip the 36-layer decode leg of the default run")
+    p.add_argument("--no-long-context", action="store_true",
+                   help="skip the 131072-token stress leg of the default run")
     p.add_argument("--decode36", action="store_true",
                    help="36 independent 32K layers decoded one after another per token "
                         "(eta=1/16, eps=0.05): tokens/s and host bytes per token, one JSON line")
@@ -553,6 +557,14 @@ def main():
     if not args.no_pivot_batch:
         log("[bench] pivotal stream at the 16-sequence batch")
         piv = pivotal_stream(torch)
+    dec36 = None
+    if not args.no_decode36:
+        log("[bench] 36-layer decode")
+        dec36 = decode_36_layers(torch)
+    longc = None
+    if not args.no_long_context:
+        log("[bench] long-context stress")
+        longc = long_context_stress(torch)
 
     out = {
         "metric": "certified decode steps/s at 32K ctx, eta=1/16; achieved HBM GB/s vs peak",
@@ -575,6 +587,8 @@ def main():
         "roofline": roof,
         "pivotal_stream": piv,
         "sketch_2bit": sk2,
+        "decode_36_layers": dec36,
+        "long_context": longc,
         "cpu_baseline": None,
         "step_stats": {"rows_certified_without_fetch": cert / rows,
                        "fetched_fraction_of_cache": fetched / n_tok,
