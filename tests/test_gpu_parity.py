@@ -218,6 +218,35 @@ def test_prefetch_and_workspace_history_do_not_change_results():
                 assert np.array_equal(runs[0][st][k], other[st][k]), (label, st, k)
 
 
+def test_staged_rows_of_another_cache_are_not_reused():
+    """One workspace used for two layers in turn (two host caches of the same shape):
+    the staging header names the cache its rows came from, so a step of layer B on a
+    workspace that layer A filled reads no row of A's cache; every output equals that of
+    layer B on a workspace of its own, bit for bit."""
+    from long_context_decode_kvfetch_amd import verkv
+    keys = ("o", "lse", "n_hat", "d_hat", "eps_after", "fetch_count", "h2d_count")
+    wa = synth.gqa_layer(seed=3, n=8192, steps=3, hkv=2, layer=0)
+    wb = synth.gqa_layer(seed=3, n=8192, steps=3, hkv=2, layer=1)
+    sa, sb, ref = _session(wa), _session(wb), _session(wb)
+    for s_ in (sa, sb, ref):
+        s_.compress()
+    assert sa.dws.numel() == sb.dws.numel()
+    sb.dws = sa.dws                                   # B borrows A's workspace
+    expect = []
+    for st in range(3):
+        ref.step(ref.queries(st))
+        r = ref.results_numpy()
+        expect.append({k: np.array(r[k]) for k in keys})
+    for st in range(3):
+        say(f"[parity] shared workspace: step {st}")
+        sa.step(sa.queries(st))                       # A stages rows of its own cache
+        sb.step(sb.queries(st))                       # then B runs on the same workspace
+        verkv.check(sb.shape, sb.cap, sb.dws)
+        got = sb.results_numpy()
+        for k in keys:
+            assert np.array_equal(np.array(got[k]), expect[st][k]), (st, k)
+
+
 # ------------------------------------------------------------------ the 2-bit sketch
 def _sketch2_of(K):
     """The oracle's 2-bit sketch of key rows exactly as the device holds them."""
