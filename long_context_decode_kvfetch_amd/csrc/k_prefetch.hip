@@ -13,8 +13,9 @@ namespace verkv {
 // ------------------------------------------------------------------ host-row prefetch
 // Stages, per KV head, the value rows of the first stage_rows entries of the previous
 // step's host-row list in the workspace (three rows in flight per lane group), records
-// each slot's token, and rebuilds the head's bitmask of prefetched tokens (block 0 of
-// the head).  Two staging buffers alternate: a row the previous step staged is copied
+// each slot's token, and sets the token's bit in the head's bitmask of prefetched
+// tokens (cleared by the sketch kernel of the same step; an OR per staged row, so the
+// mask does not depend on the order the rows are staged in).  Two staging buffers alternate: a row the previous step staged is copied
 // from the other buffer (device memory; the list entry carries its slot there), only the
 // others are read from the pinned host cache (zero-copy loads), so the host link carries
 // the rows that are new to the list.
@@ -42,27 +43,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   const int cnt = min(max(a.prev_count[unit], 0), n);
   const int ns = min(cnt, a.stage_rows);
   const int32_t *pl = a.prev_list + tok_base(a.t, b, g);
-  if (blockIdx.x == 0) {
-    uint32_t *sb = a.sbits + word_base(a.t, b, g);
-    const int W = words_of(n);
-    for (int w = tid; w < W; w += PF_NT) sb[w] = 0u;
-    __syncthreads();
-    // the list is ascending, so the tokens of one bitmask word are consecutive entries:
-    // the first entry of each word gathers the word's bits and stores it (no atomics)
-    for (int p = tid; p < ns; p += PF_NT) {
-      const int tok = pl[p] & TOKEN_MASK;
-      if (tok >= n) continue;
-      const int w = tok >> 5;
-      if (p > 0 && ((pl[p - 1] & TOKEN_MASK) >> 5) == w) continue;
-      uint32_t bits = 0u;
-      for (int q = p; q < ns && q < p + 32; ++q) {
-        const int t2 = pl[q] & TOKEN_MASK;
-        if (t2 >= n || (t2 >> 5) != w) break;
-        bits |= 1u << (t2 & 31);
-      }
-      sb[w] = bits;
-    }
-  }
+  uint32_t *sb = a.sbits + word_base(a.t, b, g);
   const int sub = tid % LPR;
   const int64_t src = tok_base(a.t, b, g);
   // which buffer to write, and whether the other one holds rows of this cache
@@ -95,7 +76,10 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   auto put = [&](int p, int tok, const uint4 &v) {
     if (p >= a.stage_rows) return;
     if (tok >= 0) *(uint4 *)(dst + (int64_t)p * ROW_BYTES + sub * 16) = v;
-    if (sub == 0) dtok[p] = tok;
+    if (sub == 0) {
+      dtok[p] = tok;
+      if (tok >= 0) atomicOr(sb + (tok >> 5), 1u << (tok & 31));
+    }
   };
   for (int p0 = blockIdx.x * RPI * 3; p0 < a.stage_rows; p0 += gridDim.x * RPI * 3) {
     const int pa = p0 + tid / LPR, pb = pa + RPI, pc = pb + RPI;

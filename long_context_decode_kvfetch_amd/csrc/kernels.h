@@ -61,6 +61,7 @@ struct SketchArgs {
   const double *r;            // [B][Hkv][n] inclusion probabilities
   double *cf0;                // [B][Hq][nchunks]  sum over L of wc (1 - r): f(0) per chunk
   uint32_t *fbits;            // [B][Hkv][W]  cleared here
+  uint32_t *sbits;            // [B][Hkv][W]  prefetched-token bits, cleared here (or null)
   uint32_t *wcount;           // [B][Hq] decision-kernel window counters, cleared here
   double *xseq;               // [B][Hq][xseq_row] team exchange sequence words, cleared here
   int32_t xseq_row;

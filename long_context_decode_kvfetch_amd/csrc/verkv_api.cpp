@@ -488,6 +488,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.r = st->r;
   sk.cf0 = reinterpret_cast<double *>(ws + L.cf0);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
+  // the prefetch below (when it runs) sets the bits of the rows it stages
+  sk.sbits = st->v_host && st->sketch_exact && L.srows > 0
+                 ? reinterpret_cast<uint32_t *>(ws + L.sbits) : nullptr;
   sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
   sk.xseq = reinterpret_cast<double *>(ws + L.xseq);
   sk.xseq_row = 2 * L.team;
@@ -504,7 +507,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   Side *sd = nullptr;
   if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
   std::unique_lock<std::mutex> lk(sd->mu);
-  const bool prefetch = st->v_host && st->sketch_exact && L.srows > 0;
+  const bool prefetch = sk.sbits != nullptr;   // host cache, exact sketch, staging rows
   const void *Vd = nullptr;
   if (prefetch) {
     if ((rc = device_view(st->v_host, &Vd)) != VERKV_OK) return rc;
