@@ -312,3 +312,67 @@ def decode_kv_head(qs, K, Vv, r, resident, kappa, eps, delta, K_sketch=None):
     out["fetch"] = F
     out["h2d"] = F[~resident[F]]
     return out
+
+
+# ----------------------------------------------------------------------------- reading R2
+# Eq. (9) writes eps_hat(L minus {i}) without saying whether lambda follows the set.  The
+# decision path above freezes lambda at its value for the full L (reading R1, the one the
+# library implements).  The variant below re-solves the bias of Definition 2, and so
+# lambda, on every candidate set of step 4 (reading R2).  Taken here for it:
+#   * the order of step 3 is R1's (g_i of eq. 9 with lambda frozen): re-solving for every
+#     single removal would cost |L| solves per row for an ordering only;
+#   * the cut of step 4 evaluates each candidate L_g[k:] with lambda solved on that set
+#     alone, and k* is the least such k, found by a scan from k = 0 (with re-solved lambda
+#     eps_hat need not fall monotonically in k, so no bisection);
+#   * the kept set L' = L_g[k*:] keeps the lambda solved on it.
+# Lemma 1 still certifies the result: lambda(L') depends on the sketch weights and r, not
+# on the draws Z.  Parity unpinned against the pages (they give no example); pinned by
+# tests/test_oracle_resolved.py (reductions to R1 where lambda does not depend on the
+# bias, brute force with an independent bisection solve on small sets).
+def eps_hat_resolved(w, r, kappa, D, l):
+    """eps_hat of one token set with the bias and lambda solved on that set alone."""
+    w = np.asarray(w, np.float64)
+    r = np.asarray(r, np.float64)
+    if w.size == 0:
+        return 0.0
+    B = solve_beta(w, r, kappa)
+    lam = clip_lambda(w, r, B, kappa)
+    return eps_hat(*token_terms(w, r, lam), D, l)
+
+
+def select_fetch_resolved(tokens, w, r, kappa, beta_i, V_i, b_i, D, l, eps):
+    """Steps 3-4 under reading R2: (F_h, k*, g) with the order of eq. (9) and k* the least
+    k with eps_hat_resolved(L_g[k:]) < eps."""
+    g = fetch_priority(beta_i, V_i, b_i, D, l)
+    order = np.lexsort((tokens, -g))
+    for k in range(order.size + 1):
+        rest = order[k:]
+        if eps_hat_resolved(w[rest], r[rest], kappa, D, l) < eps:
+            return np.sort(tokens[order[:k]]), k, g
+    raise AssertionError("eps_hat of the empty set is 0, below any eps > 0")
+
+
+def decide_head_resolved(q, K_sketch, r, kappa, eps, delta) -> HeadDecision:
+    """KVFetch steps 1-4 for one query head under reading R2.  Certification (k* = 0) is
+    the same test as R1's; a fetching row gets lambda solved on its kept set L', and its
+    beta_star, terms and L fields then describe L' (the set its certificate covers)."""
+    w, m_hat, D = sketch_weights(q, K_sketch)
+    L = np.flatnonzero(r < 1.0)
+    wL, rL = w[L], r[L]
+    B = solve_beta(wL, rL, kappa)
+    lamL = clip_lambda(wL, rL, B, kappa)
+    beta_i, V_i, b_i = token_terms(wL, rL, lamL)
+    l = log_term(delta)
+    e = eps_hat(beta_i, V_i, b_i, D, l)
+    lam = np.ones(r.shape[0])
+    lam[L] = lamL
+    if e < eps:
+        return HeadDecision(m_hat, D, B, e, True, 0, np.zeros(0, np.int64), lam,
+                            (beta_i, V_i, b_i), L)
+    F, kstar, _ = select_fetch_resolved(L, wL, rL, kappa, beta_i, V_i, b_i, D, l, eps)
+    keep = np.ones(L.size, dtype=bool)
+    keep[np.searchsorted(L, F)] = False
+    Bk = solve_beta(wL[keep], rL[keep], kappa)
+    lam[L[keep]] = clip_lambda(wL[keep], rL[keep], Bk, kappa)
+    kept_terms = token_terms(wL[keep], rL[keep], lam[L[keep]])
+    return HeadDecision(m_hat, D, Bk, e, False, kstar, F, lam, kept_terms, L[keep])

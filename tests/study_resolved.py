@@ -1,0 +1,78 @@
+"""Fetch sizes under the two readings of eq. (9)-(10): lambda frozen at the full L (R1,
+what the library implements) against lambda re-solved on each candidate set (R2, the
+oracle's variant).  Not a test: run it as a script to print the comparison.
+
+    python tests/study_resolved.py
+
+Inputs: the seeded GQA layer generator (bf16 keys with 1% planted heavy hitters per KV
+head, tau ~ Beta(0.3, 3), H = 4 sink + 128 local, q = u + N(0, 0.5 I)) at n = 4096,
+2 KV heads x 4 query rows, PoissonComp at eta = 1/16 with the oracle, the keys as the
+sketch.  R2's scan costs one fixed-point solve per candidate k, so n stays small."""
+import os
+import sys
+import time
+
+import numpy as np
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+from long_context_decode_kvfetch_amd import synth  # noqa: E402
+from oracle import kvfetch, poissoncomp  # noqa: E402
+
+
+def _rises(q, K, r, kappa, delta, stride=32):
+    """1 if R2's eps_hat over L_g[k:] goes up anywhere between samples k = 0, stride, ...;
+    the order is that of eq. (9) with lambda frozen."""
+    w, _, D = kvfetch.sketch_weights(q, K)
+    L = np.flatnonzero(r < 1.0)
+    wL, rL = w[L], r[L]
+    B = kvfetch.solve_beta(wL, rL, kappa)
+    terms = kvfetch.token_terms(wL, rL, kvfetch.clip_lambda(wL, rL, B, kappa))
+    l = kvfetch.log_term(delta)
+    g = kvfetch.fetch_priority(*terms, D, l)
+    order = np.lexsort((L, -g))
+    vals = [kvfetch.eps_hat_resolved(wL[order[k:]], rL[order[k:]], kappa, D, l)
+            for k in range(0, L.size + 1, stride)]
+    return int(any(b > a for a, b in zip(vals, vals[1:])))
+
+
+def main():
+    n, hkv, group = 4096, 2, 4
+    print("| eps | seed | rows | k* R1 (sum) | k* R2 (sum) | rows with k* R2 < R1 / = / > "
+          "| union F R1 | union F R2 | rows with R2's eps_hat rising somewhere in k |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    t0 = time.time()
+    for eps in (0.05, 0.2):
+        for seed in (0, 1):
+            wl = synth.gqa_layer(seed=seed, n=n, steps=1, hkv=hkv, group=group)
+            seq = wl.seqs[0]
+            k1 = k2 = 0
+            less = same = more = 0
+            u1 = u2 = 0
+            rising = 0
+            for g in range(hkv):
+                comp = poissoncomp.compress_head(seq.tau[g], wl.n_sink, wl.n_local, wl.eta, g,
+                                                 wl.layer, 0, wl.seed)
+                K = seq.K[g].astype(np.float64)
+                F1, F2 = [], []
+                for j in range(group):
+                    q = wl.queries[0, 0, g * group + j].astype(np.float64)
+                    a = kvfetch.decide_head(q, K, comp.r, wl.kappa, eps, wl.delta)
+                    b = kvfetch.decide_head_resolved(q, K, comp.r, wl.kappa, eps, wl.delta)
+                    k1 += a.kstar
+                    k2 += b.kstar
+                    less += b.kstar < a.kstar
+                    same += b.kstar == a.kstar
+                    more += b.kstar > a.kstar
+                    F1.append(a.fetch)
+                    F2.append(b.fetch)
+                    rising += _rises(q, K, comp.r, wl.kappa, wl.delta)
+                u1 += np.unique(np.concatenate(F1)).size
+                u2 += np.unique(np.concatenate(F2)).size
+            print(f"| {eps} | {seed} | {hkv * group} | {k1} | {k2} | {less} / {same} / {more} "
+                  f"| {u1} | {u2} | {rising} |", flush=True)
+    print(f"({time.time() - t0:.0f} s)")
+
+
+if __name__ == "__main__":
+    main()
