@@ -314,12 +314,12 @@ def decode_kv_head(qs, K, Vv, r, resident, kappa, eps, delta, K_sketch=None):
     return out
 
 
-# ----------------------------------------------------------------------------- reading R2
+# ------------------------------------------------------------ re-solved lambda (variant)
 # Eq. (9) writes eps_hat(L minus {i}) without saying whether lambda follows the set.  The
-# decision path above freezes lambda at its value for the full L (reading R1, the one the
+# decision path above freezes lambda at its value for the full L (the frozen reading, the one the
 # library implements).  The variant below re-solves the bias of Definition 2, and so
-# lambda, on every candidate set of step 4 (reading R2).  Taken here for it:
-#   * the order of step 3 is R1's (g_i of eq. 9 with lambda frozen): re-solving for every
+# lambda, on every candidate set of step 4 (the re-solved reading).  Taken here for it:
+#   * the order of step 3 is the frozen one (g_i of eq. 9): re-solving for every
 #     single removal would cost |L| solves per row for an ordering only;
 #   * the cut of step 4 evaluates each candidate L_g[k:] with lambda solved on that set
 #     alone, and k* is the least such k, found by a scan from k = 0 (with re-solved lambda
@@ -327,7 +327,7 @@ def decode_kv_head(qs, K, Vv, r, resident, kappa, eps, delta, K_sketch=None):
 #   * the kept set L' = L_g[k*:] keeps the lambda solved on it.
 # Lemma 1 still certifies the result: lambda(L') depends on the sketch weights and r, not
 # on the draws Z.  Parity unpinned against the pages (they give no example); pinned by
-# tests/test_oracle_resolved.py (reductions to R1 where lambda does not depend on the
+# tests/test_oracle_resolved.py (reductions to the frozen reading where lambda ignores the
 # bias, brute force with an independent bisection solve on small sets).
 def eps_hat_resolved(w, r, kappa, D, l):
     """eps_hat of one token set with the bias and lambda solved on that set alone."""
@@ -341,7 +341,7 @@ def eps_hat_resolved(w, r, kappa, D, l):
 
 
 def select_fetch_resolved(tokens, w, r, kappa, beta_i, V_i, b_i, D, l, eps):
-    """Steps 3-4 under reading R2: (F_h, k*, g) with the order of eq. (9) and k* the least
+    """Steps 3-4, re-solved reading: (F_h, k*, g) with the order of eq. (9) and k* the least
     k with eps_hat_resolved(L_g[k:]) < eps."""
     g = fetch_priority(beta_i, V_i, b_i, D, l)
     order = np.lexsort((tokens, -g))
@@ -353,8 +353,8 @@ def select_fetch_resolved(tokens, w, r, kappa, beta_i, V_i, b_i, D, l, eps):
 
 
 def decide_head_resolved(q, K_sketch, r, kappa, eps, delta) -> HeadDecision:
-    """KVFetch steps 1-4 for one query head under reading R2.  Certification (k* = 0) is
-    the same test as R1's; a fetching row gets lambda solved on its kept set L', and its
+    """KVFetch steps 1-4 for one query head, re-solved reading.  Certification (k* = 0) is
+    the frozen reading's test; a fetching row gets lambda solved on its kept set L', and its
     beta_star, terms and L fields then describe L' (the set its certificate covers)."""
     w, m_hat, D = sketch_weights(q, K_sketch)
     L = np.flatnonzero(r < 1.0)

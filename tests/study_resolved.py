@@ -1,5 +1,5 @@
-"""Fetch sizes under the two readings of eq. (9)-(10): lambda frozen at the full L (R1,
-what the library implements) against lambda re-solved on each candidate set (R2, the
+"""Fetch sizes under the two readings of eq. (9)-(10): lambda frozen at the full L
+(what the library implements) against lambda re-solved on each candidate set (the
 oracle's variant).  Not a test: run it as a script to print the comparison.
 
     python tests/study_resolved.py
@@ -7,7 +7,7 @@ oracle's variant).  Not a test: run it as a script to print the comparison.
 Inputs: the seeded GQA layer generator (bf16 keys with 1% planted heavy hitters per KV
 head, tau ~ Beta(0.3, 3), H = 4 sink + 128 local, q = u + N(0, 0.5 I)) at n = 4096,
 2 KV heads x 4 query rows, PoissonComp at eta = 1/16 with the oracle, the keys as the
-sketch.  R2's scan costs one fixed-point solve per candidate k, so n stays small."""
+sketch.  The re-solved scan costs one fixed-point solve per candidate k, so n stays small."""
 import os
 import sys
 import time
@@ -21,7 +21,7 @@ from oracle import kvfetch, poissoncomp  # noqa: E402
 
 
 def _rises(q, K, r, kappa, delta, stride=32):
-    """1 if R2's eps_hat over L_g[k:] goes up anywhere between samples k = 0, stride, ...;
+    """1 if the re-solved eps_hat over L_g[k:] goes up anywhere between samples k = 0, stride, ...;
     the order is that of eq. (9) with lambda frozen."""
     w, _, D = kvfetch.sketch_weights(q, K)
     L = np.flatnonzero(r < 1.0)
@@ -38,8 +38,8 @@ def _rises(q, K, r, kappa, delta, stride=32):
 
 def main():
     n, hkv, group = 4096, 2, 4
-    print("| eps | seed | rows | k* R1 (sum) | k* R2 (sum) | rows with k* R2 < R1 / = / > "
-          "| union F R1 | union F R2 | rows with R2's eps_hat rising somewhere in k |")
+    print("| eps | seed | rows | k* frozen (sum) | k* re-solved (sum) | rows with k* re-solved < frozen / = / > "
+          "| union F frozen | union F re-solved | rows with re-solved eps_hat rising somewhere in k |")
     print("|---|---|---|---|---|---|---|---|---|")
     t0 = time.time()
     for eps in (0.05, 0.2):

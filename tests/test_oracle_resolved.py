@@ -1,10 +1,10 @@
-"""Pins of the oracle's reading R2 of eq. (9)-(10) (oracle/kvfetch.py: lambda re-solved on
-each candidate set of the cut).  The pages print no worked example, so the pins are
-reductions and brute force: where lambda does not depend on the bias (kappa = inf gives
-lambda = 1, kappa = 0 gives lambda = r) R2 must fetch exactly what R1 fetches; on small
-sets the least k found by the scan must match a search that solves the bias by plain
-bisection and sums eq. (7) term by term; the bias R2 keeps is the fixed point on its kept
-set, and the kept set certifies."""
+"""Pins of the oracle's re-solved reading of eq. (9)-(10) (oracle/kvfetch.py: lambda
+re-solved on each candidate set of the cut).  The pages print no worked example, so the
+pins are reductions and brute force: where lambda does not depend on the bias (kappa = inf
+gives lambda = 1, kappa = 0 gives lambda = r) it must fetch exactly what the frozen reading
+fetches; on small sets the least k found by the scan must match a search that solves the
+bias by plain bisection and sums eq. (7) term by term; the bias it keeps is the fixed point
+on its kept set, and the kept set certifies."""
 import math
 
 import numpy as np
