@@ -245,6 +245,10 @@ const char *verkv_status_str(int32_t status);
 const char *verkv_last_error(void);
 /* ABI version: 100 * major + minor. */
 int32_t verkv_version(void);
+/* Identity of this build (static storage): the hex SHA-256 that the build script takes
+ * over the library's sources, this header and the compiler flags, so a loaded library
+ * can be checked against the sources it was built from ("unknown" if built without). */
+const char *verkv_source_hash(void);
 
 #ifdef __cplusplus
 }

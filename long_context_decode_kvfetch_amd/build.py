@@ -20,10 +20,31 @@ FLAGS = [
 ]
 
 
+HEADER = os.path.join(os.path.dirname(HERE), "include", "verkv.h")
+
+
+def source_hash() -> str:
+    """SHA-256 over every file under csrc/, the public header and the compiler flags: the
+    identity of a build, compiled into the library (verkv_source_hash) so a loaded
+    libverkv.so can be checked against the sources it claims to come from."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC))
+    for name in files:
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(HEADER, "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc, *FLAGS, f'-DVERKV_SOURCE_HASH="{source_hash()}"', "-x", "hip",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -32,6 +32,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace verkv {
 
@@ -1386,14 +1387,20 @@ size_t decide_lds_bytes(int nch_max, bool slice_cache) {
 bool decide_slice_cached(int max_n, int team) { return (max_n + team - 1) / team <= LDS_TOK; }
 
 hipError_t launch_decide(DecideArgs &a, int rows, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    // allow the largest dynamic LDS this kernel asks for (chunk scales + slice cache)
-    hipError_t e = hipFuncSetAttribute((const void *)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)std::max(decide_lds_bytes(MAX_CHUNKS, false),
-                                                     decide_lds_bytes(MAX_CACHED_CHUNKS, true)));
+  // allow the largest dynamic LDS this kernel asks for (chunk scales + slice cache), once
+  // per device (the attribute belongs to the kernel as loaded on the current device)
+  constexpr int MAX_DEV = 64;
+  static std::atomic<bool> attr_set[MAX_DEV];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute((const void *)k_decide, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)std::max(decide_lds_bytes(MAX_CHUNKS, false),
+                                          decide_lds_bytes(MAX_CACHED_CHUNKS, true)));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   a.nch_max = chunks_of(a.t.max_n);
   a.lds_cache = decide_slice_cached(a.t.max_n, a.team) ? 1 : 0;

@@ -297,7 +297,12 @@ struct Timed {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 106; }
+int32_t verkv_version(void) { return 107; }
+
+#ifndef VERKV_SOURCE_HASH
+#define VERKV_SOURCE_HASH "unknown"
+#endif
+const char *verkv_source_hash(void) { return VERKV_SOURCE_HASH; }
 
 const char *verkv_status_str(int32_t s) {
   switch (s) {
@@ -457,6 +462,14 @@ static verkv_status check_step(const verkv_shape *s, const verkv_state *st, cons
   return VERKV_OK;
 }
 
+// The value cache the step's prefetch reads (exact sketch with v_host set), resolved to
+// its device view before anything is enqueued; *Vd stays null when there is no prefetch.
+static verkv_status prefetch_source(const verkv_state *st, int srows, const void **Vd) {
+  *Vd = nullptr;
+  if (!st->v_host || !st->sketch_exact || srows <= 0) return VERKV_OK;
+  return device_view(st->v_host, Vd);
+}
+
 verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
                                double beta, double eps, double delta, verkv_step_out *out,
                                void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
@@ -476,6 +489,12 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   const Totals T = totals(t);
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
+  // every argument and the library's second stream are resolved before the first launch
+  const void *Vd = nullptr;
+  if ((rc = prefetch_source(st, L.srows, &Vd)) != VERKV_OK) return rc;
+  const bool prefetch = Vd != nullptr;   // host cache, exact sketch, staging rows
+  Side *sd = nullptr;
+  if (prefetch && (rc = side_for_device(&sd)) != VERKV_OK) return rc;
 
   SketchArgs sk;
   sk.t = t;
@@ -489,8 +508,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   sk.cf0 = reinterpret_cast<double *>(ws + L.cf0);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
   // the prefetch below (when it runs) sets the bits of the rows it stages
-  sk.sbits = st->v_host && st->sketch_exact && L.srows > 0
-                 ? reinterpret_cast<uint32_t *>(ws + L.sbits) : nullptr;
+  sk.sbits = prefetch ? reinterpret_cast<uint32_t *>(ws + L.sbits) : nullptr;
   sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
   sk.xseq = reinterpret_cast<double *>(ws + L.xseq);
   sk.xseq_row = 2 * L.team;
@@ -504,13 +522,9 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   // host-row prefetch on the library's second stream, beside the decision kernel (it
   // starts after the sketch kernel, which needs every register of the CUs): rows the
   // previous step on this workspace read from the host
-  Side *sd = nullptr;
-  if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
-  std::unique_lock<std::mutex> lk(sd->mu);
-  const bool prefetch = sk.sbits != nullptr;   // host cache, exact sketch, staging rows
-  const void *Vd = nullptr;
+  std::unique_lock<std::mutex> lk;
   if (prefetch) {
-    if ((rc = device_view(st->v_host, &Vd)) != VERKV_OK) return rc;
+    lk = std::unique_lock<std::mutex>(sd->mu);
     HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
     HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
     PrefetchArgs pa;
@@ -607,8 +621,10 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   un.piv_runs = nullptr;
   un.piv_workers = 0;
   // the list is rewritten here: the prefetch must have read it
-  if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
-  lk.unlock();
+  if (prefetch) {
+    HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
+    lk.unlock();
+  }
   {
     Timed tm(K_UNION, stream);
     HIP_TRY(launch_union(un, units, stream), "union launch");

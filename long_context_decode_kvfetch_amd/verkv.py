@@ -74,6 +74,7 @@ def _lib():
         lib.verkv_status_str.argtypes = [i32]
         lib.verkv_last_error.restype = C.c_char_p
         lib.verkv_version.restype = i32
+        lib.verkv_source_hash.restype = C.c_char_p
         lib.verkv_compress_workspace_bytes.restype = sz
         lib.verkv_compress_workspace_bytes.argtypes = [C.POINTER(Shape)]
         lib.verkv_decode_workspace_bytes.restype = sz
@@ -105,6 +106,12 @@ def _lib():
 def lib():
     """The loaded ctypes library (raises if it is not built)."""
     return _lib()
+
+
+def built_from_current_sources() -> bool:
+    """True if the loaded library carries the hash of the sources in this tree."""
+    from . import build
+    return _lib().verkv_source_hash().decode() == build.source_hash()
 
 
 def _check(status: int, what: str):
@@ -249,7 +256,9 @@ def compress(shape: LayerShape, tau: torch.Tensor, K_host: torch.Tensor, V_host:
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                C.byref(need), _stream(stream))
     if st == ECAPACITY:
-        raise VerKVError(st, "verkv_compress", f"needed cap {need.value} > {state.cap}")
+        err = VerKVError(st, "verkv_compress", f"needed cap {need.value} > {state.cap}")
+        err.needed_cap = need.value
+        raise err
     _check(st, "verkv_compress")
     return need.value
 

@@ -27,6 +27,20 @@ def say(*a):
     sys.stdout.flush()
 
 
+def require_gpu_library():
+    """Skip without a GPU; otherwise load libverkv.so and require that it was built from
+    the sources in this tree (the hash the build compiles in), so a stale library is
+    never the one tested."""
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_decode_kvfetch_amd import build, verkv
+    got = verkv.lib().verkv_source_hash().decode()
+    want = build.source_hash()
+    assert got == want, f"libverkv.so was built from other sources ({got[:12]} != {want[:12]}); rebuild it"
+
+
 def oracle_compress(wl):
     """Per sequence: list over KV heads of poissoncomp.Compressed."""
     return [oapi.compress_sequence(s.tau, wl.n_sink, wl.n_local, wl.eta, wl.layer, b, wl.seed)
@@ -137,3 +151,30 @@ def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None,
     return dict(worst_o=worst, exempt=len(exempt_units),
                 fetched=int(np.sum(res["fetch_count"])), h2d=int(np.sum(res["h2d_count"])),
                 certified=int(np.sum(res["certified"])))
+
+
+def session(wl, **kw):
+    from long_context_decode_kvfetch_amd.runner import Session
+    return Session(wl, **kw)
+
+
+def run_parity(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, sketch_of=None, **kw):
+    """Compress `wl` on the GPU, compare the state with the oracle's, run `steps` decode
+    steps (each followed by verkv_check) and compare every one; returns (session, summaries)."""
+    from long_context_decode_kvfetch_amd import verkv
+    say(f"[parity] {label}: {wl.name}")
+    sess = session(wl, **kw)
+    sess.compress()
+    ocomp = oracle_compress(wl)
+    compare_state(sess, wl, ocomp)
+    summ = []
+    for st in steps:
+        q = sess.queries(st)
+        say(f"[parity] {label}: step {st}")
+        sess.step(q, kappa=kappa, eps=eps, delta=delta)
+        verkv.check(sess.shape, sess.cap, sess.dws)
+        oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta, sketch_of=sketch_of)
+        summ.append(compare_step(sess, wl, ocomp, oo, st, kappa=kappa, eps=eps, delta=delta,
+                                 sketch_of=sketch_of))
+    say(f"[parity] {label}: {summ}")
+    return sess, summ

@@ -12,10 +12,14 @@ HEADER = os.path.join(ROOT, "include", "verkv.h")
 
 @pytest.fixture(scope="module")
 def vk():
-    from long_context_decode_kvfetch_amd import verkv
+    from long_context_decode_kvfetch_amd import build, verkv
     if not os.path.exists(verkv.LIB_PATH):
-        from long_context_decode_kvfetch_amd import build
         build.build()
+    elif not verkv.built_from_current_sources():
+        # a library left from older sources: rebuild it here (CPU) before testing it
+        verkv._LIB = None
+        build.build()
+    verkv._LIB = None
     return verkv
 
 
@@ -40,7 +44,7 @@ def test_every_declared_symbol_is_exported(vk):
 
 def test_version_and_status_strings(vk):
     lib = vk.lib()
-    assert lib.verkv_version() == 106
+    assert lib.verkv_version() == 107
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.verkv_status_str(st).decode() not in ("", "unknown status")
     assert lib.verkv_status_str(7).decode() == "unknown status"
@@ -106,6 +110,28 @@ def test_decode_step_rejects_bad_arguments_on_host(vk):
     assert call(state=nostate) == vk.EINVAL
     assert lib.verkv_decode_step(None, C.byref(st), FAKE, 1.0, 0.05, 0.05, C.byref(out), FAKE,
                                  big, None) == vk.EINVAL
+
+
+def test_library_carries_the_hash_of_these_sources(vk):
+    from long_context_decode_kvfetch_amd import build
+    got = vk.lib().verkv_source_hash().decode()
+    assert len(got) == 64 and got == build.source_hash()
+
+
+def test_decode_step_rejects_pageable_value_cache_before_any_launch(vk):
+    """A v_host that is neither pinned nor device memory is an argument error, found
+    before the first kernel is enqueued (no GPU here, so every HIP call would fail: the
+    call must return EINVAL from the pointer check, not EHIP from a launch)."""
+    import ctypes
+    lib = vk.lib()
+    sh = _shape(vk)
+    page = ctypes.create_string_buffer(1 << 16)          # ordinary pageable host memory
+    st = vk.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 640, FAKE, 1,
+                  ctypes.cast(page, ctypes.c_void_p).value, 0)
+    out = _fake_out(vk)
+    rc = lib.verkv_decode_step(C.byref(sh.c), C.byref(st), FAKE, 1.0, 0.05, 0.05, C.byref(out),
+                               FAKE, 1 << 40, None)
+    assert rc == vk.EINVAL
 
 
 def test_compress_rejects_bad_arguments_on_host(vk):

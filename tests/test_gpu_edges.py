@@ -1,0 +1,167 @@
+"""GPU parity, through the C ABI, of the cases the main parity file leaves out: the
+16-sequence ragged batch at its stated tolerance (eps = 0.05, one workgroup per query
+row streaming 8K-64K-token slices), every branch of the water-filling, exact ties in
+the fetch order, the capacity error, GQA groups other than 4 and 8, and argument
+errors that must stop a step before its first kernel."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_kvfetch_amd import synth
+from parity_util import oracle_compress, require_gpu_library, run_parity, say, session
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu_library()
+
+
+def _team_size(rows, max_n):
+    # the decision kernel's workgroups per query row as the library sizes them
+    return max(1, min(16, min(512 // max(1, rows), (max_n + 2047) // 2048)))
+
+
+def test_ragged_16_sequences_full_size_eps_0_05():
+    """The 16-sequence batch (lengths uniform in [8K, 64K], 32q/8kv, bf16, eta = 1/16) at
+    eps = 0.05: 512 query rows give one decision workgroup per row, whose slice of up to
+    64K tokens is streamed from memory on every pass (no register or LDS cache); rows
+    fetch, so selection, the lists and the host rows run at this size too."""
+    wl = synth.ragged_batch(seed=0, batch=16, steps=1, eps=0.05)
+    rows = wl.batch * wl.n_q_heads
+    assert _team_size(rows, max(s.n for s in wl.seqs)) == 1
+    _, summ = run_parity(wl, label="ragged-16 eps 0.05")
+    assert summ[0]["fetched"] > 0 and summ[0]["certified"] < rows
+
+
+# ------------------------------------------------------------------ water-filling branches
+def test_waterfill_no_budget_left():
+    """fl(eta n) equals the forced sink + local count: the remainder is 0 and every other
+    token gets r = 0 (never drawn; its weight is pure bias)."""
+    wl = synth.gqa_layer(seed=31, n=4096, steps=1, hkv=2, n_local=60, eta=1.0 / 64)
+    assert wl.eta * 4096 == 64.0 == wl.n_sink + wl.n_local
+    comp = oracle_compress(wl)[0]
+    assert all(c.rule == "none" for c in comp)
+    sess, _ = run_parity(wl, label="water-filling: none")
+    for h in sess.state_numpy():
+        assert h["piv_count"] == 64 and np.all(h["r"][4:-60] == 0.0)
+
+
+def test_waterfill_saturated():
+    """Scores are 0 except on 100 tokens per KV head while the budget leaves 892 tokens:
+    no water level qualifies, every positive-score token gets r = 1 and the rest r = 0."""
+    wl = synth.gqa_layer(seed=32, n=4096, steps=1, hkv=2, eta=0.25)
+    tau = wl.seqs[0].tau
+    rng = np.random.default_rng(5)
+    for g in range(2):
+        keep = rng.choice(np.arange(4, 4096 - 128), size=100, replace=False)
+        t = np.zeros(4096, np.float32)
+        t[keep] = tau[g, keep]
+        tau[g] = t
+    comp = oracle_compress(wl)[0]
+    assert all(c.rule == "saturated" and c.m_star == -1 for c in comp)
+    sess, _ = run_parity(wl, label="water-filling: saturated")
+    for h in sess.state_numpy():
+        assert h["piv_count"] == 4 + 128 + 100
+
+
+def test_waterfill_no_free_tokens_and_all():
+    """eta = 1 with sequences of 100 and 130 tokens (every token is a sink or local one:
+    nothing to water-fill) beside one of 2000 (the budget covers every token)."""
+    wl = synth.ragged_batch(seed=33, batch=3, n_min=100, n_max=2000, eta=1.0)
+    for b, n in enumerate((100, 130, 2000)):
+        wl.seqs[b] = synth.gqa_layer(seed=40 + b, n=n, steps=1).seqs[0]
+    sess, summ = run_parity(wl, label="water-filling: no free tokens")
+    res = sess.results_numpy()
+    assert np.all(res["certified"] == 1) and np.all(res["eps_hat"] == 0.0)
+
+
+# ------------------------------------------------------------------ exact ties in g
+def _tied(wl, groups, seed):
+    """Every non-forced key of a KV head becomes one of `groups` rows (one of them a
+    planted heavy hitter) and every score the same value: the tokens of a group have equal
+    sketch weights and r, so equal g, and the k* cut falls inside a run of hundreds of
+    exactly tied tokens, decided by token index alone."""
+    rng = np.random.default_rng(seed)
+    s = wl.seqs[0]
+    lo, hi = wl.n_sink, s.n - wl.n_local
+    for g in range(wl.n_kv_heads):
+        src = [int(s.heavy[g][0])] + list(rng.choice(np.arange(lo, hi), size=groups - 1,
+                                                     replace=False))
+        rows = s.K[g, src].copy()
+        pick = rng.integers(0, groups, size=hi - lo)
+        s.K[g, lo:hi] = rows[pick]
+    s.tau[:] = np.float32(0.3)
+    return wl
+
+
+def test_exact_ties_single_workgroup_rows():
+    """n = 2000 (one decision workgroup per row, slice held in registers), two tied groups
+    of about 900 tokens."""
+    wl = _tied(synth.gqa_layer(seed=34, n=2000, steps=1, hkv=1, n_local=64), 2, 1)
+    assert _team_size(wl.n_q_heads, 2000) == 1
+    _, summ = run_parity(wl, label="ties, T=1")
+    assert summ[0]["fetched"] > 0
+
+
+def test_exact_ties_team_rows():
+    """n = 8192 (four workgroups per row, merged histograms), two tied groups of about 4000
+    tokens: the search runs out of g bits and continues on the token index."""
+    wl = _tied(synth.gqa_layer(seed=35, n=8192, steps=1, hkv=2), 2, 2)
+    assert _team_size(wl.n_q_heads, 8192) == 4
+    _, summ = run_parity(wl, label="ties, T=4")
+    assert summ[0]["fetched"] > 0
+
+
+def test_exact_ties_full_size():
+    """The 32K GQA layer (16 workgroups per row) with three tied groups per KV head."""
+    wl = _tied(synth.gqa_layer(seed=36, n=32768, steps=1), 3, 3)
+    _, summ = run_parity(wl, label="ties, 32K")
+    assert summ[0]["fetched"] > 0
+
+
+# ------------------------------------------------------------------ capacity
+def test_capacity_error_reports_the_needed_capacity():
+    """A pivot capacity below |H u S| returns VERKV_ECAPACITY with the largest pivot count
+    (the oracle's), and a capacity of exactly that count then works."""
+    from long_context_decode_kvfetch_amd import verkv
+    wl = synth.gqa_layer(seed=37, n=8192, steps=1, hkv=2)
+    need = max(c.piv_idx.size for c in oracle_compress(wl)[0])
+    sess = session(wl, cap=64)
+    with pytest.raises(verkv.VerKVError) as ei:
+        sess.compress()
+    assert ei.value.status == verkv.ECAPACITY and ei.value.needed_cap == need
+    run_parity(wl, label="capacity exactly the pivot count", cap=need)
+
+
+# ------------------------------------------------------------------ other GQA groups
+@pytest.mark.parametrize("group,hkv,n,dtype", [(1, 4, 6000, "bf16"), (2, 3, 5000, "bf16"),
+                                                (3, 2, 4096, "f32"), (5, 2, 3000, "bf16"),
+                                                (6, 2, 8192, "bf16"), (7, 1, 4500, "f32")])
+def test_other_group_sizes(group, hkv, n, dtype):
+    wl = synth.gqa_layer(seed=50 + group, n=n, steps=1, hkv=hkv, group=group, kv_dtype=dtype)
+    run_parity(wl, label=f"G={group}")
+
+
+# ------------------------------------------------------------------ argument errors
+def test_pageable_value_cache_is_rejected_before_any_kernel():
+    """A value cache in pageable host memory is an argument error; the call returns before
+    the sketch kernel would clear k* (its sentinel survives)."""
+    from long_context_decode_kvfetch_amd import verkv
+    wl = synth.gqa_layer(seed=38, n=4096, steps=1, hkv=2)
+    sess = session(wl)
+    sess.compress()
+    pageable = torch.zeros(16, dtype=torch.bfloat16)          # not pinned
+    sess.state.c.v_host = C.c_void_p(pageable.data_ptr())
+    sess.out.kstar.fill_(-7)
+    torch.cuda.synchronize()
+    with pytest.raises(verkv.VerKVError) as ei:
+        verkv.decode_step(sess.shape, sess.state, sess.queries(0), 1.0, 0.05, 0.05, sess.out,
+                          sess.dws)
+    assert ei.value.status == verkv.EINVAL
+    torch.cuda.synchronize()
+    assert torch.all(sess.out.kstar == -7)
+    say("[parity] pageable v_host rejected, nothing enqueued")

@@ -6,17 +6,15 @@ import pytest
 import torch
 
 from long_context_decode_kvfetch_amd import synth
-from parity_util import compare_state, compare_step, oracle_compress, oracle_step, say
+from parity_util import (compare_state, compare_step, oracle_compress, oracle_step,
+                         require_gpu_library, say)
 
 pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    from long_context_decode_kvfetch_amd import verkv
-    verkv.lib()
+    require_gpu_library()
 
 
 def _session(wl, **kw):
