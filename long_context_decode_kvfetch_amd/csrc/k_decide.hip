@@ -1254,6 +1254,11 @@ __global__ __launch_bounds__(UN_NT) void k_union(UnionArgs a) {
   if (p >= cnt) return;
   const double kappa = a.params[0];
   const int tok = a.piv_idx[(int64_t)unit * a.cap + p];
+  if (tok < 0 || tok >= a.t.s[b].n) {
+    // a pivot list verkv_compress did not write: weight 0, and no read at that token
+    for (int j = 0; j < G; ++j) a.coef[((int64_t)unit * a.cap + p) * G + j] = 0.0f;
+    return;
+  }
   const double ri = a.r[tok_base(a.t, b, g) + tok];
   const bool exact = (ri >= 1.0) || ((fb[tok >> 5] >> (tok & 31)) & 1);
   for (int j = 0; j < G; ++j) {

@@ -71,6 +71,8 @@ class Session:
 
     def step(self, q: torch.Tensor, kappa=None, eps=None, delta=None, stream=None,
              out: verkv.StepBuffers | None = None):
+        if self.max_pivots is None:
+            raise RuntimeError("Session.step before compress(): the pivot state is not written")
         out = out or self.out
         wl = self.wl
         verkv.decode_step(self.shape, self.state, q, wl.kappa if kappa is None else kappa,
