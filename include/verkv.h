@@ -76,7 +76,9 @@ typedef struct {
   uint32_t layer;           /* third Philox counter word                               */
 } verkv_shape;
 
-/* GPU-resident compressed state of one layer (written by verkv_compress). */
+/* GPU-resident compressed state of one layer (written by verkv_compress; the decode
+ * calls read it as written there, so a state that no verkv_compress call of the same
+ * shape and capacity filled gives meaningless results). */
 typedef struct {
   double *r;                /* [B][Hkv][n_b] inclusion probability, 1 on H             */
   uint32_t *resident;       /* [B][Hkv][ceil(n_b/32)] bit set for tokens of H u S      */
@@ -216,6 +218,25 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
                           const void *K_host, const void *V_host, verkv_step_out *out,
                           void *workspace, size_t workspace_bytes, verkv_stream_t stream);
 size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): verkv_decode_step followed by
+ * verkv_refine, same arguments and results, with the workspace in a static device array
+ * of the library (verkv_noalloc_scratch_bytes() = 64 MiB, held on every device the
+ * library runs on until the process ends) instead of a caller buffer.  Nothing is
+ * allocated or created by the call; every kernel runs on `stream` (no second stream,
+ * no cross-step staging of host rows, which only ever saves host-link reads).
+ *   status  [device, may be NULL] the kernels OR their flags into it (4: a team
+ *           barrier timed out, 2: a fixed point did not converge); the caller clears it
+ * Returns VERKV_EWORKSPACE (with verkv_last_error naming the size) when the shape needs
+ * more scratch than the array holds, before anything is enqueued.  All calls on one
+ * device share its array and leave their contents in it (the kernels clear what must
+ * start at zero), so calls that overlap on one device race: serialise them. */
+verkv_status verkv_step_noalloc(const verkv_shape *s, const verkv_state *st, const float *q,
+                                double beta, double eps, double delta, const void *K_host,
+                                const void *V_host, verkv_step_out *out, int32_t *status,
+                                verkv_stream_t stream);
+size_t verkv_noalloc_scratch_bytes(void);
 
 /* Optional kernel timing (instrumentation).  verkv_profile_begin creates 2*max_launches
  * HIP events (the only allocation the library makes, done here and not per step) and

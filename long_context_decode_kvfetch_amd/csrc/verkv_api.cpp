@@ -126,7 +126,7 @@ struct DecodeWs {
   size_t total;
   int nsp, nsh, team;      // nsp: pivot partial slots
 };
-DecodeWs decode_layout(const SeqTable &t, int cap) {
+DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
   const Totals T = totals(t);
   const int64_t Hq = (int64_t)t.Hkv * t.G;
   const int units = t.B * t.Hkv;
@@ -160,7 +160,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap) {
   w.status = off; off = align_up(off + 64);
   w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
   // host-row prefetch: value rows staged per KV head (sized for float32 rows)
-  w.srows = std::min(STAGE_SLOTS_MAX, STAGE_ROWS_TOTAL / std::max(1, units));
+  w.srows = staging ? std::min(STAGE_SLOTS_MAX, STAGE_ROWS_TOTAL / std::max(1, units)) : 0;
   w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * 4);
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
   w.stage_alt = off; off = align_up(off + (size_t)units * w.srows * D * 4);
@@ -292,6 +292,41 @@ struct Timed {
     g_launch_ev = LaunchEvents{};
   }
 };
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of verkv_step_noalloc: a file-scope device array (each device the
+// library runs on holds its own copy until the process ends).  In host code `scratch`
+// names a host-side stand-in, not device memory; its device address is looked up once
+// per device with hipGetSymbolAddress and only that address is handed to the kernels.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+struct ScratchPtr {
+  void *p = nullptr;
+  bool set = false;
+};
+ScratchPtr g_scratch[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+verkv_status scratch_for_device(uint8_t **out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return VERKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchPtr &sp = g_scratch[dev];
+  if (!sp.set) {
+    void *ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress");
+    if (!ptr) {
+      std::snprintf(g_last_error, sizeof(g_last_error), "static scratch has no device address");
+      return VERKV_EHIP;
+    }
+    sp.p = ptr;
+    sp.set = true;
+  }
+  *out = static_cast<uint8_t *>(sp.p);
+  return VERKV_OK;
+}
 
 }  // namespace
 
@@ -470,19 +505,52 @@ static verkv_status prefetch_source(const verkv_state *st, int srows, const void
   return device_view(st->v_host, Vd);
 }
 
-verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
-                               double beta, double eps, double delta, verkv_step_out *out,
-                               void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  SeqTable t;
+// How a step uses the library's resources: the ordinary entry points stage host rows
+// across steps and run the refine side of a step on the library's second stream; the
+// allocation-free entry point does neither (everything on the caller's stream) and may
+// take the kernels' status flags in a caller-owned word instead of the workspace's.
+struct StepMode {
+  bool staging = true;
+  bool side = true;
+  int32_t *status = nullptr;
+};
+
+// Argument checks of KVFetch steps 1-4 (nothing is enqueued).
+static verkv_status decode_args(const verkv_shape *s, const verkv_state *st, const float *q,
+                                double beta, double eps, double delta, const verkv_step_out *out,
+                                SeqTable &t) {
   verkv_status rc = check_step(s, st, q, out, t);
   if (rc != VERKV_OK) return rc;
   if (!(beta >= 0.0) || !(eps > 0.0) || !(delta > 0.0 && delta < 1.0)) return VERKV_EINVAL;
   if (!out->m_hat || !out->d_sketch || !out->beta_star || !out->eps_hat || !out->certified ||
-      !out->kstar || !out->fetch_count || !out->h2d_count || !workspace)
+      !out->kstar || !out->fetch_count || !out->h2d_count)
     return VERKV_EINVAL;
   if (out->fetch_idx && out->fetch_cap < 1) return VERKV_EINVAL;
-  const DecodeWs L = decode_layout(t, st->cap);
+  return VERKV_OK;
+}
+
+// Argument checks of KVFetch step 5; resolves the host caches to their device views.
+static verkv_status refine_args(const verkv_shape *s, const verkv_state *st, const float *q,
+                                const void *K_host, const void *V_host, const verkv_step_out *out,
+                                SeqTable &t, const void **Kd, const void **Vd) {
+  verkv_status rc = check_step(s, st, q, out, t);
+  if (rc != VERKV_OK) return rc;
+  if (!K_host || !V_host || !out->eps_after || !out->n_hat || !out->d_hat || !out->o ||
+      !out->lse || !out->m_hat || !out->d_sketch || !out->beta_star || !out->h2d_count)
+    return VERKV_EINVAL;
+  if ((rc = device_view(K_host, Kd)) != VERKV_OK) return rc;
+  return device_view(V_host, Vd);
+}
+
+static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, const float *q,
+                                double beta, double eps, double delta, verkv_step_out *out,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                const StepMode &mode) {
+  SeqTable t;
+  verkv_status rc = decode_args(s, st, q, beta, eps, delta, out, t);
+  if (rc != VERKV_OK) return rc;
+  if (!workspace) return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, st->cap, mode.staging);
   if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const bool bf16 = s->kv_dtype == VERKV_BF16;
@@ -491,7 +559,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   const int rows = units * t.G;
   // every argument and the library's second stream are resolved before the first launch
   const void *Vd = nullptr;
-  if ((rc = prefetch_source(st, L.srows, &Vd)) != VERKV_OK) return rc;
+  if (mode.side && (rc = prefetch_source(st, L.srows, &Vd)) != VERKV_OK) return rc;
   const bool prefetch = Vd != nullptr;   // host cache, exact sketch, staging rows
   Side *sd = nullptr;
   if (prefetch && (rc = side_for_device(&sd)) != VERKV_OK) return rc;
@@ -565,7 +633,7 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   dc.eps_hat = out->eps_hat;
   dc.certified = out->certified;
   dc.kstar = out->kstar;
-  dc.status = reinterpret_cast<int32_t *>(ws + L.status);
+  dc.status = mode.status ? mode.status : reinterpret_cast<int32_t *>(ws + L.status);
   dc.params = reinterpret_cast<double *>(ws + L.status + 32);
   int team = L.team;
   while (team > 1 && team * rows > decide_capacity(t.max_n, team)) --team;
@@ -633,32 +701,35 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
   return VERKV_OK;
 }
 
-verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
-                          const void *K_host, const void *V_host, verkv_step_out *out,
-                          void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, const float *q,
+                                const void *K_host, const void *V_host, verkv_step_out *out,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                const StepMode &mode) {
   SeqTable t;
-  verkv_status rc = check_step(s, st, q, out, t);
-  if (rc != VERKV_OK) return rc;
-  if (!K_host || !V_host || !workspace || !out->eps_after || !out->n_hat || !out->d_hat ||
-      !out->o || !out->lse || !out->m_hat || !out->d_sketch || !out->beta_star || !out->h2d_count)
-    return VERKV_EINVAL;
-  const DecodeWs L = decode_layout(t, st->cap);
-  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
   const void *Kd = nullptr, *Vd = nullptr;
-  if ((rc = device_view(K_host, &Kd)) != VERKV_OK) return rc;
-  if ((rc = device_view(V_host, &Vd)) != VERKV_OK) return rc;
+  verkv_status rc = refine_args(s, st, q, K_host, V_host, out, t, &Kd, &Vd);
+  if (rc != VERKV_OK) return rc;
+  if (!workspace) return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, st->cap, mode.staging);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const bool bf16 = s->kv_dtype == VERKV_BF16;
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
 
+  // the resident-pivot side runs on the library's second stream (forked from and joined
+  // back into the caller's), or on the caller's stream after the host rows
   Side *sd = nullptr;
-  if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
-  std::lock_guard<std::mutex> lk(sd->mu);
-  // fork: the side stream starts where the caller's stream is now
-  HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
+  std::unique_lock<std::mutex> lk;
+  hipStream_t side = stream;
+  if (mode.side) {
+    if ((rc = side_for_device(&sd)) != VERKV_OK) return rc;
+    lk = std::unique_lock<std::mutex>(sd->mu);
+    side = sd->s;
+    // fork: the side stream starts where the caller's stream is now
+    HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
+    HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
+  }
 
   // caller's stream: rows F \ S from the host cache
   AttendArgs at;
@@ -682,7 +753,7 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   at.stage_tok = reinterpret_cast<const int32_t *>(ws + L.stage_tok);
   at.stage_alt = ws + L.stage_alt;
   at.stage_tok_alt = reinterpret_cast<const int32_t *>(ws + L.stage_tok_alt);
-  at.shdr = reinterpret_cast<const uint64_t *>(ws + L.shdr);
+  at.shdr = L.srows > 0 ? reinterpret_cast<const uint64_t *>(ws + L.shdr) : nullptr;
   at.stage_rows = L.srows;
   {
     Timed tm(K_HOST, stream);
@@ -721,8 +792,8 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
   un.piv_workers = pivot_workers(st->cap, units);
   {
-    Timed tm(K_COEF, sd->s);
-    HIP_TRY(launch_union(un, units, sd->s), "pivot coefficient launch");
+    Timed tm(K_COEF, side);
+    HIP_TRY(launch_union(un, units, side), "pivot coefficient launch");
   }
 
   AttendArgs pv;
@@ -749,8 +820,8 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   pv.shdr = nullptr;
   pv.stage_rows = 0;
   {
-    Timed tm(K_PIVOT, sd->s);
-    HIP_TRY(launch_attend(pv, units, bf16, false, false, sd->s), "pivot attention launch");
+    Timed tm(K_PIVOT, side);
+    HIP_TRY(launch_attend(pv, units, bf16, false, false, side), "pivot attention launch");
   }
 
   AfterArgs af;
@@ -764,13 +835,15 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   af.team = L.team;
   af.part = reinterpret_cast<double *>(ws + L.apart);
   {
-    Timed tm(K_AFTER, sd->s);
-    HIP_TRY(launch_after(af, rows, sd->s), "eps_after launch");
+    Timed tm(K_AFTER, side);
+    HIP_TRY(launch_after(af, rows, side), "eps_after launch");
   }
 
   // join before the finishing kernel
-  HIP_TRY(hipEventRecord(sd->join, sd->s), "hipEventRecord");
-  HIP_TRY(hipStreamWaitEvent(stream, sd->join, 0), "hipStreamWaitEvent");
+  if (mode.side) {
+    HIP_TRY(hipEventRecord(sd->join, sd->s), "hipEventRecord");
+    HIP_TRY(hipStreamWaitEvent(stream, sd->join, 0), "hipStreamWaitEvent");
+  }
 
   FinishArgs fi;
   fi.t = t;
@@ -799,6 +872,52 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
   }
   (void)rows;
   return VERKV_OK;
+}
+
+verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
+                               double beta, double eps, double delta, verkv_step_out *out,
+                               void *workspace, size_t workspace_bytes, verkv_stream_t stream) {
+  return decode_impl(s, st, q, beta, eps, delta, out, workspace, workspace_bytes,
+                     reinterpret_cast<hipStream_t>(stream), StepMode{});
+}
+
+verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
+                          const void *K_host, const void *V_host, verkv_step_out *out,
+                          void *workspace, size_t workspace_bytes, verkv_stream_t stream) {
+  return refine_impl(s, st, q, K_host, V_host, out, workspace, workspace_bytes,
+                     reinterpret_cast<hipStream_t>(stream), StepMode{});
+}
+
+size_t verkv_noalloc_scratch_bytes(void) { return STATIC_SCRATCH_BYTES; }
+
+verkv_status verkv_step_noalloc(const verkv_shape *s, const verkv_state *st, const float *q,
+                                double beta, double eps, double delta, const void *K_host,
+                                const void *V_host, verkv_step_out *out, int32_t *status,
+                                verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  // every argument of both halves is checked before the first launch
+  SeqTable t;
+  verkv_status rc = decode_args(s, st, q, beta, eps, delta, out, t);
+  if (rc != VERKV_OK) return rc;
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((rc = refine_args(s, st, q, K_host, V_host, out, t, &Kd, &Vd)) != VERKV_OK) return rc;
+  const size_t need = decode_layout(t, st->cap, false).total;
+  if (need > STATIC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "this shape needs %zu bytes of scratch; the static array holds %zu", need,
+                  STATIC_SCRATCH_BYTES);
+    return VERKV_EWORKSPACE;
+  }
+  uint8_t *ptr = nullptr;
+  if ((rc = scratch_for_device(&ptr)) != VERKV_OK) return rc;
+  StepMode mode;
+  mode.staging = false;
+  mode.side = false;
+  mode.status = status;
+  if ((rc = decode_impl(s, st, q, beta, eps, delta, out, ptr, STATIC_SCRATCH_BYTES, stream, mode)) !=
+      VERKV_OK)
+    return rc;
+  return refine_impl(s, st, q, K_host, V_host, out, ptr, STATIC_SCRATCH_BYTES, stream, mode);
 }
 
 verkv_status verkv_check(void *workspace, const verkv_shape *s, int32_t cap, verkv_stream_t stream_) {

@@ -97,6 +97,11 @@ def _lib():
         lib.verkv_profile_report.restype = i32
         lib.verkv_profile_report.argtypes = [C.POINTER(C.c_double), C.POINTER(i32), i32]
         lib.verkv_profile_end.restype = None
+        lib.verkv_step_noalloc.restype = i32
+        lib.verkv_step_noalloc.argtypes = [C.POINTER(Shape), C.POINTER(State), vp, C.c_double,
+                                           C.c_double, C.c_double, vp, vp, C.POINTER(StepOut),
+                                           vp, vp]
+        lib.verkv_noalloc_scratch_bytes.restype = sz
         lib.verkv_check.restype = i32
         lib.verkv_check.argtypes = [vp, C.POINTER(Shape), i32, vp]
         _LIB = lib
@@ -288,6 +293,17 @@ def refine(shape: LayerShape, state: LayerState, q: torch.Tensor, K_host: torch.
                                _ptr(V_host), C.byref(out.c), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)),
            "verkv_refine")
+
+
+def step_noalloc(shape: LayerShape, state: LayerState, q: torch.Tensor, beta: float, eps: float,
+                 delta: float, K_host: torch.Tensor, V_host: torch.Tensor, out: StepBuffers,
+                 status: torch.Tensor | None = None, stream=None) -> None:
+    """verkv_step_noalloc: decode step and refinement on the library's static scratch
+    (asynchronous on `stream`)."""
+    _check(_lib().verkv_step_noalloc(C.byref(shape.c), C.byref(state.c), _ptr(q), float(beta),
+                                     float(eps), float(delta), _ptr(K_host), _ptr(V_host),
+                                     C.byref(out.c), _ptr(status), _stream(stream)),
+           "verkv_step_noalloc")
 
 
 def check(shape: LayerShape, cap: int, workspace: torch.Tensor, stream=None) -> None:
