@@ -42,10 +42,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--layers", type=int, default=N_LAYERS_ROT)
     p.add_argument("--profile-steps", type=int, default=64)
-    p.add_argument("--cpu-steps", type=int, default=32)
+    p.add_argument("--cpu-steps", type=int, default=8)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-pivot-batch", action="store_true",
                    help="skip the pivotal-stream measurement at the 16-sequence batch")
+    p.add_argument("--no-nofetch", action="store_true",
+                   help="skip the no-fetch control leg (uniform scores, eps = 0.2)")
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--sweep", action="store_true",
@@ -95,11 +97,62 @@ def h2d_bandwidth(torch, nbytes=256 << 20, reps=5):
 KERNEL_SOURCES = {
     "sketch_scores": ("profiles/sketch_scores_gqa32k_traffic.md",
                       ("long_context_decode_kvfetch_amd/csrc/k_sketch.hip",
+                       "long_context_decode_kvfetch_amd/csrc/kernels.h",
                        "long_context_decode_kvfetch_amd/csrc/common.h")),
     "attend_pivots": ("profiles/attend_pivots_ragged16_kernel_trace.md",
                       ("long_context_decode_kvfetch_amd/csrc/k_attend.hip",
+                       "long_context_decode_kvfetch_amd/csrc/kernels.h",
                        "long_context_decode_kvfetch_amd/csrc/common.h")),
 }
+
+# Algorithmic bytes of the layer-step's HBM streams (the sketch is exact: the keys).
+SKETCH_ROW_BYTES = 128 * 2          # bf16 key row per (KV head, token)
+R_BYTES = 8                         # r_i, float64
+PIVOT_ROW_BYTES = 2 * 128 * 2 + 8   # bf16 K and V rows of a pivot, plus its token index and r
+WHAT_SCRATCH_BYTES = 4 * 8          # float64 sketch weights of G = 4 query rows (scratch)
+
+
+def sketch_bytes(n_tok_heads):
+    """The sketch stream: one key row and r per (KV head, token)."""
+    return n_tok_heads * (SKETCH_ROW_BYTES + R_BYTES)
+
+
+def step_algorithmic_bytes(n_tok_heads, pivot_rows):
+    """Whole layer-step: the sketch stream, the pivotal stream, and the resident and fetch
+    bitmasks (one bit per (KV head, token) each); query and output rows are negligible."""
+    return sketch_bytes(n_tok_heads) + pivot_rows * PIVOT_ROW_BYTES + 2 * n_tok_heads // 8
+
+
+def fail_on_flags(sessions, what):
+    """verkv_check on every session's workspace: a step whose team barrier timed out or
+    whose fixed point did not converge must not be counted, so the run stops here."""
+    from long_context_decode_kvfetch_amd import verkv
+    for sess in sessions:
+        try:
+            verkv.check(sess.shape, sess.cap, sess.dws)
+        except verkv.VerKVError as e:
+            print(f"bench.py: kernel flags after {what}: {e}", file=sys.stderr)
+            sys.exit(3)
+
+
+def timed(torch, run, first, count):
+    """Run steps first .. first+count-1 back to back on the current stream with an event
+    after each: (total ms, per-step ms list)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(count + 1)]
+    ev[0].record()
+    for i in range(count):
+        run(first + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(count)]
+    return ev[0].elapsed_time(ev[count]), per
+
+
+def percentiles(per):
+    import numpy as np
+    a = np.asarray(per, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
 
 
 def sources_sha256(kernel):
@@ -125,26 +178,31 @@ def profiled_traffic(kernel):
     return None
 
 
-def pivotal_stream(torch, steps=8):
-    """The resident-pivot attention (the pivotal-KV stream) timed on its own: a ragged
-    batch of 16 sequences (lengths uniform in [8K, 64K], 32q/8kv, bf16, eta = 1/16) with
-    eps large enough that every row certifies, so no host rows share the step.  Returns
-    bytes, microseconds and GB/s per launch (dispatch-stamped events)."""
+def pivotal_stream(torch, steps=8, fetch_steps=8):
+    """The 16-sequence ragged batch (lengths uniform in [8K, 64K], 32q/8kv, bf16,
+    eta = 1/16), two measurements on one compressed batch:
+      * the resident-pivot attention (the pivotal-KV stream) timed on its own: eps large
+        enough that every row certifies, so no host rows share the step; bytes,
+        microseconds and GB/s per launch (dispatch-stamped events);
+      * the batch at its stated tolerance eps = 0.05: steps/s with fetching (one decision
+        workgroup per query row), fetched share and host bytes per step."""
+    import numpy as np
     from long_context_decode_kvfetch_amd import synth, verkv
     from long_context_decode_kvfetch_amd.runner import Session
-    wl = synth.ragged_batch(seed=0, batch=16, steps=steps + 2)
+    wl = synth.ragged_batch(seed=0, batch=16, steps=steps + fetch_steps + 4)
     sess = Session(wl)
     sess.compress()
-    qs = [sess.queries(i) for i in range(steps + 2)]
+    qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
     for i in range(2):
-        sess.step(qs[i], eps=1e9)
+        sess.step(qdev[i], eps=1e9)
     torch.cuda.synchronize()
     verkv.profile_begin(16 * steps + 16)
     for i in range(2, steps + 2):
-        sess.step(qs[i], eps=1e9)
+        sess.step(qdev[i], eps=1e9)
     torch.cuda.synchronize()
     prof = verkv.profile_report()
     verkv.profile_end()
+    fail_on_flags([sess], "the pivotal-stream leg")
     ms, cnt = prof["attend_pivots"]
     us = ms / cnt * 1e3
     rows = int(sess.state.piv_count.sum().item())
@@ -152,17 +210,92 @@ def pivotal_stream(torch, steps=8):
     # algorithmic bytes per pivot row: its bf16 K and V rows (512 B) plus its token index
     # and r (8 B); the kernel reads the estimator coefficients (4 B per query row) in
     # place of index and r
-    alg = rows * (2 * 128 * 2 + 8)
+    alg = rows * PIVOT_ROW_BYTES
+    piv = {"workload": "16 sequences, n ~ U[8K, 64K], 32q/8kv, d=128, bf16, eta=1/16, "
+                       "every row certified (pivots only)",
+           "pivot_rows": rows, "kv_bytes": nbytes, "algorithmic_bytes": alg,
+           "avg_us": round(us, 2),
+           "GBps": round(alg / (us * 1e-6) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
+           "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "kv_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "traffic": profiled_traffic("attend_pivots")}
+
+    # the same batch at eps = 0.05
+    base = steps + 2
+    sess.step(qdev[base])                          # primes the cross-step staging
+    torch.cuda.synchronize()
+    ms, per = timed(torch, lambda i: sess.step(qdev[i]), base + 1, fetch_steps)
+    fail_on_flags([sess], "the 16-sequence leg at eps = 0.05")
+    sess.step(qdev[base + 1 + fetch_steps])
+    r = sess.results_numpy()
+    assert np.all(r["eps_after"] < wl.eps), "a row finished uncertified"
+    ntok = sum(s.n for s in wl.seqs) * wl.n_kv_heads
+    piv["eps_0_05"] = {"eps": wl.eps, "steps": fetch_steps,
+                       "steps_per_s": round(fetch_steps / (ms * 1e-3), 2),
+                       "ms_per_step": round(ms / fetch_steps, 3), "step_ms": percentiles(per),
+                       "rows_certified_without_fetch": float(r["certified"].mean()),
+                       "fetched_fraction_of_cache": int(r["fetch_count"].sum()) / ntok,
+                       "h2d_fraction_of_cache": int(r["h2d_count"].sum()) / ntok,
+                       "h2d_bytes_per_step": int(r["h2d_count"].sum()) * 128 * 2}
     del sess
     torch.cuda.empty_cache()
-    return {"workload": "16 sequences, n ~ U[8K, 64K], 32q/8kv, d=128, bf16, eta=1/16, "
-                        "every row certified (pivots only)",
-            "pivot_rows": rows, "kv_bytes": nbytes, "algorithmic_bytes": alg,
-            "avg_us": round(us, 2),
-            "GBps": round(alg / (us * 1e-6) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
-            "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "kv_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "traffic": profiled_traffic("attend_pivots")}
+    return piv
+
+
+def no_fetch_leg(torch, L, K=64, W=8):
+    """Control: the 32K GQA layer-step with uniform scores and no planted keys at
+    eps = 0.2, where every row certifies without fetching (eps_hat(L) is about 0.14 at
+    eta = 1/16): the step is the sketch stream, the decision and the resident pivots,
+    with no host traffic.  Steps/s and the per-kernel times over rotated layers."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import synth, verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+    per_layer = (K + W + 16 + L) // L + 1
+    sess = []
+    for layer in range(L):
+        wl = synth.gqa_layer(seed=1, n=N_CTX, steps=per_layer, layer=layer, tau_kind="uniform",
+                             hh_frac=0.0, eps=0.2)
+        s2 = Session(wl)
+        s2.compress()
+        s2.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
+        for sq in wl.seqs:
+            sq.K = sq.V = None
+        sess.append(s2)
+
+    def run(i):
+        s2 = sess[i % L]
+        s2.step(s2.qdev[(i // L) % per_layer])
+
+    for i in range(W):
+        run(i)
+    torch.cuda.synchronize()
+    ms, per = timed(torch, run, W, K)
+    fail_on_flags(sess, "the no-fetch leg")
+    verkv.profile_begin(8 * 16 + 16)
+    for i in range(W + K, W + K + 16):
+        run(i)
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    cert = nrow = fetched = 0
+    for s2 in sess:
+        s2.step(s2.qdev[0])
+        r = s2.results_numpy()
+        cert += int(r["certified"].sum())
+        nrow += r["certified"].size
+        fetched += int(r["fetch_count"].sum())
+    kern = {k: round(v[0] / v[1] * 1e3, 2) for k, v in prof.items() if v[1]}
+    piv_rows = sum(int(s2.state.piv_count.sum().item()) for s2 in sess) / L
+    alg = step_algorithmic_bytes(8 * N_CTX, piv_rows)
+    out = {"workload": "gqa decode layer-step: 32q/8kv, d=128, n=32768, bf16, exact sketch, "
+                       "eta=1/16, tau uniform, no planted keys, eps=0.2, delta=0.05, layers rotated",
+           "steps": K, "steps_per_s": round(K / (ms * 1e-3), 2), "ms_per_step": round(ms / K, 4),
+           "step_ms": percentiles(per), "rows_certified_without_fetch": cert / nrow,
+           "fetched_tokens": fetched, "step_algorithmic_bytes": int(alg),
+           "step_GBps": round(alg / (ms / K * 1e-3) / 1e9, 1), "kernel_avg_us": kern}
+    del sess
+    torch.cuda.empty_cache()
+    return out
 
 
 def sketch2_leg(torch, wls, qdevs, K2, W2):
@@ -194,6 +327,7 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    fail_on_flags(sess2, "the 2-bit sketch leg")
     verkv.profile_begin(8 * 16 + 16)
     for i in range(W2 + K2, W2 + K2 + 16):
         run(i)
@@ -206,8 +340,9 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
         h2d += int(s2.results_numpy()["h2d_count"].sum())
     sk_ms, sk_n = prof["sketch_scores"]
     sk_us = sk_ms / sk_n * 1e3
-    # per (KV head, token): the 64 B sketch row and r_i (8 B) read, 4 x 8 B weights written
-    sk_bytes = 8 * N_CTX * (64 + 8 + 4 * 8)
+    # per (KV head, token): the 64 B sketch row and r_i (8 B) read (the float64 weights the
+    # kernel writes are scratch, 4 x 8 B, not counted)
+    sk_bytes = 8 * N_CTX * (64 + R_BYTES)
     host_us = prof["attend_host"][0] / prof["attend_host"][1] * 1e3
     out = {"value": round(K2 / (ms * 1e-3), 2), "unit": "steps/s", "steps": K2,
            "ms_per_step": round(ms / K2, 4),
@@ -260,6 +395,7 @@ def eta_eps_sweep(torch, L, K=32, W=8):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1)
+            fail_on_flags(sess, f"the sweep at eta=1/{round(1 / eta)}, eps={eps}")
             cert = fetched = h2d = nrow = 0
             for s2 in sess:
                 s2.step(s2.qdev[0], eps=eps)
@@ -318,6 +454,7 @@ def decode_36_layers(torch, tokens=16, warm=2, n_layers=36):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    fail_on_flags(sess, "the 36-layer decode")
     cert = fetched = h2d = nrow = 0
     for s2 in sess:
         s2.step(s2.qdev[warm + tokens])
@@ -380,6 +517,7 @@ def long_context_stress(torch, steps=16, warm=2, planted=2048):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
+        fail_on_flags([sess], f"the long-context leg at eps={eps}")
         sess.step(qdev[warm + steps], eps=eps)
         r = sess.results_numpy()
         assert np.all(r["eps_after"] < eps), "a row finished uncertified"
@@ -412,27 +550,54 @@ def calib_copy(torch):
     del src, dst
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(steps):
-    """The oracle (as it stands) on the same workload: one layer, `steps` decode steps."""
+    """The oracle (as it stands) on the benchmark's workload: one layer, `steps` decode
+    steps of the 32K GQA layer, with every thread pool of the process limited to one
+    thread and with the default threads; plus one step of the single-head workload
+    (n = 4096, fp32, G = 8).  Prefill is excluded."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from long_context_decode_kvfetch_amd import synth
     from oracle import api as oapi
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:                                          # pragma: no cover
-        cores = os.cpu_count() or 1
     wl = synth.gqa_layer(seed=0, n=N_CTX, steps=steps, layer=0)
     s = wl.seqs[0]
     comp = oapi.compress_sequence(s.tau, wl.n_sink, wl.n_local, wl.eta, 0, 0, wl.seed)
-    t0 = time.perf_counter()
-    for st in range(steps):
-        oapi.decode_sequence(s.K, s.V, comp, wl.queries[st, 0], wl.group, wl.kappa, wl.eps, wl.delta)
-    dt = time.perf_counter() - t0
-    return {"value": steps / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} decode steps of one layer (32q/8kv, n={N_CTX}, bf16 values in "
-                      f"float64, eta=1/16), prefill excluded; {dt:.1f} s on "
-                      f"{os.cpu_count()} host cores"}
+    w1 = synth.single_head(0)
+    s1 = w1.seqs[0]
+    c1 = oapi.compress_sequence(s1.tau, w1.n_sink, w1.n_local, w1.eta, 0, 0, w1.seed)
+
+    def run():
+        t0 = time.perf_counter()
+        for st in range(steps):
+            oapi.decode_sequence(s.K, s.V, comp, wl.queries[st, 0], wl.group, wl.kappa, wl.eps,
+                                 wl.delta)
+        t1 = time.perf_counter()
+        oapi.decode_sequence(s1.K, s1.V, c1, w1.queries[0, 0], w1.group, w1.kappa, w1.eps, w1.delta)
+        return t1 - t0, time.perf_counter() - t1
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    dt_all, dt1_all = run()
+    with threadpool_limits(1):
+        dt_one, dt1_one = run()
+    return {"value": steps / dt_all, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} decode steps of one 32K GQA layer (32q/8kv, n={N_CTX}, bf16 values "
+                      f"in float64, eta=1/16), prefill excluded: {dt_all:.1f} s with the default "
+                      f"{threads} threads, {dt_one:.1f} s on one thread",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": steps / dt_one, "unit": "steps/s", "cores": 1},
+            "single_head_n4096_ms": {"default_threads": round(dt1_all * 1e3, 1),
+                                     "one_thread": round(dt1_one * 1e3, 1)}}
 
 
 def main():
@@ -465,8 +630,8 @@ def main():
         print(json.dumps({"pivotal_stream": pivotal_stream(torch)}))
         return
     K, W, L = args.steps, args.warmup, args.layers
-    total = K + W + args.profile_steps
-    per_layer = (total + L - 1) // L
+    total = K + W + args.profile_steps + 1
+    per_layer = (total + L - 1) // L + 1
     log(f"[bench] generating {L} layers (n={N_CTX}, 32q/8kv, bf16)")
     sessions = []
     for layer in range(L):
@@ -476,6 +641,10 @@ def main():
         sess.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries[:, :])).to("cuda")
         sessions.append(sess)
         log(f"[bench] layer {layer} compressed, max pivots {sess.max_pivots}, cap {sess.cap}")
+    # one step per layer before any counted step: a decode step stages the host rows the
+    # layer's previous step read, and in a running decode every layer has had one
+    for sess in sessions:
+        sess.step(sess.qdev[per_layer - 1])
     torch.cuda.synchronize()
 
     def run(step_index):
@@ -489,16 +658,11 @@ def main():
     for i in range(W):
         run(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
-    for i in range(W, W + K):
-        run(i)
-    e1.record()
-    torch.cuda.synchronize()
+    ev_ms, per_step = timed(torch, run, W, K)
     wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1)
     ms_per_step = ev_ms / K
+    fail_on_flags(sessions, "the timed steps")
     log(f"[bench] {K} steps: {wall * 1e3:.1f} ms wall, {ev_ms:.1f} ms events")
 
     # per-step statistics over one pass of every layer
@@ -523,17 +687,20 @@ def main():
     torch.cuda.synchronize()
     prof = verkv.profile_report()
     verkv.profile_end()
-    # per pivot row: its bf16 K and V rows (512 B) plus its token index and r (8 B)
-    piv_bytes = sum(int(s.state.piv_count.sum().item()) for s in sessions) / L * (2 * 128 * 2 + 8)
-    # per (KV head, token): the bf16 key row (256 B) and r_i (8 B) read, the G = 4
-    # float64 weights written (32 B); per-chunk statistics are below 0.1% and not counted
-    sketch_bytes = 8 * N_CTX * (128 * 2 + 8 + 4 * 8)
+    fail_on_flags(sessions, "the profiled steps")
+    piv_rows = sum(int(s.state.piv_count.sum().item()) for s in sessions) / L
+    piv_bytes = piv_rows * PIVOT_ROW_BYTES
+    tok_heads = 8 * N_CTX
+    sk_bytes = sketch_bytes(tok_heads)
     kern = {}
     for name, (ms, cnt) in prof.items():
         if cnt:
             kern[name] = {"avg_us": ms / cnt * 1e3, "launches": cnt}
-    kern["sketch_scores"]["algorithmic_bytes"] = sketch_bytes
-    kern["sketch_scores"]["GBps"] = sketch_bytes / (kern["sketch_scores"]["avg_us"] * 1e-6) / 1e9
+    sk = kern["sketch_scores"]
+    sk["algorithmic_bytes"] = sk_bytes
+    sk["GBps"] = sk_bytes / (sk["avg_us"] * 1e-6) / 1e9
+    # the float64 sketch weights the kernel leaves for the decision kernels: scratch
+    sk["scratch_write_bytes"] = tok_heads * WHAT_SCRATCH_BYTES
     kern["attend_pivots"]["algorithmic_bytes"] = piv_bytes
     kern["attend_pivots"]["GBps"] = piv_bytes / (kern["attend_pivots"]["avg_us"] * 1e-6) / 1e9
     kern["attend_host"]["host_bytes"] = h2d_bytes_step
@@ -550,8 +717,15 @@ def main():
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["GBps"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBS, 4),
             "traffic": profiled_traffic(dom) if dom in KERNEL_SOURCES else None,
-            "algorithmic_bytes": kern[dom]["algorithmic_bytes"]}
+            "algorithmic_bytes": kern[dom]["algorithmic_bytes"],
+            "bytes_per_unit": "264 B per (KV head, token): bf16 key row + float64 r",
+            "units_per_launch": tok_heads}
+    step_bytes = step_algorithmic_bytes(tok_heads, piv_rows)
     h2d_peak = h2d_bandwidth(torch)
+    nofetch = None
+    if not args.no_nofetch:
+        log("[bench] no-fetch control: uniform scores, eps = 0.2")
+        nofetch = no_fetch_leg(torch, L)
     sk2 = None
     if not args.no_2bit:
         log("[bench] 2-bit sketch: the same layers, rebuilt")
@@ -560,9 +734,11 @@ def main():
         sessions.clear()
         torch.cuda.empty_cache()
         sk2 = sketch2_leg(torch, wls, qdevs, K2=min(K, 64), W2=min(W, 8))
+    sessions.clear()
+    torch.cuda.empty_cache()
     piv = None
     if not args.no_pivot_batch:
-        log("[bench] pivotal stream at the 16-sequence batch")
+        log("[bench] 16-sequence batch: pivotal stream, then eps = 0.05")
         piv = pivotal_stream(torch)
     dec36 = None
     if not args.no_decode36:
@@ -592,7 +768,15 @@ def main():
                                "hitters, tau~Beta(0.3,3)",
                    "layers_rotated": L, "seq_len": N_CTX, "batch": 1},
         "roofline": roof,
+        "step_ms": percentiles(per_step),
+        "whole_step": {"algorithmic_bytes": int(step_bytes),
+                       "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                       "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "note": "sketch stream + pivotal stream + bitmasks per layer-step over "
+                               "the step time; the host rows of F minus S are counted apart "
+                               "(step_stats.h2d_bytes_per_step)"},
         "pivotal_stream": piv,
+        "no_fetch": nofetch,
         "sketch_2bit": sk2,
         "decode_36_layers": dec36,
         "long_context": longc,

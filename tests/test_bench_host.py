@@ -49,3 +49,17 @@ def test_missing_summary_gives_no_traffic(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setitem(bench.KERNEL_SOURCES, "probe", ("absent.md", ("kernel.hip",)))
     assert bench.profiled_traffic("probe") is None
+
+
+def test_algorithmic_byte_counts_of_the_32k_layer_step():
+    """264 B per (KV head, token) for the sketch stream (bf16 key row + float64 r; the
+    float64 weights the kernel writes are scratch), 520 B per pivot row, and one bit per
+    (KV head, token) for each of the resident and fetch bitmasks."""
+    tok = 8 * 32768
+    assert bench.sketch_bytes(tok) == 69206016
+    assert bench.step_algorithmic_bytes(tok, 2048 * 8) == 69206016 + 2048 * 8 * 520 + 65536
+
+
+def test_step_percentiles():
+    p = bench.percentiles([float(x) for x in range(1, 101)])
+    assert p["p50"] == 50.5 and abs(p["p10"] - 10.9) < 1e-9 and abs(p["p90"] - 90.1) < 1e-9
