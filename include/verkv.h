@@ -24,10 +24,12 @@
  *    verkv_last_error).
  *  - head_dim must be 128.  GQA group G = (query heads)/(KV heads) in 1..8.
  *
- * Layouts (sequence-major, ragged batches of B sequences with lengths n_b):
- *  - token arrays      [B][Hkv][n_b]           sequence b starts at Hkv * sum_{b'<b} n_b'
- *  - bit arrays        [B][Hkv][ceil(n_b/32)]  token i is bit (i % 32) of word i / 32
- *  - cache rows        [B][Hkv][n_b][128]      kv_dtype elements
+ * Layouts (sequence-major, ragged batches of B sequences with lengths n_b and token
+ * capacities c_b >= n_b, c_b = n_b unless verkv_shape.seq_cap is given; a sequence's
+ * per-head arrays are strided by c_b so that verkv_append can grow it in place):
+ *  - token arrays      [B][Hkv][c_b]           sequence b starts at Hkv * sum_{b'<b} c_b'
+ *  - bit arrays        [B][Hkv][ceil(c_b/32)]  token i is bit (i % 32) of word i / 32
+ *  - cache rows        [B][Hkv][c_b][128]      kv_dtype elements; tokens i < n_b are used
  *  - query rows        [B][Hq][128] float32    Hq = Hkv * G; row h uses KV head h / G
  *  - per-row outputs   [B][Hq]
  *  - pivot ids         [B][Hkv][cap]
@@ -74,6 +76,8 @@ typedef struct {
   int32_t n_local;          /* last n_local tokens are always kept (H)                 */
   int32_t kv_dtype;         /* verkv_dtype of the cache, the pivots and the sketch     */
   uint32_t layer;           /* third Philox counter word                               */
+  const int32_t *seq_cap;   /* [host][B] token capacity c_b >= n_b of each sequence's  */
+                            /* arrays, each <= VERKV_MAX_SEQ_LEN (NULL: c_b = n_b)      */
 } verkv_shape;
 
 /* GPU-resident compressed state of one layer (written by verkv_compress; the decode
@@ -109,6 +113,10 @@ typedef struct {
                             /* rows written by verkv_quantize_sketch (needs            */
                             /* sketch_exact = 0: fetched rows are scored from the host */
                             /* keys).                                                   */
+  double *level;            /* [B][Hkv] written by verkv_compress (may be NULL): the    */
+                            /* water level c of eq. 3, or the branch that set r on the */
+                            /* non-forced tokens (-1 all in H, -2 no budget left, -3   */
+                            /* every positive score saturated); verkv_append needs it. */
 } verkv_state;
 
 #define VERKV_SKETCH_ROWS 0
@@ -171,6 +179,34 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
                             void *workspace, size_t workspace_bytes, int32_t *needed_cap,
                             verkv_stream_t stream);
 size_t verkv_compress_workspace_bytes(const verkv_shape *s);
+
+/* A growing cache: token n_b is appended to every sequence b of the batch (the pages
+ * compress the cache once, at prefill, and are silent on decode-time growth; this is
+ * the reading taken, with the prefill's rule of the picx.dev summary page, "POISSONCOMP",
+ * eq. 3).  The new token joins the local window (r = 1, resident).  The token leaving
+ * the window, t = n_b - n_local (none when t < n_sink), gets the prefill's rule with the
+ * water level verkv_compress recorded in st->level: r_t = min(1, c ceil(tau_t 2^40))
+ * (1 / 0 / [tau_t > 0] for the other branches), and when 0 < r_t < 1 its Bernoulli draw
+ * from the Philox counter (t, g, layer, b) it would have had at prefill; it stays a
+ * pivot only if drawn.  With n_local = 0 the new token itself takes the rule.  The
+ * level is not re-solved.  r, the resident bits, the ascending pivot list, its count
+ * and the pivot K/V rows (re-laid out in the order the pivot attention reads them) are
+ * updated in place.
+ *   s       the shape BEFORE the append (lengths n_b); every n_b + 1 <= c_b
+ *   tau     [B][Hkv][c_b] scores; the caller has written the new token's at index n_b
+ *   K_host, [pinned host][B][Hkv][c_b][128] the cache, with the new token's rows written
+ *   V_host  at row n_b (the caller also writes its key into an exact sketch)
+ *   seed    the seed verkv_compress drew with
+ *   status  [device] 4 bytes: cleared, then the kernels OR 1 (a score outside [0, 1]),
+ *           8 (a pivot list would exceed st->cap), 16 (the state does not match the
+ *           shape); with any of them set nothing was changed
+ *   workspace at least verkv_append_workspace_bytes(s, st->cap)
+ * Asynchronous on `stream`; afterwards the caller's shape has lengths n_b + 1.  A 2-bit
+ * sketch must be re-quantised by the caller for the new rows. */
+verkv_status verkv_append(const verkv_shape *s, verkv_state *st, const float *tau,
+                          const void *K_host, const void *V_host, uint64_t seed, int32_t *status,
+                          void *workspace, size_t workspace_bytes, verkv_stream_t stream);
+size_t verkv_append_workspace_bytes(const verkv_shape *s, int32_t cap);
 
 /* Rows of 128 kv_dtype elements that st->piv_k and st->piv_v must each hold for pivot
  * capacity `cap` (0 for an invalid shape or cap < 1).  verkv_compress stores the pivot

@@ -11,12 +11,15 @@ constexpr int D = VERKV_HEAD_DIM;          // head dimension
 constexpr int SKETCH_CHUNK = 128;          // tokens per sketch-scoring wave
 constexpr int WAVE = 64;
 
-// Per-sequence offsets of a ragged batch, passed by value in kernel arguments.
+// Per-sequence offsets of a ragged batch, passed by value in kernel arguments.  A
+// sequence's token arrays are strided by its capacity (>= its length), so a sequence
+// can grow in place; with no capacity given the capacity is the length.
 struct SeqInfo {
   int32_t n;          // tokens
-  int32_t tok_off;    // sum of n over earlier sequences
-  int32_t word_off;   // sum of ceil(n/32) over earlier sequences
-  int32_t chunk_off;  // sum of ceil(n/SKETCH_CHUNK) over earlier sequences
+  int32_t cap;        // token capacity: the stride of the sequence's per-head arrays
+  int32_t tok_off;    // sum of cap over earlier sequences
+  int32_t word_off;   // sum of ceil(cap/32) over earlier sequences
+  int32_t chunk_off;  // sum of ceil(cap/SKETCH_CHUNK) over earlier sequences
 };
 struct SeqTable {
   int32_t B;
@@ -25,6 +28,7 @@ struct SeqTable {
   int32_t n_sink;
   int32_t n_local;
   int32_t max_n;
+  int32_t max_cap;
   SeqInfo s[VERKV_MAX_BATCH];
 };
 
@@ -33,16 +37,16 @@ __host__ __device__ inline int32_t chunks_of(int32_t n) { return (n + SKETCH_CHU
 
 // Offsets of unit (b, g) and of query row (b, h) in the layouts of verkv.h.
 __host__ __device__ inline int64_t tok_base(const SeqTable &t, int b, int g) {
-  return (int64_t)t.Hkv * t.s[b].tok_off + (int64_t)g * t.s[b].n;
+  return (int64_t)t.Hkv * t.s[b].tok_off + (int64_t)g * t.s[b].cap;
 }
 __host__ __device__ inline int64_t word_base(const SeqTable &t, int b, int g) {
-  return (int64_t)t.Hkv * t.s[b].word_off + (int64_t)g * words_of(t.s[b].n);
+  return (int64_t)t.Hkv * t.s[b].word_off + (int64_t)g * words_of(t.s[b].cap);
 }
 __host__ __device__ inline int64_t row_tok_base(const SeqTable &t, int b, int h) {
-  return (int64_t)t.Hkv * t.G * t.s[b].tok_off + (int64_t)h * t.s[b].n;
+  return (int64_t)t.Hkv * t.G * t.s[b].tok_off + (int64_t)h * t.s[b].cap;
 }
 __host__ __device__ inline int64_t row_chunk_base(const SeqTable &t, int b, int h) {
-  return (int64_t)t.Hkv * t.G * t.s[b].chunk_off + (int64_t)h * chunks_of(t.s[b].n);
+  return (int64_t)t.Hkv * t.G * t.s[b].chunk_off + (int64_t)h * chunks_of(t.s[b].cap);
 }
 
 // ------------------------------------------------------------------ cross-lane helpers

@@ -159,6 +159,9 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
     }
     __syncthreads();
     const int mstar = s_mstar;
+    if (a.level && tid == 0)
+      a.level[unit] = mstar == INT32_MAX ? LEVEL_SATURATED
+                                         : (b_rem - (double)mstar) / (double)kb[mstar];
     if (mstar == INT32_MAX) {
       // every positive score saturates; the budget cannot be spent
       for (int m = tid; m < nfree; m += PC_NT) {
@@ -175,6 +178,8 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   } else {
     const double v = (nfree > 0 && b_rem >= (double)nfree) ? 1.0 : 0.0;
     for (int i = lo + tid; i < hi; i += PC_NT) r[i] = v;
+    if (a.level && tid == 0)
+      a.level[unit] = (nfree == 0 || b_rem >= (double)nfree) ? LEVEL_ALL : LEVEL_NONE;
   }
   __syncthreads();
 
@@ -199,6 +204,8 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
     res[w] = bits;
     cnt += __popc(bits);
   }
+  // words past the sequence's length (capacity for appended tokens) start empty
+  for (int w = W + tid; w < words_of(a.t.s[b].cap); w += PC_NT) res[w] = 0u;
   int32_t total;
   int32_t pos = block_excl_scan<PC_NT>(cnt, iscratch, &total);
   int32_t *pidx = a.piv_idx + (int64_t)unit * a.cap;

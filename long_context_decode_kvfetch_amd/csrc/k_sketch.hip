@@ -28,7 +28,8 @@ namespace verkv {
 
 constexpr int SK_WAVES = 4;               // waves per workgroup, one chunk each
 
-// Map a flat chunk index to (sequence, KV head, chunk).
+// Map a flat chunk index (over the chunks of every head's capacity) to (sequence, KV
+// head, chunk); chunks past a head's length get c >= chunks_of(n) and do nothing.
 __device__ __forceinline__ void sketch_chunk(const SeqTable &t, int blk, int &b, int &g, int &c) {
   int lo = 0, hi = t.B - 1;
   while (lo < hi) {                       // last sequence whose first chunk <= blk
@@ -37,7 +38,7 @@ __device__ __forceinline__ void sketch_chunk(const SeqTable &t, int blk, int &b,
   }
   b = lo;
   const int rel = blk - t.Hkv * t.s[b].chunk_off;
-  const int nch = chunks_of(t.s[b].n);
+  const int nch = chunks_of(t.s[b].cap);
   g = rel / nch;
   c = rel % nch;
 }
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   int b, g, c;
   sketch_chunk(a.t, flat, b, g, c);
   const int n = a.t.s[b].n;
+  if (c >= chunks_of(n)) return;            // capacity beyond the sequence's length
   const int Hq = a.t.Hkv * G;
   const int sidx = lane & (LPT - 1);        // lane within the token's group
   const int tsub = lane / LPT;              // token of the load step

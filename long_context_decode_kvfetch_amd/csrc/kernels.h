@@ -19,7 +19,39 @@ struct CompressArgs {
   uint64_t *keys_a;           // workspace [B][Hkv][n]
   uint64_t *keys_b;           // workspace [B][Hkv][n]
   int32_t *status;            // workspace [0]: error bits, [1]: max pivot count
+  double *level;              // [B][Hkv] water level c, or the branch code (null: not kept)
 };
+
+// Branch codes kept in verkv_state.level where eq. (3)'s water level is not used.
+constexpr double LEVEL_ALL = -1.0;        // every non-forced token has r = 1
+constexpr double LEVEL_NONE = -2.0;       // no budget left: r = 0
+constexpr double LEVEL_SATURATED = -3.0;  // every positive score saturated: r = [tau > 0]
+
+// One token appended to every sequence of a batch (the growing cache).
+struct AppendArgs {
+  SeqTable t;                 // lengths before the append (token n_b is appended)
+  const float *tau;           // [B][Hkv][cap] scores; the new token's at index n_b
+  const double *level;        // [B][Hkv] from PoissonComp
+  double *r;                  // [B][Hkv][cap]
+  uint32_t *resident;         // [B][Hkv][W]
+  int32_t *piv_idx;           // [B][Hkv][cap_piv]
+  int32_t *piv_count;         // [B][Hkv]
+  int32_t cap;                // pivot capacity
+  uint64_t seed;
+  uint32_t layer;
+  int32_t *status;            // caller's word: 1 tau outside [0, 1], 8 pivot capacity, 16 state
+  int4 *plan;                 // workspace [B*Hkv]: {drop position or -1, new count, token n kept, old count}
+  double *plan_r;             // workspace [B*Hkv]: r of the token that gets the rule
+  // pivot rows, re-laid out in the order of the new counts' schedule
+  const uint8_t *K_host, *V_host;   // device views of the cache (the new token's rows)
+  uint8_t *piv_k, *piv_v;
+  uint8_t *rows_k, *rows_v;   // workspace [B*Hkv][cap_piv][row]: rows in list order
+  const int4 *sched_old, *runs_old, *sched_new, *runs_new;
+  int32_t workers;
+  int32_t row_bytes;
+  int64_t rows;               // rows allocated in piv_k / piv_v
+};
+constexpr int32_t APPEND_BAD = 1 | 8 | 16;
 
 struct GatherArgs {
   SeqTable t;
@@ -244,7 +276,17 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem,
   return hipGetLastError();
 }
 
+// every argument block is passed by value and must fit the kernel argument segment
+static_assert(sizeof(CompressArgs) <= 4096 && sizeof(AppendArgs) <= 4096 && sizeof(GatherArgs) <= 4096 && sizeof(PlanArgs) <= 4096 &&
+                  sizeof(SketchArgs) <= 4096 && sizeof(DecideArgs) <= 4096 && sizeof(AfterArgs) <= 4096 &&
+                  sizeof(UnionArgs) <= 4096 && sizeof(PrefetchArgs) <= 4096 && sizeof(AttendArgs) <= 4096 &&
+                  sizeof(FinishArgs) <= 4096,
+              "kernel arguments exceed 4 KiB");
+
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
+hipError_t launch_append_plan(const AppendArgs &a, int units, hipStream_t st);
+hipError_t launch_append_copy(const AppendArgs &a, int units, bool in, hipStream_t st);
+hipError_t launch_append_apply(const AppendArgs &a, int units, hipStream_t st);
 hipError_t launch_gather_pivots(const GatherArgs &a, int units, hipStream_t st);
 hipError_t launch_pivot_schedule(const PlanArgs &a, hipStream_t st);
 hipError_t launch_sketch(const SketchArgs &a, bool bf16, hipStream_t st);

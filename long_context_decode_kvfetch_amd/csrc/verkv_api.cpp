@@ -38,7 +38,7 @@ uint64_t shape_ident(const SeqTable &t, bool bf16) {
     for (int k = 0; k < 8; ++k) { h ^= (v >> (8 * k)) & 0xFF; h *= 1099511628211ull; }
   };
   mix((uint64_t)t.B); mix((uint64_t)t.Hkv); mix((uint64_t)t.G); mix(bf16 ? 1 : 0);
-  for (int b = 0; b < t.B; ++b) mix((uint64_t)t.s[b].n);
+  for (int b = 0; b < t.B; ++b) { mix((uint64_t)t.s[b].n); mix((uint64_t)t.s[b].cap); }
   return h;
 }
 
@@ -59,16 +59,19 @@ verkv_status make_table(const verkv_shape *s, SeqTable &t) {
   int64_t tok = 0, words = 0, chunks = 0;
   for (int b = 0; b < s->batch; ++b) {
     const int32_t n = s->seq_len[b];
-    if (n < 1) return VERKV_EINVAL;
-    if (n > VERKV_MAX_SEQ_LEN) return VERKV_EUNSUPPORTED;
+    const int32_t cap = s->seq_cap ? s->seq_cap[b] : n;
+    if (n < 1 || cap < n) return VERKV_EINVAL;
+    if (cap > VERKV_MAX_SEQ_LEN) return VERKV_EUNSUPPORTED;
     t.s[b].n = n;
+    t.s[b].cap = cap;
     t.s[b].tok_off = (int32_t)tok;
     t.s[b].word_off = (int32_t)words;
     t.s[b].chunk_off = (int32_t)chunks;
-    tok += n;
-    words += words_of(n);
-    chunks += chunks_of(n);
+    tok += cap;
+    words += words_of(cap);
+    chunks += chunks_of(cap);
     t.max_n = std::max(t.max_n, n);
+    t.max_cap = std::max(t.max_cap, cap);
   }
   // every flat index below must stay inside int32 element counts per array
   const int64_t hq = (int64_t)s->n_kv_heads * s->group;
@@ -81,10 +84,10 @@ struct Totals {
 };
 Totals totals(const SeqTable &t) {
   Totals r;
-  for (int b = 0; b < t.B; ++b) {
-    r.tok += t.s[b].n;
-    r.words += words_of(t.s[b].n);
-    r.chunks += chunks_of(t.s[b].n);
+  for (int b = 0; b < t.B; ++b) {     // array extents: capacities
+    r.tok += t.s[b].cap;
+    r.words += words_of(t.s[b].cap);
+    r.chunks += chunks_of(t.s[b].cap);
   }
   return r;
 }
@@ -134,7 +137,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
   DecodeWs w;
   w.nsp = pivot_slots(cap, units);
   w.nsh = host_splits(units);
-  w.team = team_size((int)rows, t.max_n);
+  w.team = team_size((int)rows, t.max_cap);      // sized for the longest the arrays may hold
   const int64_t tm = w.team > 1 ? w.team : 0;       // member histograms only for teams
   size_t off = 0;
   w.xseq = off;   off = align_up(off + 8 * (size_t)(rows * 2 * w.team));
@@ -354,6 +357,110 @@ const char *verkv_status_str(int32_t s) {
 
 const char *verkv_last_error(void) { return g_last_error; }
 
+}  // extern "C"
+
+namespace {
+struct AppendWs {
+  size_t plan, plan_r, sold, rold, snew, rnew, rows_k, rows_v, total;
+};
+AppendWs append_layout(const SeqTable &t, int cap, int row_bytes) {
+  const int64_t units = (int64_t)t.B * t.Hkv;
+  AppendWs w;
+  size_t off = 0;
+  w.plan = off;   off = align_up(off + 16 * (size_t)units);
+  w.plan_r = off; off = align_up(off + 8 * (size_t)units);
+  w.sold = off;   off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
+  w.rold = off;   off = align_up(off + 16 * (size_t)units);
+  w.snew = off;   off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
+  w.rnew = off;   off = align_up(off + 16 * (size_t)units);
+  w.rows_k = off; off = align_up(off + (size_t)units * cap * row_bytes);
+  w.rows_v = off; off = align_up(off + (size_t)units * cap * row_bytes);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t verkv_append_workspace_bytes(const verkv_shape *s, int32_t cap) {
+  SeqTable t;
+  if (cap < 1 || make_table(s, t) != VERKV_OK) return 0;
+  return append_layout(t, cap, row_bytes(s)).total;
+}
+
+verkv_status verkv_append(const verkv_shape *s, verkv_state *st, const float *tau,
+                          const void *K_host, const void *V_host, uint64_t seed, int32_t *status,
+                          void *workspace, size_t workspace_bytes, verkv_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!st || !tau || !K_host || !V_host || !status || !workspace) return VERKV_EINVAL;
+  if (!st->r || !st->resident || !st->piv_idx || !st->piv_count || !st->piv_k || !st->piv_v ||
+      !st->level || st->cap < 1)
+    return VERKV_EINVAL;
+  for (int b = 0; b < t.B; ++b) {
+    if (t.s[b].n + 1 > t.s[b].cap) {
+      std::snprintf(g_last_error, sizeof(g_last_error),
+                    "sequence %d has no capacity left (length %d, capacity %d)", b, t.s[b].n,
+                    t.s[b].cap);
+      return VERKV_EINVAL;
+    }
+  }
+  const int rb = row_bytes(s);
+  const AppendWs L = append_layout(t, st->cap, rb);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
+  const void *Kd = nullptr, *Vd = nullptr;
+  if ((rc = device_view(K_host, &Kd)) != VERKV_OK) return rc;
+  if ((rc = device_view(V_host, &Vd)) != VERKV_OK) return rc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const int units = t.B * t.Hkv;
+  AppendArgs a;
+  a.t = t;
+  a.tau = tau;
+  a.level = st->level;
+  a.r = st->r;
+  a.resident = st->resident;
+  a.piv_idx = st->piv_idx;
+  a.piv_count = st->piv_count;
+  a.cap = st->cap;
+  a.seed = seed;
+  a.layer = s->layer;
+  a.status = status;
+  a.plan = reinterpret_cast<int4 *>(ws + L.plan);
+  a.plan_r = reinterpret_cast<double *>(ws + L.plan_r);
+  a.K_host = static_cast<const uint8_t *>(Kd);
+  a.V_host = static_cast<const uint8_t *>(Vd);
+  a.piv_k = static_cast<uint8_t *>(st->piv_k);
+  a.piv_v = static_cast<uint8_t *>(st->piv_v);
+  a.rows_k = ws + L.rows_k;
+  a.rows_v = ws + L.rows_v;
+  a.sched_old = reinterpret_cast<const int4 *>(ws + L.sold);
+  a.runs_old = reinterpret_cast<const int4 *>(ws + L.rold);
+  a.sched_new = reinterpret_cast<const int4 *>(ws + L.snew);
+  a.runs_new = reinterpret_cast<const int4 *>(ws + L.rnew);
+  a.workers = pivot_workers(st->cap, units);
+  a.row_bytes = rb;
+  a.rows = pivot_rows(st->cap, units);
+  // the schedule of the counts before and after the append, for the pivot rows' places
+  PlanArgs pl;
+  pl.t = t;
+  pl.piv_count = st->piv_count;
+  pl.cap = st->cap;
+  pl.workers = a.workers;
+  pl.sched = reinterpret_cast<int4 *>(ws + L.sold);
+  pl.runs = reinterpret_cast<int4 *>(ws + L.rold);
+  HIP_TRY(launch_append_plan(a, units, stream), "append plan launch");
+  HIP_TRY(launch_pivot_schedule(pl, stream), "pivot schedule launch");
+  HIP_TRY(launch_append_copy(a, units, false, stream), "append copy-out launch");
+  HIP_TRY(launch_append_apply(a, units, stream), "append apply launch");
+  pl.sched = reinterpret_cast<int4 *>(ws + L.snew);
+  pl.runs = reinterpret_cast<int4 *>(ws + L.rnew);
+  HIP_TRY(launch_pivot_schedule(pl, stream), "pivot schedule launch");
+  HIP_TRY(launch_append_copy(a, units, true, stream), "append copy-in launch");
+  return VERKV_OK;
+}
+
 size_t verkv_compress_workspace_bytes(const verkv_shape *s) {
   SeqTable t;
   if (make_table(s, t) != VERKV_OK) return 0;
@@ -433,6 +540,7 @@ verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *
   a.keys_a = reinterpret_cast<uint64_t *>(ws + L.ka);
   a.keys_b = reinterpret_cast<uint64_t *>(ws + L.kb);
   a.status = status;
+  a.level = st->level;
   const int units = t.B * t.Hkv;
   {
     Timed tm(K_POISSON, stream);
@@ -635,7 +743,7 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   dc.kstar = out->kstar;
   dc.status = mode.status ? mode.status : reinterpret_cast<int32_t *>(ws + L.status);
   dc.params = reinterpret_cast<double *>(ws + L.status + 32);
-  int team = L.team;
+  int team = std::min(L.team, team_size(rows, t.max_n));
   while (team > 1 && team * rows > decide_capacity(t.max_n, team)) --team;
   dc.team = team;
   dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;

@@ -14,8 +14,16 @@ from . import verkv
 from .synth import Workload
 
 
-def _cat(arrs):
-    return np.concatenate([a.reshape(-1) for a in arrs])
+def _cat(arrs, caps=None):
+    """Sequence-major concatenation of per-sequence [Hkv][n][...] arrays, each padded with
+    zeros to its capacity along the token axis."""
+    if caps is None:
+        return np.concatenate([a.reshape(-1) for a in arrs])
+    out = []
+    for a, c in zip(arrs, caps):
+        pad = [(0, 0), (0, int(c) - a.shape[1])] + [(0, 0)] * (a.ndim - 2)
+        out.append(np.pad(a, pad).reshape(-1))
+    return np.concatenate(out)
 
 
 class Session:
@@ -23,15 +31,17 @@ class Session:
 
     def __init__(self, wl: Workload, cap: int | None = None, device: str = "cuda",
                  host_pinned: bool = True, seed: int | None = None, sketch_exact: bool = True,
-                 prefetch: bool = True, sketch_2bit: bool = False):
+                 prefetch: bool = True, sketch_2bit: bool = False, grow: int = 0):
+        """grow: token slots reserved past each sequence's length for append()."""
         self.wl = wl
         self.device = device
         lens = [s.n for s in wl.seqs]
+        caps = [n + int(grow) for n in lens] if grow else None
         self.shape = verkv.LayerShape(lens, wl.n_kv_heads, wl.group, wl.n_sink, wl.n_local,
-                                      wl.kv_dtype, wl.layer)
+                                      wl.kv_dtype, wl.layer, caps)
         dt = self.shape.torch_dtype
-        K = torch.from_numpy(_cat([s.K for s in wl.seqs])).to(dt)
-        V = torch.from_numpy(_cat([s.V for s in wl.seqs])).to(dt)
+        K = torch.from_numpy(_cat([s.K for s in wl.seqs], caps)).to(dt)
+        V = torch.from_numpy(_cat([s.V for s in wl.seqs], caps)).to(dt)
         if host_pinned:
             self.K_host = torch.empty(K.shape, dtype=dt, pin_memory=True)
             self.V_host = torch.empty(V.shape, dtype=dt, pin_memory=True)
@@ -43,27 +53,64 @@ class Session:
         if sketch_2bit:
             # the 2-bit sketch of the keys (64 B per token row), quantised on the device
             # from the host cache; fetched rows are then scored from the host keys
-            nbytes = self.shape.total_tokens * self.shape.n_kv_heads * verkv.SKETCH2_ROW_BYTES
+            nbytes = self.shape.total_slots * self.shape.n_kv_heads * verkv.SKETCH2_ROW_BYTES
             self.sketch = torch.empty(nbytes, dtype=torch.uint8, device=device)
             verkv.quantize_sketch(self.shape, self.K_host, self.sketch)
             sketch_exact = False
         else:
             self.sketch = K.to(device)          # exact sketch: the keys, device resident
-        self.tau = torch.from_numpy(_cat([s.tau for s in wl.seqs]).astype(np.float32)).to(device)
+        self.tau = torch.from_numpy(_cat([s.tau for s in wl.seqs], caps).astype(np.float32)).to(device)
         self.cap = int(cap) if cap else verkv.default_cap(self.shape, wl.eta)
         self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device, sketch_exact,
                                       v_host=self.V_host if (host_pinned and prefetch) else None,
                                       sketch_format=verkv.SKETCH_2BIT if sketch_2bit else verkv.SKETCH_ROWS)
         self.cws = verkv.workspace(self.shape.compress_workspace_bytes(), device)
         self.dws = verkv.workspace(self.shape.decode_workspace_bytes(self.cap), device)
-        self.out = verkv.StepBuffers(self.shape, device=device)
+        self.out = verkv.StepBuffers(self.shape, fetch_cap=max(self.shape.caps), device=device)
         self.seed = wl.seed if seed is None else seed
         self.max_pivots = None
+        self.sketch_2bit = sketch_2bit
+        self.aws = None
+        self.astatus = None
 
     def compress(self, stream=None):
         self.max_pivots = verkv.compress(self.shape, self.tau, self.K_host, self.V_host,
                                          self.wl.eta, self.seed, self.state, self.cws, stream)
         return self.max_pivots
+
+    def _slot(self, b: int, g: int, i: int) -> int:
+        """Flat token slot of (sequence b, KV head g, token i) in the capacity-strided arrays."""
+        caps = self.shape.caps
+        return self.shape.n_kv_heads * sum(caps[:b]) + g * caps[b] + i
+
+    def append(self, k_rows: np.ndarray, v_rows: np.ndarray, tau_new: np.ndarray, stream=None):
+        """Append one token to every sequence: k_rows, v_rows [B][Hkv][128] (values the cache
+        dtype holds exactly), tau_new [B][Hkv].  Writes the rows into the host cache and the
+        exact sketch, the scores into tau, calls verkv_append and grows the shape.  Returns
+        the status word (a device tensor; nonzero means nothing changed)."""
+        if self.max_pivots is None:
+            raise RuntimeError("Session.append before compress()")
+        if self.sketch_2bit:
+            raise NotImplementedError("append with a 2-bit sketch needs the new rows re-quantised")
+        if self.aws is None:
+            self.aws = verkv.workspace(self.shape.append_workspace_bytes(self.cap), self.device)
+            self.astatus = torch.zeros(1, dtype=torch.int32, device=self.device)
+        dt = self.shape.torch_dtype
+        hkv = self.shape.n_kv_heads
+        idx = [self._slot(b, g, n) for b, n in enumerate(self.shape.seq_lens) for g in range(hkv)]
+        kr = torch.from_numpy(np.ascontiguousarray(k_rows, dtype=np.float32).reshape(-1, 128)).to(dt)
+        vr = torch.from_numpy(np.ascontiguousarray(v_rows, dtype=np.float32).reshape(-1, 128)).to(dt)
+        it = torch.tensor(idx, dtype=torch.long)
+        self.K_host.view(-1, 128)[it] = kr.to(self.K_host.device)
+        self.V_host.view(-1, 128)[it] = vr.to(self.V_host.device)
+        itd = it.to(self.device)
+        if not self.sketch_2bit:
+            self.sketch.view(-1, 128)[itd] = kr.to(self.device)
+        self.tau[itd] = torch.from_numpy(np.ascontiguousarray(tau_new, dtype=np.float32).reshape(-1)).to(self.device)
+        verkv.append(self.shape, self.state, self.tau, self.K_host, self.V_host, self.seed,
+                     self.astatus, self.aws, stream)
+        self.shape = self.shape.grown(1)
+        return self.astatus
 
     def queries(self, step: int) -> torch.Tensor:
         """Query rows of one step as a device tensor [B][Hq][128] (float32)."""
@@ -91,15 +138,15 @@ class Session:
         pidx = self.state.piv_idx.view(-1, self.cap).cpu().numpy()
         out = []
         roff, woff = 0, 0
-        for b, n in enumerate(self.shape.seq_lens):
-            W = (n + 31) // 32
+        for b, (n, c) in enumerate(zip(self.shape.seq_lens, self.shape.caps)):
+            W = (c + 31) // 32
             for g in range(self.shape.n_kv_heads):
                 u = b * self.shape.n_kv_heads + g
                 bits = np.unpackbits(res[woff + g * W: woff + (g + 1) * W].view(np.uint8),
                                      bitorder="little")[:n].astype(bool)
-                out.append(dict(r=r[roff + g * n: roff + (g + 1) * n], resident=bits,
+                out.append(dict(r=r[roff + g * c: roff + g * c + n], resident=bits,
                                 piv_idx=pidx[u, :min(int(cnt[u]), self.cap)], piv_count=int(cnt[u])))
-            roff += self.shape.n_kv_heads * n
+            roff += self.shape.n_kv_heads * c
             woff += self.shape.n_kv_heads * W
         return out
 

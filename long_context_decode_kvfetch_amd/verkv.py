@@ -39,14 +39,14 @@ class Shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_kv_heads", C.c_int32), ("group", C.c_int32),
                 ("head_dim", C.c_int32), ("seq_len", C.POINTER(C.c_int32)),
                 ("n_sink", C.c_int32), ("n_local", C.c_int32), ("kv_dtype", C.c_int32),
-                ("layer", C.c_uint32)]
+                ("layer", C.c_uint32), ("seq_cap", C.POINTER(C.c_int32))]
 
 
 class State(C.Structure):
     _fields_ = [("r", C.c_void_p), ("resident", C.c_void_p), ("piv_idx", C.c_void_p),
                 ("piv_count", C.c_void_p), ("piv_k", C.c_void_p), ("piv_v", C.c_void_p),
                 ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32),
-                ("v_host", C.c_void_p), ("sketch_format", C.c_int32)]
+                ("v_host", C.c_void_p), ("sketch_format", C.c_int32), ("level", C.c_void_p)]
 
 
 SKETCH_ROWS, SKETCH_2BIT, SKETCH2_ROW_BYTES = 0, 1, 64
@@ -83,6 +83,11 @@ def _lib():
         lib.verkv_pivot_rows.argtypes = [C.POINTER(Shape), i32]
         lib.verkv_quantize_sketch.restype = i32
         lib.verkv_quantize_sketch.argtypes = [C.POINTER(Shape), vp, vp, vp]
+        lib.verkv_append.restype = i32
+        lib.verkv_append.argtypes = [C.POINTER(Shape), C.POINTER(State), vp, vp, vp, C.c_uint64,
+                                     vp, vp, sz, vp]
+        lib.verkv_append_workspace_bytes.restype = sz
+        lib.verkv_append_workspace_bytes.argtypes = [C.POINTER(Shape), i32]
         lib.verkv_compress.restype = i32
         lib.verkv_compress.argtypes = [C.POINTER(Shape), vp, vp, vp, C.c_double, C.c_uint64,
                                        C.POINTER(State), vp, sz, C.POINTER(i32), vp]
@@ -145,12 +150,31 @@ class LayerShape:
     n_local: int
     kv_dtype: str = "bf16"
     layer: int = 0
+    seq_caps: list | None = None     # token capacity per sequence (None: the lengths)
 
     def __post_init__(self):
         self._lens = (C.c_int32 * len(self.seq_lens))(*[int(x) for x in self.seq_lens])
+        caps = self.seq_caps if self.seq_caps is not None else self.seq_lens
+        self._caps = (C.c_int32 * len(caps))(*[int(x) for x in caps])
         self.c = Shape(len(self.seq_lens), self.n_kv_heads, self.group, HEAD_DIM,
                        C.cast(self._lens, C.POINTER(C.c_int32)), self.n_sink, self.n_local,
-                       BF16 if self.kv_dtype == "bf16" else F32, self.layer)
+                       BF16 if self.kv_dtype == "bf16" else F32, self.layer,
+                       C.cast(self._caps, C.POINTER(C.c_int32)))
+
+    def grown(self, by: int = 1) -> "LayerShape":
+        """The same layer after `by` tokens were appended to every sequence."""
+        return LayerShape([n + by for n in self.seq_lens], self.n_kv_heads, self.group,
+                          self.n_sink, self.n_local, self.kv_dtype, self.layer,
+                          list(self.caps))
+
+    @property
+    def caps(self):
+        return list(self.seq_caps) if self.seq_caps is not None else list(self.seq_lens)
+
+    @property
+    def total_slots(self):
+        """Token slots of the capacity-strided arrays (sum of capacities)."""
+        return int(sum(self.caps))
 
     @property
     def batch(self):
@@ -167,6 +191,9 @@ class LayerShape:
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.kv_dtype == "bf16" else torch.float32
+
+    def append_workspace_bytes(self, cap: int) -> int:
+        return int(_lib().verkv_append_workspace_bytes(C.byref(self.c), int(cap)))
 
     def compress_workspace_bytes(self) -> int:
         return int(_lib().verkv_compress_workspace_bytes(C.byref(self.c)))
@@ -194,8 +221,8 @@ class LayerState:
     def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda",
                  sketch_exact: bool = True, v_host: torch.Tensor | None = None,
                  sketch_format: int = SKETCH_ROWS):
-        hkv, tot = shape.n_kv_heads, shape.total_tokens
-        words = sum((n + 31) // 32 for n in shape.seq_lens)
+        hkv, tot = shape.n_kv_heads, shape.total_slots
+        words = sum((n + 31) // 32 for n in shape.caps)
         units = shape.batch * hkv
         self.shape = shape
         self.cap = int(cap)
@@ -206,12 +233,13 @@ class LayerState:
         prow = shape.pivot_rows(cap)            # pivot K/V rows, stored in schedule order
         self.piv_k = torch.empty(prow * HEAD_DIM, dtype=shape.torch_dtype, device=device)
         self.piv_v = torch.empty(prow * HEAD_DIM, dtype=shape.torch_dtype, device=device)
+        self.level = torch.empty(units, dtype=torch.float64, device=device)
         self.sketch = sketch
         self.v_host = v_host                    # kept alive with the state
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
                        _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch),
                        1 if sketch_exact else 0, _ptr(v_host) if v_host is not None else None,
-                       int(sketch_format))
+                       int(sketch_format), _ptr(self.level))
 
 
 class StepBuffers:
@@ -268,9 +296,21 @@ def compress(shape: LayerShape, tau: torch.Tensor, K_host: torch.Tensor, V_host:
     return need.value
 
 
+def append(shape: LayerShape, state: LayerState, tau: torch.Tensor, K_host: torch.Tensor,
+           V_host: torch.Tensor, seed: int, status: torch.Tensor, workspace: torch.Tensor,
+           stream=None) -> None:
+    """verkv_append: token n_b appended to every sequence (asynchronous on `stream`);
+    `shape` has the lengths before the append, `status` is a 4-byte device word."""
+    _check(_lib().verkv_append(C.byref(shape.c), C.byref(state.c), _ptr(tau), _ptr(K_host),
+                               _ptr(V_host), int(seed) & ((1 << 64) - 1), _ptr(status),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)),
+           "verkv_append")
+
+
 def quantize_sketch(shape: LayerShape, K: torch.Tensor, sketch: torch.Tensor, stream=None) -> None:
     """verkv_quantize_sketch: the 2-bit sketch rows of K (asynchronous on `stream`)."""
-    need = shape.total_tokens * shape.n_kv_heads * SKETCH2_ROW_BYTES
+    need = shape.total_slots * shape.n_kv_heads * SKETCH2_ROW_BYTES
     if sketch.numel() * sketch.element_size() < need:
         raise ValueError(f"sketch buffer holds {sketch.numel() * sketch.element_size()} B, needs {need}")
     _check(_lib().verkv_quantize_sketch(C.byref(shape.c), _ptr(K), _ptr(sketch), _stream(stream)),
