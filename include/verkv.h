@@ -255,6 +255,24 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
                           void *workspace, size_t workspace_bytes, verkv_stream_t stream);
 size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
 
+/* verkv_decode_step with options.  flags:
+ *   VERKV_STEP_RESOLVED  the other reading of eqs. (9)-(10) (picx.dev summary page,
+ *       "KVFETCH" steps 3-4): eq. (9) writes eps_hat(L \ {i}) without saying whether
+ *       the shrinkage bias of Definition 2 follows the set.  verkv_decode_step keeps
+ *       lambda frozen at its value for the full L; with this flag the order is still
+ *       eq. (9)'s g (lambda frozen), but k* of eq. (10) is the least k for which
+ *       eps_hat(L_g[k:]) with the bias solved on L_g[k:] alone is below eps, and the
+ *       kept set L_g[k*:] keeps that bias (beta_star, the pivot coefficients and
+ *       eps_after use it).  Certification (k* = 0) is the same test.  For beta = 0 or
+ *       +INFINITY lambda does not depend on the bias: both readings make the same cut,
+ *       and this one reports the kept set's bias sum(w (1 - lambda)) over L_g[k*:].
+ * Other bits give VERKV_EINVAL.  verkv_refine follows as usual. */
+#define VERKV_STEP_RESOLVED 1u
+verkv_status verkv_decode_step_ex(const verkv_shape *s, const verkv_state *st, const float *q,
+                                  double beta, double eps, double delta, verkv_step_out *out,
+                                  void *workspace, size_t workspace_bytes, uint32_t flags,
+                                  verkv_stream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): verkv_decode_step followed by
  * verkv_refine, same arguments and results, with the workspace in a static device array
@@ -282,10 +300,10 @@ size_t verkv_noalloc_scratch_bytes(void);
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
  * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 host-row prefetch, 11 2-bit
- * sketch quantiser), and
+ * sketch quantiser, 12 re-solved cut), and
  * clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 12
+#define VERKV_PROFILE_KINDS 13
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverkv.so")
-SOURCES = ["k_compress.hip", "k_append.hip", "k_sketch.hip", "k_quant.hip", "k_decide.hip", "k_attend.hip",
+SOURCES = ["k_compress.hip", "k_append.hip", "k_sketch.hip", "k_quant.hip", "k_decide.hip", "k_resolve.hip", "k_attend.hip",
            "k_prefetch.hip", "verkv_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -133,6 +133,29 @@ struct DecideArgs {
   double *bprev;             // [rows] B* of the last step (Newton start), kept in the workspace
   int32_t nch_max;           // chunk scales held in dynamic LDS
   int32_t lds_cache;         // 1: the launch reserved LDS for the (w, r) slice cache
+  int32_t resolved;          // 1: stop after the certificate (k_resolve makes the cut)
+  double *gpar;              // [rows][4] out when resolved: V, b1, b2, sqrt(X) of the full L
+};
+
+// The cut of eqs. (9)-(10) with the bias re-solved on every candidate set.
+struct ResolveArgs {
+  SeqTable t;
+  const double *wc, *cscale, *cf0, *r;
+  uint32_t *fbits;
+  double kappa, eps, l;
+  const double *d_sketch;
+  double *beta_star;         // in: bias of the full L; out: bias of the kept set
+  const uint8_t *certified;
+  int32_t *kstar;
+  const double *gpar;        // [rows][4] V, b1, b2 and sqrt(X) of the full L (from k_decide)
+  int32_t *status;
+  int32_t team, xcd_map, team_ws;
+  double *xseq, *part;
+  uint32_t *hcnt;
+  uint64_t *wkey;
+  uint32_t *wlo;
+  uint32_t *wcount;
+  int32_t nch_max, lds_cache;
 };
 
 struct AfterArgs {
@@ -280,7 +303,7 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem,
 static_assert(sizeof(CompressArgs) <= 4096 && sizeof(AppendArgs) <= 4096 && sizeof(GatherArgs) <= 4096 && sizeof(PlanArgs) <= 4096 &&
                   sizeof(SketchArgs) <= 4096 && sizeof(DecideArgs) <= 4096 && sizeof(AfterArgs) <= 4096 &&
                   sizeof(UnionArgs) <= 4096 && sizeof(PrefetchArgs) <= 4096 && sizeof(AttendArgs) <= 4096 &&
-                  sizeof(FinishArgs) <= 4096,
+                  sizeof(FinishArgs) <= 4096 && sizeof(ResolveArgs) <= 4096,
               "kernel arguments exceed 4 KiB");
 
 hipError_t launch_poissoncomp(const CompressArgs &a, int units, hipStream_t st);
@@ -296,8 +319,11 @@ hipError_t launch_union(const UnionArgs &a, int units, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, int units, bool bf16, bool host, bool exact,
                          hipStream_t st);
 hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st);
+hipError_t launch_resolve(ResolveArgs &a, int rows, hipStream_t st);
+int resolve_blocks_per_cu(int nch_max, bool slice_cache);
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
 hipError_t launch_prefetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st);
 int decide_blocks_per_cu(int max_n, int team);
+bool decide_slice_cached(int max_n, int team);
 
 }  // namespace verkv

@@ -124,7 +124,7 @@ int team_size(int rows, int max_n) {
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
-  size_t stage, stage_tok, stage_alt, stage_tok_alt, shdr, sbits, h2dc, psched, pruns;
+  size_t stage, stage_tok, stage_alt, stage_tok_alt, shdr, sbits, h2dc, psched, pruns, gpar;
   int srows;
   size_t total;
   int nsp, nsh, team;      // nsp: pivot partial slots
@@ -173,6 +173,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
   w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
   w.pruns = off;     off = align_up(off + 16 * (size_t)units);
+  w.gpar = off;      off = align_up(off + 32 * (size_t)rows);
   w.total = off;
   return w;
 }
@@ -266,7 +267,7 @@ verkv_status side_for_device(Side **out) {
 
 // ---------------------------------------------------------------- optional kernel timing
 enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER,
-                K_COEF, K_PREFETCH, K_QUANT, K_COUNT };
+                K_COEF, K_PREFETCH, K_QUANT, K_RESOLVE, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -621,6 +622,7 @@ struct StepMode {
   bool staging = true;
   bool side = true;
   int32_t *status = nullptr;
+  uint32_t flags = 0;        // VERKV_STEP_* of verkv_decode_step_ex
 };
 
 // Argument checks of KVFetch steps 1-4 (nothing is enqueued).
@@ -743,8 +745,23 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   dc.kstar = out->kstar;
   dc.status = mode.status ? mode.status : reinterpret_cast<int32_t *>(ws + L.status);
   dc.params = reinterpret_cast<double *>(ws + L.status + 32);
+  // the re-solved cut (k_resolve); at kappa 0 and infinity lambda does not depend on
+  // the bias, so it cuts where the frozen reading does and differs only in the bias it
+  // reports (that of the kept set)
+  const bool resolved = (mode.flags & VERKV_STEP_RESOLVED) != 0;
   int team = std::min(L.team, team_size(rows, t.max_n));
   while (team > 1 && team * rows > decide_capacity(t.max_n, team)) --team;
+  if (resolved) {
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    auto fits = [&](int tm) {
+      return tm * rows <= cus * resolve_blocks_per_cu(chunks_of(t.max_n),
+                                                      decide_slice_cached(t.max_n, tm));
+    };
+    while (team > 1 && !fits(team)) --team;
+  }
   dc.team = team;
   dc.xcd_map = (team > 1 && rows % 8 == 0) ? 1 : 0;
   dc.team_ws = L.team;
@@ -759,6 +776,8 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   dc.wlo = reinterpret_cast<uint32_t *>(ws + L.wlo);
   dc.wcount = sk.wcount;
   dc.phase_clock = nullptr;
+  dc.resolved = resolved ? 1 : 0;
+  dc.gpar = reinterpret_cast<double *>(ws + L.gpar);
 #ifdef VERKV_PHASE_TIMING
   if (workspace_bytes >= L.total + (size_t)rows * team * 64 * 8)
     dc.phase_clock = reinterpret_cast<uint64_t *>(ws + L.total);
@@ -766,6 +785,37 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   {
     Timed tm(K_DECIDE, stream);
     HIP_TRY(launch_decide(dc, rows, stream), "decide launch");
+  }
+  if (resolved) {
+    ResolveArgs rv;
+    rv.t = t;
+    rv.wc = sk.wc;
+    rv.cscale = dc.cscale;
+    rv.cf0 = sk.cf0;
+    rv.r = st->r;
+    rv.fbits = sk.fbits;
+    rv.kappa = beta;
+    rv.eps = eps;
+    rv.l = dc.l;
+    rv.d_sketch = out->d_sketch;
+    rv.beta_star = out->beta_star;
+    rv.certified = out->certified;
+    rv.kstar = out->kstar;
+    rv.gpar = dc.gpar;
+    rv.status = dc.status;
+    rv.team = dc.team;
+    rv.xcd_map = dc.xcd_map;
+    rv.team_ws = dc.team_ws;
+    rv.xseq = dc.xseq;
+    rv.part = dc.part;
+    rv.hcnt = dc.hcnt;
+    rv.wkey = dc.wkey;
+    rv.wlo = dc.wlo;
+    rv.wcount = dc.wcount;
+    rv.nch_max = dc.nch_max;
+    rv.lds_cache = dc.lds_cache;
+    Timed tm(K_RESOLVE, stream);
+    HIP_TRY(launch_resolve(rv, rows, stream), "resolve launch");
   }
 
   UnionArgs un;
@@ -987,6 +1037,17 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
                                void *workspace, size_t workspace_bytes, verkv_stream_t stream) {
   return decode_impl(s, st, q, beta, eps, delta, out, workspace, workspace_bytes,
                      reinterpret_cast<hipStream_t>(stream), StepMode{});
+}
+
+verkv_status verkv_decode_step_ex(const verkv_shape *s, const verkv_state *st, const float *q,
+                                  double beta, double eps, double delta, verkv_step_out *out,
+                                  void *workspace, size_t workspace_bytes, uint32_t flags,
+                                  verkv_stream_t stream) {
+  if (flags & ~(uint32_t)VERKV_STEP_RESOLVED) return VERKV_EINVAL;
+  StepMode mode;
+  mode.flags = flags;
+  return decode_impl(s, st, q, beta, eps, delta, out, workspace, workspace_bytes,
+                     reinterpret_cast<hipStream_t>(stream), mode);
 }
 
 verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,

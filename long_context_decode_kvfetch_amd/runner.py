@@ -117,14 +117,14 @@ class Session:
         return torch.from_numpy(np.ascontiguousarray(self.wl.queries[step])).to(self.device)
 
     def step(self, q: torch.Tensor, kappa=None, eps=None, delta=None, stream=None,
-             out: verkv.StepBuffers | None = None):
+             out: verkv.StepBuffers | None = None, resolved: bool = False):
         if self.max_pivots is None:
             raise RuntimeError("Session.step before compress(): the pivot state is not written")
         out = out or self.out
         wl = self.wl
         verkv.decode_step(self.shape, self.state, q, wl.kappa if kappa is None else kappa,
                           wl.eps if eps is None else eps, wl.delta if delta is None else delta,
-                          out, self.dws, stream)
+                          out, self.dws, stream, resolved=resolved)
         verkv.refine(self.shape, self.state, q, self.K_host, self.V_host, out, self.dws, stream)
         return out
 

@@ -20,10 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 12
+PROFILE_KINDS = 13
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
                 "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef", "prefetch",
-                "quantize_sketch"]
+                "quantize_sketch", "resolve"]
 
 
 class VerKVError(RuntimeError):
@@ -94,6 +94,10 @@ def _lib():
         lib.verkv_decode_step.restype = i32
         lib.verkv_decode_step.argtypes = [C.POINTER(Shape), C.POINTER(State), vp, C.c_double,
                                           C.c_double, C.c_double, C.POINTER(StepOut), vp, sz, vp]
+        lib.verkv_decode_step_ex.restype = i32
+        lib.verkv_decode_step_ex.argtypes = [C.POINTER(Shape), C.POINTER(State), vp, C.c_double,
+                                             C.c_double, C.c_double, C.POINTER(StepOut), vp, sz,
+                                             C.c_uint32, vp]
         lib.verkv_refine.restype = i32
         lib.verkv_refine.argtypes = [C.POINTER(Shape), C.POINTER(State), vp, vp, vp,
                                      C.POINTER(StepOut), vp, sz, vp]
@@ -317,9 +321,22 @@ def quantize_sketch(shape: LayerShape, K: torch.Tensor, sketch: torch.Tensor, st
            "verkv_quantize_sketch")
 
 
+STEP_RESOLVED = 1
+
+
 def decode_step(shape: LayerShape, state: LayerState, q: torch.Tensor, beta: float, eps: float,
-                delta: float, out: StepBuffers, workspace: torch.Tensor, stream=None) -> None:
-    """verkv_decode_step (asynchronous on `stream`)."""
+                delta: float, out: StepBuffers, workspace: torch.Tensor, stream=None,
+                resolved: bool = False) -> None:
+    """verkv_decode_step, or verkv_decode_step_ex with VERKV_STEP_RESOLVED (the bias
+    re-solved on each candidate set of the k* cut); asynchronous on `stream`."""
+    if resolved:
+        _check(_lib().verkv_decode_step_ex(C.byref(shape.c), C.byref(state.c), _ptr(q),
+                                           float(beta), float(eps), float(delta), C.byref(out.c),
+                                           _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           STEP_RESOLVED, _stream(stream)),
+               "verkv_decode_step_ex")
+        return
     _check(_lib().verkv_decode_step(C.byref(shape.c), C.byref(state.c), _ptr(q), float(beta),
                                     float(eps), float(delta), C.byref(out.c), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),

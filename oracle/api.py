@@ -28,17 +28,18 @@ def append_sequence(comp, tau_new, n_sink, n_local, layer, stream, seed):
                                      stream, seed) for g in range(len(comp))]
 
 
-def decode_sequence(K, V, comp, q_rows, group, kappa, eps, delta, K_sketch=None):
+def decode_sequence(K, V, comp, q_rows, group, kappa, eps, delta, K_sketch=None, resolved=None):
     """K, V: [Hkv][n][d]; q_rows: [Hkv*G][d].  Returns a dict of per-row arrays
     (m_hat, D, beta_star, eps_hat, certified, kstar, eps_after, n_hat, d_hat, o,
-    lse) and per-KV-head lists fetch / h2d (ascending token ids)."""
+    lse) and per-KV-head lists fetch / h2d (ascending token ids).  resolved: None for the
+    frozen reading of eq. (9)-(10), "scan" or "bisect" for the re-solved one."""
     hkv = K.shape[0]
     rows = []
     for g in range(hkv):
         qs = q_rows[g * group:(g + 1) * group]
         Ks = None if K_sketch is None else K_sketch[g]
         rows.append(kvfetch.decode_kv_head(qs, K[g], V[g], comp[g].r, comp[g].resident,
-                                           kappa, eps, delta, Ks))
+                                           kappa, eps, delta, Ks, resolved))
     keys = [k for k in rows[0] if k not in ("fetch", "h2d")]
     out = {k: np.concatenate([np.atleast_1d(r[k]) if np.ndim(r[k]) < 2 else r[k] for r in rows])
            for k in keys}

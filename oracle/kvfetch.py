@@ -279,12 +279,18 @@ def estimate(q, K, Vv, r, resident, fetched, lam, m_hat):
     return cw @ Vu, float(np.sum(cw))
 
 
-def decode_kv_head(qs, K, Vv, r, resident, kappa, eps, delta, K_sketch=None):
+def decode_kv_head(qs, K, Vv, r, resident, kappa, eps, delta, K_sketch=None, resolved=None):
     """One KV head, its G query rows: decisions, union F, estimator, refinement.
+    resolved: None for the frozen reading of eq. (9)-(10); "scan" or "bisect" for the
+    re-solved reading (decide_head_resolved, k* by the scan or by bisection).
 
     Returns a dict of per-row lists and the KV-head fetch set."""
     Ks = K if K_sketch is None else K_sketch
-    decs = [decide_head(q, Ks, r, kappa, eps, delta) for q in qs]
+    if resolved is None:
+        decs = [decide_head(q, Ks, r, kappa, eps, delta) for q in qs]
+    else:
+        decs = [decide_head_resolved(q, Ks, r, kappa, eps, delta, bisect=resolved == "bisect")
+                for q in qs]
     F = np.unique(np.concatenate([d.fetch for d in decs])) if decs else np.zeros(0, np.int64)
     F = F.astype(np.int64)
     inF = np.zeros(r.shape[0], dtype=bool)
@@ -352,7 +358,38 @@ def select_fetch_resolved(tokens, w, r, kappa, beta_i, V_i, b_i, D, l, eps):
     raise AssertionError("eps_hat of the empty set is 0, below any eps > 0")
 
 
-def decide_head_resolved(q, K_sketch, r, kappa, eps, delta) -> HeadDecision:
+def select_fetch_resolved_bisect(tokens, w, r, kappa, beta_i, V_i, b_i, D, l, eps):
+    """Steps 3-4 of the re-solved reading with k* found by bisection over k.
+
+    eps_hat of L_g[k:] with the bias solved on that set is non-increasing in k: for
+    S' inside S the bias function of S' lies below that of S at every B, so its fixed
+    point is no larger; lambda_i, V_i and b_i are non-decreasing in B, so V(S') <= V(S)
+    and b(S') <= b(S); and eq. (7)'s numerator grows with each of beta, V and b.  The
+    least k with eps_hat < eps is therefore the boundary of a monotone predicate, and
+    bisection over k in [0, |L|] (the empty set has eps_hat = 0) finds the scan's k*
+    with about log2 |L| solves instead of up to |L|.  Rounding can break monotonicity
+    only between candidates whose eps_hat agree to rounding, so the two differ only when
+    eps_hat at the cut is within rounding of eps."""
+    g = fetch_priority(beta_i, V_i, b_i, D, l)
+    order = np.lexsort((tokens, -g))
+
+    def certifies(k):
+        rest = order[k:]
+        return eps_hat_resolved(w[rest], r[rest], kappa, D, l) < eps
+
+    lo, hi = 0, order.size                 # certifies(hi) holds: the empty set
+    if certifies(0):
+        hi = 0
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if certifies(mid):
+            hi = mid
+        else:
+            lo = mid
+    return np.sort(tokens[order[:hi]]), hi, g
+
+
+def decide_head_resolved(q, K_sketch, r, kappa, eps, delta, bisect=False) -> HeadDecision:
     """KVFetch steps 1-4 for one query head, re-solved reading.  Certification (k* = 0) is
     the frozen reading's test; a fetching row gets lambda solved on its kept set L', and its
     beta_star, terms and L fields then describe L' (the set its certificate covers)."""
@@ -369,7 +406,8 @@ def decide_head_resolved(q, K_sketch, r, kappa, eps, delta) -> HeadDecision:
     if e < eps:
         return HeadDecision(m_hat, D, B, e, True, 0, np.zeros(0, np.int64), lam,
                             (beta_i, V_i, b_i), L)
-    F, kstar, _ = select_fetch_resolved(L, wL, rL, kappa, beta_i, V_i, b_i, D, l, eps)
+    select = select_fetch_resolved_bisect if bisect else select_fetch_resolved
+    F, kstar, _ = select(L, wL, rL, kappa, beta_i, V_i, b_i, D, l, eps)
     keep = np.ones(L.size, dtype=bool)
     keep[np.searchsorted(L, F)] = False
     Bk = solve_beta(wL[keep], rL[keep], kappa)

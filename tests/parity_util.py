@@ -47,9 +47,10 @@ def oracle_compress(wl):
             for b, s in enumerate(wl.seqs)]
 
 
-def oracle_step(wl, comp, step, kappa=None, eps=None, delta=None, sketch_of=None):
+def oracle_step(wl, comp, step, kappa=None, eps=None, delta=None, sketch_of=None, resolved=None):
     """The oracle's step for every sequence; `sketch_of` maps a KV head's key rows to the
-    sketch keys its weights come from (None: the keys themselves)."""
+    sketch keys its weights come from (None: the keys themselves); `resolved` selects the
+    re-solved reading of eqs. (9)-(10) ("scan" or "bisect"; None: lambda frozen)."""
     kappa = wl.kappa if kappa is None else kappa
     eps = wl.eps if eps is None else eps
     delta = wl.delta if delta is None else delta
@@ -57,8 +58,28 @@ def oracle_step(wl, comp, step, kappa=None, eps=None, delta=None, sketch_of=None
     for b, s in enumerate(wl.seqs):
         Ks = None if sketch_of is None else np.stack([sketch_of(s.K[g]) for g in range(s.K.shape[0])])
         outs.append(oapi.decode_sequence(s.K, s.V, comp[b], wl.queries[step, b], wl.group,
-                                         kappa, eps, delta, K_sketch=Ks))
+                                         kappa, eps, delta, K_sketch=Ks, resolved=resolved))
     return outs
+
+
+def cut_near_threshold_resolved(comp_bg, q, kappa, eps, delta, K, kstars):
+    """Re-solved reading: True if eps_hat of L_g[k:] (bias solved on it) lies within NEAR
+    of eps at any cut k the two sides found, or just before it."""
+    w, _, D = okf.sketch_weights(q, K)
+    r = comp_bg.r
+    L = np.flatnonzero(r < 1.0)
+    wL, rL = w[L], r[L]
+    l = okf.log_term(delta)
+    B = okf.solve_beta(wL, rL, kappa)
+    terms = okf.token_terms(wL, rL, okf.clip_lambda(wL, rL, B, kappa))
+    order = np.lexsort((L, -okf.fetch_priority(*terms, D, l)))
+    for k0 in kstars:
+        for k in (k0 - 1, k0):
+            if 0 <= k <= L.size:
+                v = okf.eps_hat_resolved(wL[order[k:]], rL[order[k:]], kappa, D, l)
+                if abs(v - eps) <= NEAR * eps:
+                    return True
+    return False
 
 
 def cut_near_threshold(wl, comp_bg, q, kappa, eps, delta, K):
@@ -100,7 +121,7 @@ def rel_l2(a, b):
 
 
 def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None, tol=2e-3,
-                 sketch_of=None):
+                 sketch_of=None, resolved=None):
     """Compare one step; returns a dict of summary numbers."""
     kappa = wl.kappa if kappa is None else kappa
     eps = wl.eps if eps is None else eps
@@ -115,7 +136,8 @@ def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None,
         sl = slice(b * hq, (b + 1) * hq)
         np.testing.assert_allclose(res["m_hat"][sl], oo["m_hat"], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(res["d_sketch"][sl], oo["D"], rtol=1e-9)
-        np.testing.assert_allclose(res["beta_star"][sl], oo["beta_star"], rtol=1e-9, atol=1e-300)
+        if resolved is None:
+            np.testing.assert_allclose(res["beta_star"][sl], oo["beta_star"], rtol=1e-9, atol=1e-300)
         np.testing.assert_allclose(res["eps_hat"][sl], oo["eps_hat"], rtol=1e-9, atol=1e-300)
         for h in range(hq):
             row = b * hq + h
@@ -124,11 +146,22 @@ def compare_step(sess, wl, ocomp, oouts, step, kappa=None, eps=None, delta=None,
             if bool(res["certified"][row]) != bool(oo["certified"][h]) or \
                     int(res["kstar"][row]) != int(oo["kstar"][h]):
                 Kd = s.K[g] if sketch_of is None else sketch_of(s.K[g])
-                near = cut_near_threshold(wl, ocomp[b][g], wl.queries[step, b, h], kappa, eps,
-                                          delta, Kd)
+                if resolved is None:
+                    near = cut_near_threshold(wl, ocomp[b][g], wl.queries[step, b, h], kappa, eps,
+                                              delta, Kd)
+                else:
+                    near = cut_near_threshold_resolved(
+                        ocomp[b][g], wl.queries[step, b, h], kappa, eps, delta, Kd,
+                        (int(res["kstar"][row]), int(oo["kstar"][h])))
                 assert near, (b, h, "decision", res["certified"][row], oo["certified"][h],
                               res["kstar"][row], oo["kstar"][h], res["eps_hat"][row])
                 exempt_units.add((b, g))
+        if resolved is not None:
+            # the kept set's bias (the full L's for certified rows)
+            for h in range(hq):
+                if (b, h // G) not in exempt_units:
+                    np.testing.assert_allclose(res["beta_star"][b * hq + h], oo["beta_star"][h],
+                                               rtol=1e-9, atol=1e-300)
         for g in range(wl.n_kv_heads):
             u = b * wl.n_kv_heads + g
             if (b, g) in exempt_units:
@@ -158,7 +191,8 @@ def session(wl, **kw):
     return Session(wl, **kw)
 
 
-def run_parity(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, sketch_of=None, **kw):
+def run_parity(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, sketch_of=None,
+               resolved=None, **kw):
     """Compress `wl` on the GPU, compare the state with the oracle's, run `steps` decode
     steps (each followed by verkv_check) and compare every one; returns (session, summaries)."""
     from long_context_decode_kvfetch_amd import verkv
@@ -171,10 +205,11 @@ def run_parity(wl, steps=(0,), label="", kappa=None, eps=None, delta=None, sketc
     for st in steps:
         q = sess.queries(st)
         say(f"[parity] {label}: step {st}")
-        sess.step(q, kappa=kappa, eps=eps, delta=delta)
+        sess.step(q, kappa=kappa, eps=eps, delta=delta, resolved=resolved is not None)
         verkv.check(sess.shape, sess.cap, sess.dws)
-        oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta, sketch_of=sketch_of)
+        oo = oracle_step(wl, ocomp, st, kappa=kappa, eps=eps, delta=delta, sketch_of=sketch_of,
+                         resolved=resolved)
         summ.append(compare_step(sess, wl, ocomp, oo, st, kappa=kappa, eps=eps, delta=delta,
-                                 sketch_of=sketch_of))
+                                 sketch_of=sketch_of, resolved=resolved))
     say(f"[parity] {label}: {summ}")
     return sess, summ

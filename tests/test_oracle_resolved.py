@@ -121,3 +121,53 @@ def test_kept_bias_is_the_fixed_point_and_certifies(seed):
     assert abs(d.beta_star - kf.bias_of(wk, rk, d.beta_star, 1.0)) <= 1e-12 * max(1.0, d.beta_star)
     assert kf.eps_hat(*d.terms, D, kf.log_term(0.05)) < 0.05
     assert np.all(d.lam[d.fetch] == kf.decide_head(q, K, r, 1.0, 0.05, 0.05).lam[d.fetch])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bisection_finds_the_scans_cut(seed):
+    """k* by bisection over k equals the scan's least k (eps_hat of the re-solved reading
+    is non-increasing in k), on rows whose candidates all stay clear of eps."""
+    q, K, r = _row(200 + seed, n=400)
+    w, _, D = kf.sketch_weights(q, K)
+    L = np.flatnonzero(r < 1.0)
+    wL, rL = w[L], r[L]
+    l = kf.log_term(0.05)
+    B = kf.solve_beta(wL, rL, 1.0)
+    bi, Vi, b_i = kf.token_terms(wL, rL, kf.clip_lambda(wL, rL, B, 1.0))
+    eps = 0.25 * kf.eps_hat(bi, Vi, b_i, D, l)
+    F1, k1, g = kf.select_fetch_resolved(L, wL, rL, 1.0, bi, Vi, b_i, D, l, eps)
+    F2, k2, _ = kf.select_fetch_resolved_bisect(L, wL, rL, 1.0, bi, Vi, b_i, D, l, eps)
+    assert k1 > 0 and k1 == k2 and np.array_equal(F1, F2)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_resolved_eps_hat_is_monotone_in_k(seed):
+    """The property the bisection rests on, checked at every k of a 300-token row."""
+    q, K, r = _row(300 + seed)
+    w, _, D = kf.sketch_weights(q, K)
+    L = np.flatnonzero(r < 1.0)
+    wL, rL = w[L], r[L]
+    l = kf.log_term(0.05)
+    B = kf.solve_beta(wL, rL, 1.0)
+    terms = kf.token_terms(wL, rL, kf.clip_lambda(wL, rL, B, 1.0))
+    order = np.lexsort((L, -kf.fetch_priority(*terms, D, l)))
+    vals = [kf.eps_hat_resolved(wL[order[k:]], rL[order[k:]], 1.0, D, l) for k in range(L.size + 1)]
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(vals, vals[1:]))
+    assert vals[-1] == 0.0
+
+
+def test_resolved_decode_of_a_kv_head_certifies_every_row():
+    """decode_kv_head with the re-solved reading: every row ends with eps_hat(L' minus F)
+    below eps, the union F is at most the frozen reading's here, and both forms of the
+    cut agree."""
+    q, K, r = _row(400)
+    rng = np.random.default_rng(1)
+    V = rng.standard_normal(K.shape)
+    qs = [q, q * 1.2, -q]
+    resident = r >= 1.0
+    a = kf.decode_kv_head(qs, K, V, r, resident, 1.0, 0.05, 0.05, resolved="scan")
+    b = kf.decode_kv_head(qs, K, V, r, resident, 1.0, 0.05, 0.05, resolved="bisect")
+    fz = kf.decode_kv_head(qs, K, V, r, resident, 1.0, 0.05, 0.05)
+    assert np.array_equal(a["fetch"], b["fetch"]) and np.array_equal(a["kstar"], b["kstar"])
+    assert np.all(a["eps_after"] < 0.05)
+    assert a["fetch"].size <= fz["fetch"].size
