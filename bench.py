@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-pivot-batch", action="store_true",
                    help="skip the pivotal-stream measurement at the 16-sequence batch")
+    p.add_argument("--no-resolved", action="store_true",
+                   help="skip the leg with the re-solved reading of eqs. (9)-(10)")
     p.add_argument("--no-nofetch", action="store_true",
                    help="skip the no-fetch control leg (uniform scores, eps = 0.2)")
     p.add_argument("--no-2bit", action="store_true",
@@ -240,6 +242,48 @@ def pivotal_stream(torch, steps=8, fetch_steps=8):
     del sess
     torch.cuda.empty_cache()
     return piv
+
+
+def resolved_leg(torch, sessions, K=64, W=8, P=16):
+    """The same rotated 32K layers with the re-solved reading of eqs. (9)-(10) (the bias
+    solved on each candidate set of the k* cut, verkv_decode_step_ex): steps/s, what is
+    fetched and what crosses the host link, and the kernel times."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import verkv
+    L = len(sessions)
+    per_layer = sessions[0].qdev.shape[0]
+
+    def run(i):
+        s2 = sessions[i % L]
+        s2.step(s2.qdev[(i // L) % per_layer], resolved=True)
+
+    for i in range(W):
+        run(i)
+    torch.cuda.synchronize()
+    ms, per = timed(torch, run, W, K)
+    fail_on_flags(sessions, "the re-solved reading leg")
+    verkv.profile_begin(9 * P + 16)
+    for i in range(W + K, W + K + P):
+        run(i)
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    cert = fetched = h2d = nrow = 0
+    for s2 in sessions:
+        s2.step(s2.qdev[0], resolved=True)
+        r = s2.results_numpy()
+        assert np.all(r["eps_after"] < s2.wl.eps), "a row finished uncertified"
+        cert += int(r["certified"].sum())
+        fetched += int(r["fetch_count"].sum())
+        h2d += int(r["h2d_count"].sum())
+        nrow += r["certified"].size
+    ntok = L * N_CTX * 8
+    return {"workload": "the rotated 32K GQA layers of the headline line, re-solved reading",
+            "steps": K, "steps_per_s": round(K / (ms * 1e-3), 2), "ms_per_step": round(ms / K, 4),
+            "step_ms": percentiles(per), "rows_certified_without_fetch": cert / nrow,
+            "fetched_fraction_of_cache": fetched / ntok, "h2d_fraction_of_cache": h2d / ntok,
+            "h2d_bytes_per_step": h2d / L * 128 * 2,
+            "kernel_avg_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in prof.items() if v[1]}}
 
 
 def no_fetch_leg(torch, L, K=64, W=8):
@@ -722,6 +766,10 @@ def main():
             "units_per_launch": tok_heads}
     step_bytes = step_algorithmic_bytes(tok_heads, piv_rows)
     h2d_peak = h2d_bandwidth(torch)
+    resolved = None
+    if not args.no_resolved:
+        log("[bench] re-solved reading of eqs. (9)-(10) on the same layers")
+        resolved = resolved_leg(torch, sessions, K=min(K, 64), W=min(W, 8))
     nofetch = None
     if not args.no_nofetch:
         log("[bench] no-fetch control: uniform scores, eps = 0.2")
@@ -777,6 +825,7 @@ def main():
                                "(step_stats.h2d_bytes_per_step)"},
         "pivotal_stream": piv,
         "no_fetch": nofetch,
+        "resolved_reading": resolved,
         "sketch_2bit": sk2,
         "decode_36_layers": dec36,
         "long_context": longc,
