@@ -210,6 +210,29 @@ __device__ __forceinline__ void newton_add(NewtonAcc &v, double ri, double wi, d
   top2_merge(v.bc1, v.bc2, pmid ? 0.0 : bc, 0.0);
   top2_merge(v.bm1, v.bm2, pmid ? kappa * mx * iq : 0.0, 0.0);
 }
+// The four fields a Newton step needs (the linear model c0 - c1 B of f on the piece and
+// the piece's ends), reduced over the block exactly as block_newton reduces them.
+struct Lin { double c0, c1, lo, hi; };
+__device__ __forceinline__ Lin block_lin(const NewtonAcc &a, double *scr /*[4*DC_NW]*/) {
+  double c0 = wave_sum(a.c0), c1 = wave_sum(a.c1);
+  double lo = wave_max(a.lo), hi = wave_min(a.hi);
+  const int w = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  if (lane == 0) {
+    double *q = scr + w;
+    q[0] = c0; q[DC_NW] = c1; q[2 * DC_NW] = lo; q[3 * DC_NW] = hi;
+  }
+  __syncthreads();
+  const int k = lane & 15;
+  const bool in = k < DC_NW;
+  const double *q = scr + (in ? k : 0);
+  Lin o;
+  o.c0 = sum16(in ? q[0] : 0.0); o.c1 = sum16(in ? q[DC_NW] : 0.0);
+  o.lo = max16(in ? q[2 * DC_NW] : 0.0); o.hi = min16(in ? q[3 * DC_NW] : INFINITY);
+  __syncthreads();
+  return o;
+}
+
 __device__ __forceinline__ NewtonAcc block_newton(NewtonAcc v, double *scr /*[NQ*DC_NW]*/) {
   v.c0 = wave_sum(v.c0); v.c1 = wave_sum(v.c1);
   v.vc = wave_sum(v.vc); v.vm = wave_sum(v.vm); v.cnt = wave_sum(v.cnt);

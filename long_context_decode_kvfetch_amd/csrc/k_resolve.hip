@@ -94,6 +94,15 @@ __global__ __launch_bounds__(DC_NT) void k_resolve(ResolveArgs a) {
     __syncthreads();                                                        \
   } while (0)
 
+  double rb0[TR], wb0[TR];                   // the slice, loaded ahead (LDS cache only)
+  if (lcache) {
+#pragma unroll
+    for (int k = 0; k < TR; ++k) {
+      const int i = s0 + tid + k * DC_NT;
+      rb0[k] = i < s1 ? rr[i] : 2.0;
+      wb0[k] = i < s1 ? wcr[i] : 0.0;
+    }
+  }
   // chunk scales exp(m_c - m_hat) (the decision kernel's), f(0) of the full L
   const double *cs = a.cscale + row_chunk_base(a.t, b, h);
   const double *cz = a.cf0 + row_chunk_base(a.t, b, h);
@@ -104,11 +113,14 @@ __global__ __launch_bounds__(DC_NT) void k_resolve(ResolveArgs a) {
   }
   const double f0 = block_sum<DC_NT>(zloc, scr);   // its barrier also publishes s_scale
   if (lcache) {
-    for (int i = s0 + tid; i < s1; i += DC_NT) {
-      const double ri = rr[i];
+#pragma unroll
+    for (int k = 0; k < TR; ++k) {
+      const int i = s0 + tid + k * DC_NT;
+      if (i >= s1) continue;
+      const double ri = rb0[k];
       const bool inL = ri < 1.0;
       s_r[i - s0] = ri;
-      s_w[i - s0] = inL ? wcr[i] * s_scale[i / SKETCH_CHUNK] : 0.0;
+      s_w[i - s0] = inL ? wb0[k] * s_scale[i / SKETCH_CHUNK] : 0.0;
       s_ir[i - s0] = inL && ri > 0.0 ? 1.0 / ri : 0.0;
       s_rq[i - s0] = inL ? ri / (1.0 - ri) : 0.0;
     }
@@ -210,32 +222,47 @@ __global__ __launch_bounds__(DC_NT) void k_resolve(ResolveArgs a) {
       NewtonAcc v{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
       FOR_T(
         if (key < tk || (key == tk && lo < tl)) newton_add(v, ri, wi, ir, rq, B, kappa, inv_kappa);)
-      NewtonAcc o = block_newton(v, scr);
+      // the step needs the linear model and its piece; the eq. (7) totals of the pass
+      // are reduced once the root lies on that piece
+      Lin lm = block_lin(v, scr);
       if (T > 1) {
         double *sl = SLOT();
         if (tid == 0) {
           double *q = sl + m * PART;
-          xput(q + 0, o.c0); xput(q + 1, o.c1); xput(q + 2, o.lo); xput(q + 3, o.hi);
-          xput(q + 4, o.vc); xput(q + 5, o.vm); xput(q + 6, o.cnt); xput(q + 7, o.bc1);
-          xput(q + 8, o.bc2); xput(q + 9, o.bm1); xput(q + 10, o.bm2);
+          xput(q + 0, lm.c0); xput(q + 1, lm.c1); xput(q + 2, lm.lo); xput(q + 3, lm.hi);
         }
         TEAM_STAGE(sl);
-        o = NewtonAcc{0.0, 0.0, 0.0, INFINITY, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        lm = Lin{0.0, 0.0, 0.0, INFINITY};
         for (int k = 0; k < T; ++k) {
           const double *q = s_part + k * PART;
-          o.c0 += q[0]; o.c1 += q[1]; o.lo = fmax(o.lo, q[2]); o.hi = fmin(o.hi, q[3]);
-          o.vc += q[4]; o.vm += q[5]; o.cnt += q[6];
-          top2_merge(o.bc1, o.bc2, q[7], q[8]);
-          top2_merge(o.bm1, o.bm2, q[9], q[10]);
+          lm.c0 += q[0]; lm.c1 += q[1]; lm.lo = fmax(lm.lo, q[2]); lm.hi = fmin(lm.hi, q[3]);
         }
         __syncthreads();
       }
-      const double hB = B * (1.0 + o.c1) - o.c0;
-      double Bn = o.c0 / (1.0 + o.c1);
-      bool on_piece = (Bn >= o.lo && Bn <= o.hi);
+      const double hB = B * (1.0 + lm.c1) - lm.c0;
+      double Bn = lm.c0 / (1.0 + lm.c1);
+      bool on_piece = (Bn >= lm.lo && Bn <= lm.hi);
       if (!on_piece && hB == 0.0) { Bn = B; on_piece = true; }
       if (eval_only) { Bn = B; on_piece = true; }  // the model of B's own piece, at B
       if (on_piece) {
+        NewtonAcc o = block_newton(v, scr);
+        if (T > 1) {
+          double *sl = SLOT();
+          if (tid == 0) {
+            double *q = sl + m * PART;
+            xput(q + 4, o.vc); xput(q + 5, o.vm); xput(q + 6, o.cnt); xput(q + 7, o.bc1);
+            xput(q + 8, o.bc2); xput(q + 9, o.bm1); xput(q + 10, o.bm2);
+          }
+          TEAM_STAGE(sl);
+          o = NewtonAcc{lm.c0, lm.c1, lm.lo, lm.hi, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+          for (int k = 0; k < T; ++k) {
+            const double *q = s_part + k * PART;
+            o.vc += q[4]; o.vm += q[5]; o.cnt += q[6];
+            top2_merge(o.bc1, o.bc2, q[7], q[8]);
+            top2_merge(o.bm1, o.bm2, q[9], q[10]);
+          }
+          __syncthreads();
+        }
         // eq. (7) on this piece at Bn: bias c0 - Bn c1, V = vc + Bn^2 vm, b the larger of
         // the constant b_i and Bn times the largest mid-piece coefficient
         Bout = Bn;

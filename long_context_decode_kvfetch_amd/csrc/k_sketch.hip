@@ -116,7 +116,12 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   const int Hq = a.t.Hkv * G;
   const int sidx = lane & (LPT - 1);        // lane within the token's group
   const int tsub = lane / LPT;              // token of the load step
-  const int rsel = LPT == 8 ? (sidx >> 1) & 3 : (sidx >> 2) & 3;   // row of four it ends with
+  // G = 4 over 8 lanes: lane s keeps query row (slot ^ pm) in register slot `slot`, with
+  // pm = 0, 0, 1, 1, 3, 3, 2, 2 for s = 0..7, so every level of the reduce-scatter keeps
+  // and sends the same slots in every lane (no per-lane selects); it ends with row pm.
+  constexpr bool PERM = (G == 4 && LPT == 8);
+  const int pm = (((sidx >> 2) & 1) << 1) | (((sidx >> 1) ^ (sidx >> 2)) & 1);
+  const int rsel = PERM ? pm : (LPT == 8 ? (sidx >> 1) & 3 : (sidx >> 2) & 3);   // row it ends with
   const bool writer = LPT == 8 ? (sidx & 1) == 0 : (sidx & 3) == 0;
   const int base = c * CH;
   double (*sc)[CH] = s_sc[wv];
@@ -144,7 +149,8 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   double qd[G][EPT];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float *qr = a.q + ((int64_t)b * Hq + g * G + j) * D;
+    const int jr = PERM ? (j ^ pm) : j;       // the query row of register slot j
+    const float *qr = a.q + ((int64_t)b * Hq + g * G + jr) * D;
 #pragma unroll
     for (int p = 0; p < PPL; ++p)
 #pragma unroll
@@ -215,8 +221,19 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
       const int tk = (bi * SB + k) * TPS + tsub;        // token within the chunk
 #pragma unroll
       for (int q4 = 0; q4 < NG4; ++q4) {
-        const double v = LPT == 8 ? reduce_scatter4x8(acc + 4 * q4, sidx)
-                                  : reduce_scatter4x16(acc + 4 * q4, sidx);
+        double v;
+        if constexpr (PERM) {
+          // lanes i and 7-i: keep slots 0, 1 and add the partner's slots 2, 3 (its rows
+          // 0, 1 here); lanes i and i^2: keep slot 0, add the partner's slot 1; then the
+          // pair i, i^1 holds the same row
+          double k0 = acc[0] + dpp_d<DPP_HALF_MIRROR>(acc[2]);
+          const double k1 = acc[1] + dpp_d<DPP_HALF_MIRROR>(acc[3]);
+          k0 += dpp_d<DPP_XOR2>(k1);
+          v = k0 + dpp_d<DPP_XOR1>(k0);
+        } else {
+          v = LPT == 8 ? reduce_scatter4x8(acc + 4 * q4, sidx)
+                       : reduce_scatter4x16(acc + 4 * q4, sidx);
+        }
         const int j = 4 * q4 + rsel;
         const double sv = base + tk < n ? v * a.inv_sqrt_d : -INFINITY;
         if (writer && j < G) sc[j][tk] = sv;
@@ -242,9 +259,12 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
     m = fmax(m, shfl_xor_d(m, 16));
     m = fmax(m, shfl_xor_d(m, 32));
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-      mrow[j] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(m), 2 * j),
-                                 __builtin_amdgcn_readlane(__double2loint(m), 2 * j));
+    for (int j = 0; j < G; ++j) {
+      // the lane that ends with row j: 2 j, or 0, 2, 6, 4 for the permuted slots
+      const int lj = PERM ? (j == 0 ? 0 : j == 1 ? 2 : j == 2 ? 6 : 4) : 2 * j;
+      mrow[j] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(m), lj),
+                                 __builtin_amdgcn_readlane(__double2loint(m), lj));
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
