@@ -235,7 +235,19 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
  *          step prefetches, and the rows staged for it (see verkv_state.v_host).
  *          Results do not depend on these: zero-filled or foreign contents only cost
  *          time (staged rows carry the identity of the cache they came from).
- * No host synchronisation and no host-memory traffic. */
+ * No host synchronisation and no host-memory traffic.
+ * out->o and out->lse are not written here: verkv_refine always follows, also when
+ * every row is certified (then it finishes o from the resident-pivot partials and
+ * reads nothing from the host).  The split is for overlap, not for skipping: the
+ * resident-pivot attention runs beside the host reads inside verkv_refine, so a
+ * step that finished certified rows here would put that attention on the critical
+ * path of the rows that fetch.
+ * One decode step per device at a time: the decision kernel groups the workgroups of
+ * a query row into a team that exchanges partials through memory, and sizes the
+ * teams so that every member is resident on the device at once.  Steps issued on
+ * two streams of one device could leave members of each waiting for CUs the other
+ * holds; the waits are bounded (status bit 4, verkv_check) but the step's results
+ * are then wrong.  Serialise decode steps on one device (one stream, or events). */
 verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, const float *q,
                                double beta, double eps, double delta, verkv_step_out *out,
                                void *workspace, size_t workspace_bytes, verkv_stream_t stream);

@@ -22,6 +22,19 @@ FLAGS = [
 
 HEADER = os.path.join(os.path.dirname(HERE), "include", "verkv.h")
 
+# A second build with AddressSanitizer and UndefinedBehaviorSanitizer on the host code
+# only (the C ABI's argument checks, layouts and launch set-up; the GPU code is built
+# as usual).  It needs the sanitizer runtime preloaded into the process that loads it
+# (tests/test_host_sanitizers.py does that for the host ABI tests).
+SANITIZED_LIB = os.path.join(HERE, "libverkv_hostsan.so")
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-shared-libsan",
+]
+
 
 def source_hash() -> str:
     """SHA-256 over every file under csrc/, the public header and the compiler flags: the
@@ -40,10 +53,21 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def build(verbose: bool = False) -> str:
+def sanitizer_runtime() -> str:
+    """The AddressSanitizer runtime of the compiler that builds SANITIZED_LIB."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return found[-1]
+
+
+def build(verbose: bool = False, sanitize_host: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, f'-DVERKV_SOURCE_HASH="{source_hash()}"', "-x", "hip",
+    out = SANITIZED_LIB if sanitize_host else LIB
+    tmp = out + ".tmp"
+    extra = HOST_SANITIZE if sanitize_host else []
+    cmd = [hipcc, *FLAGS, *extra, f'-DVERKV_SOURCE_HASH="{source_hash()}"', "-x", "hip",
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -51,8 +75,8 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libverkv.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -423,6 +423,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     }                                                                          \
   }
 
+  STAMP();
   const double thr = eps * Dd;
   double bel_beta = 0.0, bel_V = 0.0, bel_b = 0.0;     // tokens below the window
   uint64_t pkey = 0;
@@ -568,6 +569,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
     lev = L;
     const uint32_t cntj = h_cnt[j];
     __syncthreads();
+    STAMP();
     if (cntj <= (uint32_t)WIN) break;
   }
 
@@ -593,6 +595,7 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
           if (p < WIN) { w_key[p] = key; w_lo[p] = lo; }
         }
       })
+    STAMP();
     Red4 bo = block_red4(bel, scr);
     int wcount;
     if (T > 1) {

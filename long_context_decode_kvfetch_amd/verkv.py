@@ -15,7 +15,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libverkv.so")
+# VERKV_LIBRARY names another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("VERKV_LIBRARY") or os.path.join(_HERE, "libverkv.so")
 
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
