@@ -50,6 +50,8 @@ def parse():
                    help="skip the leg with the re-solved reading of eqs. (9)-(10)")
     p.add_argument("--no-nofetch", action="store_true",
                    help="skip the no-fetch control leg (uniform scores, eps = 0.2)")
+    p.add_argument("--no-gather", action="store_true",
+                   help="skip the host-fetch comparison (zero-copy kernel against memcpy per run)")
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--sweep", action="store_true",
@@ -338,6 +340,107 @@ def no_fetch_leg(torch, L, K=64, W=8):
            "fetched_tokens": fetched, "step_algorithmic_bytes": int(alg),
            "step_GBps": round(alg / (ms / K * 1e-3) / 1e9, 1), "kernel_avg_us": kern}
     del sess
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_gather_leg(torch, wl, qdev, reps=3):
+    """KVFetch step 5's host fetch moved three ways, for the F minus S value rows of one
+    step of the 32K GQA layer (the rows the step needs from CPU memory):
+      zero_copy   the host-row kernel of the decode path, which reads the rows in place
+                  (zero-copy loads) and forms their attention terms, with cross-step
+                  staging off so every row crosses the link;
+      memcpy_runs verkv_gather_rows_memcpy: one hipMemcpyAsync per run of consecutive
+                  rows, from the host copy of the fetch list;
+      cpu_gather_bulk  the rows gathered by the CPU into a pinned buffer, then one copy;
+    and, as the link's ceiling, one contiguous copy of the same byte count."""
+    import numpy as np
+    from long_context_decode_kvfetch_amd import verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+    sess = Session(wl, prefetch=False)
+    sess.compress()
+    for i in range(2):
+        sess.step(qdev[i])
+    torch.cuda.synchronize()
+    res = sess.results_numpy()
+    st = sess.state_numpy()
+    lists = [F[~h["resident"][F]].astype(np.int32) for F, h in zip(res["fetch"], st)]
+    row_bytes = 128 * 2
+    nrows = int(sum(x.size for x in lists))
+    nbytes = nrows * row_bytes
+    cap = sess.shape.caps[0]
+    head_bytes = cap * row_bytes
+    V = sess.V_host
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    verkv.profile_begin(16 * reps + 16)
+    for i in range(reps):
+        sess.step(qdev[2 + i])
+    torch.cuda.synchronize()
+    prof = verkv.profile_report()
+    verkv.profile_end()
+    zc_ms, zc_n = prof["attend_host"]
+    zc_us = zc_ms / zc_n * 1e3
+    h2d = int(sess.results_numpy()["h2d_count"].sum()) * row_bytes
+
+    def runs_copy():
+        off, runs = 0, 0
+        for u, x in enumerate(lists):
+            runs += verkv.gather_rows_memcpy(V.data_ptr() + u * head_bytes, row_bytes, x,
+                                             dst.data_ptr() + off)
+            off += x.size * row_bytes
+        return runs
+    runs_copy()
+    torch.cuda.synchronize()
+    gpu_ms, cpu_ms = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        e0.record()
+        runs = runs_copy()
+        e1.record()
+        cpu_ms.append((time.perf_counter() - t0) * 1e3)
+        torch.cuda.synchronize()
+        gpu_ms.append(e0.elapsed_time(e1))
+    runs_us = float(np.median(gpu_ms)) * 1e3
+    # the rows are identical to the host cache's
+    chk = dst[: lists[0].size * row_bytes].view(torch.bfloat16).view(-1, 128).cpu()
+    ref = V.view(-1, cap, 128)[0][torch.from_numpy(lists[0]).long()]
+    assert torch.equal(chk, ref), "memcpy gather moved the wrong rows"
+
+    bounce = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    bview = bounce.view(torch.bfloat16).view(-1, 128)
+    heads = V.view(-1, cap, 128)
+    idx_t = [torch.from_numpy(x).long() for x in lists]
+    g_ms, c_ms = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        off = 0
+        for u, x in enumerate(idx_t):
+            torch.index_select(heads[u], 0, x, out=bview[off:off + x.numel()])
+            off += x.numel()
+        g_ms.append((time.perf_counter() - t0) * 1e3)
+        e0.record()
+        dst.copy_(bounce, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        c_ms.append(e0.elapsed_time(e1))
+    bulk_us = float(np.median(c_ms)) * 1e3
+    gather_us = float(np.median(g_ms)) * 1e3
+    out = {"workload": "F minus S value rows of one step of the 32K GQA layer (bf16, 256 B per row)",
+           "rows": nrows, "bytes": nbytes, "runs": int(runs),
+           "mean_run_rows": round(nrows / max(1, runs), 2),
+           "zero_copy": {"us": round(zc_us, 1), "GBps": round(h2d / (zc_us * 1e-6) / 1e9, 1),
+                         "host_bytes": h2d,
+                         "note": "host-row kernel of the decode path, attention terms included, staging off"},
+           "memcpy_runs": {"us": round(runs_us, 1), "GBps": round(nbytes / (runs_us * 1e-6) / 1e9, 2),
+                           "cpu_issue_ms": round(float(np.median(cpu_ms)), 2)},
+           "cpu_gather_bulk": {"us": round(gather_us + bulk_us, 1), "cpu_gather_us": round(gather_us, 1),
+                               "copy_us": round(bulk_us, 1), "threads": torch.get_num_threads(),
+                               "GBps": round(nbytes / ((gather_us + bulk_us) * 1e-6) / 1e9, 1)},
+           "contiguous_copy_ceiling": {"us": round(bulk_us, 1),
+                                       "GBps": round(nbytes / (bulk_us * 1e-6) / 1e9, 1)}}
+    del sess, dst, bounce
     torch.cuda.empty_cache()
     return out
 
@@ -774,6 +877,10 @@ def main():
     if not args.no_nofetch:
         log("[bench] no-fetch control: uniform scores, eps = 0.2")
         nofetch = no_fetch_leg(torch, L)
+    gather = None
+    if not args.no_gather:
+        log("[bench] host fetch: zero-copy kernel against memcpy per run")
+        gather = host_gather_leg(torch, sessions[0].wl, sessions[0].qdev)
     sk2 = None
     if not args.no_2bit:
         log("[bench] 2-bit sketch: the same layers, rebuilt")
@@ -825,6 +932,7 @@ def main():
                                "(step_stats.h2d_bytes_per_step)"},
         "pivotal_stream": piv,
         "no_fetch": nofetch,
+        "host_fetch_variants": gather,
         "resolved_reading": resolved,
         "sketch_2bit": sk2,
         "decode_36_layers": dec36,

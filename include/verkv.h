@@ -304,6 +304,27 @@ verkv_status verkv_step_noalloc(const verkv_shape *s, const verkv_state *st, con
                                 verkv_stream_t stream);
 size_t verkv_noalloc_scratch_bytes(void);
 
+/* The memcpy form of the host fetch of KVFetch step 5 (picx.dev summary page,
+ * "KVFETCH" step 5: the rows of F \ S move from CPU memory to the GPU; the abstract
+ * page notes that these transfers can dominate decode latency).  The decode path does
+ * not use it: verkv_refine reads those rows in place with zero-copy loads from its
+ * kernels, which needs no host copy of the fetch list and no call per run.  This entry
+ * point is the alternative for comparison, and for callers that want the rows
+ * themselves: rows idx[0..count) of the row array `src` (row_bytes each) are copied
+ * to dst[0..count) with one hipMemcpyAsync per run of consecutive indices, on
+ * `stream`.
+ *   src    pinned host memory (or device memory), not owned
+ *   idx    [count] strictly ascending row indices >= 0, HOST memory (read during the
+ *          call; a list produced by verkv_decode_step must be copied to the host first)
+ *   dst    [count][row_bytes] device memory, written asynchronously
+ *   runs   [host, may be NULL] number of copies issued
+ * VERKV_EINVAL for NULL pointers, count < 0, row_bytes = 0 or a list that is not
+ * strictly ascending (checked before any copy is issued); VERKV_EHIP if a copy cannot
+ * be enqueued (copies issued before it stay enqueued). */
+verkv_status verkv_gather_rows_memcpy(const void *src, size_t row_bytes, const int32_t *idx,
+                                      int32_t count, void *dst, int64_t *runs,
+                                      verkv_stream_t stream);
+
 /* Optional kernel timing (instrumentation).  verkv_profile_begin creates 2*max_launches
  * HIP events (the only allocation the library makes, done here and not per step) and
  * turns recording on: every kernel launched afterwards by this library, up to

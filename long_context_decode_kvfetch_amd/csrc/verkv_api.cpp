@@ -1142,6 +1142,34 @@ int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kind
   return VERKV_OK;
 }
 
+verkv_status verkv_gather_rows_memcpy(const void *src, size_t row_bytes, const int32_t *idx,
+                                      int32_t count, void *dst, int64_t *runs,
+                                      verkv_stream_t stream) {
+  if (runs) *runs = 0;
+  if (!src || !dst || row_bytes == 0 || count < 0 || (count > 0 && !idx)) return VERKV_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    if (idx[i] < 0 || (i > 0 && idx[i] <= idx[i - 1])) {
+      std::snprintf(g_last_error, sizeof(g_last_error), "row list is not ascending at entry %d", (int)i);
+      return VERKV_EINVAL;
+    }
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t *s8 = static_cast<const uint8_t *>(src);
+  uint8_t *d8 = static_cast<uint8_t *>(dst);
+  int64_t nrun = 0;
+  for (int32_t i = 0; i < count;) {
+    int32_t j = i + 1;
+    while (j < count && idx[j] == idx[j - 1] + 1) ++j;      // one run of consecutive rows
+    HIP_TRY(hipMemcpyAsync(d8 + (size_t)i * row_bytes, s8 + (size_t)idx[i] * row_bytes,
+                           (size_t)(j - i) * row_bytes, hipMemcpyHostToDevice, st),
+            "hipMemcpyAsync");
+    ++nrun;
+    i = j;
+  }
+  if (runs) *runs = nrun;
+  return VERKV_OK;
+}
+
 void verkv_profile_end(void) {
   for (auto &e : g_prof.ev)
     if (e) (void)hipEventDestroy(e);

@@ -112,6 +112,8 @@ def _lib():
                                            C.c_double, C.c_double, vp, vp, C.POINTER(StepOut),
                                            vp, vp]
         lib.verkv_noalloc_scratch_bytes.restype = sz
+        lib.verkv_gather_rows_memcpy.restype = i32
+        lib.verkv_gather_rows_memcpy.argtypes = [vp, sz, vp, i32, vp, C.POINTER(C.c_int64), vp]
         lib.verkv_check.restype = i32
         lib.verkv_check.argtypes = [vp, C.POINTER(Shape), i32, vp]
         _LIB = lib
@@ -362,6 +364,20 @@ def step_noalloc(shape: LayerShape, state: LayerState, q: torch.Tensor, beta: fl
                                      float(eps), float(delta), _ptr(K_host), _ptr(V_host),
                                      C.byref(out.c), _ptr(status), _stream(stream)),
            "verkv_step_noalloc")
+
+
+def gather_rows_memcpy(src_ptr: int, row_bytes: int, idx, dst_ptr: int, stream=None) -> int:
+    """verkv_gather_rows_memcpy: rows idx (ascending, host int32 array) of the row array
+    at src_ptr to dst_ptr, one hipMemcpyAsync per run of consecutive rows (asynchronous
+    on `stream`).  Returns the number of copies issued."""
+    import numpy as np
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    runs = C.c_int64(0)
+    _check(_lib().verkv_gather_rows_memcpy(C.c_void_p(src_ptr), int(row_bytes),
+                                           idx.ctypes.data_as(C.c_void_p), int(idx.size),
+                                           C.c_void_p(dst_ptr), C.byref(runs), _stream(stream)),
+           "verkv_gather_rows_memcpy")
+    return runs.value
 
 
 def check(shape: LayerShape, cap: int, workspace: torch.Tensor, stream=None) -> None:

@@ -162,3 +162,25 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(verkv, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         verkv.lib()
+
+
+def test_gather_rows_memcpy_checks_its_list_before_copying(vk):
+    """The memcpy form of the host fetch rejects a bad list before it issues any copy
+    (the pointers below are never dereferenced: no copy is enqueued)."""
+    lib = vk.lib()
+    import numpy as np
+    runs = C.c_int64(-1)
+    bad = np.array([3, 5, 5, 9], dtype=np.int32)
+    st = lib.verkv_gather_rows_memcpy(C.c_void_p(16), 256, bad.ctypes.data_as(C.c_void_p), 4,
+                                      C.c_void_p(16), C.byref(runs), None)
+    assert st == vk.EINVAL and runs.value == 0
+    assert "ascending" in lib.verkv_last_error().decode()
+    neg = np.array([-1, 2], dtype=np.int32)
+    assert lib.verkv_gather_rows_memcpy(C.c_void_p(16), 256, neg.ctypes.data_as(C.c_void_p), 2,
+                                        C.c_void_p(16), None, None) == vk.EINVAL
+    assert lib.verkv_gather_rows_memcpy(None, 256, None, 0, C.c_void_p(16), None, None) == vk.EINVAL
+    assert lib.verkv_gather_rows_memcpy(C.c_void_p(16), 0, None, 0, C.c_void_p(16), None, None) == vk.EINVAL
+    runs.value = -1
+    assert lib.verkv_gather_rows_memcpy(C.c_void_p(16), 256, None, 0, C.c_void_p(16),
+                                        C.byref(runs), None) == vk.OK
+    assert runs.value == 0

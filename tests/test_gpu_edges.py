@@ -165,3 +165,23 @@ def test_pageable_value_cache_is_rejected_before_any_kernel():
     torch.cuda.synchronize()
     assert torch.all(sess.out.kstar == -7)
     say("[parity] pageable v_host rejected, nothing enqueued")
+
+
+# ------------------------------------------------------------------ memcpy form of the host fetch
+def test_gather_rows_memcpy_moves_the_listed_rows():
+    """verkv_gather_rows_memcpy copies exactly the listed rows of a pinned row array, one
+    copy per run of consecutive rows (runs of 1, several and the last row included)."""
+    from long_context_decode_kvfetch_amd import verkv
+    rng = np.random.default_rng(5)
+    rows = torch.from_numpy(rng.standard_normal((5000, 128)).astype(np.float32)).to(torch.bfloat16)
+    src = torch.empty(rows.shape, dtype=rows.dtype, pin_memory=True)
+    src.copy_(rows)
+    idx = np.unique(np.concatenate([rng.choice(4990, 1200, replace=False), np.arange(4990, 5000),
+                                    np.arange(100, 140)])).astype(np.int32)
+    dst = torch.full((idx.size, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    runs = verkv.gather_rows_memcpy(src.data_ptr(), 256, idx, dst.data_ptr())
+    torch.cuda.synchronize()
+    want = int(1 + np.count_nonzero(np.diff(idx) != 1))
+    assert runs == want
+    assert torch.equal(dst.cpu(), rows[torch.from_numpy(idx).long()])
+    say(f"[gather] {idx.size} rows in {runs} copies")
