@@ -52,6 +52,8 @@ def parse():
                    help="skip the no-fetch control leg (uniform scores, eps = 0.2)")
     p.add_argument("--no-gather", action="store_true",
                    help="skip the host-fetch comparison (zero-copy kernel against memcpy per run)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the leg replaying each layer-step as a captured HIP graph")
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--sweep", action="store_true",
@@ -341,6 +343,49 @@ def no_fetch_leg(torch, L, K=64, W=8):
            "step_GBps": round(alg / (ms / K * 1e-3) / 1e9, 1), "kernel_avg_us": kern}
     del sess
     torch.cuda.empty_cache()
+    return out
+
+
+def graph_leg(torch, sessions, K=64, W=8):
+    """The 32K layer-step (verkv_decode_step + verkv_refine, staging on) captured once per
+    layer into a HIP graph and replayed over the rotated layers, against the same steps
+    launched kernel by kernel; both copy the step's queries into the layer's query buffer
+    first.  Steps/s and per-step percentiles of both."""
+    from long_context_decode_kvfetch_amd import verkv
+    L = len(sessions)
+    per = sessions[0].qdev.shape[0]
+    qbuf = [s.qdev[0].clone() for s in sessions]
+    for s, qb in zip(sessions, qbuf):
+        s.step(qb)
+    torch.cuda.synchronize()
+    graphs = []
+    for s, qb in zip(sessions, qbuf):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.step(qb)
+        graphs.append(g)
+
+    def run_graph(i):
+        j = i % L
+        qbuf[j].copy_(sessions[j].qdev[(i // L) % per])
+        graphs[j].replay()
+
+    def run_eager(i):
+        j = i % L
+        qbuf[j].copy_(sessions[j].qdev[(i // L) % per])
+        sessions[j].step(qbuf[j])
+
+    out = {"workload": "the rotated 32K GQA layers of the headline line, one graph per layer"}
+    for name, run in (("eager", run_eager), ("graph", run_graph), ("eager_again", run_eager)):
+        for i in range(W):
+            run(i)
+        torch.cuda.synchronize()
+        ms, per_step = timed(torch, run, W, K)
+        fail_on_flags(sessions, f"the {name} steps of the graph leg")
+        out[name] = {"steps": K, "steps_per_s": round(K / (ms * 1e-3), 2),
+                     "ms_per_step": round(ms / K, 4), "step_ms": percentiles(per_step)}
+    del graphs
+    torch.cuda.synchronize()
     return out
 
 
@@ -877,6 +922,10 @@ def main():
     if not args.no_nofetch:
         log("[bench] no-fetch control: uniform scores, eps = 0.2")
         nofetch = no_fetch_leg(torch, L)
+    graph = None
+    if not args.no_graph:
+        log("[bench] one HIP graph per layer-step, replayed")
+        graph = graph_leg(torch, sessions, K=min(K, 64), W=min(W, 8))
     gather = None
     if not args.no_gather:
         log("[bench] host fetch: zero-copy kernel against memcpy per run")
@@ -933,6 +982,7 @@ def main():
         "pivotal_stream": piv,
         "no_fetch": nofetch,
         "host_fetch_variants": gather,
+        "graph_replay": graph,
         "resolved_reading": resolved,
         "sketch_2bit": sk2,
         "decode_36_layers": dec36,
