@@ -543,7 +543,11 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
                              "GBps": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1)},
            "h2d_bytes_per_step": h2d / L * 2 * 128 * 2,
            "host_kernel_avg_us": round(host_us, 1),
-           "note": "K and V rows of F minus S cross the host link (the sketch is not exact)"}
+           "prefetch_avg_us": round(prof["prefetch"][0] / max(1, prof["prefetch"][1]) * 1e3, 1),
+           "note": "the K and V rows of F minus S are read from CPU memory (the sketch is not "
+                   "exact); rows the previous step of the layer read are staged, key beside "
+                   "value, during the decision kernel and read from the workspace instead "
+                   "(h2d_bytes_per_step counts every F minus S row)"}
     del sess2
     torch.cuda.empty_cache()
     return out

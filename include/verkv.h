@@ -98,8 +98,9 @@ typedef struct {
                             /* KVFetch step 5 reads only the value rows and takes the  */
                             /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
   const void *v_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the value     */
-                            /* cache verkv_refine reads (may be NULL).  With it and    */
-                            /* sketch_exact, verkv_decode_step stages value rows that  */
+                            /* cache verkv_refine reads (may be NULL).  With it (and,   */
+                            /* when sketch_exact is 0, with k_host as well),            */
+                            /* verkv_decode_step stages value rows that                */
                             /* the previous step on the same workspace read from the   */
                             /* host in the workspace while the decision kernel runs    */
                             /* (rows it staged the step before are copied within the   */
@@ -117,6 +118,13 @@ typedef struct {
                             /* water level c of eq. 3, or the branch that set r on the */
                             /* non-forced tokens (-1 all in H, -2 no budget left, -3   */
                             /* every positive score saturated); verkv_append needs it. */
+  const void *k_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the key cache  */
+                            /* (may be NULL).  When sketch_exact is 0 the host fetch   */
+                            /* reads key rows too; with k_host and v_host both set,     */
+                            /* the prefetch stages each row's key beside its value      */
+                            /* (same rules as v_host above; staged rows are reused only */
+                            /* for the same pair of caches).  Ignored when sketch_exact */
+                            /* is 1.  Without it a non-exact sketch stages nothing.     */
 } verkv_state;
 
 #define VERKV_SKETCH_ROWS 0

@@ -104,18 +104,24 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
       if (p < p1) {
         int tok = p;
         const uint8_t *vsrc = nullptr;
+        const uint8_t *ksrc = nullptr;
         if constexpr (HOST) {
-          // a list entry is token | (prefetch slot + 1) << TOKEN_BITS; the slot's row is
-          // used when the slot still holds this token
+          // a list entry is token | (prefetch slot + 1) << TOKEN_BITS; the slot's rows
+          // are used when the slot still holds this token
           const int32_t e = list[p];
           tok = e & TOKEN_MASK;
           const int slot = (int)((uint32_t)e >> TOKEN_BITS) - 1;
-          if (slot >= 0 && slot < a.stage_rows && stage_tok[(int64_t)unit * a.stage_rows + slot] == tok)
-            vsrc = stage + ((int64_t)unit * a.stage_rows + slot) * ROW_BYTES + slice;
+          if (slot >= 0 && slot < a.stage_rows && stage_tok[(int64_t)unit * a.stage_rows + slot] == tok) {
+            vsrc = stage + ((int64_t)unit * a.stage_rows + slot) * a.stage_stride + slice;
+            if (!EXACT && a.stage_kv) ksrc = vsrc + ROW_BYTES;
+          }
         }
         bt.tk[u] = tok;
         const int64_t rowi = src_base + tok;
-        if (!EXACT) bt.kr[u] = *(const uint4 *)(a.krows + rowi * ROW_BYTES + slice);
+        if (!EXACT) {
+          if (!ksrc) ksrc = a.krows + rowi * ROW_BYTES + slice;
+          bt.kr[u] = *(const uint4 *)ksrc;
+        }
         if (!vsrc) vsrc = a.vrows + rowi * ROW_BYTES + slice;
         bt.vr[u] = *(const uint4 *)vsrc;
         if constexpr (!HOST) {

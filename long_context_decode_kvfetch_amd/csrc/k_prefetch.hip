@@ -1,5 +1,5 @@
 // Host-row prefetch for gfx950: between two decode steps of a layer the fetch sets
-// overlap heavily, so the value rows the previous step read from the host (KVFetch
+// overlap heavily, so the rows the previous step read from the host (KVFetch
 // step 5, "Verify Before You Fetch", picx.dev summary page) are copied into the
 // workspace while the current step's decision kernel runs; the host-row kernel of the
 // current step takes those it needs from there instead of the host link.  The values
@@ -29,12 +29,16 @@ constexpr int PF_NT = 256;
 constexpr int PF_GRID = 256;               // blocks per launch: at most one per CU, so each
                                            // fits beside a decision-kernel workgroup
 
-template <bool BF16>
+// With a key cache (krows: the sketch is not exact, so the host-row kernel scores the
+// fetched rows from the host keys) a slot holds the value row and then the key row,
+// and both come from the other buffer or the host together.
+template <bool BF16, bool KV>
 __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_prefetch(PrefetchArgs a) {
   using RS = RowSlice<BF16>;
   constexpr int LPR = D / RS::EPL;         // lanes per row (16 or 32)
   constexpr int RPI = PF_NT / LPR;         // rows per block iteration
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
+  constexpr int INFL = KV ? 2 : 3;         // slots in flight per lane group
   const int unit = blockIdx.y;
   const int b = unit / a.t.Hkv;
   const int g = unit % a.t.Hkv;
@@ -46,6 +50,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   uint32_t *sb = a.sbits + word_base(a.t, b, g);
   const int sub = tid % LPR;
   const int64_t src = tok_base(a.t, b, g);
+  const int64_t SS = a.stage_stride;
   // which buffer to write, and whether the other one holds rows of this cache
   const uint64_t *h = a.shdr;
   const bool have_old = h && h[0] == STAGE_MAGIC && h[1] == a.ident_ptr &&
@@ -53,50 +58,70 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   const int cur = have_old ? 1 - (int)h[3] : 0;
   if (h && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.shdr[4] = (uint64_t)cur;
   const int64_t ubase = (int64_t)unit * a.stage_rows;
-  uint8_t *dst = (cur ? a.stage_alt : a.stage) + ubase * ROW_BYTES;
+  uint8_t *dst = (cur ? a.stage_alt : a.stage) + ubase * SS;
   int32_t *dtok = (cur ? a.stage_tok_alt : a.stage_tok) + ubase;
-  const uint8_t *osrc = (cur ? a.stage : a.stage_alt) + ubase * ROW_BYTES;
+  const uint8_t *osrc = (cur ? a.stage : a.stage_alt) + ubase * SS;
   const uint32_t *otok = reinterpret_cast<const uint32_t *>((cur ? a.stage_tok : a.stage_tok_alt) + ubase);
-  // three rows per lane group in flight (named registers: an indexed array here would be
+  // slots in flight per lane group in named registers (an indexed array here would be
   // placed in LDS, which must stay free for the decision kernel beside this one)
   // an entry of the previous list carries the slot its token had in the buffer the
   // previous step staged (the other buffer now), checked against that slot's token
-  auto fetch = [&](int p, uint4 &v) -> int {
+  auto fetch = [&](int p, uint4 &v, uint4 &k) -> int {
     if (p >= ns) return -1;
     const int32_t e = pl[p];
     const int tok = e & TOKEN_MASK;
     if (tok >= n) return -1;
     const int j = (int)((uint32_t)e >> TOKEN_BITS) - 1;
-    if (have_old && j >= 0 && j < a.stage_rows && otok[j] == (uint32_t)tok)
-      v = *(const uint4 *)(osrc + (int64_t)j * ROW_BYTES + sub * 16);
-    else
+    if (have_old && j >= 0 && j < a.stage_rows && otok[j] == (uint32_t)tok) {
+      const uint8_t *o = osrc + (int64_t)j * SS + sub * 16;
+      v = *(const uint4 *)o;
+      if (KV) k = *(const uint4 *)(o + ROW_BYTES);
+    } else {
       v = *(const uint4 *)(a.vrows + (src + tok) * ROW_BYTES + sub * 16);
+      if (KV) k = *(const uint4 *)(a.krows + (src + tok) * ROW_BYTES + sub * 16);
+    }
     return tok;
   };
-  auto put = [&](int p, int tok, const uint4 &v) {
+  auto put = [&](int p, int tok, const uint4 &v, const uint4 &k) {
     if (p >= a.stage_rows) return;
-    if (tok >= 0) *(uint4 *)(dst + (int64_t)p * ROW_BYTES + sub * 16) = v;
+    if (tok >= 0) {
+      uint8_t *d = dst + (int64_t)p * SS + sub * 16;
+      *(uint4 *)d = v;
+      if (KV) *(uint4 *)(d + ROW_BYTES) = k;
+    }
     if (sub == 0) {
       dtok[p] = tok;
       if (tok >= 0) atomicOr(sb + (tok >> 5), 1u << (tok & 31));
     }
   };
-  for (int p0 = blockIdx.x * RPI * 3; p0 < a.stage_rows; p0 += gridDim.x * RPI * 3) {
-    const int pa = p0 + tid / LPR, pb = pa + RPI, pc = pb + RPI;
-    uint4 va = make_uint4(0, 0, 0, 0), vb = va, vc = va;
-    const int ta = fetch(pa, va);
-    const int tb = fetch(pb, vb);
-    const int tc = fetch(pc, vc);
-    put(pa, ta, va);
-    put(pb, tb, vb);
-    put(pc, tc, vc);
+  for (int p0 = blockIdx.x * RPI * INFL; p0 < a.stage_rows; p0 += gridDim.x * RPI * INFL) {
+    const int pa = p0 + tid / LPR, pb = pa + RPI;
+    uint4 va = make_uint4(0, 0, 0, 0), vb = va, ka = va, kb = va;
+    const int ta = fetch(pa, va, ka);
+    const int tb = fetch(pb, vb, kb);
+    if constexpr (KV) {
+      put(pa, ta, va, ka);
+      put(pb, tb, vb, kb);
+    } else {
+      const int pc = pb + RPI;
+      uint4 vc = make_uint4(0, 0, 0, 0);
+      const int tc = fetch(pc, vc, kb);
+      put(pa, ta, va, ka);
+      put(pb, tb, vb, kb);
+      put(pc, tc, vc, kb);
+    }
   }
 }
 
 hipError_t launch_prefetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st) {
   const int per_unit = std::max(1, PF_GRID / std::max(1, units));
-  if (bf16) return launch_kernel(k_prefetch<true>, dim3(per_unit, units), dim3(PF_NT), 0, st, a);
-  return launch_kernel(k_prefetch<false>, dim3(per_unit, units), dim3(PF_NT), 0, st, a);
+  const dim3 grid(per_unit, units);
+  if (a.krows) {
+    if (bf16) return launch_kernel(k_prefetch<true, true>, grid, dim3(PF_NT), 0, st, a);
+    return launch_kernel(k_prefetch<false, true>, grid, dim3(PF_NT), 0, st, a);
+  }
+  if (bf16) return launch_kernel(k_prefetch<true, false>, grid, dim3(PF_NT), 0, st, a);
+  return launch_kernel(k_prefetch<false, false>, grid, dim3(PF_NT), 0, st, a);
 }
 
 }  // namespace verkv

@@ -199,7 +199,10 @@ struct PrefetchArgs {
   const int32_t *prev_list;  // [B][Hkv][n] entries of the previous list (token | slot << 20)
   const int32_t *prev_count; // [B][Hkv]
   const uint8_t *vrows;      // host value cache (device view) [B][Hkv][n][128]
-  uint8_t *stage;            // [B*Hkv][stage_rows][128] kv dtype: staging buffer 0
+  const uint8_t *krows;      // host key cache (device view), staged beside the values when
+                             //   the sketch is not exact; null: values only
+  uint8_t *stage;            // [B*Hkv][stage_rows] slots of stage_stride bytes: the value
+                             //   row, then (krows set) the key row; staging buffer 0
   int32_t *stage_tok;        // [B*Hkv][stage_rows] token of each slot, -1 if none
   uint8_t *stage_alt;        // staging buffer 1 (the buffers alternate from step to step)
   int32_t *stage_tok_alt;
@@ -208,6 +211,7 @@ struct PrefetchArgs {
   uint64_t ident_shape;      //   value cache's device address and a hash of the shape
   uint32_t *sbits;           // [B][Hkv][W] bit per prefetched token
   int32_t stage_rows;
+  int32_t stage_stride;      // bytes per slot: one row, or two with krows
 };
 
 struct AttendArgs {
@@ -233,6 +237,8 @@ struct AttendArgs {
   const int32_t *stage_tok_alt;  // buffer this step's prefetch wrote (null: buffer 0)
   const uint64_t *shdr;
   int32_t stage_rows;
+  int32_t stage_stride;      // bytes per slot (the value row first)
+  int32_t stage_kv;          // 1: a slot also holds the key row, after the value row
 };
 
 struct FinishArgs {

@@ -336,7 +336,7 @@ verkv_status scratch_for_device(uint8_t **out) {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 107; }
+int32_t verkv_version(void) { return 108; }
 
 #ifndef VERKV_SOURCE_HASH
 #define VERKV_SOURCE_HASH "unknown"
@@ -606,12 +606,44 @@ static verkv_status check_step(const verkv_shape *s, const verkv_state *st, cons
   return VERKV_OK;
 }
 
-// The value cache the step's prefetch reads (exact sketch with v_host set), resolved to
-// its device view before anything is enqueued; *Vd stays null when there is no prefetch.
-static verkv_status prefetch_source(const verkv_state *st, int srows, const void **Vd) {
+// The caches the step's prefetch reads, resolved to their device views before anything
+// is enqueued: the value cache (v_host), and with a sketch that is not exact the key
+// cache too (k_host; without it that mode stages nothing).  *Vd stays null when there
+// is no prefetch; *Kd is set only when keys are staged.
+static verkv_status prefetch_source(const verkv_state *st, int srows, const void **Vd,
+                                    const void **Kd) {
   *Vd = nullptr;
-  if (!st->v_host || !st->sketch_exact || srows <= 0) return VERKV_OK;
-  return device_view(st->v_host, Vd);
+  *Kd = nullptr;
+  if (!st->v_host || srows <= 0) return VERKV_OK;
+  if (!st->sketch_exact && !st->k_host) return VERKV_OK;
+  verkv_status rc = device_view(st->v_host, Vd);
+  if (rc == VERKV_OK && !st->sketch_exact) rc = device_view(st->k_host, Kd);
+  if (rc != VERKV_OK) *Vd = nullptr;
+  return rc;
+}
+
+// Staging slots: the workspace reserves srows float32-sized rows per KV head and
+// buffer; a slot holds the value row, or the value and the key row (keys staged), so
+// with float32 rows and keys the slot count halves.
+struct StageGeom {
+  int rows;
+  int stride;
+  bool kv;
+};
+static StageGeom stage_geom(int srows, bool bf16, bool kv) {
+  const int row = VERKV_HEAD_DIM * (bf16 ? 2 : 4);
+  const int stride = kv ? 2 * row : row;
+  return StageGeom{kv ? (int)((int64_t)srows * VERKV_HEAD_DIM * 4 / stride) : srows, stride, kv};
+}
+
+// The identity staged rows are published under: the shape, and the key cache's
+// address when keys are staged beside the values (the value cache's address is the
+// other half).
+static uint64_t stage_ident(const SeqTable &t, bool bf16, const void *Kd) {
+  uint64_t h = shape_ident(t, bf16);
+  const uint64_t k = reinterpret_cast<uint64_t>(Kd);
+  for (int i = 0; i < 8; ++i) { h ^= (k >> (8 * i)) & 0xFF; h *= 1099511628211ull; }
+  return h;
 }
 
 // How a step uses the library's resources: the ordinary entry points stage host rows
@@ -668,9 +700,10 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
   // every argument and the library's second stream are resolved before the first launch
-  const void *Vd = nullptr;
-  if (mode.side && (rc = prefetch_source(st, L.srows, &Vd)) != VERKV_OK) return rc;
-  const bool prefetch = Vd != nullptr;   // host cache, exact sketch, staging rows
+  const void *Vd = nullptr, *Kd = nullptr;
+  if (mode.side && (rc = prefetch_source(st, L.srows, &Vd, &Kd)) != VERKV_OK) return rc;
+  const bool prefetch = Vd != nullptr;   // host cache(s) and staging rows
+  const StageGeom sg = stage_geom(L.srows, s->kv_dtype == VERKV_BF16, Kd != nullptr);
   Side *sd = nullptr;
   if (prefetch && (rc = side_for_device(&sd)) != VERKV_OK) return rc;
 
@@ -710,15 +743,17 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     pa.prev_list = reinterpret_cast<const int32_t *>(ws + L.h2d);
     pa.prev_count = reinterpret_cast<const int32_t *>(ws + L.h2dc);
     pa.vrows = static_cast<const uint8_t *>(Vd);
+    pa.krows = static_cast<const uint8_t *>(Kd);
     pa.stage = ws + L.stage;
     pa.stage_tok = reinterpret_cast<int32_t *>(ws + L.stage_tok);
     pa.stage_alt = ws + L.stage_alt;
     pa.stage_tok_alt = reinterpret_cast<int32_t *>(ws + L.stage_tok_alt);
     pa.shdr = reinterpret_cast<uint64_t *>(ws + L.shdr);
     pa.ident_ptr = reinterpret_cast<uint64_t>(Vd);
-    pa.ident_shape = shape_ident(t, bf16);
+    pa.ident_shape = stage_ident(t, bf16, Kd);
     pa.sbits = reinterpret_cast<uint32_t *>(ws + L.sbits);
-    pa.stage_rows = L.srows;
+    pa.stage_rows = sg.rows;
+    pa.stage_stride = sg.stride;
     {
       Timed tm(K_PREFETCH, sd->s);
       HIP_TRY(launch_prefetch(pa, units, bf16, sd->s), "prefetch launch");
@@ -841,7 +876,7 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   un.sbits = prefetch ? reinterpret_cast<const uint32_t *>(ws + L.sbits) : nullptr;
   un.shdr = prefetch ? reinterpret_cast<uint64_t *>(ws + L.shdr) : nullptr;
   un.ident_ptr = reinterpret_cast<uint64_t>(Vd);
-  un.ident_shape = shape_ident(t, bf16);
+  un.ident_shape = stage_ident(t, bf16, Kd);
   un.h2d_count_ws = reinterpret_cast<int32_t *>(ws + L.h2dc);
   un.piv_sched = nullptr;
   un.piv_runs = nullptr;
@@ -912,7 +947,12 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   at.stage_alt = ws + L.stage_alt;
   at.stage_tok_alt = reinterpret_cast<const int32_t *>(ws + L.stage_tok_alt);
   at.shdr = L.srows > 0 ? reinterpret_cast<const uint64_t *>(ws + L.shdr) : nullptr;
-  at.stage_rows = L.srows;
+  // the slot geometry of this state's prefetch (list entries carry slots only for rows
+  // that a prefetch with this geometry staged)
+  const StageGeom sg = stage_geom(L.srows, bf16, !st->sketch_exact && st->k_host && st->v_host);
+  at.stage_rows = sg.rows;
+  at.stage_stride = sg.stride;
+  at.stage_kv = sg.kv ? 1 : 0;
   {
     Timed tm(K_HOST, stream);
     HIP_TRY(launch_attend(at, units, bf16, true, st->sketch_exact != 0, stream),
@@ -977,6 +1017,8 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   pv.stage_tok_alt = nullptr;
   pv.shdr = nullptr;
   pv.stage_rows = 0;
+  pv.stage_stride = 0;
+  pv.stage_kv = 0;
   {
     Timed tm(K_PIVOT, side);
     HIP_TRY(launch_attend(pv, units, bf16, false, false, side), "pivot attention launch");

@@ -63,6 +63,7 @@ class Session:
         self.cap = int(cap) if cap else verkv.default_cap(self.shape, wl.eta)
         self.state = verkv.LayerState(self.shape, self.cap, self.sketch, device, sketch_exact,
                                       v_host=self.V_host if (host_pinned and prefetch) else None,
+                                      k_host=self.K_host if (host_pinned and prefetch and not sketch_exact) else None,
                                       sketch_format=verkv.SKETCH_2BIT if sketch_2bit else verkv.SKETCH_ROWS)
         self.cws = verkv.workspace(self.shape.compress_workspace_bytes(), device)
         self.dws = verkv.workspace(self.shape.decode_workspace_bytes(self.cap), device)

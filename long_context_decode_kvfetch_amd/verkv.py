@@ -47,7 +47,8 @@ class State(C.Structure):
     _fields_ = [("r", C.c_void_p), ("resident", C.c_void_p), ("piv_idx", C.c_void_p),
                 ("piv_count", C.c_void_p), ("piv_k", C.c_void_p), ("piv_v", C.c_void_p),
                 ("cap", C.c_int32), ("sketch", C.c_void_p), ("sketch_exact", C.c_int32),
-                ("v_host", C.c_void_p), ("sketch_format", C.c_int32), ("level", C.c_void_p)]
+                ("v_host", C.c_void_p), ("sketch_format", C.c_int32), ("level", C.c_void_p),
+                ("k_host", C.c_void_p)]
 
 
 SKETCH_ROWS, SKETCH_2BIT, SKETCH2_ROW_BYTES = 0, 1, 64
@@ -227,7 +228,7 @@ class LayerState:
 
     def __init__(self, shape: LayerShape, cap: int, sketch: torch.Tensor, device="cuda",
                  sketch_exact: bool = True, v_host: torch.Tensor | None = None,
-                 sketch_format: int = SKETCH_ROWS):
+                 sketch_format: int = SKETCH_ROWS, k_host: torch.Tensor | None = None):
         hkv, tot = shape.n_kv_heads, shape.total_slots
         words = sum((n + 31) // 32 for n in shape.caps)
         units = shape.batch * hkv
@@ -243,10 +244,12 @@ class LayerState:
         self.level = torch.empty(units, dtype=torch.float64, device=device)
         self.sketch = sketch
         self.v_host = v_host                    # kept alive with the state
+        self.k_host = k_host
         self.c = State(_ptr(self.r), _ptr(self.resident), _ptr(self.piv_idx), _ptr(self.piv_count),
                        _ptr(self.piv_k), _ptr(self.piv_v), self.cap, _ptr(sketch),
                        1 if sketch_exact else 0, _ptr(v_host) if v_host is not None else None,
-                       int(sketch_format), _ptr(self.level))
+                       int(sketch_format), _ptr(self.level),
+                       _ptr(k_host) if k_host is not None else None)
 
 
 class StepBuffers:

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(vk):
 
 def test_version_and_status_strings(vk):
     lib = vk.lib()
-    assert lib.verkv_version() == 107
+    assert lib.verkv_version() == 108
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.verkv_status_str(st).decode() not in ("", "unknown status")
     assert lib.verkv_status_str(7).decode() == "unknown status"

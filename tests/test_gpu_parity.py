@@ -180,10 +180,13 @@ def test_philox_layer_word():
     _run(synth.gqa_layer(seed=3, n=8192, steps=1, layer=35), label="layer 35")
 
 
-def test_prefetch_and_workspace_history_do_not_change_results():
+@pytest.mark.parametrize("sketch_2bit", [False, True], ids=["exact sketch", "2-bit sketch"])
+def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit):
     """Three steps on one layer with the host-row prefetch on, off, and on with a
     workspace that starts out as random bytes: every output is bit-identical (the
-    prefetched rows are the same host rows; a foreign workspace only costs time)."""
+    prefetched rows are the same host rows; a foreign workspace only costs time).  With
+    the 2-bit sketch the prefetch stages each row's key beside its value (the host fetch
+    scores fetched rows from the host keys there), and the prefetch kernel must run."""
     from long_context_decode_kvfetch_amd import verkv
     wl = synth.gqa_layer(seed=2, n=8192, steps=3, hkv=2)
     keys = ("o", "lse", "n_hat", "d_hat", "beta_star", "eps_hat", "kstar", "certified",
@@ -191,7 +194,8 @@ def test_prefetch_and_workspace_history_do_not_change_results():
     runs = []
     for label, kw, scramble in (("prefetch", {}, False), ("no prefetch", {"prefetch": False}, False),
                                 ("random workspace", {}, True)):
-        say(f"[parity] history: {label}")
+        say(f"[parity] history: {label}, {'2-bit' if sketch_2bit else 'exact'} sketch")
+        kw = dict(kw, sketch_2bit=sketch_2bit)
         sess = _session(wl, **kw)
         sess.compress()
         if scramble:
@@ -204,11 +208,15 @@ def test_prefetch_and_workspace_history_do_not_change_results():
             except Exception:
                 pass
         steps = []
+        verkv.profile_begin(64)
         for st in range(3):
             sess.step(sess.queries(st))
             verkv.check(sess.shape, sess.cap, sess.dws)
             r = sess.results_numpy()
             steps.append({k: np.array(r[k]) for k in keys})
+        launches = verkv.profile_report()["prefetch"][1]
+        verkv.profile_end()
+        assert launches == (0 if "prefetch" in kw else 3), (label, launches)
         runs.append(steps)
     for label, other in (("no prefetch", runs[1]), ("random workspace", runs[2])):
         for st in range(3):
