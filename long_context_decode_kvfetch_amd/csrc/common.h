@@ -30,6 +30,8 @@ struct SeqTable {
   int32_t max_n;
   int32_t max_cap;
   SeqInfo s[VERKV_MAX_BATCH];
+  uint8_t order[VERKV_MAX_BATCH];   // sequences by length, longest first (ties by index):
+                                    // the order row-per-workgroup launches dispatch them
 };
 
 __host__ __device__ inline int32_t words_of(int32_t n) { return (n + 31) >> 5; }

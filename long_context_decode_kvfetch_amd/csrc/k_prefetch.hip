@@ -38,7 +38,7 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   constexpr int LPR = D / RS::EPL;         // lanes per row (16 or 32)
   constexpr int RPI = PF_NT / LPR;         // rows per block iteration
   constexpr int ROW_BYTES = D * (BF16 ? 2 : 4);
-  constexpr int INFL = KV ? 2 : 3;         // slots in flight per lane group
+  constexpr int INFL = KV ? 1 : 2;         // slots in flight per lane group
   const int unit = blockIdx.y;
   const int b = unit / a.t.Hkv;
   const int g = unit % a.t.Hkv;
@@ -95,20 +95,17 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
     }
   };
   for (int p0 = blockIdx.x * RPI * INFL; p0 < a.stage_rows; p0 += gridDim.x * RPI * INFL) {
-    const int pa = p0 + tid / LPR, pb = pa + RPI;
-    uint4 va = make_uint4(0, 0, 0, 0), vb = va, ka = va, kb = va;
+    const int pa = p0 + tid / LPR;
+    uint4 va = make_uint4(0, 0, 0, 0), ka = va;
     const int ta = fetch(pa, va, ka);
-    const int tb = fetch(pb, vb, kb);
     if constexpr (KV) {
       put(pa, ta, va, ka);
-      put(pb, tb, vb, kb);
     } else {
-      const int pc = pb + RPI;
-      uint4 vc = make_uint4(0, 0, 0, 0);
-      const int tc = fetch(pc, vc, kb);
+      const int pb = pa + RPI;
+      uint4 vb = make_uint4(0, 0, 0, 0);
+      const int tb = fetch(pb, vb, ka);
       put(pa, ta, va, ka);
-      put(pb, tb, vb, kb);
-      put(pc, tc, vc, kb);
+      put(pb, tb, vb, ka);
     }
   }
 }

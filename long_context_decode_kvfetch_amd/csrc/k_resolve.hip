@@ -49,6 +49,10 @@ __global__ __launch_bounds__(DC_NT) void k_resolve(ResolveArgs a) {
     row = blockIdx.x / T;
     m = blockIdx.x % T;
   }
+  {                                     // dispatch order: the longest sequences' rows first
+    const int hq = a.t.Hkv * a.t.G;
+    row = (int)a.t.order[row / hq] * hq + row % hq;
+  }
   if (a.certified[row]) return;              // the whole team: no fetch for this row
   const int Hq = a.t.Hkv * a.t.G;
   const int b = row / Hq;

@@ -73,6 +73,11 @@ verkv_status make_table(const verkv_shape *s, SeqTable &t) {
     t.max_n = std::max(t.max_n, n);
     t.max_cap = std::max(t.max_cap, cap);
   }
+  // longest sequences first: a launch with more workgroups than the device holds at once
+  // then starts the longest rows in its first round
+  for (int b = 0; b < t.B; ++b) t.order[b] = (uint8_t)b;
+  std::stable_sort(t.order, t.order + t.B,
+                   [&](uint8_t x, uint8_t y) { return t.s[x].n > t.s[y].n; });
   // every flat index below must stay inside int32 element counts per array
   const int64_t hq = (int64_t)s->n_kv_heads * s->group;
   if (tok * hq > INT32_MAX || chunks * hq * (int64_t)s->n_kv_heads > INT32_MAX) return VERKV_EUNSUPPORTED;
