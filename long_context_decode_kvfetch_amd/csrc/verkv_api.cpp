@@ -738,12 +738,15 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   // host-row prefetch on the library's second stream, beside the decision kernel (it
   // starts after the sketch kernel, which needs every register of the CUs): rows the
   // previous step on this workspace read from the host
+  // The fork point is the end of the sketch kernel; the prefetch itself is enqueued after
+  // the decision kernel, so that the decision workgroups are placed on the CUs before the
+  // prefetch blocks are (enqueued first, the prefetch delayed the start of the last team
+  // members by 13-15 us).
   std::unique_lock<std::mutex> lk;
+  PrefetchArgs pa;
   if (prefetch) {
     lk = std::unique_lock<std::mutex>(sd->mu);
     HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
-    HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
-    PrefetchArgs pa;
     pa.t = t;
     pa.prev_list = reinterpret_cast<const int32_t *>(ws + L.h2d);
     pa.prev_count = reinterpret_cast<const int32_t *>(ws + L.h2dc);
@@ -759,12 +762,17 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     pa.sbits = reinterpret_cast<uint32_t *>(ws + L.sbits);
     pa.stage_rows = sg.rows;
     pa.stage_stride = sg.stride;
+  }
+  auto launch_pf = [&]() -> verkv_status {
+    if (!prefetch) return VERKV_OK;
+    HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
     {
       Timed tm(K_PREFETCH, sd->s);
       HIP_TRY(launch_prefetch(pa, units, bf16, sd->s), "prefetch launch");
     }
     HIP_TRY(hipEventRecord(sd->pref, sd->s), "hipEventRecord");
-  }
+    return VERKV_OK;
+  };
 
   DecideArgs dc;
   dc.t = t;
@@ -826,6 +834,7 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     Timed tm(K_DECIDE, stream);
     HIP_TRY(launch_decide(dc, rows, stream), "decide launch");
   }
+  if ((rc = launch_pf()) != VERKV_OK) return rc;
   if (resolved) {
     ResolveArgs rv;
     rv.t = t;
