@@ -54,6 +54,8 @@ def parse():
                    help="skip the host-fetch comparison (zero-copy kernel against memcpy per run)")
     p.add_argument("--no-graph", action="store_true",
                    help="skip the leg replaying each layer-step as a captured HIP graph")
+    p.add_argument("--no-staging", action="store_true",
+                   help="skip the sweep over the staging slots per KV head")
     p.add_argument("--no-2bit", action="store_true",
                    help="skip the 2-bit sketch leg (the same layers with a 2-bit key sketch)")
     p.add_argument("--sweep", action="store_true",
@@ -343,6 +345,52 @@ def no_fetch_leg(torch, L, K=64, W=8):
            "step_GBps": round(alg / (ms / K * 1e-3) / 1e9, 1), "kernel_avg_us": kern}
     del sess
     torch.cuda.empty_cache()
+    return out
+
+
+def staging_leg(torch, wls, qdevs, K=64, W=8, slots=(2048, 8192, 16384)):
+    """The 32K GQA layer-step over the rotated layers with the cross-step staging sized at
+    `slots` rows per KV head (the library's default is 4095 here): steps/s, the device
+    memory the two staging buffers take per layer (bf16 value rows), and the host-row
+    kernel's time.  More slots keep more of the previous step's host rows on the device,
+    at the cost of device memory the method otherwise keeps free."""
+    from long_context_decode_kvfetch_amd import verkv
+    from long_context_decode_kvfetch_amd.runner import Session
+    out = {"workload": "the rotated 32K GQA layers of the headline line", "settings": []}
+    for ns in slots:
+        sess = []
+        for wl, q in zip(wls, qdevs):
+            s2 = Session(wl, stage_slots=ns)
+            s2.compress()
+            s2.qdev = q
+            sess.append(s2)
+        L = len(sess)
+        per = qdevs[0].shape[0]
+
+        def run(i):
+            s2 = sess[i % L]
+            s2.step(s2.qdev[(i // L) % per])
+        for i in range(W + L):
+            run(i)
+        torch.cuda.synchronize()
+        ms, per_step = timed(torch, run, W + L, K)
+        fail_on_flags(sess, f"the staging leg at {ns} slots")
+        verkv.profile_begin(16 * 16 + 16)
+        for i in range(W + L + K, W + L + K + 16):
+            run(i)
+        torch.cuda.synchronize()
+        prof = verkv.profile_report()
+        verkv.profile_end()
+        out["settings"].append({
+            "stage_slots": ns, "steps_per_s": round(K / (ms * 1e-3), 2),
+            "step_ms": percentiles(per_step),
+            "staging_bytes_per_layer": 2 * 8 * ns * 128 * 2,
+            "host_rows_us": round(prof["attend_host"][0] / prof["attend_host"][1] * 1e3, 1),
+            "prefetch_us": round(prof["prefetch"][0] / max(1, prof["prefetch"][1]) * 1e3, 1),
+            "decide_us": round(prof["decide"][0] / prof["decide"][1] * 1e3, 1)})
+        log(f"[bench] staging {ns} slots: {out['settings'][-1]['steps_per_s']} steps/s")
+        del sess
+        torch.cuda.empty_cache()
     return out
 
 
@@ -926,6 +974,11 @@ def main():
     if not args.no_nofetch:
         log("[bench] no-fetch control: uniform scores, eps = 0.2")
         nofetch = no_fetch_leg(torch, L)
+    staging = None
+    if not args.no_staging:
+        log("[bench] staging slots per KV head: sweep")
+        staging = staging_leg(torch, [s.wl for s in sessions], [s.qdev for s in sessions],
+                              K=min(K, 64), W=min(W, 8))
     graph = None
     if not args.no_graph:
         log("[bench] one HIP graph per layer-step, replayed")
@@ -987,6 +1040,7 @@ def main():
         "no_fetch": nofetch,
         "host_fetch_variants": gather,
         "graph_replay": graph,
+        "staging_slots": staging,
         "resolved_reading": resolved,
         "sketch_2bit": sk2,
         "decode_36_layers": dec36,

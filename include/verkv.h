@@ -78,6 +78,14 @@ typedef struct {
   uint32_t layer;           /* third Philox counter word                               */
   const int32_t *seq_cap;   /* [host][B] token capacity c_b >= n_b of each sequence's  */
                             /* arrays, each <= VERKV_MAX_SEQ_LEN (NULL: c_b = n_b)      */
+  int32_t stage_slots;      /* rows per KV head the cross-step staging of host rows    */
+                            /* holds (see verkv_state.v_host); 0: min(4095, 32768 /     */
+                            /* (B Hkv)).  At most 2^(32 - t) - 1 where t is the bits of  */
+                            /* the largest capacity (a host-row list entry packs the    */
+                            /* token and its slot + 1 into 32 bits): 131071 at 32K      */
+                            /* tokens, 4095 at 2^20 (VERKV_EINVAL beyond, checked with  */
+                            /* the shape).  The decode workspace grows by about         */
+                            /* 2 x 512 B x B x Hkv per slot.                             */
 } verkv_shape;
 
 /* GPU-resident compressed state of one layer (written by verkv_compress; the decode

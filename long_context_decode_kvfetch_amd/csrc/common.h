@@ -32,7 +32,18 @@ struct SeqTable {
   SeqInfo s[VERKV_MAX_BATCH];
   uint8_t order[VERKV_MAX_BATCH];   // sequences by length, longest first (ties by index):
                                     // the order row-per-workgroup launches dispatch them
+  int32_t tok_bits;                 // bits of a token id in a host-row list entry (the
+                                    // largest capacity's), the prefetch slot + 1 above them
+  int32_t stage_slots;              // staging slots per KV head asked for (0: default)
 };
+
+// A host-row list entry: token | (prefetch slot + 1) << tok_bits, as uint32.
+__host__ __device__ inline int entry_token(int32_t e, int tb) {
+  return (int)((uint32_t)e & ((1u << tb) - 1u));
+}
+__host__ __device__ inline int entry_slot(int32_t e, int tb) {   // -1: not prefetched
+  return (int)((uint32_t)e >> tb) - 1;
+}
 
 __host__ __device__ inline int32_t words_of(int32_t n) { return (n + 31) >> 5; }
 __host__ __device__ inline int32_t chunks_of(int32_t n) { return (n + SKETCH_CHUNK - 1) / SKETCH_CHUNK; }

@@ -106,11 +106,11 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
         const uint8_t *vsrc = nullptr;
         const uint8_t *ksrc = nullptr;
         if constexpr (HOST) {
-          // a list entry is token | (prefetch slot + 1) << TOKEN_BITS; the slot's rows
+          // a list entry is token | (prefetch slot + 1) << tok_bits; the slot's rows
           // are used when the slot still holds this token
           const int32_t e = list[p];
-          tok = e & TOKEN_MASK;
-          const int slot = (int)((uint32_t)e >> TOKEN_BITS) - 1;
+          tok = entry_token(e, a.t.tok_bits);
+          const int slot = entry_slot(e, a.t.tok_bits);
           if (slot >= 0 && slot < a.stage_rows && stage_tok[(int64_t)unit * a.stage_rows + slot] == tok) {
             vsrc = stage + ((int64_t)unit * a.stage_rows + slot) * a.stage_stride + slice;
             if (!EXACT && a.stage_kv) ksrc = vsrc + ROW_BYTES;

@@ -851,7 +851,7 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
       if (inh) {
         // host-row entry: the token, and its prefetch slot + 1 when it was prefetched
         const uint32_t slot1 = ((sg >> lane) & 1ull) ? (uint32_t)(ps + __popcll(sg & below) + 1) : 0u;
-        hl[ph + (int32_t)__popcll(hsel & below)] = (int32_t)((uint32_t)tok | (slot1 << TOKEN_BITS));
+        hl[ph + (int32_t)__popcll(hsel & below)] = (int32_t)((uint32_t)tok | (slot1 << a.t.tok_bits));
       }
       pf += (int32_t)__popcll(f);
       ph += (int32_t)__popcll(hsel);

@@ -69,9 +69,9 @@ __global__ __launch_bounds__(PF_NT) __attribute__((amdgpu_num_vgpr(32))) void k_
   auto fetch = [&](int p, uint4 &v, uint4 &k) -> int {
     if (p >= ns) return -1;
     const int32_t e = pl[p];
-    const int tok = e & TOKEN_MASK;
+    const int tok = entry_token(e, a.t.tok_bits);
     if (tok >= n) return -1;
-    const int j = (int)((uint32_t)e >> TOKEN_BITS) - 1;
+    const int j = entry_slot(e, a.t.tok_bits);
     if (have_old && j >= 0 && j < a.stage_rows && otok[j] == (uint32_t)tok) {
       const uint8_t *o = osrc + (int64_t)j * SS + sub * 16;
       v = *(const uint4 *)o;

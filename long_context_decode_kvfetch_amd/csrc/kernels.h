@@ -264,10 +264,8 @@ constexpr int DECIDE_THREADS = 512;
 constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
 constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
-constexpr int TOKEN_BITS = 20;    // host-row list entry: token | (prefetch slot + 1) << 20
-constexpr int32_t TOKEN_MASK = (1 << TOKEN_BITS) - 1;
-constexpr int STAGE_SLOTS_MAX = 4095;    // slot + 1 fits the 12 bits above the token
-constexpr int STAGE_ROWS_TOTAL = 32768;  // prefetched rows per call, over all KV heads
+constexpr int STAGE_SLOTS_DEFAULT = 4095;  // staging slots per KV head by default (at most),
+constexpr int STAGE_ROWS_TOTAL = 32768;    // and at most this many over all KV heads
 // Staging header words: [0] magic, [1] [2] identity of the staged rows' cache, [3] the
 // buffer the last published step staged, [4] the buffer this step's prefetch writes.
 constexpr int STAGE_HDR_WORDS = 8;

@@ -39,6 +39,7 @@ uint64_t shape_ident(const SeqTable &t, bool bf16) {
   };
   mix((uint64_t)t.B); mix((uint64_t)t.Hkv); mix((uint64_t)t.G); mix(bf16 ? 1 : 0);
   for (int b = 0; b < t.B; ++b) { mix((uint64_t)t.s[b].n); mix((uint64_t)t.s[b].cap); }
+  mix((uint64_t)(uint32_t)t.stage_slots);
   return h;
 }
 
@@ -72,6 +73,16 @@ verkv_status make_table(const verkv_shape *s, SeqTable &t) {
     chunks += chunks_of(cap);
     t.max_n = std::max(t.max_n, n);
     t.max_cap = std::max(t.max_cap, cap);
+  }
+  // host-row list entries: the token in the low tok_bits bits, the staging slot + 1 above
+  t.tok_bits = 1;
+  while ((1 << t.tok_bits) < t.max_cap) ++t.tok_bits;
+  t.stage_slots = s->stage_slots;
+  if (s->stage_slots < 0 || (int64_t)s->stage_slots > (int64_t)(1ll << (32 - t.tok_bits)) - 1) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "stage_slots %d exceeds %lld for a capacity of %d tokens", (int)s->stage_slots,
+                  (long long)((1ll << (32 - t.tok_bits)) - 1), (int)t.max_cap);
+    return VERKV_EINVAL;
   }
   // longest sequences first: a launch with more workgroups than the device holds at once
   // then starts the longest rows in its first round
@@ -168,7 +179,9 @@ DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
   w.status = off; off = align_up(off + 64);
   w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
   // host-row prefetch: value rows staged per KV head (sized for float32 rows)
-  w.srows = staging ? std::min(STAGE_SLOTS_MAX, STAGE_ROWS_TOTAL / std::max(1, units)) : 0;
+  w.srows = !staging ? 0
+            : t.stage_slots > 0 ? t.stage_slots
+                                : std::min(STAGE_SLOTS_DEFAULT, STAGE_ROWS_TOTAL / std::max(1, units));
   w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * 4);
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
   w.stage_alt = off; off = align_up(off + (size_t)units * w.srows * D * 4);
@@ -341,7 +354,7 @@ verkv_status scratch_for_device(uint8_t **out) {
 
 extern "C" {
 
-int32_t verkv_version(void) { return 108; }
+int32_t verkv_version(void) { return 109; }
 
 #ifndef VERKV_SOURCE_HASH
 #define VERKV_SOURCE_HASH "unknown"

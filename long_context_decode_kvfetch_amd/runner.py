@@ -31,14 +31,16 @@ class Session:
 
     def __init__(self, wl: Workload, cap: int | None = None, device: str = "cuda",
                  host_pinned: bool = True, seed: int | None = None, sketch_exact: bool = True,
-                 prefetch: bool = True, sketch_2bit: bool = False, grow: int = 0):
-        """grow: token slots reserved past each sequence's length for append()."""
+                 prefetch: bool = True, sketch_2bit: bool = False, grow: int = 0,
+                 stage_slots: int = 0):
+        """grow: token slots reserved past each sequence's length for append();
+        stage_slots: rows per KV head of the cross-step staging (0: the library's default)."""
         self.wl = wl
         self.device = device
         lens = [s.n for s in wl.seqs]
         caps = [n + int(grow) for n in lens] if grow else None
         self.shape = verkv.LayerShape(lens, wl.n_kv_heads, wl.group, wl.n_sink, wl.n_local,
-                                      wl.kv_dtype, wl.layer, caps)
+                                      wl.kv_dtype, wl.layer, caps, stage_slots)
         dt = self.shape.torch_dtype
         K = torch.from_numpy(_cat([s.K for s in wl.seqs], caps)).to(dt)
         V = torch.from_numpy(_cat([s.V for s in wl.seqs], caps)).to(dt)

@@ -40,7 +40,8 @@ class Shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("n_kv_heads", C.c_int32), ("group", C.c_int32),
                 ("head_dim", C.c_int32), ("seq_len", C.POINTER(C.c_int32)),
                 ("n_sink", C.c_int32), ("n_local", C.c_int32), ("kv_dtype", C.c_int32),
-                ("layer", C.c_uint32), ("seq_cap", C.POINTER(C.c_int32))]
+                ("layer", C.c_uint32), ("seq_cap", C.POINTER(C.c_int32)),
+                ("stage_slots", C.c_int32)]
 
 
 class State(C.Structure):
@@ -159,6 +160,7 @@ class LayerShape:
     kv_dtype: str = "bf16"
     layer: int = 0
     seq_caps: list | None = None     # token capacity per sequence (None: the lengths)
+    stage_slots: int = 0             # cross-step staging rows per KV head (0: the default)
 
     def __post_init__(self):
         self._lens = (C.c_int32 * len(self.seq_lens))(*[int(x) for x in self.seq_lens])
@@ -167,13 +169,13 @@ class LayerShape:
         self.c = Shape(len(self.seq_lens), self.n_kv_heads, self.group, HEAD_DIM,
                        C.cast(self._lens, C.POINTER(C.c_int32)), self.n_sink, self.n_local,
                        BF16 if self.kv_dtype == "bf16" else F32, self.layer,
-                       C.cast(self._caps, C.POINTER(C.c_int32)))
+                       C.cast(self._caps, C.POINTER(C.c_int32)), int(self.stage_slots))
 
     def grown(self, by: int = 1) -> "LayerShape":
         """The same layer after `by` tokens were appended to every sequence."""
         return LayerShape([n + by for n in self.seq_lens], self.n_kv_heads, self.group,
                           self.n_sink, self.n_local, self.kv_dtype, self.layer,
-                          list(self.caps))
+                          list(self.caps), self.stage_slots)
 
     @property
     def caps(self):

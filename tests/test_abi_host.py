@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(vk):
 
 def test_version_and_status_strings(vk):
     lib = vk.lib()
-    assert lib.verkv_version() == 108
+    assert lib.verkv_version() == 109
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.verkv_status_str(st).decode() not in ("", "unknown status")
     assert lib.verkv_status_str(7).decode() == "unknown status"
@@ -184,3 +184,34 @@ def test_gather_rows_memcpy_checks_its_list_before_copying(vk):
     assert lib.verkv_gather_rows_memcpy(C.c_void_p(16), 256, None, 0, C.c_void_p(16),
                                         C.byref(runs), None) == vk.OK
     assert runs.value == 0
+
+
+def test_stage_slots_grow_the_workspace_within_the_packing_limit(vk):
+    """A host-row list entry packs the token (the bits of the largest capacity) and its
+    staging slot + 1 into 32 bits: 32768-token capacities leave 17 bits (131071 slots),
+    2^20 leaves 12 (4095).  Beyond that the shape is refused (workspace size 0, and a
+    decode step returns VERKV_EINVAL before any work)."""
+    base = vk.LayerShape([32768], 8, 4, 4, 128, "bf16")
+    big = vk.LayerShape([32768], 8, 4, 4, 128, "bf16", stage_slots=16384)
+    limit = vk.LayerShape([32768], 8, 4, 4, 128, "bf16", stage_slots=131071)
+    over = vk.LayerShape([32768], 8, 4, 4, 128, "bf16", stage_slots=131072)
+    a, b, c = (x.decode_workspace_bytes(2624) for x in (base, big, limit))
+    assert 0 < a < b < c
+    # two buffers of float32-sized rows and a token per slot, per KV head
+    assert b - a >= 2 * 8 * (16384 - 4095) * (512 + 4) - 4096
+    assert over.decode_workspace_bytes(2624) == 0
+    longest = vk.LayerShape([1 << 20], 1, 4, 4, 128, "bf16", stage_slots=4095)
+    assert longest.decode_workspace_bytes(64) > 0
+    assert vk.LayerShape([1 << 20], 1, 4, 4, 128, "bf16", stage_slots=4096).decode_workspace_bytes(64) == 0
+    assert vk.LayerShape([1000], 1, 4, 4, 128, "bf16", stage_slots=-1).decode_workspace_bytes(64) == 0
+    lib = vk.lib()
+    st = _fake_state(vk, 2624)
+    step = vk.StepOut()
+    for name, _ in vk.StepOut._fields_:
+        if name != "fetch_cap":
+            setattr(step, name, FAKE)
+    step.fetch_cap = 1
+    rc = lib.verkv_decode_step(C.byref(over.c), C.byref(st), C.c_void_p(FAKE), 1.0, 0.05, 0.05,
+                               C.byref(step), C.c_void_p(FAKE), 1 << 40, None)
+    assert rc == vk.EINVAL
+    assert "stage_slots" in lib.verkv_last_error().decode()

@@ -180,13 +180,16 @@ def test_philox_layer_word():
     _run(synth.gqa_layer(seed=3, n=8192, steps=1, layer=35), label="layer 35")
 
 
-@pytest.mark.parametrize("sketch_2bit", [False, True], ids=["exact sketch", "2-bit sketch"])
-def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit):
+@pytest.mark.parametrize("sketch_2bit,stage_slots", [(False, 0), (True, 0), (False, 8192)],
+                         ids=["exact sketch", "2-bit sketch", "exact sketch, 8192 slots"])
+def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit, stage_slots):
     """Three steps on one layer with the host-row prefetch on, off, and on with a
     workspace that starts out as random bytes: every output is bit-identical (the
     prefetched rows are the same host rows; a foreign workspace only costs time).  With
     the 2-bit sketch the prefetch stages each row's key beside its value (the host fetch
-    scores fetched rows from the host keys there), and the prefetch kernel must run."""
+    scores fetched rows from the host keys there), and the prefetch kernel must run.  With
+    8192 staging slots per KV head the host-row lists (about 5K rows per head here) carry
+    slot numbers above 4095 in the bits the 8192-token capacity leaves free."""
     from long_context_decode_kvfetch_amd import verkv
     wl = synth.gqa_layer(seed=2, n=8192, steps=3, hkv=2)
     keys = ("o", "lse", "n_hat", "d_hat", "beta_star", "eps_hat", "kstar", "certified",
@@ -195,7 +198,7 @@ def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit):
     for label, kw, scramble in (("prefetch", {}, False), ("no prefetch", {"prefetch": False}, False),
                                 ("random workspace", {}, True)):
         say(f"[parity] history: {label}, {'2-bit' if sketch_2bit else 'exact'} sketch")
-        kw = dict(kw, sketch_2bit=sketch_2bit)
+        kw = dict(kw, sketch_2bit=sketch_2bit, stage_slots=stage_slots)
         sess = _session(wl, **kw)
         sess.compress()
         if scramble:
