@@ -834,6 +834,20 @@ def cpu_baseline(steps):
     dt_all, dt1_all = run()
     with threadpool_limits(1):
         dt_one, dt1_one = run()
+
+    # bounded samples of the other shapes, default threads: the 16-sequence batch by one
+    # sequence of its mean length (lengths uniform in [8K, 64K]), and one step of the 131K
+    # stress shape (eta = 1/32, no planted keys)
+    def one_step(wl_):
+        sq = wl_.seqs[0]
+        cp = oapi.compress_sequence(sq.tau, wl_.n_sink, wl_.n_local, wl_.eta, 0, 0, wl_.seed)
+        t0 = time.perf_counter()
+        oapi.decode_sequence(sq.K, sq.V, cp, wl_.queries[0, 0], wl_.group, wl_.kappa, wl_.eps, wl_.delta)
+        return time.perf_counter() - t0
+    n_mean = (8192 + 65536) // 2
+    dt_b = one_step(synth.gqa_layer(seed=0, n=n_mean, steps=1, layer=0))
+    del wl, s, comp
+    dt_l = one_step(synth.long_context(seed=0, n=131072, steps=1, eps=0.05))
     return {"value": steps / dt_all, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} decode steps of one 32K GQA layer (32q/8kv, n={N_CTX}, bf16 values "
                       f"in float64, eta=1/16), prefill excluded: {dt_all:.1f} s with the default "
@@ -841,7 +855,13 @@ def cpu_baseline(steps):
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "single_thread": {"value": steps / dt_one, "unit": "steps/s", "cores": 1},
             "single_head_n4096_ms": {"default_threads": round(dt1_all * 1e3, 1),
-                                     "one_thread": round(dt1_one * 1e3, 1)}}
+                                     "one_thread": round(dt1_one * 1e3, 1)},
+            "batch16_step_s": {"value": round(16 * dt_b, 2),
+                               "sample": f"one step of one {n_mean}-token sequence (the batch's mean "
+                                         f"length) took {dt_b:.2f} s; x 16 sequences"},
+            "long_context_131k_step_s": {"value": round(dt_l, 2),
+                                         "sample": "one step of the 131072-token layer, eta=1/32, "
+                                                   "eps=0.05, no planted keys"}}
 
 
 def main():
