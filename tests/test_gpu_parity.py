@@ -180,8 +180,9 @@ def test_philox_layer_word():
     _run(synth.gqa_layer(seed=3, n=8192, steps=1, layer=35), label="layer 35")
 
 
-@pytest.mark.parametrize("sketch_2bit,stage_slots", [(False, 0), (True, 0), (False, 8192)],
-                         ids=["exact sketch", "2-bit sketch", "exact sketch, 8192 slots"])
+@pytest.mark.parametrize("sketch_2bit,stage_slots", [(False, 0), (True, 0), (False, 8192), (True, 6000)],
+                         ids=["exact sketch", "2-bit sketch", "exact sketch, 8192 slots",
+                              "2-bit sketch, 6000 slots"])
 def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit, stage_slots):
     """Three steps on one layer with the host-row prefetch on, off, and on with a
     workspace that starts out as random bytes: every output is bit-identical (the
