@@ -71,6 +71,9 @@ def parse():
     p.add_argument("--decode36", action="store_true",
                    help="36 independent 32K layers decoded one after another per token "
                         "(eta=1/16, eps=0.05): tokens/s and host bytes per token, one JSON line")
+    p.add_argument("--decode36-grid", action="store_true",
+                   help="the 36-layer decode over eta in {1/8, 1/16, 1/32} x eps in {0.02, 0.05, 0.1} "
+                        "(8 tokens each): tokens/s and host bytes per token, one JSON line")
     p.add_argument("--long-context", action="store_true",
                    help="one 131072-token sequence, eta=1/32, keys planted on non-resident "
                         "tokens, eps in {0.05, 0.1, 0.2, 0.3, 0.5}: steps/s and fetched share, one JSON line")
@@ -662,18 +665,20 @@ def eta_eps_sweep(torch, L, K=32, W=8):
                         "delta=0.05, layers rotated", "layers": L, "steps": K, "settings": rows}
 
 
-def decode_36_layers(torch, tokens=16, warm=2, n_layers=36):
+def decode_36_layers(torch, tokens=16, warm=2, n_layers=36, eta=1.0 / 16, eps_list=(0.05,)):
     """A full decode of one sequence through 36 layers shaped like the 32K GQA layer
     (independent caches, Philox layer word = layer index): every generated token runs
     the 36 layer-steps back to back on one stream, each with its own query rows.  Reports
     tokens/s, milliseconds per layer-step and the bytes that crossed the host link per
-    token against the full cache (K and V of 36 layers)."""
+    token against the full cache (K and V of 36 layers), for each eps in `eps_list` on
+    the same compressed layers (one dict, or a list when several eps are asked for)."""
     import numpy as np
     from long_context_decode_kvfetch_amd import synth
     from long_context_decode_kvfetch_amd.runner import Session
+    runs = len(eps_list)
     sess = []
     for layer in range(n_layers):
-        wl = synth.gqa_layer(seed=0, n=N_CTX, steps=tokens + warm + 1, layer=layer)
+        wl = synth.gqa_layer(seed=0, n=N_CTX, steps=runs * (tokens + warm + 1), layer=layer, eta=eta)
         s2 = Session(wl)
         s2.compress()
         s2.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries)).to("cuda")
@@ -681,50 +686,55 @@ def decode_36_layers(torch, tokens=16, warm=2, n_layers=36):
             sq.K = sq.V = None
         sess.append(s2)
         if layer % 6 == 5:
-            log(f"[bench] decode36: {layer + 1} layers compressed")
+            log(f"[bench] decode36 eta=1/{round(1 / eta)}: {layer + 1} layers compressed")
     torch.cuda.synchronize()
+    outs = []
+    for k, eps in enumerate(eps_list):
+        q0 = k * (tokens + warm + 1)
 
-    def token(t):
+        def token(t):
+            for s2 in sess:
+                s2.step(s2.qdev[q0 + t], eps=eps)
+
+        for t in range(warm):
+            token(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warm, warm + tokens):
+            token(t)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        fail_on_flags(sess, "the 36-layer decode")
+        cert = fetched = h2d = nrow = 0
         for s2 in sess:
-            s2.step(s2.qdev[t])
-
-    for t in range(warm):
-        token(t)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for t in range(warm, warm + tokens):
-        token(t)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    fail_on_flags(sess, "the 36-layer decode")
-    cert = fetched = h2d = nrow = 0
-    for s2 in sess:
-        s2.step(s2.qdev[warm + tokens])
-        r = s2.results_numpy()
-        assert np.all(r["eps_after"] < s2.wl.eps), "a row finished uncertified"
-        cert += int(r["certified"].sum())
-        fetched += int(r["fetch_count"].sum())
-        h2d += int(r["h2d_count"].sum())
-        nrow += r["certified"].size
-    ntok = n_layers * N_CTX * 8
-    full = n_layers * 8 * N_CTX * 128 * 2 * 2                # K and V, bf16, all layers
-    resident = sum(int(s2.state.piv_count.sum().item()) for s2 in sess)
-    out = {"workload": f"{n_layers} layers x (32q/8kv, d=128, n={N_CTX}, bf16, exact sketch), "
-                       "eta=1/16, eps=0.05, delta=0.05, one sequence",
-           "layers": n_layers, "tokens": tokens, "tokens_per_s": round(tokens / (ms * 1e-3), 2),
-           "ms_per_token": round(ms / tokens, 3),
-           "ms_per_layer_step": round(ms / tokens / n_layers, 4),
-           "rows_certified_without_fetch": cert / nrow,
-           "fetched_fraction_of_cache": fetched / ntok,
-           "h2d_bytes_per_token": h2d * 128 * 2,
-           "h2d_fraction_of_full_cache_bytes": h2d * 128 * 2 / full,
-           "full_cache_bytes": full,
-           "resident_pivot_fraction": resident / ntok}
+            s2.step(s2.qdev[q0 + warm + tokens], eps=eps)
+            r = s2.results_numpy()
+            assert np.all(r["eps_after"] < eps), "a row finished uncertified"
+            cert += int(r["certified"].sum())
+            fetched += int(r["fetch_count"].sum())
+            h2d += int(r["h2d_count"].sum())
+            nrow += r["certified"].size
+        ntok = n_layers * N_CTX * 8
+        full = n_layers * 8 * N_CTX * 128 * 2 * 2                # K and V, bf16, all layers
+        resident = sum(int(s2.state.piv_count.sum().item()) for s2 in sess)
+        outs.append({"workload": f"{n_layers} layers x (32q/8kv, d=128, n={N_CTX}, bf16, exact sketch), "
+                                 f"eta=1/{round(1 / eta)}, eps={eps}, delta=0.05, one sequence",
+                     "layers": n_layers, "tokens": tokens, "eta": eta, "eps": eps,
+                     "tokens_per_s": round(tokens / (ms * 1e-3), 2),
+                     "ms_per_token": round(ms / tokens, 3),
+                     "ms_per_layer_step": round(ms / tokens / n_layers, 4),
+                     "rows_certified_without_fetch": cert / nrow,
+                     "fetched_fraction_of_cache": fetched / ntok,
+                     "h2d_bytes_per_token": h2d * 128 * 2,
+                     "h2d_fraction_of_full_cache_bytes": h2d * 128 * 2 / full,
+                     "full_cache_bytes": full,
+                     "resident_pivot_fraction": resident / ntok})
+        log(f"[bench] decode36 eta=1/{round(1 / eta)} eps={eps}: {outs[-1]['tokens_per_s']} tokens/s")
     del sess
     torch.cuda.empty_cache()
-    return out
+    return outs[0] if runs == 1 else outs
 
 
 def long_context_stress(torch, steps=16, warm=2, planted=2048):
@@ -883,6 +893,12 @@ def main():
         return
     if args.decode36:
         print(json.dumps({"decode_36_layers": decode_36_layers(torch)}))
+        return
+    if args.decode36_grid:
+        grid = []
+        for eta in (1.0 / 8, 1.0 / 16, 1.0 / 32):
+            grid += decode_36_layers(torch, tokens=8, eta=eta, eps_list=(0.02, 0.05, 0.1))
+        print(json.dumps({"decode_36_layers_grid": grid}))
         return
     if args.long_context:
         print(json.dumps({"long_context": long_context_stress(torch)}))
