@@ -351,12 +351,12 @@ def no_fetch_leg(torch, L, K=64, W=8):
     return out
 
 
-def staging_leg(torch, wls, qdevs, K=64, W=8, slots=(2048, 8192, 16384)):
+def staging_leg(torch, wls, qdevs, K=64, W=8, slots=(2048, 4096, 16384, 32768)):
     """The 32K GQA layer-step over the rotated layers with the cross-step staging sized at
-    `slots` rows per KV head (the library's default is 4095 here): steps/s, the device
-    memory the two staging buffers take per layer (bf16 value rows), and the host-row
-    kernel's time.  More slots keep more of the previous step's host rows on the device,
-    at the cost of device memory the method otherwise keeps free."""
+    `slots` rows per KV head (the library's default is 8192 here): steps/s, the device
+    memory the staging area takes per layer (bf16 value rows), and the host-row kernel's
+    time.  More slots keep more of the previous step's host rows on the device, at the
+    cost of device memory the method otherwise keeps free."""
     from long_context_decode_kvfetch_amd import verkv
     from long_context_decode_kvfetch_amd.runner import Session
     out = {"workload": "the rotated 32K GQA layers of the headline line", "settings": []}
@@ -387,7 +387,7 @@ def staging_leg(torch, wls, qdevs, K=64, W=8, slots=(2048, 8192, 16384)):
         out["settings"].append({
             "stage_slots": ns, "steps_per_s": round(K / (ms * 1e-3), 2),
             "step_ms": percentiles(per_step),
-            "staging_bytes_per_layer": 2 * 8 * ns * 128 * 2,
+            "staging_bytes_per_layer": 8 * ns * 128 * 2,
             "host_rows_us": round(prof["attend_host"][0] / prof["attend_host"][1] * 1e3, 1),
             "prefetch_us": round(prof["prefetch"][0] / max(1, prof["prefetch"][1]) * 1e3, 1),
             "decide_us": round(prof["decide"][0] / prof["decide"][1] * 1e3, 1)})

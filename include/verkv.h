@@ -78,14 +78,16 @@ typedef struct {
   uint32_t layer;           /* third Philox counter word                               */
   const int32_t *seq_cap;   /* [host][B] token capacity c_b >= n_b of each sequence's  */
                             /* arrays, each <= VERKV_MAX_SEQ_LEN (NULL: c_b = n_b)      */
-  int32_t stage_slots;      /* rows per KV head the cross-step staging of host rows    */
-                            /* holds (see verkv_state.v_host); 0: min(4095, 32768 /     */
-                            /* (B Hkv)).  At most 2^(32 - t) - 1 where t is the bits of  */
-                            /* the largest capacity (a host-row list entry packs the    */
-                            /* token and its slot + 1 into 32 bits): 131071 at 32K      */
-                            /* tokens, 4095 at 2^20 (VERKV_EINVAL beyond, checked with  */
-                            /* the shape).  The decode workspace grows by about         */
-                            /* 2 x 512 B x B x Hkv per slot.                             */
+  int32_t stage_slots;      /* host rows per KV head the cross-step staging holds (see */
+                            /* verkv_state.v_host); 0: min(8192, 65536 / (B Hkv), the   */
+                            /* limit below).  When key rows are staged beside the       */
+                            /* values (sketch_exact 0) a slot takes two rows, so half   */
+                            /* as many tokens are staged.  At most 2^(32 - t) - 1 where  */
+                            /* t is the bits of the largest capacity (a host-row list   */
+                            /* entry packs the token and its slot + 1 into 32 bits):    */
+                            /* 131071 at 32K tokens, 4095 at 2^20 (VERKV_EINVAL beyond, */
+                            /* checked with the shape).  The decode workspace grows by  */
+                            /* about (row bytes + 12 B) x B x Hkv per slot.             */
 } verkv_shape;
 
 /* GPU-resident compressed state of one layer (written by verkv_compress; the decode
@@ -107,16 +109,18 @@ typedef struct {
                             /* weights w_i = w_hat_i of step 1; 0: it reads K and V.   */
   const void *v_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the value     */
                             /* cache verkv_refine reads (may be NULL).  With it (and,   */
-                            /* when sketch_exact is 0, with k_host as well),            */
-                            /* verkv_decode_step stages value rows that                */
-                            /* the previous step on the same workspace read from the   */
-                            /* host in the workspace while the decision kernel runs    */
-                            /* (rows it staged the step before are copied within the   */
-                            /* workspace, the others read from v_host); verkv_refine   */
-                            /* then takes the rows it needs from there.  Staged rows   */
-                            /* are reused only for the same v_host address and shape,  */
-                            /* so the rows of v_host must not change between the steps */
-                            /* that share a workspace.  Results do not depend on it.   */
+                            /* when sketch_exact is 0, with k_host as well), the steps  */
+                            /* on one workspace keep host rows staged in it: the rows   */
+                            /* of the first stage_slots entries of a step's host-row    */
+                            /* list, planned at the end of verkv_refine and read from   */
+                            /* v_host by the next verkv_decode_step while its decision  */
+                            /* kernel runs (a row staged already stays where it is);    */
+                            /* verkv_refine then takes the rows it needs from there.    */
+                            /* Staged rows are reused only for the same v_host address  */
+                            /* and array layout (capacities), so the rows of v_host     */
+                            /* must not change between the steps that share a           */
+                            /* workspace (rows appended by verkv_append are new rows).  */
+                            /* Results do not depend on it.                             */
   int32_t sketch_format;    /* VERKV_SKETCH_ROWS (0): `sketch` holds kv_dtype rows as   */
                             /* above; VERKV_SKETCH_2BIT (1): `sketch` holds 64-byte     */
                             /* rows written by verkv_quantize_sketch (needs            */
@@ -129,7 +133,7 @@ typedef struct {
   const void *k_host;       /* [pinned host][B][Hkv][n_b][128] kv_dtype: the key cache  */
                             /* (may be NULL).  When sketch_exact is 0 the host fetch   */
                             /* reads key rows too; with k_host and v_host both set,     */
-                            /* the prefetch stages each row's key beside its value      */
+                            /* the staging keeps each row's key beside its value        */
                             /* (same rules as v_host above; staged rows are reused only */
                             /* for the same pair of caches).  Ignored when sketch_exact */
                             /* is 1.  Without it a non-exact sketch stages nothing.     */
@@ -247,8 +251,9 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
  *   workspace at least verkv_decode_workspace_bytes(s, st->cap); pass the same
  *          workspace to verkv_refine for this step.  Between steps it keeps each
  *          row's B*, which the next step on it takes as the starting point of its
- *          fixed-point search, the list of host rows the step read, which the next
- *          step prefetches, and the rows staged for it (see verkv_state.v_host).
+ *          fixed-point search, the list of host rows the step read, and the staged
+ *          rows with the plan verkv_refine made for the next step (see
+ *          verkv_state.v_host).
  *          Results do not depend on these: zero-filled or foreign contents only cost
  *          time (staged rows carry the identity of the cache they came from).
  * No host synchronisation and no host-memory traffic.
@@ -348,11 +353,11 @@ verkv_status verkv_gather_rows_memcpy(const void *src, size_t row_bytes, const i
  * waits for the recorded launches, writes per kernel kind the summed duration in ms
  * and the launch count (kinds: 0 PoissonComp, 1 pivot gather, 2 sketch scores,
  * 3 decision, 4 union/lists, 5 resident-pivot attention, 6 host-row attention,
- * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 host-row prefetch, 11 2-bit
- * sketch quantiser, 12 re-solved cut), and
+ * 7 finish, 8 eps_after partials, 9 pivot coefficients, 10 staging copies, 11 2-bit
+ * sketch quantiser, 12 re-solved cut, 13 staging plan), and
  * clears the record.  verkv_profile_end destroys the events.  Not
  * thread safe; meant for benchmarks. */
-#define VERKV_PROFILE_KINDS 13
+#define VERKV_PROFILE_KINDS 14
 int32_t verkv_profile_begin(int32_t max_launches);
 int32_t verkv_profile_report(double *total_ms, int32_t *launches, int32_t n_kinds);
 void verkv_profile_end(void);

@@ -79,10 +79,9 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   const int64_t src_base = HOST ? tok_base(a.t, b, g) : (int64_t)unit * a.cap;
   const int32_t *list = HOST ? a.list + tok_base(a.t, b, g) : nullptr;
   (void)list;
-  // the staging buffer this step's prefetch wrote
-  const bool alt = HOST && a.shdr && a.shdr[4] == 1;
-  const uint8_t *stage = alt ? a.stage_alt : a.stage;
-  const int32_t *stage_tok = alt ? a.stage_tok_alt : a.stage_tok;
+  // the staging area: rows of this cache kept across steps, and the token of each slot
+  const uint8_t *stage = a.stage;
+  const int32_t *stage_tok = a.stage_tok;
   (void)stage;
   (void)stage_tok;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
@@ -106,8 +105,8 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
         const uint8_t *vsrc = nullptr;
         const uint8_t *ksrc = nullptr;
         if constexpr (HOST) {
-          // a list entry is token | (prefetch slot + 1) << tok_bits; the slot's rows
-          // are used when the slot still holds this token
+          // a list entry is token | (staging slot + 1) << tok_bits; the slot's rows
+          // are used when the slot holds this token
           const int32_t e = list[p];
           tok = entry_token(e, a.t.tok_bits);
           const int slot = entry_slot(e, a.t.tok_bits);

@@ -755,8 +755,8 @@ __global__ __launch_bounds__(DC_NT) void k_decide(DecideArgs a) {
 // gives each wave its first list position, pass 2 walks the groups in order, one lane
 // per token, and writes the set bits with a ballot prefix so that consecutive list
 // entries come from consecutive lanes (whole-line stores).  Lists are ascending.  A
-// host-row entry also carries the token's prefetch slot + 1 (its rank among the
-// prefetched tokens of the head) above TOKEN_BITS, 0 when it was not prefetched.
+// host-row entry also carries the token's staging slot + 1 above tok_bits (0 when the
+// token is not staged); the host-row kernel checks the slot's token before using it.
 constexpr int LS_NT = 256;
 constexpr int LS_NB = 32;
 
@@ -781,66 +781,65 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
     const uint64_t hi32 = 2 * gi + 1 < W ? wd[2 * gi + 1] : 0u;
     return lo32 | (hi32 << 32);
   };
-  // the prefetch of this step has finished (it runs before this kernel): publish which
-  // buffer it staged and for which cache, for the next step's prefetch
-  if (a.shdr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    a.shdr[3] = a.shdr[4];
+  // the staging copies of this step have finished (they run before this kernel); when
+  // they ran for this cache, entries are tagged with their slots and the header names
+  // this cache as the one whose rows the maps hold
+  const bool staged = a.shdr && a.shdr[6] == 1ull;
+  if (staged && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     a.shdr[1] = a.ident_ptr;
     a.shdr[2] = a.ident_shape;
     a.shdr[0] = STAGE_MAGIC;
   }
-  // prefetched tokens (their rank is the prefetch slot)
-  const uint32_t *sbw = a.sbits ? a.sbits + word_base(a.t, b, g) : nullptr;
-  auto staged_bits = [&](int gi) -> uint64_t { return sbw ? group_bits(sbw, gi) : 0ull; };
-  // tokens of F, of F \ S and prefetched tokens before this block's run
-  int32_t cf = 0, ch = 0, cs = 0;
+  // the staging slot of each token of this head (-1: not staged), or none
+  const int32_t *smap = (staged && a.slot_of) ? a.slot_of + tok_base(a.t, b, g) : nullptr;
+  // tokens of F and of F \ S before this block's run
+  int32_t cf = 0, ch = 0;
   for (int gi = tid; gi < B0; gi += LS_NT) {
     const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
     cf += __popcll(f);
     ch += __popcll(f & ~r);
-    cs += __popcll(staged_bits(gi));
   }
-  int32_t bf, bh, bs;
+  int32_t bf, bh;
   (void)block_excl_scan<LS_NT>(cf, iscr, &bf);
   (void)block_excl_scan<LS_NT>(ch, iscr, &bh);
-  (void)block_excl_scan<LS_NT>(cs, iscr, &bs);
   // this block's run, split over its waves
   const int gpw = (B1 - B0 + NWV - 1) / NWV;
   const int ga = min(B1, B0 + wv * gpw), gb = min(B1, ga + gpw);
   cf = 0;
   ch = 0;
-  cs = 0;
   for (int gi = ga + lane; gi < gb; gi += WAVE) {
     const uint64_t f = group_bits(fb, gi), r = group_bits(res, gi);
     cf += __popcll(f);
     ch += __popcll(f & ~r);
-    cs += __popcll(staged_bits(gi));
   }
   cf = (int32_t)wave_sum_i64(cf);
   ch = (int32_t)wave_sum_i64(ch);
-  cs = (int32_t)wave_sum_i64(cs);
-  int32_t tf, th, ts;
+  int32_t tf, th;
   int32_t pf = block_excl_scan<LS_NT>(lane == 0 ? cf : 0, iscr, &tf);
   int32_t ph = block_excl_scan<LS_NT>(lane == 0 ? ch : 0, iscr, &th);
-  int32_t ps = block_excl_scan<LS_NT>(lane == 0 ? cs : 0, iscr, &ts);
   pf = bf + __shfl(pf, 0, WAVE);            // the wave's first positions (lane 0's)
   ph = bh + __shfl(ph, 0, WAVE);
-  ps = bs + __shfl(ps, 0, WAVE);
   int32_t *fl = a.fetch_idx ? a.fetch_idx + (int64_t)unit * a.fetch_cap : nullptr;
   int32_t *hl = a.h2d_idx + tok_base(a.t, b, g);
   const uint64_t below = (1ull << lane) - 1ull;
+  // the slot of this lane's token in group gi (-1 past n or without staging)
+  auto slot_at = [&](int gi) -> int32_t {
+    const int tok = 64 * gi + lane;
+    return (smap && gi < gb && tok < n) ? smap[tok] : -1;
+  };
   for (int c0 = ga; c0 < gb; c0 += WAVE) {
     // lane j holds group c0 + j; the walk below takes them in order by shuffle
-    uint64_t fl_l = 0, rl_l = 0, sl_l = 0;
+    uint64_t fl_l = 0, rl_l = 0;
     if (c0 + lane < gb) {
       fl_l = group_bits(fb, c0 + lane);
       rl_l = group_bits(res, c0 + lane);
-      sl_l = staged_bits(c0 + lane);
     }
     const int nj = min(WAVE, gb - c0);
+    int32_t sl_next = slot_at(c0);          // one group ahead of the walk
     for (int jj = 0; jj < nj; ++jj) {
       const uint64_t f = __shfl(fl_l, jj, WAVE), r = __shfl(rl_l, jj, WAVE);
-      const uint64_t sg = __shfl(sl_l, jj, WAVE);
+      const int32_t sl = sl_next;
+      sl_next = slot_at(c0 + jj + 1);
       const uint64_t hsel = f & ~r;
       const bool inf = (f >> lane) & 1ull, inh = (hsel >> lane) & 1ull;
       const int tok = 64 * (c0 + jj) + lane;
@@ -849,13 +848,12 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
         if (fl && pos < a.fetch_cap) fl[pos] = tok;
       }
       if (inh) {
-        // host-row entry: the token, and its prefetch slot + 1 when it was prefetched
-        const uint32_t slot1 = ((sg >> lane) & 1ull) ? (uint32_t)(ps + __popcll(sg & below) + 1) : 0u;
+        // host-row entry: the token, and its staging slot + 1 when it is staged
+        const uint32_t slot1 = (sl >= 0 && sl < a.stage_rows) ? (uint32_t)sl + 1u : 0u;
         hl[ph + (int32_t)__popcll(hsel & below)] = (int32_t)((uint32_t)tok | (slot1 << a.t.tok_bits));
       }
       pf += (int32_t)__popcll(f);
       ph += (int32_t)__popcll(hsel);
-      ps += (int32_t)__popcll(sg);
     }
   }
   if (blockIdx.x == LS_NB - 1 && tid == 0) {
@@ -869,7 +867,7 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
 // Every resident pivot gets its estimator coefficient for every query row of the
 // group: 1 on H and on S n F, lambda_i / r_i on S \ F (Definition 2 with the fetched
 // tokens exact).
-constexpr int UN_NT = 1024;
+constexpr int UN_NT = 256;              // small blocks: they fit beside the host-row kernel
 
 // The work schedule of the pivot attention, computed by one workgroup.  The pivots of
 // KV head u fall into nc_u = ceil(cnt_u / PIVOT_CHUNK) chunks; the chunks of all heads,

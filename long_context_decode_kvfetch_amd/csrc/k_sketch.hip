@@ -126,15 +126,11 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void k_sketch(SketchArgs a) {
   const int base = c * CH;
   double (*sc)[CH] = s_sc[wv];
 
-  // clear this chunk's words of the fetch bitmask (and of the prefetched-token bitmask
-  // the prefetch kernel fills after this kernel), and on chunk 0 the per-row counters
+  // clear this chunk's words of the fetch bitmask, and on chunk 0 the per-row counters
   // of the decision kernel for the G rows of this head
   if (lane < CH / 32) {
     const int w = c * (CH / 32) + lane;
-    if (w < words_of(n)) {
-      a.fbits[word_base(a.t, b, g) + w] = 0u;
-      if (a.sbits) a.sbits[word_base(a.t, b, g) + w] = 0u;
-    }
+    if (w < words_of(n)) a.fbits[word_base(a.t, b, g) + w] = 0u;
   }
   if (c == 0) {
     const int64_t row0 = ((int64_t)b * a.t.Hkv + g) * G;

@@ -93,7 +93,6 @@ struct SketchArgs {
   const double *r;            // [B][Hkv][n] inclusion probabilities
   double *cf0;                // [B][Hq][nchunks]  sum over L of wc (1 - r): f(0) per chunk
   uint32_t *fbits;            // [B][Hkv][W]  cleared here
-  uint32_t *sbits;            // [B][Hkv][W]  prefetched-token bits, cleared here (or null)
   uint32_t *wcount;           // [B][Hq] decision-kernel window counters, cleared here
   double *xseq;               // [B][Hq][xseq_row] team exchange sequence words, cleared here
   int32_t xseq_row;
@@ -182,7 +181,9 @@ struct UnionArgs {
   float *coef;               // [B][Hkv][cap][G]
   int32_t coef_pass;         // 0: fetch lists (grid y = 1); 1: pivot coefficients
   const double *params;      // coefficient pass: params[0] = kappa of the step (device)
-  const uint32_t *sbits;     // lists: [B][Hkv][W] prefetched tokens, or null
+  const int32_t *slot_of;    // lists: [B][Hkv][cap] staging slot of each token (-1: none),
+                             //   or null without staging
+  int32_t stage_rows;        // lists: staging slots per KV head
   uint64_t *shdr;            // lists: staging header to publish (null without a prefetch)
   uint64_t ident_ptr, ident_shape;
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
@@ -192,24 +193,29 @@ struct UnionArgs {
   int32_t piv_workers;       // workers the pivot attention launches
 };
 
-// Host-row prefetch: the first stage_rows entries of the previous step's host-row list
-// of each KV head are copied into the workspace (value rows only, exact sketch).
+// Cross-step staging of host rows (k_prefetch.hip).  A slot keeps its row from step to
+// step; each step makes the tokens of the first stage_rows entries of the previous step's
+// host-row list resident, reading only the rows not yet staged over the host link, into
+// slots whose tokens that list no longer holds.  slot_of and stage_tok map tokens to
+// slots and back; a pair that does not agree is not a staged row.  The plan reads the
+// list of the step that just ran (prev_list, prev_count: that step's list and count).
 struct PrefetchArgs {
   SeqTable t;
-  const int32_t *prev_list;  // [B][Hkv][n] entries of the previous list (token | slot << 20)
+  const int32_t *prev_list;  // [B][Hkv][n] entries of the previous list (token | slot + 1 above tok_bits)
   const int32_t *prev_count; // [B][Hkv]
   const uint8_t *vrows;      // host value cache (device view) [B][Hkv][n][128]
   const uint8_t *krows;      // host key cache (device view), staged beside the values when
                              //   the sketch is not exact; null: values only
   uint8_t *stage;            // [B*Hkv][stage_rows] slots of stage_stride bytes: the value
-                             //   row, then (krows set) the key row; staging buffer 0
-  int32_t *stage_tok;        // [B*Hkv][stage_rows] token of each slot, -1 if none
-  uint8_t *stage_alt;        // staging buffer 1 (the buffers alternate from step to step)
-  int32_t *stage_tok_alt;
-  uint64_t *shdr;            // staging header (STAGE_HDR_WORDS), see k_prefetch
+                             //   row, then (krows set) the key row
+  int32_t *stage_tok;        // [B*Hkv][stage_rows] token each slot holds, -1 if none
+  int32_t *slot_of;          // [B][Hkv][cap] slot holding each token, -1 if none
+  int32_t *pf_new;           // [B*Hkv][stage_rows] plan: the tokens to bring in, in list order
+  int32_t *pf_slot;          // [B*Hkv][stage_rows] plan: the slot each of them takes
+  int32_t *pf_count;         // [B*Hkv] plan: how many
+  uint64_t *shdr;            // staging header (STAGE_HDR_WORDS)
   uint64_t ident_ptr;        // identity of the cache the staged rows come from: the host
   uint64_t ident_shape;      //   value cache's device address and a hash of the shape
-  uint32_t *sbits;           // [B][Hkv][W] bit per prefetched token
   int32_t stage_rows;
   int32_t stage_stride;      // bytes per slot: one row, or two with krows
 };
@@ -231,11 +237,8 @@ struct AttendArgs {
   const int4 *runs;          // pivots: per KV head first slot, partials, first chunk
   const double *wc;          // host source with exact sketch: weights w_hat = wc * cscale
   const double *cscale;
-  const uint8_t *stage;      // host source: prefetched value rows [B*Hkv][stage_rows][128]
+  const uint8_t *stage;      // host source: staged value rows [B*Hkv][stage_rows][stride]
   const int32_t *stage_tok;  //   and their tokens (a list entry's slot is checked against it)
-  const uint8_t *stage_alt;  //   the second staging buffer and its tokens; shdr names the
-  const int32_t *stage_tok_alt;  // buffer this step's prefetch wrote (null: buffer 0)
-  const uint64_t *shdr;
   int32_t stage_rows;
   int32_t stage_stride;      // bytes per slot (the value row first)
   int32_t stage_kv;          // 1: a slot also holds the key row, after the value row
@@ -264,12 +267,14 @@ constexpr int DECIDE_THREADS = 512;
 constexpr int TEAM_MIN_TOKENS = 2048;   // tokens per team member, at least
 constexpr int WIN = 512;         // final window of the k* search
 constexpr int GATHER_ROWS = 64;   // pivot rows per gather workgroup
-constexpr int STAGE_SLOTS_DEFAULT = 4095;  // staging slots per KV head by default (at most),
-constexpr int STAGE_ROWS_TOTAL = 32768;    // and at most this many over all KV heads
-// Staging header words: [0] magic, [1] [2] identity of the staged rows' cache, [3] the
-// buffer the last published step staged, [4] the buffer this step's prefetch writes.
+constexpr int STAGE_SLOTS_DEFAULT = 8192;  // staged rows per KV head by default (at most),
+constexpr int STAGE_ROWS_TOTAL = 65536;    // and at most this many over all KV heads
+// Staging header words: [0] magic, [1] [2] the cache whose rows the maps hold (published
+// by the list kernel); [3] [4] the cache the pending plan was made for, [5] its magic
+// (written by the plan); [6] 1 when this step's copies ran (written by the copies).
 constexpr int STAGE_HDR_WORDS = 8;
 constexpr uint64_t STAGE_MAGIC = 0x7665726b76535447ull;
+constexpr uint64_t PLAN_MAGIC = 0x7665726b76504c4eull;
 constexpr int SKETCH2_ROW_BYTES = 64;   // a 2-bit sketch row: 32 B of codes, 8 float32
 constexpr int PIVOT_CHUNK = 32;   // pivot rows per schedule chunk (whole row batches)
 constexpr int PIVOT_WORKERS = 768;  // persistent pivot-attention workgroups (3 per CU)
@@ -326,7 +331,8 @@ hipError_t launch_after(const AfterArgs &a, int rows, hipStream_t st);
 hipError_t launch_resolve(ResolveArgs &a, int rows, hipStream_t st);
 int resolve_blocks_per_cu(int nch_max, bool slice_cache);
 hipError_t launch_finish(const FinishArgs &a, int rows, hipStream_t st);
-hipError_t launch_prefetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st);
+hipError_t launch_stage_plan(const PrefetchArgs &a, int units, hipStream_t st);
+hipError_t launch_stage_fetch(const PrefetchArgs &a, int units, bool bf16, hipStream_t st);
 int decide_blocks_per_cu(int max_n, int team);
 bool decide_slice_cached(int max_n, int team);
 

@@ -30,15 +30,17 @@ verkv_status hip_fail(hipError_t e, const char *where) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// FNV-1a over the shape of a layer: with the host cache's address it names the rows a
-// workspace's staging buffers hold
+// FNV-1a over the layout of a layer's arrays: with the host cache's address it names the
+// rows a workspace's staging area holds.  The sequence lengths are left out: a cache that
+// grows (verkv_append) keeps the rows it had, and every staged token is checked against
+// the current length.
 uint64_t shape_ident(const SeqTable &t, bool bf16) {
   uint64_t h = 1469598103934665603ull;
   auto mix = [&](uint64_t v) {
     for (int k = 0; k < 8; ++k) { h ^= (v >> (8 * k)) & 0xFF; h *= 1099511628211ull; }
   };
   mix((uint64_t)t.B); mix((uint64_t)t.Hkv); mix((uint64_t)t.G); mix(bf16 ? 1 : 0);
-  for (int b = 0; b < t.B; ++b) { mix((uint64_t)t.s[b].n); mix((uint64_t)t.s[b].cap); }
+  for (int b = 0; b < t.B; ++b) mix((uint64_t)t.s[b].cap);
   mix((uint64_t)(uint32_t)t.stage_slots);
   return h;
 }
@@ -136,16 +138,25 @@ int team_size(int rows, int max_n) {
   return std::max(1, std::min(TEAM_MAX, std::min(by_cu, by_len)));
 }
 
+// Host rows staged per KV head: the shape's stage_slots, or by default up to
+// STAGE_SLOTS_DEFAULT per KV head and STAGE_ROWS_TOTAL in all, within what a list entry
+// can name.
+int stage_rows_of(const SeqTable &t, int units) {
+  if (t.stage_slots > 0) return t.stage_slots;
+  const int64_t lim = (1ll << (32 - t.tok_bits)) - 1;
+  return (int)std::min<int64_t>(lim, std::min(STAGE_SLOTS_DEFAULT, STAGE_ROWS_TOTAL / std::max(1, units)));
+}
+
 // Decode workspace layout.
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
-  size_t stage, stage_tok, stage_alt, stage_tok_alt, shdr, sbits, h2dc, psched, pruns, gpar;
+  size_t stage, stage_tok, slot_of, pf_new, pf_slot, pf_cnt, shdr, h2dc, psched, pruns, gpar;
   int srows;
   size_t total;
   int nsp, nsh, team;      // nsp: pivot partial slots
 };
-DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
+DecodeWs decode_layout(const SeqTable &t, int cap, bool bf16, bool staging = true) {
   const Totals T = totals(t);
   const int64_t Hq = (int64_t)t.Hkv * t.G;
   const int units = t.B * t.Hkv;
@@ -178,16 +189,16 @@ DecodeWs decode_layout(const SeqTable &t, int cap, bool staging = true) {
   w.hpart = off;  off = align_up(off + 4 * (size_t)units * w.nsh * t.G * (D + 1));
   w.status = off; off = align_up(off + 64);
   w.bprev = off;  off = align_up(off + 8 * (size_t)rows);
-  // host-row prefetch: value rows staged per KV head (sized for float32 rows)
-  w.srows = !staging ? 0
-            : t.stage_slots > 0 ? t.stage_slots
-                                : std::min(STAGE_SLOTS_DEFAULT, STAGE_ROWS_TOTAL / std::max(1, units));
-  w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * 4);
+  // cross-step staging of host rows: srows rows of the cache's dtype per KV head, the
+  // maps between slots and tokens, and the plan of each step
+  w.srows = !staging ? 0 : stage_rows_of(t, units);
+  w.stage = off;     off = align_up(off + (size_t)units * w.srows * D * (bf16 ? 2 : 4));
   w.stage_tok = off; off = align_up(off + 4 * (size_t)units * w.srows);
-  w.stage_alt = off; off = align_up(off + (size_t)units * w.srows * D * 4);
-  w.stage_tok_alt = off; off = align_up(off + 4 * (size_t)units * w.srows);
+  w.slot_of = off;   off = align_up(off + (w.srows > 0 ? 4 * (size_t)(t.Hkv * T.tok) : 0));
+  w.pf_new = off;    off = align_up(off + 4 * (size_t)units * w.srows);
+  w.pf_slot = off;   off = align_up(off + 4 * (size_t)units * w.srows);
+  w.pf_cnt = off;    off = align_up(off + 4 * (size_t)units);
   w.shdr = off;      off = align_up(off + 8 * (size_t)STAGE_HDR_WORDS);
-  w.sbits = off;     off = align_up(off + 4 * (size_t)(t.Hkv * T.words));
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
   w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
   w.pruns = off;     off = align_up(off + 16 * (size_t)units);
@@ -260,7 +271,7 @@ int decide_capacity(int max_n, int team) {
 // call are recorded under a per-device lock.
 struct Side {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, pref = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, pref = nullptr, dec = nullptr;
   std::mutex mu;
 };
 constexpr int MAX_DEVICES = 64;
@@ -278,6 +289,7 @@ verkv_status side_for_device(Side **out) {
     HIP_TRY(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming), "hipEventCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming), "hipEventCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&sd.pref, hipEventDisableTiming), "hipEventCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&sd.dec, hipEventDisableTiming), "hipEventCreateWithFlags");
   }
   *out = &sd;
   return VERKV_OK;
@@ -285,7 +297,7 @@ verkv_status side_for_device(Side **out) {
 
 // ---------------------------------------------------------------- optional kernel timing
 enum KernelId { K_POISSON = 0, K_GATHER, K_SKETCH, K_DECIDE, K_UNION, K_PIVOT, K_HOST, K_FINISH, K_AFTER,
-                K_COEF, K_PREFETCH, K_QUANT, K_RESOLVE, K_COUNT };
+                K_COEF, K_PREFETCH, K_QUANT, K_RESOLVE, K_PLAN, K_COUNT };
 struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> ev;       // pairs
@@ -515,7 +527,7 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap) {
 size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap) {
   SeqTable t;
   if (cap < 1 || make_table(s, t) != VERKV_OK) return 0;
-  return decode_layout(t, cap).total;
+  return decode_layout(t, cap, s->kv_dtype == VERKV_BF16).total;
 }
 
 verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *K_host,
@@ -640,9 +652,9 @@ static verkv_status prefetch_source(const verkv_state *st, int srows, const void
   return rc;
 }
 
-// Staging slots: the workspace reserves srows float32-sized rows per KV head and
-// buffer; a slot holds the value row, or the value and the key row (keys staged), so
-// with float32 rows and keys the slot count halves.
+// Staging slots: the workspace reserves srows rows of the cache's dtype per KV head; a
+// slot holds the value row, or the value and the key row (keys staged), so with keys
+// the slot count halves.
 struct StageGeom {
   int rows;
   int stride;
@@ -650,8 +662,7 @@ struct StageGeom {
 };
 static StageGeom stage_geom(int srows, bool bf16, bool kv) {
   const int row = VERKV_HEAD_DIM * (bf16 ? 2 : 4);
-  const int stride = kv ? 2 * row : row;
-  return StageGeom{kv ? (int)((int64_t)srows * VERKV_HEAD_DIM * 4 / stride) : srows, stride, kv};
+  return StageGeom{kv ? srows / 2 : srows, kv ? 2 * row : row, kv};
 }
 
 // The identity staged rows are published under: the shape, and the key cache's
@@ -662,6 +673,66 @@ static uint64_t stage_ident(const SeqTable &t, bool bf16, const void *Kd) {
   const uint64_t k = reinterpret_cast<uint64_t>(Kd);
   for (int i = 0; i < 8; ++i) { h ^= (k >> (8 * i)) & 0xFF; h *= 1099511628211ull; }
   return h;
+}
+
+// The pivot-coefficient pass of a step on workspace ws (with the pivot attention's
+// schedule in its extra workgroup).
+static UnionArgs coef_args(const SeqTable &t, const verkv_state *st, uint8_t *ws, const DecodeWs &L,
+                           const verkv_step_out *out, int units) {
+  UnionArgs un;
+  un.t = t;
+  un.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  un.resident = st->resident;
+  un.piv_idx = st->piv_idx;
+  un.piv_count = st->piv_count;
+  un.cap = st->cap;
+  un.r = st->r;
+  un.wc = reinterpret_cast<const double *>(ws + L.wc);
+  un.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  un.beta_star = out->beta_star;
+  un.kappa = 0.0;
+  un.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa of the step
+  un.fetch_idx = nullptr;
+  un.fetch_cap = 0;
+  un.fetch_count = nullptr;
+  un.h2d_count = nullptr;
+  un.h2d_idx = nullptr;
+  un.coef = reinterpret_cast<float *>(ws + L.coef);
+  un.coef_pass = 1;
+  un.slot_of = nullptr;
+  un.stage_rows = 0;
+  un.shdr = nullptr;
+  un.ident_ptr = 0;
+  un.ident_shape = 0;
+  un.h2d_count_ws = nullptr;
+  un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
+  un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
+  un.piv_workers = pivot_workers(st->cap, units);
+  return un;
+}
+
+// The staging arguments of a step on workspace ws: the copies (decode) and the plan for
+// the next step (refine) share them.
+static PrefetchArgs stage_args(const SeqTable &t, uint8_t *ws, const DecodeWs &L, const void *Vd,
+                               const void *Kd, bool bf16, const StageGeom &sg) {
+  PrefetchArgs pa;
+  pa.t = t;
+  pa.prev_list = reinterpret_cast<const int32_t *>(ws + L.h2d);
+  pa.prev_count = reinterpret_cast<const int32_t *>(ws + L.h2dc);
+  pa.vrows = static_cast<const uint8_t *>(Vd);
+  pa.krows = static_cast<const uint8_t *>(Kd);
+  pa.stage = ws + L.stage;
+  pa.stage_tok = reinterpret_cast<int32_t *>(ws + L.stage_tok);
+  pa.slot_of = reinterpret_cast<int32_t *>(ws + L.slot_of);
+  pa.pf_new = reinterpret_cast<int32_t *>(ws + L.pf_new);
+  pa.pf_slot = reinterpret_cast<int32_t *>(ws + L.pf_slot);
+  pa.pf_count = reinterpret_cast<int32_t *>(ws + L.pf_cnt);
+  pa.shdr = reinterpret_cast<uint64_t *>(ws + L.shdr);
+  pa.ident_ptr = reinterpret_cast<uint64_t>(Vd);
+  pa.ident_shape = stage_ident(t, bf16, Kd);
+  pa.stage_rows = sg.rows;
+  pa.stage_stride = sg.stride;
+  return pa;
 }
 
 // How a step uses the library's resources: the ordinary entry points stage host rows
@@ -710,10 +781,10 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   verkv_status rc = decode_args(s, st, q, beta, eps, delta, out, t);
   if (rc != VERKV_OK) return rc;
   if (!workspace) return VERKV_EINVAL;
-  const DecodeWs L = decode_layout(t, st->cap, mode.staging);
+  const bool bf16 = s->kv_dtype == VERKV_BF16;
+  const DecodeWs L = decode_layout(t, st->cap, bf16, mode.staging);
   if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  const bool bf16 = s->kv_dtype == VERKV_BF16;
   const Totals T = totals(t);
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
@@ -721,9 +792,9 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   const void *Vd = nullptr, *Kd = nullptr;
   if (mode.side && (rc = prefetch_source(st, L.srows, &Vd, &Kd)) != VERKV_OK) return rc;
   const bool prefetch = Vd != nullptr;   // host cache(s) and staging rows
-  const StageGeom sg = stage_geom(L.srows, s->kv_dtype == VERKV_BF16, Kd != nullptr);
+  const StageGeom sg = stage_geom(L.srows, bf16, Kd != nullptr);
   Side *sd = nullptr;
-  if (prefetch && (rc = side_for_device(&sd)) != VERKV_OK) return rc;
+  if (mode.side && (rc = side_for_device(&sd)) != VERKV_OK) return rc;
 
   SketchArgs sk;
   sk.t = t;
@@ -736,8 +807,6 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   sk.r = st->r;
   sk.cf0 = reinterpret_cast<double *>(ws + L.cf0);
   sk.fbits = reinterpret_cast<uint32_t *>(ws + L.fbits);
-  // the prefetch below (when it runs) sets the bits of the rows it stages
-  sk.sbits = prefetch ? reinterpret_cast<uint32_t *>(ws + L.sbits) : nullptr;
   sk.wcount = reinterpret_cast<uint32_t *>(ws + L.wcount);
   sk.xseq = reinterpret_cast<double *>(ws + L.xseq);
   sk.xseq_row = 2 * L.team;
@@ -748,40 +817,25 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     HIP_TRY(launch_sketch(sk, bf16, stream), "sketch launch");
   }
 
-  // host-row prefetch on the library's second stream, beside the decision kernel (it
-  // starts after the sketch kernel, which needs every register of the CUs): rows the
-  // previous step on this workspace read from the host
-  // The fork point is the end of the sketch kernel; the prefetch itself is enqueued after
-  // the decision kernel, so that the decision workgroups are placed on the CUs before the
-  // prefetch blocks are (enqueued first, the prefetch delayed the start of the last team
-  // members by 13-15 us).
+  // staging copies on the library's second stream, beside the decision kernel (they
+  // start after the sketch kernel, which needs every register of the CUs): the rows the
+  // plan of the previous step on this workspace brings in.  The fork point is the end of
+  // the sketch kernel; the copies are enqueued after the decision kernel, so that the
+  // decision workgroups are placed on the CUs before the copy blocks are (enqueued
+  // first, they delayed the start of the last team members by 13-15 us).
   std::unique_lock<std::mutex> lk;
+  if (mode.side) lk = std::unique_lock<std::mutex>(sd->mu);
   PrefetchArgs pa;
   if (prefetch) {
-    lk = std::unique_lock<std::mutex>(sd->mu);
     HIP_TRY(hipEventRecord(sd->fork, stream), "hipEventRecord");
-    pa.t = t;
-    pa.prev_list = reinterpret_cast<const int32_t *>(ws + L.h2d);
-    pa.prev_count = reinterpret_cast<const int32_t *>(ws + L.h2dc);
-    pa.vrows = static_cast<const uint8_t *>(Vd);
-    pa.krows = static_cast<const uint8_t *>(Kd);
-    pa.stage = ws + L.stage;
-    pa.stage_tok = reinterpret_cast<int32_t *>(ws + L.stage_tok);
-    pa.stage_alt = ws + L.stage_alt;
-    pa.stage_tok_alt = reinterpret_cast<int32_t *>(ws + L.stage_tok_alt);
-    pa.shdr = reinterpret_cast<uint64_t *>(ws + L.shdr);
-    pa.ident_ptr = reinterpret_cast<uint64_t>(Vd);
-    pa.ident_shape = stage_ident(t, bf16, Kd);
-    pa.sbits = reinterpret_cast<uint32_t *>(ws + L.sbits);
-    pa.stage_rows = sg.rows;
-    pa.stage_stride = sg.stride;
+    pa = stage_args(t, ws, L, Vd, Kd, bf16, sg);
   }
   auto launch_pf = [&]() -> verkv_status {
     if (!prefetch) return VERKV_OK;
     HIP_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0), "hipStreamWaitEvent");
     {
       Timed tm(K_PREFETCH, sd->s);
-      HIP_TRY(launch_prefetch(pa, units, bf16, sd->s), "prefetch launch");
+      HIP_TRY(launch_stage_fetch(pa, units, bf16, sd->s), "staging copy launch");
     }
     HIP_TRY(hipEventRecord(sd->pref, sd->s), "hipEventRecord");
     return VERKV_OK;
@@ -900,7 +954,8 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   un.coef = reinterpret_cast<float *>(ws + L.coef);
   un.params = nullptr;
   un.coef_pass = 0;
-  un.sbits = prefetch ? reinterpret_cast<const uint32_t *>(ws + L.sbits) : nullptr;
+  un.slot_of = prefetch && sg.rows > 0 ? reinterpret_cast<const int32_t *>(ws + L.slot_of) : nullptr;
+  un.stage_rows = prefetch ? sg.rows : 0;
   un.shdr = prefetch ? reinterpret_cast<uint64_t *>(ws + L.shdr) : nullptr;
   un.ident_ptr = reinterpret_cast<uint64_t>(Vd);
   un.ident_shape = stage_ident(t, bf16, Kd);
@@ -908,11 +963,18 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   un.piv_sched = nullptr;
   un.piv_runs = nullptr;
   un.piv_workers = 0;
-  // the list is rewritten here: the prefetch must have read it
-  if (prefetch) {
-    HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
-    lk.unlock();
+  // the estimator coefficients of the resident pivots and the pivot schedule need only
+  // the decisions: on the second stream they run beside the list kernel, before the
+  // host-row kernel of verkv_refine fills the CUs
+  if (mode.side) {
+    UnionArgs cf = coef_args(t, st, ws, L, out, units);
+    HIP_TRY(hipEventRecord(sd->dec, stream), "hipEventRecord");
+    HIP_TRY(hipStreamWaitEvent(sd->s, sd->dec, 0), "hipStreamWaitEvent");
+    Timed tm(K_COEF, sd->s);
+    HIP_TRY(launch_union(cf, units, sd->s), "pivot coefficient launch");
   }
+  // the list kernel tags entries with the slots the copies filled
+  if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
   {
     Timed tm(K_UNION, stream);
     HIP_TRY(launch_union(un, units, stream), "union launch");
@@ -930,12 +992,15 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   verkv_status rc = refine_args(s, st, q, K_host, V_host, out, t, &Kd, &Vd);
   if (rc != VERKV_OK) return rc;
   if (!workspace) return VERKV_EINVAL;
-  const DecodeWs L = decode_layout(t, st->cap, mode.staging);
+  const bool bf16 = s->kv_dtype == VERKV_BF16;
+  const DecodeWs L = decode_layout(t, st->cap, bf16, mode.staging);
   if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  const bool bf16 = s->kv_dtype == VERKV_BF16;
   const int units = t.B * t.Hkv;
   const int rows = units * t.G;
+  // the caches the next step's staging reads (resolved before anything is enqueued)
+  const void *Vs = nullptr, *Ks = nullptr;
+  if (mode.side && (rc = prefetch_source(st, L.srows, &Vs, &Ks)) != VERKV_OK) return rc;
 
   // the resident-pivot side runs on the library's second stream (forked from and joined
   // back into the caller's), or on the caller's stream after the host rows
@@ -971,9 +1036,6 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   at.cscale = reinterpret_cast<const double *>(ws + L.cscale);
   at.stage = ws + L.stage;
   at.stage_tok = reinterpret_cast<const int32_t *>(ws + L.stage_tok);
-  at.stage_alt = ws + L.stage_alt;
-  at.stage_tok_alt = reinterpret_cast<const int32_t *>(ws + L.stage_tok_alt);
-  at.shdr = L.srows > 0 ? reinterpret_cast<const uint64_t *>(ws + L.shdr) : nullptr;
   // the slot geometry of this state's prefetch (list entries carry slots only for rows
   // that a prefetch with this geometry staged)
   const StageGeom sg = stage_geom(L.srows, bf16, !st->sketch_exact && st->k_host && st->v_host);
@@ -986,37 +1048,10 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
             "host attention launch");
   }
 
-  // side stream: estimator coefficients of the resident pivots, their attention
-  // partials, then eps_after
-  UnionArgs un;
-  un.t = t;
-  un.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
-  un.resident = st->resident;
-  un.piv_idx = st->piv_idx;
-  un.piv_count = st->piv_count;
-  un.cap = st->cap;
-  un.r = st->r;
-  un.wc = reinterpret_cast<const double *>(ws + L.wc);
-  un.cscale = reinterpret_cast<const double *>(ws + L.cscale);
-  un.beta_star = out->beta_star;
-  un.kappa = 0.0;
-  un.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa of the step
-  un.fetch_idx = nullptr;
-  un.fetch_cap = 0;
-  un.fetch_count = nullptr;
-  un.h2d_count = nullptr;
-  un.h2d_idx = nullptr;
-  un.coef = reinterpret_cast<float *>(ws + L.coef);
-  un.coef_pass = 1;
-  un.sbits = nullptr;
-  un.shdr = nullptr;
-  un.ident_ptr = 0;
-  un.ident_shape = 0;
-  un.h2d_count_ws = nullptr;
-  un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
-  un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
-  un.piv_workers = pivot_workers(st->cap, units);
-  {
+  // the estimator coefficients of the resident pivots: on the second stream they were
+  // computed by verkv_decode_step; on the caller's stream they are computed here
+  const UnionArgs un = coef_args(t, st, ws, L, out, units);
+  if (!mode.side) {
     Timed tm(K_COEF, side);
     HIP_TRY(launch_union(un, units, side), "pivot coefficient launch");
   }
@@ -1040,9 +1075,6 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   pv.cscale = nullptr;
   pv.stage = nullptr;
   pv.stage_tok = nullptr;
-  pv.stage_alt = nullptr;
-  pv.stage_tok_alt = nullptr;
-  pv.shdr = nullptr;
   pv.stage_rows = 0;
   pv.stage_stride = 0;
   pv.stage_kv = 0;
@@ -1066,6 +1098,12 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
     HIP_TRY(launch_after(af, rows, side), "eps_after launch");
   }
 
+  // the staging plan of the next step, from this step's list, last on the second stream
+  if (Vs) {
+    const PrefetchArgs pl = stage_args(t, ws, L, Vs, Ks, bf16, stage_geom(L.srows, bf16, Ks != nullptr));
+    Timed tm(K_PLAN, side);
+    HIP_TRY(launch_stage_plan(pl, units, side), "staging plan launch");
+  }
   // join before the finishing kernel
   if (mode.side) {
     HIP_TRY(hipEventRecord(sd->join, sd->s), "hipEventRecord");
@@ -1139,7 +1177,7 @@ verkv_status verkv_step_noalloc(const verkv_shape *s, const verkv_state *st, con
   if (rc != VERKV_OK) return rc;
   const void *Kd = nullptr, *Vd = nullptr;
   if ((rc = refine_args(s, st, q, K_host, V_host, out, t, &Kd, &Vd)) != VERKV_OK) return rc;
-  const size_t need = decode_layout(t, st->cap, false).total;
+  const size_t need = decode_layout(t, st->cap, s->kv_dtype == VERKV_BF16, false).total;
   if (need > STATIC_SCRATCH_BYTES) {
     std::snprintf(g_last_error, sizeof(g_last_error),
                   "this shape needs %zu bytes of scratch; the static array holds %zu", need,
@@ -1164,7 +1202,7 @@ verkv_status verkv_check(void *workspace, const verkv_shape *s, int32_t cap, ver
   verkv_status rc = make_table(s, t);
   if (rc != VERKV_OK) return rc;
   if (!workspace || cap < 1) return VERKV_EINVAL;
-  const DecodeWs L = decode_layout(t, cap);
+  const DecodeWs L = decode_layout(t, cap, s->kv_dtype == VERKV_BF16);
   int32_t *status = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + L.status);
   int32_t h = 0;
   HIP_TRY(hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, stream), "hipMemcpyAsync");

@@ -21,10 +21,10 @@ LIB_PATH = os.environ.get("VERKV_LIBRARY") or os.path.join(_HERE, "libverkv.so")
 OK, EINVAL, EBUDGET, ECAPACITY, EHIP, EUNSUPPORTED, EWORKSPACE = 0, -1, -2, -3, -4, -5, -6
 BF16, F32 = 0, 1
 HEAD_DIM = 128
-PROFILE_KINDS = 13
+PROFILE_KINDS = 14
 KERNEL_NAMES = ["poissoncomp", "gather_pivots", "sketch_scores", "decide", "union_lists",
                 "attend_pivots", "attend_host", "finish", "eps_after", "pivot_coef", "prefetch",
-                "quantize_sketch", "resolve"]
+                "quantize_sketch", "resolve", "stage_plan"]
 
 
 class VerKVError(RuntimeError):

@@ -197,8 +197,9 @@ def test_stage_slots_grow_the_workspace_within_the_packing_limit(vk):
     over = vk.LayerShape([32768], 8, 4, 4, 128, "bf16", stage_slots=131072)
     a, b, c = (x.decode_workspace_bytes(2624) for x in (base, big, limit))
     assert 0 < a < b < c
-    # two buffers of float32-sized rows and a token per slot, per KV head
-    assert b - a >= 2 * 8 * (16384 - 4095) * (512 + 4) - 4096
+    # per slot and KV head: one bf16 row, its token, and the two plan entries (the default
+    # is 8192 slots per KV head at this shape)
+    assert b - a >= 8 * (16384 - 8192) * (256 + 3 * 4) - 4096
     assert over.decode_workspace_bytes(2624) == 0
     longest = vk.LayerShape([1 << 20], 1, 4, 4, 128, "bf16", stage_slots=4095)
     assert longest.decode_workspace_bytes(64) > 0

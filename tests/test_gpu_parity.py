@@ -184,11 +184,11 @@ def test_philox_layer_word():
                          ids=["exact sketch", "2-bit sketch", "exact sketch, 8192 slots",
                               "2-bit sketch, 6000 slots"])
 def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit, stage_slots):
-    """Three steps on one layer with the host-row prefetch on, off, and on with a
-    workspace that starts out as random bytes: every output is bit-identical (the
-    prefetched rows are the same host rows; a foreign workspace only costs time).  With
-    the 2-bit sketch the prefetch stages each row's key beside its value (the host fetch
-    scores fetched rows from the host keys there), and the prefetch kernel must run.  With
+    """Three steps on one layer with the cross-step staging of host rows on, off, and on
+    with a workspace that starts out as random bytes: every output is bit-identical (the
+    staged rows are the same host rows; a foreign workspace only costs time).  With the
+    2-bit sketch each row's key is staged beside its value (the host fetch scores fetched
+    rows from the host keys there), and the staging copies must run on every step.  With
     8192 staging slots per KV head the host-row lists (about 5K rows per head here) carry
     slot numbers above 4095 in the bits the 8192-token capacity leaves free."""
     from long_context_decode_kvfetch_amd import verkv
@@ -255,6 +255,44 @@ def test_staged_rows_of_another_cache_are_not_reused():
         got = sb.results_numpy()
         for k in keys:
             assert np.array_equal(np.array(got[k]), expect[st][k]), (st, k)
+
+
+def test_staging_slots_survive_evictions_and_cache_switches():
+    """Eight steps on one workspace shared by two layers (two host caches of the same
+    shape) in the order A A B A B B A A, with a staging area of 1500 rows per KV head
+    against host-row lists of about 5K rows: every plan evicts and refills slots, and a
+    plan made for one cache must not be carried out for the other.  Every output equals
+    that of the same layer without staging, bit for bit; the staged copies run on every
+    step (they do nothing when the pending plan names the other cache)."""
+    from long_context_decode_kvfetch_amd import verkv
+    keys = ("o", "lse", "n_hat", "d_hat", "eps_after", "fetch_count", "h2d_count", "kstar")
+    wa = synth.gqa_layer(seed=4, n=8192, steps=8, hkv=2, layer=0)
+    wb = synth.gqa_layer(seed=4, n=8192, steps=8, hkv=2, layer=1)
+    sa, sb = _session(wa, stage_slots=1500), _session(wb, stage_slots=1500)
+    ra, rb = _session(wa, prefetch=False), _session(wb, prefetch=False)
+    for s_ in (sa, sb, ra, rb):
+        s_.compress()
+    sb.dws = sa.dws                                   # one staging area for both caches
+    order = "AABABBAA"
+    taken = {"A": 0, "B": 0}
+    verkv.profile_begin(512)                          # room for every launch of the 16 steps
+    for i, name in enumerate(order):
+        sess, ref = (sa, ra) if name == "A" else (sb, rb)
+        st = taken[name]
+        taken[name] += 1
+        say(f"[parity] staging slots: step {i} on cache {name} (its step {st})")
+        sess.step(sess.queries(st))
+        verkv.check(sess.shape, sess.cap, sess.dws)
+        got = sess.results_numpy()
+        got = {k: np.array(got[k]) for k in keys}
+        ref.step(ref.queries(st))
+        want = ref.results_numpy()
+        for k in keys:
+            assert np.array_equal(got[k], np.array(want[k])), (i, name, k)
+        assert int(got["h2d_count"].sum()) > 2 * 1500          # the lists outgrow the area
+    launches = verkv.profile_report()
+    verkv.profile_end()
+    assert launches["prefetch"][1] == len(order) and launches["stage_plan"][1] == len(order)
 
 
 # ------------------------------------------------------------------ the 2-bit sketch
