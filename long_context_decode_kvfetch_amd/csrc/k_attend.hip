@@ -50,11 +50,11 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   const int grp = lane / LPT;
   const int d0 = sub * EPL;
 
+  // the list in batches of STEP * U consecutive entries, dealt round-robin to the
+  // workgroups of the head: the staged rows (the list's first entries) and the rows
+  // read over the host link are spread evenly over the workgroups
   const int cnt = HOST ? a.count[unit] : min(a.count[unit], a.cap);
-  int per = (cnt + a.nsplit - 1) / a.nsplit;
-  per = ((per + STEP - 1) / STEP) * STEP;
-  const int p0 = split * per;
-  const int p1 = min(cnt, p0 + per);
+  const int p1 = cnt;
 
   float qf[G][EPL];
   float mh[G];
@@ -184,17 +184,18 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
     }
   };
   constexpr int SU = STEP * U;
+  const int stride = a.nsplit * SU;
   Batch A, B;
-  int base = p0;
+  int base = split * SU;
   if (base < p1) issue(base, A);
   while (base < p1) {
-    if (base + SU < p1) issue(base + SU, B);
+    if (base + stride < p1) issue(base + stride, B);
     consume(A);
-    base += SU;
+    base += stride;
     if (base >= p1) break;
-    if (base + SU < p1) issue(base + SU, A);
+    if (base + stride < p1) issue(base + stride, A);
     consume(B);
-    base += SU;
+    base += stride;
   }
 
   // every row group of every wave leaves its partial in LDS; each output element is
