@@ -28,17 +28,18 @@ constexpr int Q_BITS = 40;
 constexpr int IDX_BITS = 20;                 // token index < 2^20 inside the sort key
 constexpr uint64_t IDX_MASK = (1ull << IDX_BITS) - 1;
 
-// Stable LSD radix sort of `n` 64-bit keys in src (8 passes of 8 bits); the result is
-// back in `src`.  One workgroup.  Within a tile of PC_NT keys the rank of a key among
-// equal digits is found with wave ballots, so equal digits keep their input order.
-__device__ void block_radix_sort(uint64_t *src, uint64_t *dst, int n, uint32_t *hist,
-                                 uint32_t *wcnt /*[PC_NW][256]*/) {
+// Stable LSD radix sort of `n` 64-bit keys in src by their bits from `lo_bit` up (an
+// even number of passes of 8 bits, `passes`); the result is back in `src`.  Keys that
+// agree in those bits keep their input order.  One workgroup.  Within a tile of PC_NT
+// keys the rank of a key among equal digits is found with wave ballots.
+__device__ void block_radix_sort(uint64_t *src, uint64_t *dst, int n, int lo_bit, int passes,
+                                 uint32_t *hist, uint32_t *wcnt /*[PC_NW][256]*/) {
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wv = tid / WAVE;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 8 * pass;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = lo_bit + 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += PC_NT) atomicAdd(&hist[(src[i] >> shift) & 255], 1u);
@@ -83,10 +84,33 @@ __device__ void block_radix_sort(uint64_t *src, uint64_t *dst, int n, uint32_t *
   }
 }
 
+// Inclusive suffix sums of v over the workgroup's threads (thread t gets the sum over
+// threads >= t), exact in 64-bit integers, and the workgroup's total.
+__device__ uint64_t block_suffix_sum_u64(uint64_t v, uint64_t *wsum /*[PC_NW]*/, uint64_t *total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wv = tid / WAVE;
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const uint64_t o = __shfl_down(v, off, WAVE);
+    if (lane + off < WAVE) v += o;
+  }
+  if (lane == 0) wsum[wv] = v;            // lane 0 holds its wave's total
+  __syncthreads();
+  uint64_t after = 0, tot = 0;
+  for (int w = 0; w < PC_NW; ++w) {
+    const uint64_t x = wsum[w];
+    after += w > wv ? x : 0ull;
+    tot += x;
+  }
+  __syncthreads();                        // wsum is reused by the next call
+  *total = tot;
+  return v + after;
+}
+
 __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wcnt[PC_NW * 256];
-  __shared__ uint64_t scan[PC_NT];
+  __shared__ uint64_t wsum[PC_NW];
   __shared__ int32_t iscratch[PC_NW];
   __shared__ int32_t s_mstar;
 
@@ -115,7 +139,9 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   }
 
   if (nfree > 0 && b_rem > 0.0 && b_rem < (double)nfree) {
-    // sort keys: (2^40 - Q) << 20 | index  ->  ascending = Q descending, index ascending
+    // sort keys: (2^40 - Q) << 20 | index  ->  ascending = Q descending, index ascending.
+    // They are written in index order and the sort is stable, so sorting by bits 20-60
+    // (2^40 - Q < 2^41) alone gives the order of the whole keys: six passes, not eight.
     for (int j = tid; j < nfree; j += PC_NT) {
       const int i = lo + j;
       const float x = tau[i];
@@ -124,7 +150,8 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
       ka[j] = (((1ull << Q_BITS) - q) << IDX_BITS) | (uint64_t)i;
     }
     __syncthreads();
-    block_radix_sort(ka, kb, nfree, hist, wcnt);
+    static_assert(IDX_BITS + Q_BITS + 1 <= IDX_BITS + 8 * 6, "six passes cover 2^40 - Q");
+    block_radix_sort(ka, kb, nfree, IDX_BITS, 6, hist, wcnt);
 
     // exact suffix sums S_m of Q over ranks, tile by tile from the end -> kb[m]
     uint64_t carry = 0;
@@ -132,17 +159,10 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
     for (int tix = ntile - 1; tix >= 0; --tix) {
       const int m = tix * PC_NT + tid;
       const uint64_t q = (m < nfree) ? ((1ull << Q_BITS) - (ka[m] >> IDX_BITS)) : 0ull;
-      scan[tid] = q;
-      __syncthreads();
-      for (int off = 1; off < PC_NT; off <<= 1) {
-        const uint64_t v = (tid + off < PC_NT) ? scan[tid + off] : 0ull;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-      }
-      if (m < nfree) kb[m] = scan[tid] + carry;
-      carry += scan[0];
-      __syncthreads();
+      uint64_t tile = 0;
+      const uint64_t sfx = block_suffix_sum_u64(q, wsum, &tile);
+      if (m < nfree) kb[m] = sfx + carry;
+      carry += tile;
     }
 
     // m*: smallest rank whose water level leaves it unsaturated
