@@ -869,7 +869,8 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
 // tokens exact).
 constexpr int UN_NT = 256;              // small blocks: they fit beside the host-row kernel
 
-// The work schedule of the pivot attention, computed by one workgroup.  The pivots of
+// The work schedule of the pivot attention, computed by one workgroup (a scan over the
+// heads, then one thread per worker).  The pivots of
 // KV head u fall into nc_u = ceil(cnt_u / PIVOT_CHUNK) chunks; the chunks of all heads,
 // head after head, form one sequence of NC chunks, and worker w of P = min(workers, NC)
 // takes chunks [floor(w NC / P), floor((w + 1) NC / P)): every worker gets the same
@@ -898,6 +899,7 @@ __device__ void pivot_schedule(const PlanArgs &a) {
     a.sched[2 * w + 1] = make_int4(0, 0, 0, 0);
   }
   if (threadIdx.x == 0) a.sched[2 * a.workers] = make_int4((int)NC, (int)P, 0, 0);
+  // per head, tile by tile: C_u, runs_u and S_u (runs[u])
   int64_t carry = 0, slot_carry = 0;
   for (int t0 = 0; t0 < units; t0 += UN_NT) {
     const int u = t0 + threadIdx.x;
@@ -907,36 +909,49 @@ __device__ void pivot_schedule(const PlanArgs &a) {
     carry += tile;
     // workers whose first chunk lies in [Cu, Cu + nc_u); run 0 belongs to an earlier
     // worker unless one of them starts exactly at Cu
-    int64_t wlo = 0, whi = 0;
-    int extra = 0, runs = 0;
+    int runs = 0;
     if (ncu > 0) {
-      wlo = (Cu * P + NC - 1) / NC;
-      whi = ((Cu + ncu) * P + NC - 1) / NC;
-      extra = (wlo < whi && wlo * NC / P == Cu) ? 0 : 1;
+      const int64_t wlo = (Cu * P + NC - 1) / NC;
+      const int64_t whi = ((Cu + ncu) * P + NC - 1) / NC;
+      const int extra = (wlo < whi && wlo * NC / P == Cu) ? 0 : 1;
       runs = (int)(whi - wlo) + extra;
     }
     int32_t tile_runs = 0;
     const int64_t Su = slot_carry + block_excl_scan<UN_NT>(runs, s_scan, &tile_runs);
     slot_carry += tile_runs;
-    if (u >= units) continue;
-    const int cnt = min(max(a.piv_count[u], 0), a.cap);
-    for (int64_t w = wlo; w < whi; ++w) {
-      const int64_t c0 = w * NC / P, c1 = (w + 1) * NC / P;
-      const int k0 = (int)(c0 - Cu);
-      const int take = (int)min((int64_t)(ncu - k0), c1 - c0);
-      const int p0 = k0 * PIVOT_CHUNK;
-      const int left = (int)(c1 - c0) - take;
-      a.sched[2 * w] = make_int4(u, p0, min(cnt, p0 + take * PIVOT_CHUNK), (int)(Su + (w - wlo) + extra));
-      // the second run, when it is the next head's (which then starts at slot S_u + runs_u)
-      int4 second = make_int4(-1, 0, 0, left);
-      if (left > 0 && u + 1 < units) {
-        const int cn = min(max(a.piv_count[u + 1], 0), a.cap);
-        const int t2 = min((cn + PIVOT_CHUNK - 1) / PIVOT_CHUNK, left);
-        if (t2 > 0) second = make_int4(u + 1, min(cn, t2 * PIVOT_CHUNK), (int)Su + runs, left - t2);
-      }
-      a.sched[2 * w + 1] = second;
+    if (u < units) a.runs[u] = make_int4((int)Su, runs, (int)Cu, 0);
+  }
+  __threadfence_block();
+  __syncthreads();
+  // per worker: its first chunk's head (the last head with C_u <= c0; a head without
+  // chunks shares C_u with the next one), then the same entries as that head's loop
+  for (int64_t w = threadIdx.x; w < P; w += UN_NT) {
+    const int64_t c0 = w * NC / P, c1 = (w + 1) * NC / P;
+    int lo = 0, hi = units - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)a.runs[mid].z <= c0) lo = mid; else hi = mid - 1;
     }
-    a.runs[u] = make_int4((int)Su, runs, (int)Cu, 0);
+    const int u = lo;
+    const int4 ru = a.runs[u];
+    const int64_t Cu = ru.z;
+    const int ncu = nc_of(u);
+    const int64_t wlo = (Cu * P + NC - 1) / NC;
+    const int extra = (wlo * NC / P == Cu) ? 0 : 1;
+    const int cnt = min(max(a.piv_count[u], 0), a.cap);
+    const int k0 = (int)(c0 - Cu);
+    const int take = (int)min((int64_t)(ncu - k0), c1 - c0);
+    const int p0 = k0 * PIVOT_CHUNK;
+    const int left = (int)(c1 - c0) - take;
+    a.sched[2 * w] = make_int4(u, p0, min(cnt, p0 + take * PIVOT_CHUNK), (int)(ru.x + (w - wlo) + extra));
+    // the second run, when it is the next head's (which then starts at slot S_u + runs_u)
+    int4 second = make_int4(-1, 0, 0, left);
+    if (left > 0 && u + 1 < units) {
+      const int cn = min(max(a.piv_count[u + 1], 0), a.cap);
+      const int t2 = min((cn + PIVOT_CHUNK - 1) / PIVOT_CHUNK, left);
+      if (t2 > 0) second = make_int4(u + 1, min(cn, t2 * PIVOT_CHUNK), ru.x + ru.y, left - t2);
+    }
+    a.sched[2 * w + 1] = second;
   }
 }
 
