@@ -711,58 +711,6 @@ static UnionArgs coef_args(const SeqTable &t, const verkv_state *st, uint8_t *ws
   return un;
 }
 
-// The resident-pivot side of a step (KVFetch step 5 over H u S, eq. 5 with the
-// coefficients of the coefficient pass) and the partial certificate terms of eps_after:
-// both need only the decisions, not the host-row list.
-static verkv_status launch_pivot_side(const SeqTable &t, const verkv_state *st, const float *q,
-                                      const verkv_step_out *out, uint8_t *ws, const DecodeWs &L,
-                                      bool bf16, hipStream_t s) {
-  const int units = t.B * t.Hkv;
-  const int rows = units * t.G;
-  const UnionArgs un = coef_args(t, st, ws, L, out, units);
-  AttendArgs pv;
-  pv.t = t;
-  pv.q = q;
-  pv.m_hat = out->m_hat;
-  pv.inv_sqrt_d = (float)(1.0 / std::sqrt((double)VERKV_HEAD_DIM));
-  pv.krows = static_cast<const uint8_t *>(st->piv_k);
-  pv.vrows = static_cast<const uint8_t *>(st->piv_v);
-  pv.count = st->piv_count;
-  pv.list = nullptr;
-  pv.coef = reinterpret_cast<const float *>(ws + L.coef);
-  pv.cap = st->cap;
-  pv.part = reinterpret_cast<float *>(ws + L.ppart);
-  pv.nsplit = un.piv_workers;
-  pv.sched = un.piv_sched;
-  pv.runs = un.piv_runs;
-  pv.wc = nullptr;
-  pv.cscale = nullptr;
-  pv.stage = nullptr;
-  pv.stage_tok = nullptr;
-  pv.stage_rows = 0;
-  pv.stage_stride = 0;
-  pv.stage_kv = 0;
-  {
-    Timed tm(K_PIVOT, s);
-    HIP_TRY(launch_attend(pv, units, bf16, false, false, s), "pivot attention launch");
-  }
-  AfterArgs af;
-  af.t = t;
-  af.wc = reinterpret_cast<const double *>(ws + L.wc);
-  af.cscale = reinterpret_cast<const double *>(ws + L.cscale);
-  af.r = st->r;
-  af.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
-  af.beta_star = out->beta_star;
-  af.params = reinterpret_cast<const double *>(ws + L.status + 32);
-  af.team = L.team;
-  af.part = reinterpret_cast<double *>(ws + L.apart);
-  {
-    Timed tm(K_AFTER, s);
-    HIP_TRY(launch_after(af, rows, s), "eps_after launch");
-  }
-  return VERKV_OK;
-}
-
 // The staging arguments of a step on workspace ws: the copies (decode) and the plan for
 // the next step (refine) share them.
 static PrefetchArgs stage_args(const SeqTable &t, uint8_t *ws, const DecodeWs &L, const void *Vd,
@@ -1022,14 +970,8 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     UnionArgs cf = coef_args(t, st, ws, L, out, units);
     HIP_TRY(hipEventRecord(sd->dec, stream), "hipEventRecord");
     HIP_TRY(hipStreamWaitEvent(sd->s, sd->dec, 0), "hipStreamWaitEvent");
-    {
-      Timed tm(K_COEF, sd->s);
-      HIP_TRY(launch_union(cf, units, sd->s), "pivot coefficient launch");
-    }
-    // the resident-pivot attention and eps_after follow on the second stream (verkv_refine
-    // joins them): with few host rows they are the step's critical path, and they need
-    // nothing the list kernel writes
-    if ((rc = launch_pivot_side(t, st, q, out, ws, L, bf16, sd->s)) != VERKV_OK) return rc;
+    Timed tm(K_COEF, sd->s);
+    HIP_TRY(launch_union(cf, units, sd->s), "pivot coefficient launch");
   }
   // the list kernel tags entries with the slots the copies filled
   if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
@@ -1106,16 +1048,54 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
             "host attention launch");
   }
 
-  // the estimator coefficients of the resident pivots, the resident-pivot attention and
-  // eps_after: with the second stream verkv_decode_step enqueued them there; without it
-  // they run here on the caller's stream
+  // the estimator coefficients of the resident pivots: on the second stream they were
+  // computed by verkv_decode_step; on the caller's stream they are computed here
   const UnionArgs un = coef_args(t, st, ws, L, out, units);
   if (!mode.side) {
-    {
-      Timed tm(K_COEF, side);
-      HIP_TRY(launch_union(un, units, side), "pivot coefficient launch");
-    }
-    if ((rc = launch_pivot_side(t, st, q, out, ws, L, bf16, side)) != VERKV_OK) return rc;
+    Timed tm(K_COEF, side);
+    HIP_TRY(launch_union(un, units, side), "pivot coefficient launch");
+  }
+
+  AttendArgs pv;
+  pv.t = t;
+  pv.q = q;
+  pv.m_hat = out->m_hat;
+  pv.inv_sqrt_d = at.inv_sqrt_d;
+  pv.krows = static_cast<const uint8_t *>(st->piv_k);
+  pv.vrows = static_cast<const uint8_t *>(st->piv_v);
+  pv.count = st->piv_count;
+  pv.list = nullptr;
+  pv.coef = reinterpret_cast<const float *>(ws + L.coef);
+  pv.cap = st->cap;
+  pv.part = reinterpret_cast<float *>(ws + L.ppart);
+  pv.nsplit = un.piv_workers;
+  pv.sched = un.piv_sched;
+  pv.runs = un.piv_runs;
+  pv.wc = nullptr;
+  pv.cscale = nullptr;
+  pv.stage = nullptr;
+  pv.stage_tok = nullptr;
+  pv.stage_rows = 0;
+  pv.stage_stride = 0;
+  pv.stage_kv = 0;
+  {
+    Timed tm(K_PIVOT, side);
+    HIP_TRY(launch_attend(pv, units, bf16, false, false, side), "pivot attention launch");
+  }
+
+  AfterArgs af;
+  af.t = t;
+  af.wc = reinterpret_cast<const double *>(ws + L.wc);
+  af.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  af.r = st->r;
+  af.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  af.beta_star = out->beta_star;
+  af.params = reinterpret_cast<const double *>(ws + L.status + 32);
+  af.team = L.team;
+  af.part = reinterpret_cast<double *>(ws + L.apart);
+  {
+    Timed tm(K_AFTER, side);
+    HIP_TRY(launch_after(af, rows, side), "eps_after launch");
   }
 
   // the staging plan of the next step, from this step's list, last on the second stream
@@ -1144,7 +1124,7 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   fi.d_sketch = out->d_sketch;
   fi.beta_star = out->beta_star;
   fi.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa, l of the step
-  fi.after_part = reinterpret_cast<const double *>(ws + L.apart);
+  fi.after_part = af.part;
   fi.team = L.team;
   fi.eps_after = out->eps_after;
   fi.n_hat = out->n_hat;
