@@ -278,10 +278,11 @@ verkv_status verkv_decode_step(const verkv_shape *s, const verkv_state *st, cons
  * loads issued by the kernels) with their exact terms, and the finished rows:
  * o = N_hat / D_hat, lse, n_hat, d_hat and eps_after = eps_hat(L \ F).
  * Must follow verkv_decode_step on the same stream with the same workspace, q, s
- * and st.  The resident-pivot and eps_after kernels run on a second stream of the
- * library (one per device, default priority) while the host rows stream in on
- * `stream`; the call joins it back into `stream` before the finishing kernel, so
- * every result is ordered on `stream` as usual.  Rows whose KV head fetched nothing
+ * and st.  The resident-pivot attention runs on a second stream of the library (one
+ * per device, default priority; verkv_decode_step put the pivot coefficients and the
+ * eps_after terms there) while the host rows stream in on `stream`; the call joins
+ * that stream back into `stream` before the finishing kernel, so every result is
+ * ordered on `stream` as usual.  Rows whose KV head fetched nothing
  * are finished from the resident partials alone. */
 verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const float *q,
                           const void *K_host, const void *V_host, verkv_step_out *out,

@@ -711,6 +711,26 @@ static UnionArgs coef_args(const SeqTable &t, const verkv_state *st, uint8_t *ws
   return un;
 }
 
+// The partial certificate terms of eps_after = eps_hat(L \ F): they need only the
+// decisions of the step.
+static verkv_status launch_after_terms(const SeqTable &t, const verkv_state *st,
+                                       const verkv_step_out *out, uint8_t *ws, const DecodeWs &L,
+                                       hipStream_t s) {
+  AfterArgs af;
+  af.t = t;
+  af.wc = reinterpret_cast<const double *>(ws + L.wc);
+  af.cscale = reinterpret_cast<const double *>(ws + L.cscale);
+  af.r = st->r;
+  af.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
+  af.beta_star = out->beta_star;
+  af.params = reinterpret_cast<const double *>(ws + L.status + 32);
+  af.team = L.team;
+  af.part = reinterpret_cast<double *>(ws + L.apart);
+  Timed tm(K_AFTER, s);
+  HIP_TRY(launch_after(af, t.B * t.Hkv * t.G, s), "eps_after launch");
+  return VERKV_OK;
+}
+
 // The staging arguments of a step on workspace ws: the copies (decode) and the plan for
 // the next step (refine) share them.
 static PrefetchArgs stage_args(const SeqTable &t, uint8_t *ws, const DecodeWs &L, const void *Vd,
@@ -970,8 +990,13 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
     UnionArgs cf = coef_args(t, st, ws, L, out, units);
     HIP_TRY(hipEventRecord(sd->dec, stream), "hipEventRecord");
     HIP_TRY(hipStreamWaitEvent(sd->s, sd->dec, 0), "hipStreamWaitEvent");
-    Timed tm(K_COEF, sd->s);
-    HIP_TRY(launch_union(cf, units, sd->s), "pivot coefficient launch");
+    {
+      Timed tm(K_COEF, sd->s);
+      HIP_TRY(launch_union(cf, units, sd->s), "pivot coefficient launch");
+    }
+    // eps_after's terms too: small, and off the chain verkv_refine puts on this stream
+    // (the pivot attention, which starts after the list kernel, then the plan)
+    if ((rc = launch_after_terms(t, st, out, ws, L, sd->s)) != VERKV_OK) return rc;
   }
   // the list kernel tags entries with the slots the copies filled
   if (prefetch) HIP_TRY(hipStreamWaitEvent(stream, sd->pref, 0), "hipStreamWaitEvent");
@@ -1083,20 +1108,8 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
     HIP_TRY(launch_attend(pv, units, bf16, false, false, side), "pivot attention launch");
   }
 
-  AfterArgs af;
-  af.t = t;
-  af.wc = reinterpret_cast<const double *>(ws + L.wc);
-  af.cscale = reinterpret_cast<const double *>(ws + L.cscale);
-  af.r = st->r;
-  af.fbits = reinterpret_cast<const uint32_t *>(ws + L.fbits);
-  af.beta_star = out->beta_star;
-  af.params = reinterpret_cast<const double *>(ws + L.status + 32);
-  af.team = L.team;
-  af.part = reinterpret_cast<double *>(ws + L.apart);
-  {
-    Timed tm(K_AFTER, side);
-    HIP_TRY(launch_after(af, rows, side), "eps_after launch");
-  }
+  // eps_after's terms: verkv_decode_step put them on the second stream; without it, here
+  if (!mode.side && (rc = launch_after_terms(t, st, out, ws, L, side)) != VERKV_OK) return rc;
 
   // the staging plan of the next step, from this step's list, last on the second stream
   if (Vs) {
@@ -1124,7 +1137,7 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   fi.d_sketch = out->d_sketch;
   fi.beta_star = out->beta_star;
   fi.params = reinterpret_cast<const double *>(ws + L.status + 32);   // kappa, l of the step
-  fi.after_part = af.part;
+  fi.after_part = reinterpret_cast<const double *>(ws + L.apart);
   fi.team = L.team;
   fi.eps_after = out->eps_after;
   fi.n_hat = out->n_hat;
