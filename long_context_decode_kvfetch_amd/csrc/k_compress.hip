@@ -107,10 +107,131 @@ __device__ uint64_t block_suffix_sum_u64(uint64_t v, uint64_t *wsum /*[PC_NW]*/,
   return v + after;
 }
 
+constexpr int PC_SEL_CAP = 4096;             // keys the select path sorts in LDS (a power of 2)
+
+// The water level from the M smallest keys alone (M = min(n_free, ceil(B_rem)) <= PC_SEL_CAP):
+// m* must satisfy B_rem - m > 0, so it and every rank below it are among them.  An MSD
+// radix select narrows a prefix of the 64-bit key until the keys at or below it (which
+// hold the M smallest) fit in LDS; those are sorted there (bitonic), and
+// S_m = (sum of Q over ranks m..M-1) + (total - sum over the M).  A token's rank is below
+// m* exactly when its key is below the key of rank m* (keys are distinct).  Same r, level
+// and arithmetic as sorting all keys.
+__device__ void poissoncomp_select(const CompressArgs &a, int unit, const uint64_t *ka, uint64_t *kb,
+                                   double *r, int nfree, int M, double b_rem, int64_t total,
+                                   uint32_t *hist, int64_t *isum, uint64_t *wsum, uint64_t *s_col,
+                                   int32_t *s_sel) {
+  const int tid = threadIdx.x;
+  auto q_of = [](uint64_t k) -> uint64_t { return (1ull << Q_BITS) - (k >> IDX_BITS); };
+  // narrow the prefix: keys k with (k >> sh) <= pre are collected (sh = 64: all keys)
+  uint64_t pre = 0;
+  int sh = 64;
+  int64_t kk = M;                          // rank of the M-th smallest key among those at pre
+  int64_t match = nfree;                   // keys whose bits above sh equal pre
+  while ((int64_t)M - kk + match > PC_SEL_CAP) {
+    const int ns = sh - 8;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < nfree; j += PC_NT) {
+      const uint64_t k = ka[j];
+      if (sh == 64 || (k >> sh) == pre) atomicAdd(&hist[(k >> ns) & 255], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {                        // the bucket holding the kk-th of them
+      int b = 0;
+      int64_t left = kk;
+      while (b < 255 && left > (int64_t)hist[b]) { left -= hist[b]; ++b; }
+      s_sel[0] = b;
+      s_sel[1] = (int32_t)left;
+      s_sel[2] = (int32_t)hist[b];
+    }
+    __syncthreads();
+    pre = (sh == 64 ? 0ull : (pre << 8)) | (uint64_t)s_sel[0];
+    kk = s_sel[1];
+    match = s_sel[2];
+    sh = ns;
+    __syncthreads();                       // s_sel is rewritten by the next pass
+  }
+  // collect, pad to a power of two, sort ascending
+  if (tid == 0) s_sel[0] = 0;
+  __syncthreads();
+  for (int j = tid; j < nfree; j += PC_NT) {
+    const uint64_t k = ka[j];
+    if (sh == 64 || (k >> sh) <= pre) {
+      const int at = atomicAdd(&s_sel[0], 1);
+      if (at < PC_SEL_CAP) s_col[at] = k;
+    }
+  }
+  __syncthreads();
+  const int ncol = min(s_sel[0], PC_SEL_CAP);
+  int p2 = 1;
+  while (p2 < ncol) p2 <<= 1;
+  for (int i = ncol + tid; i < p2; i += PC_NT) s_col[i] = ~0ull;
+  __syncthreads();
+  for (int k2 = 2; k2 <= p2; k2 <<= 1) {
+    for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+      for (int i = tid; i < p2; i += PC_NT) {
+        const int l = i ^ j2;
+        if (l > i) {
+          const uint64_t x = s_col[i], y = s_col[l];
+          if ((x > y) == ((i & k2) == 0)) {
+            s_col[i] = y;
+            s_col[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // S_m for the M ranks -> kb[m]
+  int64_t part = 0;
+  for (int m = tid; m < M; m += PC_NT) part += (int64_t)q_of(s_col[m]);
+  const int64_t sum_m = block_sum_i64<PC_NT>(part, isum);
+  uint64_t carry = (uint64_t)(total - sum_m);
+  for (int tix = (M + PC_NT - 1) / PC_NT - 1; tix >= 0; --tix) {
+    const int m = tix * PC_NT + tid;
+    const uint64_t q = m < M ? q_of(s_col[m]) : 0ull;
+    uint64_t tile = 0;
+    const uint64_t sfx = block_suffix_sum_u64(q, wsum, &tile);
+    if (m < M) kb[m] = sfx + carry;
+    carry += tile;
+  }
+  // m*: smallest rank whose water level leaves it unsaturated
+  if (tid == 0) s_sel[0] = INT32_MAX;
+  __syncthreads();
+  for (int m = tid; m < M; m += PC_NT) {
+    const double rem = b_rem - (double)m;
+    const uint64_t sm = kb[m];
+    if (rem > 0.0 && sm > 0) {
+      const double c = rem / (double)sm;
+      if (c * (double)q_of(s_col[m]) < 1.0) atomicMin(&s_sel[0], m);
+    }
+  }
+  __syncthreads();
+  const int mstar = s_sel[0];
+  if (a.level && tid == 0)
+    a.level[unit] = mstar == INT32_MAX ? LEVEL_SATURATED : (b_rem - (double)mstar) / (double)kb[mstar];
+  if (mstar == INT32_MAX) {                // every positive score saturates
+    for (int j = tid; j < nfree; j += PC_NT) {
+      const uint64_t k = ka[j];
+      r[(int)(k & IDX_MASK)] = q_of(k) > 0 ? 1.0 : 0.0;
+    }
+  } else {
+    const double c = (b_rem - (double)mstar) / (double)kb[mstar];
+    const uint64_t th = s_col[mstar];
+    for (int j = tid; j < nfree; j += PC_NT) {
+      const uint64_t k = ka[j];
+      r[(int)(k & IDX_MASK)] = k < th ? 1.0 : c * (double)q_of(k);
+    }
+  }
+}
+
 __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wcnt[PC_NW * 256];
   __shared__ uint64_t wsum[PC_NW];
+  __shared__ int64_t isum[PC_NW];
+  __shared__ uint64_t s_col[PC_SEL_CAP];
+  __shared__ int32_t s_sel[3];
   __shared__ int32_t iscratch[PC_NW];
   __shared__ int32_t s_mstar;
 
@@ -139,17 +260,25 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
   }
 
   if (nfree > 0 && b_rem > 0.0 && b_rem < (double)nfree) {
-    // sort keys: (2^40 - Q) << 20 | index  ->  ascending = Q descending, index ascending.
-    // They are written in index order and the sort is stable, so sorting by bits 20-60
-    // (2^40 - Q < 2^41) alone gives the order of the whole keys: six passes, not eight.
+    // sort keys: (2^40 - Q) << 20 | index  ->  ascending = Q descending, index ascending,
+    // and the exact total of Q
+    int64_t qsum = 0;
     for (int j = tid; j < nfree; j += PC_NT) {
       const int i = lo + j;
       const float x = tau[i];
       const double xs = (double)(x > 0.0f ? x : 0.0f) * 0x1.0p40;
       const uint64_t q = (uint64_t)ceil(xs);
       ka[j] = (((1ull << Q_BITS) - q) << IDX_BITS) | (uint64_t)i;
+      qsum += (int64_t)q;
     }
-    __syncthreads();
+    const int64_t total = block_sum_i64<PC_NT>(qsum, isum);   // its barriers publish ka
+    // m* needs B_rem - m > 0, so only the M smallest keys can be ranks below it or m*
+    const int M = (int)fmin((double)nfree, ceil(b_rem));
+    if (M <= PC_SEL_CAP) {
+      poissoncomp_select(a, unit, ka, kb, r, nfree, M, b_rem, total, hist, isum, wsum, s_col, s_sel);
+    } else {
+    // They are written in index order and the sort is stable, so sorting by bits 20-60
+    // (2^40 - Q < 2^41) alone gives the order of the whole keys: six passes, not eight.
     static_assert(IDX_BITS + Q_BITS + 1 <= IDX_BITS + 8 * 6, "six passes cover 2^40 - Q");
     block_radix_sort(ka, kb, nfree, IDX_BITS, 6, hist, wcnt);
 
@@ -194,6 +323,7 @@ __global__ __launch_bounds__(PC_NT) void k_poissoncomp(CompressArgs a) {
         const uint64_t q = (1ull << Q_BITS) - (ka[m] >> IDX_BITS);
         r[(int)(ka[m] & IDX_MASK)] = (m < mstar) ? 1.0 : c * (double)q;
       }
+    }
     }
   } else {
     const double v = (nfree > 0 && b_rem >= (double)nfree) ? 1.0 : 0.0;
