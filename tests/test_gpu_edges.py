@@ -185,3 +185,65 @@ def test_gather_rows_memcpy_moves_the_listed_rows():
     assert runs == want
     assert torch.equal(dst.cpu(), rows[torch.from_numpy(idx).long()])
     say(f"[gather] {idx.size} rows in {runs} copies")
+
+
+def _compress_matches_oracle(wl, label):
+    """Compress on the GPU only and compare r (float64 bits), the resident mask and the
+    pivot lists with the oracle; returns the oracle's compressed heads."""
+    from parity_util import compare_state
+    say(f"[parity] {label}: {wl.name}")
+    sess = session(wl)
+    sess.compress()
+    ocomp = oracle_compress(wl)
+    compare_state(sess, wl, ocomp)
+    return ocomp[0]
+
+
+@pytest.mark.parametrize("budget", [4227.5, 4228.0, 4228.5])
+def test_waterfill_budget_at_the_select_limit(budget):
+    """The prefill finds the water level from the ceil(B_rem) smallest sort keys when
+    there are at most 4096 of them, and sorts all keys otherwise.  With 132 forced tokens
+    of 65536 the budgets 4227.5, 4228 and 4228.5 leave B_rem = 4095.5, 4096 and 4096.5:
+    the last two sides of the limit and one just inside it, each bit-exact."""
+    n = 65536
+    wl = synth.gqa_layer(seed=61, n=n, steps=1, hkv=2, eta=budget / n)
+    assert wl.eta * n == budget
+    # small scores with 200 large ones per KV head, so that the level saturates those
+    rng = np.random.default_rng(7)
+    for g in range(2):
+        t = wl.seqs[0].tau[g] * np.float32(0.05)
+        big = rng.choice(np.arange(4, n - 128), size=200, replace=False)
+        t[big] = rng.uniform(0.5, 1.0, size=200).astype(np.float32)
+        wl.seqs[0].tau[g] = t
+    comp = _compress_matches_oracle(wl, f"water-filling at eta n = {budget}")
+    assert all(c.rule == "water" and c.m_star == 200 for c in comp)
+
+
+def test_waterfill_heavy_ties_and_zeros():
+    """Scores on four levels at n = 32768 (0, 0.001, 0.002 and 1.0 on 1% of the tokens):
+    the sort keys of a level differ only in their token index, the tokens at 1.0
+    saturate and the water level sits at the end of their tie group, so the select
+    narrows its prefix into the index bits and ranks below m* are told apart by index."""
+    wl = synth.gqa_layer(seed=62, n=32768, steps=1, hkv=2)
+    rng = np.random.default_rng(8)
+    levels = np.array([0.0, 0.001, 0.002, 1.0], np.float32)
+    for g in range(2):
+        wl.seqs[0].tau[g] = levels[rng.choice(4, size=32768, p=[0.09, 0.7, 0.2, 0.01])]
+    comp = _compress_matches_oracle(wl, "water-filling with heavy ties")
+    for g, c in enumerate(comp):
+        ones = int(np.sum(wl.seqs[0].tau[g][4:32768 - 128] == 1.0))
+        assert c.rule == "water" and c.m_star == ones > 0, (c.m_star, ones)
+
+
+def test_waterfill_saturated_on_the_select_path():
+    """n = 32768 with 2000 positive scores per KV head and a budget of 3964 free tokens:
+    no water level qualifies (every positive score saturates) on the select path."""
+    wl = synth.gqa_layer(seed=63, n=32768, steps=1, hkv=2, eta=1.0 / 8)
+    rng = np.random.default_rng(9)
+    for g in range(2):
+        t = np.zeros(32768, np.float32)
+        keep = rng.choice(np.arange(4, 32768 - 128), size=2000, replace=False)
+        t[keep] = wl.seqs[0].tau[g, keep]
+        wl.seqs[0].tau[g] = t
+    comp = _compress_matches_oracle(wl, "water-filling saturated, select path")
+    assert all(c.rule == "saturated" and c.m_star == -1 for c in comp)
