@@ -242,7 +242,7 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
  * eps_hat(L), the certified flag, and when it fails the fetch order g (eq. 9) and k*
  * (eq. 10); per KV head the union F of the group's fetch sets, the fetch list and the
  * estimator coefficients of the resident pivots (1 on H u (S n F), lambda_i / r_i on
- * S \ F).
+ * S \ F); per row the partial terms of eps_hat(L \ F) that verkv_refine finishes.
  *   q      [B][Hq][128] float32
  *   beta   multiplier kappa of the bias term inside the clip: 1 is the paper's
  *          estimator, +INFINITY gives lambda = 1 (Horvitz-Thompson), 0 gives
@@ -256,7 +256,8 @@ size_t verkv_pivot_rows(const verkv_shape *s, int32_t cap);
  *          verkv_state.v_host).
  *          Results do not depend on these: zero-filled or foreign contents only cost
  *          time (staged rows carry the identity of the cache they came from).
- * No host synchronisation and no host-memory traffic.
+ * No host synchronisation.  Host memory is read only by the staging copies (the rows
+ * the previous step's plan asked for, see verkv_state.v_host).
  * out->o and out->lse are not written here: verkv_refine always follows, also when
  * every row is certified (then it finishes o from the resident-pivot partials and
  * reads nothing from the host).  The split is for overlap, not for skipping: the
