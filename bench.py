@@ -949,18 +949,21 @@ def main():
     log(f"[bench] {K} steps: {wall * 1e3:.1f} ms wall, {ev_ms:.1f} ms events")
 
     # per-step statistics over one pass of every layer
-    cert, fetched, h2d, rows, n_tok = 0, 0, 0, 0, 0
+    cert, fetched, h2d, staged, rows, n_tok = 0, 0, 0, 0, 0, 0
     for sess in sessions:
         sess.step(sess.qdev[0])
         r = sess.results_numpy()
         cert += int(r["certified"].sum())
         fetched += int(r["fetch_count"].sum())
         h2d += int(r["h2d_count"].sum())
+        staged += sess.staged_rows()          # of those, rows served by the staging area
         rows += r["certified"].size
         n_tok += N_CTX * sess.shape.n_kv_heads
         assert np.all(r["eps_after"] < sess.wl.eps), "a row finished uncertified"
-    # exact sketch: only the value rows of F minus S cross the host link (256 B each)
+    # exact sketch: only the value rows of F minus S are read (256 B each); the staged ones
+    # come from the workspace, the rest over the host link
     h2d_bytes_step = h2d / L * 128 * 2
+    link_bytes_step = (h2d - staged) / L * 128 * 2
 
     # kernel durations with HIP events around every launch of the profiled steps
     P = args.profile_steps
@@ -988,6 +991,8 @@ def main():
     kern["attend_pivots"]["GBps"] = piv_bytes / (kern["attend_pivots"]["avg_us"] * 1e-6) / 1e9
     kern["attend_host"]["host_bytes"] = h2d_bytes_step
     kern["attend_host"]["GBps"] = h2d_bytes_step / (kern["attend_host"]["avg_us"] * 1e-6) / 1e9
+    kern["attend_host"]["link_bytes"] = link_bytes_step
+    kern["attend_host"]["link_GBps"] = link_bytes_step / (kern["attend_host"]["avg_us"] * 1e-6) / 1e9
     # The roofline kernel is the sketch scoring pass: the HBM stream on the step's
     # critical path.  The host-row kernel is bound by the host link (reported against
     # the pinned-copy rate below); the resident-pivot and eps_after kernels run on the
@@ -1090,6 +1095,9 @@ def main():
                        "h2d_fraction_of_cache": h2d / n_tok,
                        "h2d_bytes_per_step": h2d_bytes_step,
                        "h2d_GBps_per_step": h2d_bytes_step / (ms_per_step * 1e-3) / 1e9,
+                       "staged_bytes_per_step": h2d_bytes_step - link_bytes_step,
+                       "host_link_bytes_per_step": link_bytes_step,
+                       "host_link_GBps_per_step": link_bytes_step / (ms_per_step * 1e-3) / 1e9,
                        "pinned_h2d_copy_GBps": round(h2d_peak, 1),
                        "wall_ms_per_step": wall * 1e3 / K},
         "kernels": kern,

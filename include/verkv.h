@@ -289,6 +289,15 @@ verkv_status verkv_refine(const verkv_shape *s, const verkv_state *st, const flo
                           const void *K_host, const void *V_host, verkv_step_out *out,
                           void *workspace, size_t workspace_bytes, verkv_stream_t stream);
 size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap);
+/* Of the rows F \ S the last verkv_refine on `workspace` needed (KVFetch step 5, picx.dev
+ * summary page, "KVFETCH" step 5; out->h2d_count per KV head), how many it took from the
+ * cross-step staging area instead of the host link, summed over the batch's KV heads
+ * (*rows).  Each verkv_decode_step clears the count, and the host-row kernel adds to it.
+ * The rest crossed the link.  workspace: the one the step used, of workspace_bytes
+ * (at least verkv_decode_workspace_bytes(s, cap)).  Synchronises `stream`.  Errors:
+ * VERKV_EINVAL (null pointers, cap < 1), VERKV_EWORKSPACE, a shape error as for a step. */
+verkv_status verkv_staged_rows(void *workspace, size_t workspace_bytes, const verkv_shape *s,
+                               int32_t cap, verkv_stream_t stream, int64_t *rows);
 
 /* verkv_decode_step with options.  flags:
  *   VERKV_STEP_RESOLVED  the other reading of eqs. (9)-(10) (picx.dev summary page,

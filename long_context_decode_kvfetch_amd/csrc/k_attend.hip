@@ -86,6 +86,7 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
   (void)stage_tok;
   const int64_t slice = (int64_t)d0 * (BF16 ? 2 : 4);
 
+  int staged_n = 0;                          // rows this lane group took from the staging area
   // Rows go in batches of STEP * U; the loads of the next batch (and, for pivots, its
   // coefficients) are issued before the current batch is reduced, so every wave keeps
   // a batch in flight while it computes.
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
           if (slot >= 0 && slot < a.stage_rows && stage_tok[(int64_t)unit * a.stage_rows + slot] == tok) {
             vsrc = stage + ((int64_t)unit * a.stage_rows + slot) * a.stage_stride + slice;
             if (!EXACT && a.stage_kv) ksrc = vsrc + ROW_BYTES;
+            staged_n += sub == 0 ? 1 : 0;
           }
         }
         bt.tk[u] = tok;
@@ -198,6 +200,11 @@ __global__ __launch_bounds__(AT_NT) void k_attend(AttendArgs a) {
     base += stride;
   }
 
+  if constexpr (HOST) {                      // staged rows of this wave, for the step's count
+    const int64_t w = wave_sum_i64(staged_n);
+    if (lane == 0 && w > 0 && a.stg_cnt) atomicAdd(&a.stg_cnt[unit], (int32_t)w);
+  }
+  (void)staged_n;
   // every row group of every wave leaves its partial in LDS; each output element is
   // then summed over the AT_NW x TPW groups in a fixed order
   if (sub == 0) {

@@ -785,6 +785,7 @@ __global__ __launch_bounds__(LS_NT) void k_lists(UnionArgs a) {
   // they ran for this cache, entries are tagged with their slots and the header names
   // this cache as the one whose rows the maps hold
   const bool staged = a.shdr && a.shdr[6] == 1ull;
+  if (a.stg_cnt && blockIdx.x == 0 && tid == 0) a.stg_cnt[unit] = 0;   // this step's count
   if (staged && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     a.shdr[1] = a.ident_ptr;
     a.shdr[2] = a.ident_shape;

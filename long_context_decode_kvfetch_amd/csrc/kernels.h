@@ -187,6 +187,7 @@ struct UnionArgs {
   uint64_t *shdr;            // lists: staging header to publish (null without a prefetch)
   uint64_t ident_ptr, ident_shape;
   int32_t *h2d_count_ws;     // lists: [B][Hkv] |F \ S| kept in the workspace for the next step
+  int32_t *stg_cnt;          // lists: [B][Hkv] staged-row counters of the host-row kernel, cleared
   // coefficient pass: the work schedule of the pivot attention (one extra workgroup)
   int4 *piv_sched;           // [2 PIVOT_WORKERS + 1] per worker: first run, chunks after it
   int4 *piv_runs;            // [B][Hkv] first partial slot, partials, first chunk, 0
@@ -242,6 +243,7 @@ struct AttendArgs {
   int32_t stage_rows;
   int32_t stage_stride;      // bytes per slot (the value row first)
   int32_t stage_kv;          // 1: a slot also holds the key row, after the value row
+  int32_t *stg_cnt;          // host source: [B][Hkv] rows taken from the staging area (added to)
 };
 
 struct FinishArgs {

@@ -151,7 +151,7 @@ int stage_rows_of(const SeqTable &t, int units) {
 struct DecodeWs {
   size_t wc, cstat, cscale, fbits, h2d, coef, ppart, hpart, status;
   size_t xseq, wcount, part, hcnt, hbeta, hV, hmax, wkey, wlo, apart, cf0, bprev;
-  size_t stage, stage_tok, slot_of, pf_new, pf_slot, pf_cnt, shdr, h2dc, psched, pruns, gpar;
+  size_t stage, stage_tok, slot_of, pf_new, pf_slot, pf_cnt, shdr, h2dc, stg, psched, pruns, gpar;
   int srows;
   size_t total;
   int nsp, nsh, team;      // nsp: pivot partial slots
@@ -200,6 +200,7 @@ DecodeWs decode_layout(const SeqTable &t, int cap, bool bf16, bool staging = tru
   w.pf_cnt = off;    off = align_up(off + 4 * (size_t)units);
   w.shdr = off;      off = align_up(off + 8 * (size_t)STAGE_HDR_WORDS);
   w.h2dc = off;      off = align_up(off + 4 * (size_t)units);
+  w.stg = off;       off = align_up(off + 4 * (size_t)units);   // staged rows the host-row kernel used
   w.psched = off;    off = align_up(off + 16 * (size_t)(2 * PIVOT_WORKERS + 1));
   w.pruns = off;     off = align_up(off + 16 * (size_t)units);
   w.gpar = off;      off = align_up(off + 32 * (size_t)rows);
@@ -530,6 +531,27 @@ size_t verkv_decode_workspace_bytes(const verkv_shape *s, int32_t cap) {
   return decode_layout(t, cap, s->kv_dtype == VERKV_BF16).total;
 }
 
+verkv_status verkv_staged_rows(void *workspace, size_t workspace_bytes, const verkv_shape *s,
+                               int32_t cap, verkv_stream_t stream_, int64_t *rows) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  SeqTable t;
+  verkv_status rc = make_table(s, t);
+  if (rc != VERKV_OK) return rc;
+  if (!workspace || !rows || cap < 1) return VERKV_EINVAL;
+  const DecodeWs L = decode_layout(t, cap, s->kv_dtype == VERKV_BF16);
+  if (workspace_bytes < L.total) return VERKV_EWORKSPACE;
+  const int units = t.B * t.Hkv;
+  std::vector<int32_t> cnt((size_t)units, 0);
+  HIP_TRY(hipMemcpyAsync(cnt.data(), static_cast<uint8_t *>(workspace) + L.stg,
+                         sizeof(int32_t) * (size_t)units, hipMemcpyDeviceToHost, stream),
+          "hipMemcpyAsync");
+  HIP_TRY(hipStreamSynchronize(stream), "hipStreamSynchronize");
+  int64_t sum = 0;
+  for (int32_t c : cnt) sum += c;
+  *rows = sum;
+  return VERKV_OK;
+}
+
 verkv_status verkv_compress(const verkv_shape *s, const float *tau, const void *K_host,
                             const void *V_host, double eta, uint64_t seed, verkv_state *st,
                             void *workspace, size_t workspace_bytes, int32_t *needed_cap,
@@ -705,6 +727,7 @@ static UnionArgs coef_args(const SeqTable &t, const verkv_state *st, uint8_t *ws
   un.ident_ptr = 0;
   un.ident_shape = 0;
   un.h2d_count_ws = nullptr;
+  un.stg_cnt = nullptr;
   un.piv_sched = reinterpret_cast<int4 *>(ws + L.psched);
   un.piv_runs = reinterpret_cast<int4 *>(ws + L.pruns);
   un.piv_workers = pivot_workers(st->cap, units);
@@ -980,6 +1003,7 @@ static verkv_status decode_impl(const verkv_shape *s, const verkv_state *st, con
   un.ident_ptr = reinterpret_cast<uint64_t>(Vd);
   un.ident_shape = stage_ident(t, bf16, Kd);
   un.h2d_count_ws = reinterpret_cast<int32_t *>(ws + L.h2dc);
+  un.stg_cnt = reinterpret_cast<int32_t *>(ws + L.stg);
   un.piv_sched = nullptr;
   un.piv_runs = nullptr;
   un.piv_workers = 0;
@@ -1067,6 +1091,7 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   at.stage_rows = sg.rows;
   at.stage_stride = sg.stride;
   at.stage_kv = sg.kv ? 1 : 0;
+  at.stg_cnt = reinterpret_cast<int32_t *>(ws + L.stg);
   {
     Timed tm(K_HOST, stream);
     HIP_TRY(launch_attend(at, units, bf16, true, st->sketch_exact != 0, stream),
@@ -1103,6 +1128,7 @@ static verkv_status refine_impl(const verkv_shape *s, const verkv_state *st, con
   pv.stage_rows = 0;
   pv.stage_stride = 0;
   pv.stage_kv = 0;
+  pv.stg_cnt = nullptr;
   {
     Timed tm(K_PIVOT, side);
     HIP_TRY(launch_attend(pv, units, bf16, false, false, side), "pivot attention launch");

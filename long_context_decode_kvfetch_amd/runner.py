@@ -131,6 +131,10 @@ class Session:
         verkv.refine(self.shape, self.state, q, self.K_host, self.V_host, out, self.dws, stream)
         return out
 
+    def staged_rows(self) -> int:
+        """Rows of the last step's F minus S taken from the staging area, not the host link."""
+        return verkv.staged_rows(self.shape, self.cap, self.dws)
+
     # ---------------------------------------------------------------- host-side views
     def state_numpy(self):
         """r, resident mask, pivot lists per (sequence, KV head)."""

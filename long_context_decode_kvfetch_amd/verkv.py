@@ -82,6 +82,8 @@ def _lib():
         lib.verkv_compress_workspace_bytes.argtypes = [C.POINTER(Shape)]
         lib.verkv_decode_workspace_bytes.restype = sz
         lib.verkv_decode_workspace_bytes.argtypes = [C.POINTER(Shape), i32]
+        lib.verkv_staged_rows.restype = i32
+        lib.verkv_staged_rows.argtypes = [vp, sz, C.POINTER(Shape), i32, vp, C.POINTER(C.c_int64)]
         lib.verkv_pivot_rows.restype = sz
         lib.verkv_pivot_rows.argtypes = [C.POINTER(Shape), i32]
         lib.verkv_quantize_sketch.restype = i32
@@ -383,6 +385,16 @@ def gather_rows_memcpy(src_ptr: int, row_bytes: int, idx, dst_ptr: int, stream=N
                                            C.c_void_p(dst_ptr), C.byref(runs), _stream(stream)),
            "verkv_gather_rows_memcpy")
     return runs.value
+
+
+def staged_rows(shape: LayerShape, cap: int, workspace: torch.Tensor, stream=None) -> int:
+    """verkv_staged_rows: rows of the last refine on `workspace` taken from the staging area
+    instead of the host link (synchronises `stream`)."""
+    rows = C.c_int64(0)
+    _check(_lib().verkv_staged_rows(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    C.byref(shape.c), int(cap), _stream(stream), C.byref(rows)),
+           "verkv_staged_rows")
+    return int(rows.value)
 
 
 def check(shape: LayerShape, cap: int, workspace: torch.Tensor, stream=None) -> None:

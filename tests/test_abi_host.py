@@ -216,3 +216,18 @@ def test_stage_slots_grow_the_workspace_within_the_packing_limit(vk):
                                C.byref(step), C.c_void_p(FAKE), 1 << 40, None)
     assert rc == vk.EINVAL
     assert "stage_slots" in lib.verkv_last_error().decode()
+
+
+def test_staged_rows_checks_its_arguments_on_host(vk):
+    """verkv_staged_rows refuses a null workspace or result and a workspace smaller than
+    the step's layout before it touches the device."""
+    lib = vk.lib()
+    sh = _shape(vk)
+    rows = C.c_int64(-1)
+    need = sh.decode_workspace_bytes(640)
+    assert lib.verkv_staged_rows(None, need, C.byref(sh.c), 640, None, C.byref(rows)) == vk.EINVAL
+    assert lib.verkv_staged_rows(C.c_void_p(FAKE), need, C.byref(sh.c), 640, None, None) == vk.EINVAL
+    assert lib.verkv_staged_rows(C.c_void_p(FAKE), need, C.byref(sh.c), 0, None, C.byref(rows)) == vk.EINVAL
+    assert lib.verkv_staged_rows(C.c_void_p(FAKE), need - 1, C.byref(sh.c), 640, None,
+                                 C.byref(rows)) == vk.EWORKSPACE
+    assert rows.value == -1

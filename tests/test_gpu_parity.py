@@ -218,6 +218,12 @@ def test_prefetch_and_workspace_history_do_not_change_results(sketch_2bit, stage
             verkv.check(sess.shape, sess.cap, sess.dws)
             r = sess.results_numpy()
             steps.append({k: np.array(r[k]) for k in keys})
+            # rows served from the staging area: none without staging or before a plan exists
+            staged = sess.staged_rows()
+            if "prefetch" in kw or st == 0:
+                assert staged == 0, (label, st, staged)
+            else:
+                assert 0 < staged <= int(r["h2d_count"].sum()), (label, st, staged)
         launches = verkv.profile_report()["prefetch"][1]
         verkv.profile_end()
         assert launches == (0 if "prefetch" in kw else 3), (label, launches)
