@@ -373,13 +373,14 @@ def staging_leg(torch, wls, qdevs, K=64, W=8, slots=(2048, 4096, 16384, 32768)):
         def run(i):
             s2 = sess[i % L]
             s2.step(s2.qdev[(i // L) % per])
-        for i in range(W + L):
+        W0 = max(W + L, 2 * L)                # at least two steps per layer: staging primed
+        for i in range(W0):
             run(i)
         torch.cuda.synchronize()
-        ms, per_step = timed(torch, run, W + L, K)
+        ms, per_step = timed(torch, run, W0, K)
         fail_on_flags(sess, f"the staging leg at {ns} slots")
         verkv.profile_begin(16 * 16 + 16)
-        for i in range(W + L + K, W + L + K + 16):
+        for i in range(W0 + K, W0 + K + 16):
             run(i)
         torch.cuda.synchronize()
         prof = verkv.profile_report()
@@ -563,6 +564,7 @@ def sketch2_leg(torch, wls, qdevs, K2, W2):
         s2 = sess2[i % L]
         s2.step(s2.qdev[(i // L) % per_layer])
 
+    W2 = max(W2, 2 * L)                      # at least two steps per layer: staging primed
     for i in range(W2):
         run(i)
     torch.cuda.synchronize()
@@ -914,7 +916,7 @@ def main():
         return
     K, W, L = args.steps, args.warmup, args.layers
     total = K + W + args.profile_steps + 1
-    per_layer = (total + L - 1) // L + 1
+    per_layer = (total + L - 1) // L + 2
     log(f"[bench] generating {L} layers (n={N_CTX}, 32q/8kv, bf16)")
     sessions = []
     for layer in range(L):
@@ -924,10 +926,12 @@ def main():
         sess.qdev = torch.from_numpy(np.ascontiguousarray(wl.queries[:, :])).to("cuda")
         sessions.append(sess)
         log(f"[bench] layer {layer} compressed, max pivots {sess.max_pivots}, cap {sess.cap}")
-    # one step per layer before any counted step: a decode step stages the host rows the
-    # layer's previous step read, and in a running decode every layer has had one
-    for sess in sessions:
-        sess.step(sess.qdev[per_layer - 1])
+    # two steps per layer before any counted step, as every layer of a running decode has
+    # had: the first leaves a staging plan for the whole area (nothing is staged yet), the
+    # second copies it; from then on a step copies only the rows new to the list
+    for prime in (2, 1):
+        for sess in sessions:
+            sess.step(sess.qdev[per_layer - prime])
     torch.cuda.synchronize()
 
     def run(step_index):
